@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for MLA paged-latent decode.
+
+This module holds only random draws and their packing into arrays: no step of
+the method (no cache write, no quantization, no attention arithmetic).  Both the
+HIP path's tests/bench and the CPU oracle consume what it produces.
+
+Shapes follow DeepSeek-V3's MLA (kv_lora_rank 512, rope 64, qk_nope 128,
+v_head 128, 64-token pages) as described on the source page "vLLM 源码完全拆解
+(三十七):MLA 注意力后端" (§从模型层看, §缓存的形状).  The named workloads are:
+
+* ``tiny``      B=2, q_len=1, N=16, seq {37, 100}, 16-page pool, bf16, with the
+                absorption weights.
+* ``tp_share``  B=64, q_len=1, N=16, seq ~ U{1024..4096}, 8192-page pool, bf16,
+                absorbed query given directly.
+* ``full_head`` B=32, q_len=1, N=128, seq 8192 each, 8192-page pool, bf16, with
+                the absorption weights W_UK_T[128,128,512] and W_UV[128,512,128].
+* ``fp8``       B=128, q_len=1, N=128, seq lognormal (median 2048, sigma 1.0,
+                clipped to [64, 32768]), pool max(8192, 1.25 x needed), fp8 rows.
+* ``spec_long`` B=8, q_len=2, N=128, seq {131072, 65536, ..., 1024},
+                pool 1.25 x 4080 pages, bf16.
+
+Every value is drawn N(0, 1) except the weights, N(0, 1/512) (variance), and
+rounded to bfloat16 (round to nearest even) so that both sides see identical
+bits.  Seeds are ``20260 + index``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+L, R, P, V = 512, 64, 128, 128
+ROW = L + R
+PAGE = 64
+KV_BF16, KV_FP8 = 0, 1
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 draws to bfloat16 bit patterns (nearest, ties to even)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return u.astype(np.uint16)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    B: int
+    q_len: int
+    N: int
+    kv_dtype: int
+    num_pages: int
+    seq_lens: np.ndarray          # int32 [B]
+    block_table: np.ndarray       # int32 [B, max_pages], -1 past the used pages
+    kv_rows: np.ndarray           # uint16 bf16 bits [num_pages, 64, 576]: source row of every slot
+    new_slots: np.ndarray         # int64 [B*q_len]: slots of the step's new tokens
+    new_rows: np.ndarray          # uint16 bf16 bits [B*q_len, 576]: the step's new token rows
+    q: np.ndarray | None          # uint16 bf16 bits [B, q_len, N, 576] absorbed query
+    q_nope: np.ndarray | None     # uint16 [B, q_len, N, 128]
+    q_pe: np.ndarray | None       # uint16 [B, q_len, N, 64]
+    w_uk_t: np.ndarray | None     # uint16 [N, 128, 512]
+    w_uv: np.ndarray | None       # uint16 [N, 512, 128]
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum())
+
+    @property
+    def max_pages(self) -> int:
+        return self.block_table.shape[1]
+
+
+def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return to_bf16_bits(x)
+
+
+def make_workload(name: str, B: int, q_len: int, N: int, seq_lens, num_pages: int | None,
+                  kv_dtype: int, with_weights: bool, seed: int, pool_factor: float = 1.25,
+                  min_pool: int = 0) -> Workload:
+    """Draw one synthetic decode batch.
+
+    Pages are placed at random: a random permutation of the pool is dealt out to
+    the requests in order, so logically adjacent pages are physically scattered.
+    Block-table entries past a request's last page are -1.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq = np.asarray(seq_lens, dtype=np.int64)
+    assert seq.shape == (B,)
+    pages_per = (seq + PAGE - 1) // PAGE
+    need = int(pages_per.sum())
+    if num_pages is None:
+        num_pages = max(min_pool, int(math.ceil(pool_factor * need)))
+    assert num_pages >= need, "pool too small"
+    max_pages = max(1, int(pages_per.max()))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    cur = 0
+    for b in range(B):
+        n = int(pages_per[b])
+        bt[b, :n] = perm[cur:cur + n]
+        cur += n
+    kv_rows = _normal_bf16(rng, (num_pages, PAGE, ROW))
+    T = B * q_len
+    new_rows = _normal_bf16(rng, (T, ROW))
+    new_slots = np.full(T, -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(q_len):
+            pos = int(seq[b]) - q_len + t
+            if pos >= 0:
+                new_slots[b * q_len + t] = int(bt[b, pos // PAGE]) * PAGE + pos % PAGE
+    q = q_nope = q_pe = w_uk_t = w_uv = None
+    if with_weights:
+        q_nope = _normal_bf16(rng, (B, q_len, N, P))
+        q_pe = _normal_bf16(rng, (B, q_len, N, R))
+        w_uk_t = _normal_bf16(rng, (N, P, L), std=1.0 / math.sqrt(512.0))
+        w_uv = _normal_bf16(rng, (N, L, V), std=1.0 / math.sqrt(512.0))
+    else:
+        q = _normal_bf16(rng, (B, q_len, N, ROW))
+    return Workload(name, B, q_len, N, kv_dtype, num_pages, seq.astype(np.int32), bt,
+                    kv_rows, new_slots, new_rows, q, q_nope, q_pe, w_uk_t, w_uv, seed)
+
+
+def tiny() -> Workload:
+    return make_workload("tiny", 2, 1, 16, [37, 100], 16, KV_BF16, True, 20260)
+
+
+def tp_share() -> Workload:
+    rng = np.random.Generator(np.random.PCG64(20261 + 1000))
+    seq = rng.integers(1024, 4096, size=64, endpoint=True)
+    return make_workload("tp_share", 64, 1, 16, seq, 8192, KV_BF16, False, 20261)
+
+
+def full_head() -> Workload:
+    return make_workload("full_head", 32, 1, 128, [8192] * 32, 8192, KV_BF16, True, 20262)
+
+
+def fp8() -> Workload:
+    rng = np.random.Generator(np.random.PCG64(20263 + 1000))
+    seq = np.clip(np.rint(np.exp(rng.normal(math.log(2048.0), 1.0, size=128))), 64, 32768)
+    return make_workload("fp8", 128, 1, 128, seq.astype(np.int64), None, KV_FP8, False, 20263,
+                         min_pool=8192)
+
+
+def spec_long() -> Workload:
+    seq = [131072, 65536, 32768, 16384, 8192, 4096, 2048, 1024]
+    return make_workload("spec_long", 8, 2, 128, seq, int(math.ceil(1.25 * 4080)), KV_BF16,
+                         False, 20264)
+
+
+CONFIGS = {"tiny": tiny, "tp_share": tp_share, "full_head": full_head, "fp8": fp8,
+           "spec_long": spec_long}
+
+
+def random_fp8_rows(rng: np.random.Generator, n_rows: int, max_code_exp: int = 8,
+                    scale_lo: float = 0.25, scale_hi: float = 4.0) -> np.ndarray:
+    """Raw fp8 cache rows with random codes and independent random K/V scales.
+
+    Codes are drawn with exponent field <= ``max_code_exp`` (never NaN); the
+    two float32 scales are drawn independently, so K and V dequantize
+    differently.  Returns uint8 ``[n_rows, 584]``.
+    """
+    sign = rng.integers(0, 2, size=(n_rows, ROW)) << 7
+    e = rng.integers(0, max_code_exp + 1, size=(n_rows, ROW)) << 3
+    m = rng.integers(0, 8, size=(n_rows, ROW))
+    codes = (sign | e | m).astype(np.uint8)
+    ks = rng.uniform(scale_lo, scale_hi, size=n_rows).astype("<f4")
+    vs = rng.uniform(scale_lo, scale_hi, size=n_rows).astype("<f4")
+    rows = np.empty((n_rows, ROW + 8), dtype=np.uint8)
+    rows[:, :ROW] = codes
+    rows[:, ROW:ROW + 4] = ks.view(np.uint8).reshape(n_rows, 4)
+    rows[:, ROW + 4:] = vs.view(np.uint8).reshape(n_rows, 4)
+    return rows

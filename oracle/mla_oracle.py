@@ -1,0 +1,373 @@
+"""Plain, slow CPU oracle for MLA decode over a paged 576-element latent cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant generator with the HIP library; the two meet only on the seeded
+inputs produced by ``mla_inputs``.
+
+Everything here is float64 NumPy written straight from the definitions on the
+source pages (cited per function).  Page short names used in citations:
+
+* [vLLM-MLA]   "vLLM 源码完全拆解(三十七):MLA 注意力后端——矩阵吸收之后,576 维
+                latent KV 如何被四种内核读走"
+* [TRTLLM-TP]  "TensorRT-LLM 源码完全拆解(十二):注意力层的张量并行——head 怎么切、
+                MLA 为什么不能照切"
+* [Triton-MLA] "Triton und MLA: portable Attention und Latent-Space-Attention"
+
+Conventions (readings of the pages, listed in the design doc):
+
+* A cache row is ``[kv_c (L=512) | k_pe (R=64)]``; a page holds 64 rows
+  ([vLLM-MLA] §缓存的形状, §FlashMLA).  bf16 rows are 1152 bytes; fp8 rows are
+  576 e4m3fn codes followed by two float32 scales, K then V, 584 bytes.
+* ``seq_lens[b]`` counts every cached token including the ``q_len`` new ones;
+  query row ``t`` sees the first ``seq_lens[b] - q_len + 1 + t`` tokens
+  ([vLLM-MLA] §Triton MLA, causal via per-row seq_len).
+* Softmax scale is ``1/sqrt(qk_nope + qk_rope) = 1/sqrt(192)`` even though the
+  absorbed dot product is 576 wide ([vLLM-MLA] §两套算法).
+* ``lse`` is the natural-log log-sum-exp of the *scaled* scores
+  ([Triton-MLA] §Entwurfsmotivation: lse_base_on_e).  A row that sees no token
+  has ``o = 0`` and ``lse = -inf`` ([vLLM-MLA] §Prefill, empty partials).
+
+Parity status: every public function below is pinned by a ``-m "not gpu"``
+test in ``tests/test_oracle_pins.py`` (closed forms, brute force, library
+routines, printed numbers); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --- layout constants, as printed on the pages -------------------------------
+KV_LORA_RANK = 512          # L  ([vLLM-MLA] §从模型层看)
+ROPE_DIM = 64               # R
+QK_NOPE_DIM = 128           # P
+V_HEAD_DIM = 128            # V
+ROW_ELEMS = KV_LORA_RANK + ROPE_DIM   # 576, the cached head_size
+PAGE_TOKENS = 64            # FlashMLA page size ([vLLM-MLA] §缓存的形状)
+E4M3_MAX = 448.0            # largest finite OCP e4m3fn value
+
+KV_BF16 = 0
+KV_FP8 = 1
+
+
+def row_bytes(kv_dtype: int, row_elems: int = ROW_ELEMS) -> int:
+    """Bytes of one cached token row.
+
+    [vLLM-MLA] §缓存的形状: bf16 stores 2 bytes per element; fp8 stores one
+    byte per element and appends two float32 scales (one for K, one for V).
+    """
+    if kv_dtype == KV_BF16:
+        return 2 * row_elems
+    if kv_dtype == KV_FP8:
+        return row_elems + 2 * 4
+    raise ValueError("unknown kv dtype")
+
+
+def default_scale(qk_nope: int = QK_NOPE_DIM, qk_rope: int = ROPE_DIM) -> float:
+    """Softmax scale of absorbed decode: ``(qk_nope + qk_rope) ** -0.5``.
+
+    [vLLM-MLA] §两套算法: the absorbed and un-absorbed dot products are the same
+    scalar, so the scale keeps the 192-wide value.
+    """
+    return (qk_nope + qk_rope) ** -0.5
+
+
+# --- number formats ----------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Value of bfloat16 bit patterns: the top 16 bits of an IEEE float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_value(code: np.ndarray) -> np.ndarray:
+    """Value of OCP e4m3fn codes from the format definition.
+
+    1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
+    subnormal (``2^-6 * m/8``); there is no infinity and only ``S.1111.111``
+    is NaN, so the largest finite magnitude is ``2^8 * 1.75 = 448``.
+    """
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = np.ldexp(m / 8.0, -6)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_value(np.arange(0, 127))   # codes 0x00..0x7E, increasing
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Round float values to e4m3fn codes: nearest, ties to even, saturating.
+
+    Brute force over the 127 non-negative finite codes: pick the closest value;
+    on an exact tie pick the even code (even mantissa); magnitudes at or above
+    448 map to 448.  The sign bit is kept (so -0.0 and tiny negatives give
+    0x80).  Input values are taken exactly as given (callers pass float32).
+    """
+    v = np.asarray(x, dtype=np.float64)
+    a = np.abs(v)
+    idx = np.searchsorted(_E4M3_POS, a)          # first table value >= a
+    hi = np.clip(idx, 0, 126)
+    lo = np.clip(idx - 1, 0, 126)
+    d_hi = np.abs(_E4M3_POS[hi] - a)
+    d_lo = np.abs(a - _E4M3_POS[lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi)
+    code = np.where(a >= E4M3_MAX, 126, code)
+    neg = np.signbit(v)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize_row(x_bits: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """Quantize one 576-element bf16 row to e4m3fn codes plus a float32 scale.
+
+    The pages only say that fp8 rows carry one float32 scale for K and one for
+    V ([vLLM-MLA] §缓存的形状) and that the multiply is skipped when the
+    scale is 1 ([vLLM-MLA] §写缓存).  Reading used here: per-token scale
+    ``s = amax / 448`` (float32 division; ``s = 1`` for an all-zero row) and
+    ``code_i = e4m3(x_i / s)`` with an IEEE float32 division per element, so
+    the row's largest magnitude maps to 448.
+    """
+    xf = bf16_bits_to_f64(x_bits).astype(np.float32)
+    amax = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(E4M3_MAX))
+    if s == 0:
+        s = np.float32(1.0)
+    q = (xf / s).astype(np.float32)
+    return e4m3_encode(q), s
+
+
+# --- a1: cache write ---------------------------------------------------------
+def cache_write(pool: np.ndarray, kv_c_bits: np.ndarray, k_pe_bits: np.ndarray,
+                slot_mapping: np.ndarray, kv_dtype: int) -> np.ndarray:
+    """Scatter token rows into the paged pool; returns the updated pool.
+
+    [vLLM-MLA] §写缓存: latent and k_pe of token ``t`` land in one row at
+    ``slot_mapping[t]``; with 64-token pages the row is page ``slot // 64``,
+    offset ``slot % 64``.  Negative slots are padding and are skipped.
+    ``pool`` is a uint8 array ``[num_pages, 64, row_bytes]``.
+    """
+    out = pool.copy()
+    rb = out.shape[2]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        page, off = divmod(int(slot), PAGE_TOKENS)
+        row_bits = np.concatenate([np.asarray(kv_c_bits[t], np.uint16),
+                                   np.asarray(k_pe_bits[t], np.uint16)])
+        if kv_dtype == KV_BF16:
+            out[page, off, :] = row_bits.astype("<u2").view(np.uint8)
+        else:
+            codes, s = fp8_quantize_row(row_bits)
+            n = row_bits.size
+            out[page, off, :n] = codes
+            out[page, off, n:n + 4] = np.array([s], "<f4").view(np.uint8)
+            out[page, off, n + 4:n + 8] = np.array([s], "<f4").view(np.uint8)
+            assert rb == n + 8
+    return out
+
+
+def row_views(rows: np.ndarray, kv_dtype: int, row_elems: int = ROW_ELEMS,
+              latent: int = KV_LORA_RANK) -> tuple[np.ndarray, np.ndarray]:
+    """Decode raw cache rows into the K view (all elements) and V view (latent).
+
+    bf16: both views are the stored values.  fp8: K = code * k_scale over all
+    elements, V = code * v_scale over the latent part ([vLLM-MLA] §缓存的形状:
+    one scale for K and one for V; the latent doubles as V).
+    """
+    rows = np.asarray(rows, dtype=np.uint8)
+    if kv_dtype == KV_BF16:
+        vals = bf16_bits_to_f64(rows.reshape(rows.shape[0], -1).view("<u2"))
+        return vals, vals[:, :latent]
+    codes = rows[:, :row_elems]
+    k_scale = rows[:, row_elems:row_elems + 4].copy().view("<f4").astype(np.float64)
+    v_scale = rows[:, row_elems + 4:row_elems + 8].copy().view("<f4").astype(np.float64)
+    vals = e4m3_value(codes)
+    return vals * k_scale, vals[:, :latent] * v_scale
+
+
+def gather_rows(pool: np.ndarray, block_table_row: np.ndarray, n: int) -> np.ndarray:
+    """Raw rows of logical tokens ``0..n-1`` of one request.
+
+    Token ``j`` lives in physical page ``block_table_row[j // 64]`` at offset
+    ``j % 64`` ([vLLM-MLA] §Metadata: block_table; §FlashMLA: paged cache).
+    """
+    j = np.arange(n)
+    pages = np.asarray(block_table_row, dtype=np.int64)[j // PAGE_TOKENS]
+    return pool[pages, j % PAGE_TOKENS, :]
+
+
+# --- a4 + a5: absorbed MQA decode, definition form ---------------------------
+def visible_tokens(seq_len: int, q_len: int, t: int) -> int:
+    """Tokens seen by query row ``t``: ``seq_len - q_len + 1 + t``, floored at 0.
+
+    [vLLM-MLA] §Triton MLA: multi-token decode adds ``arange(1 - q_len, 1)`` to
+    ``seq_lens`` per row and clamps at 0, which is causality within the block.
+    """
+    return max(0, seq_len - q_len + 1 + t)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
+           ) -> tuple[np.ndarray, np.ndarray]:
+    """Textbook softmax attention of query rows ``q[H, D]`` over ``n`` keys.
+
+    ``s = scale * q K^T``, ``lse = m + ln sum exp(s - m)``, ``p = exp(s - lse)``,
+    ``o = p V``.  With no keys: ``o = 0``, ``lse = -inf``.
+    """
+    H = q.shape[0]
+    if K.shape[0] == 0:
+        return np.zeros((H, V.shape[1])), np.full(H, -np.inf)
+    s = scale * (q @ K.T)
+    m = s.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    p = np.exp(s - lse[:, None])
+    return p @ V, lse
+
+
+def decode(q: np.ndarray, pool: np.ndarray, kv_dtype: int, block_table: np.ndarray,
+           seq_lens: np.ndarray, scale: float, row_elems: int = ROW_ELEMS,
+           latent: int = KV_LORA_RANK) -> tuple[np.ndarray, np.ndarray]:
+    """Absorbed-MQA decode over the paged cache, as its plain definition.
+
+    ``q`` is ``[B, q_len, N, row_elems]`` (absorbed query ``[q_l,nope | q_pe]``);
+    returns ``o[B, q_len, N, latent]`` and ``lse[B, q_len, N]`` (float64).
+    Every head scores against the whole row and the latent part is V
+    ([vLLM-MLA] §两套算法 data-movement-friendly form; §FlashMLA: one KV head
+    shared by all query heads; [Triton-MLA] §Datenfluss).  No splits, no online
+    softmax: the gathered keys are attended in one pass.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, q_len, N, _ = q.shape
+    o = np.zeros((B, q_len, N, latent))
+    lse = np.full((B, q_len, N), -np.inf)
+    for b in range(B):
+        n_all = int(seq_lens[b])
+        if n_all <= 0:
+            continue
+        K_all, V_all = row_views(gather_rows(pool, block_table[b], n_all), kv_dtype,
+                                 row_elems, latent)
+        for t in range(q_len):
+            n = visible_tokens(n_all, q_len, t)
+            o[b, t], lse[b, t] = attend(q[b, t], K_all[:n], V_all[:n], scale)
+    return o, lse
+
+
+def merge(o_parts: np.ndarray, lse_parts: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Combine attention partials over disjoint token sets (axis 0 = part).
+
+    [vLLM-MLA] §Prefill (merge_attn_states): each part is re-weighted by
+    ``exp(lse_s - max lse)``; parts with ``lse = -inf`` weigh zero.  Result
+    ``o = sum w_s o_s / sum w_s``, ``lse = max + ln sum w_s``; all parts empty
+    gives ``o = 0``, ``lse = -inf``.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    safe_m = np.where(np.isfinite(m), m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - safe_m), 0.0)
+    wsum = w.sum(axis=0)
+    o = (w[..., None] * o_parts).sum(axis=0) / np.where(wsum > 0, wsum, 1.0)[..., None]
+    lse = np.where(wsum > 0, safe_m + np.log(np.where(wsum > 0, wsum, 1.0)), -np.inf)
+    return o, lse
+
+
+# --- a2 / a6: absorption and up-projection ----------------------------------
+def absorb(q_nope: np.ndarray, q_pe: np.ndarray | None, w_uk_t: np.ndarray) -> np.ndarray:
+    """Absorbed query ``[q_nope . W_UK_T[h] | q_pe]`` per token and head.
+
+    ``q_nope[T, N, P]``, ``W_UK_T[N, P, L]`` ([vLLM-MLA] §权重准备: W_UK is
+    permuted to ``[N, P, L]`` so one batched GEMM serves all heads; §两套算法:
+    ``q_l,nope = q_nope W_UK^T``); ``q_pe[T, N, R]`` is appended unchanged
+    ([TRTLLM-TP] §吸收: the product is written into the front of a
+    ``[T, N, L + R]`` fused query).  Returns float64 ``[T, N, L(+R)]``.
+    """
+    ql = np.einsum("thp,hpl->thl", np.asarray(q_nope, np.float64),
+                   np.asarray(w_uk_t, np.float64))
+    if q_pe is None:
+        return ql
+    return np.concatenate([ql, np.asarray(q_pe, np.float64)], axis=-1)
+
+
+def up_v(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Per-head up-projection ``o_lat[t,h,:] . W_UV[h]`` → ``[T, N, V]``.
+
+    [vLLM-MLA] §两套算法 (_v_up_proj): ``[N, B, L] @ W_UV[N, L, V]`` written
+    back token-major.
+    """
+    return np.einsum("thl,hlv->thv", np.asarray(o_lat, np.float64),
+                     np.asarray(w_uv, np.float64))
+
+
+# --- the un-absorbed oracle --------------------------------------------------
+def mla_unabsorbed(q_nope: np.ndarray, q_pe: np.ndarray, pool: np.ndarray, kv_dtype: int,
+                   block_table: np.ndarray, seq_lens: np.ndarray, w_uk_t: np.ndarray,
+                   w_uv: np.ndarray, scale: float, heads: list[int] | None = None,
+                   batches: list[int] | None = None, row_elems: int = ROW_ELEMS,
+                   latent: int = KV_LORA_RANK) -> tuple[np.ndarray, np.ndarray]:
+    """MLA attention computed the compute-friendly way, with no absorption.
+
+    Every visible cached latent is up-projected per head to
+    ``k_nope = W_UK[h] c`` (P values) and ``v = c W_UV[h]`` (V values); the key
+    is ``[k_nope, k_pe]`` with the single rope key broadcast to all heads, and
+    plain softmax attention runs with the 192-wide query ``[q_nope, q_pe]``
+    ([vLLM-MLA] §从模型层看 decoupled RoPE, §两套算法 compute-friendly form).
+    For fp8 rows the latent's K view uses ``k_scale`` and its V view
+    ``v_scale``.
+
+    ``q_nope[B, q_len, N, P]``, ``q_pe[B, q_len, N, R]``.  Returns
+    ``y[B, q_len, N, V]`` and ``lse[B, q_len, N]`` (NaN where not computed when
+    ``heads``/``batches`` restrict the work).
+    """
+    q_nope = np.asarray(q_nope, np.float64)
+    q_pe = np.asarray(q_pe, np.float64)
+    wk = np.asarray(w_uk_t, np.float64)
+    wv = np.asarray(w_uv, np.float64)
+    B, q_len, N, _ = q_nope.shape
+    Vd = wv.shape[2]
+    heads = list(range(N)) if heads is None else heads
+    batches = list(range(B)) if batches is None else batches
+    y = np.full((B, q_len, N, Vd), np.nan)
+    lse = np.full((B, q_len, N), np.nan)
+    for b in batches:
+        n_all = max(0, int(seq_lens[b]))
+        Kv, Vv = row_views(gather_rows(pool, block_table[b], n_all), kv_dtype, row_elems, latent) \
+            if n_all > 0 else (np.zeros((0, row_elems)), np.zeros((0, latent)))
+        c_k, k_pe = Kv[:, :latent], Kv[:, latent:]
+        for h in heads:
+            k_nope = c_k @ wk[h].T          # [n, P]
+            v = Vv @ wv[h]                  # [n, V]
+            K = np.concatenate([k_nope, k_pe], axis=1)
+            for t in range(q_len):
+                n = visible_tokens(n_all, q_len, t)
+                qh = np.concatenate([q_nope[b, t, h], q_pe[b, t, h]])[None, :]
+                o, l = attend(qh, K[:n], v[:n], scale)
+                y[b, t, h], lse[b, t, h] = o[0], l[0]
+    return y, lse
+
+
+# --- byte arithmetic used as printed pins ------------------------------------
+def mha_row_bytes(num_heads: int = 128, qk_dim: int = 192, v_dim: int = 128,
+                  elem_bytes: int = 2) -> int:
+    """Per-token per-layer bytes of an un-compressed MHA cache: ``N (QK + V)``."""
+    return num_heads * (qk_dim + v_dim) * elem_bytes
+
+
+def page_bytes(kv_dtype: int) -> int:
+    """Bytes of one 64-token page of one layer."""
+    return PAGE_TOKENS * row_bytes(kv_dtype)
+
+
+def request_bytes(seq_len: int, layers: int, kv_dtype: int) -> int:
+    """Cache bytes of one request across ``layers`` layers."""
+    return seq_len * layers * row_bytes(kv_dtype)
+
+
+def log2e() -> float:
+    return 1.0 / math.log(2.0)

@@ -1,0 +1,429 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Printed numbers from the pages (tests/golden), closed forms, invariants that the
+method's definition implies, brute force in pure Python loops, and library
+routines (torch's float64 SDPA, logsumexp, bfloat16 and float8_e4m3fn codecs).
+A plausible slip in the oracle (a dropped rope term, the 576-wide scale, a
+transposed weight, a wrong causal offset, a lost scale factor) fails at least
+one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+import mla_inputs as MI
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "page_arithmetic.json")
+
+
+# ----------------------------------------------------------------------------
+# printed byte arithmetic
+# ----------------------------------------------------------------------------
+def test_printed_byte_arithmetic():
+    g = json.load(open(GOLD))
+    bf, f8 = O.row_bytes(O.KV_BF16), O.row_bytes(O.KV_FP8)
+    assert bf == g["row_bytes_bf16"] and f8 == g["row_bytes_fp8"]
+    mha = O.mha_row_bytes()
+    assert mha == g["mha_row_bytes_128h_qk192_v128"]
+    assert mha // bf == g["mha_over_mla_ratio_floor"]
+    L, S = g["layers"], g["context_tokens"]
+    assert bf * L == g["per_token_all_layers_bf16"]
+    assert round(bf * L / 1024, 1) == g["per_token_all_layers_bf16_kib"]
+    assert round(O.request_bytes(S, L, O.KV_BF16) / 1e9, 2) == g["request_128k_bf16_gb"]
+    assert round(O.request_bytes(S, L, O.KV_BF16) / 2**30, 2) == g["request_128k_bf16_gib"]
+    assert O.page_bytes(O.KV_BF16) == g["page_bytes_bf16"] == g["page_kib_bf16"] * 1024
+    assert S // O.PAGE_TOKENS == g["pages_per_128k"]
+    assert f8 * L == g["per_token_all_layers_fp8"]
+    assert round(f8 * L / 1024, 1) == g["per_token_all_layers_fp8_kib"]
+    assert round(O.request_bytes(S, L, O.KV_FP8) / 1e9, 2) == g["request_128k_fp8_gb"]
+    assert round(O.request_bytes(S, L, O.KV_FP8) / 2**30, 2) == g["request_128k_fp8_gib"]
+    assert round(mha * L * S / 1e9) == g["mha_request_128k_gb"]
+    gqa = O.mha_row_bytes(num_heads=8, qk_dim=128, v_dim=128)
+    assert gqa == g["gqa8_row_bytes"]
+    assert round(gqa * L * S / 1e9, 1) == g["gqa8_request_128k_gb"]
+    assert round(gqa / bf, 1) == g["gqa8_over_mla_ratio"]
+    assert round(64 * 1024 * O.ROW_ELEMS * 2 / 1e6, 1) == g["gather_workspace_64k_rows_mb"]
+    assert 128 * 128 * 2 == g["trtllm_mha_elems_per_token"]
+    assert O.ROW_ELEMS == g["trtllm_mla_elems_per_token"]
+
+
+def test_scale_is_192_wide():
+    assert O.default_scale() == pytest.approx(1 / math.sqrt(192), rel=1e-15)
+    assert O.default_scale() != pytest.approx(1 / math.sqrt(576), rel=1e-3)
+
+
+# ----------------------------------------------------------------------------
+# number formats against torch's codecs
+# ----------------------------------------------------------------------------
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2**16, size=20000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]       # drop inf/nan encodings
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.bf16_bits_to_f64(bits), ref)
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert set(np.flatnonzero(np.isnan(got))) == {0x7F, 0xFF}
+    assert np.nanmax(got) == 448.0 and np.nanmin(got) == -448.0
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(2)
+    pos = O.e4m3_value(np.arange(0, 127))
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([
+        rng.standard_normal(20000) * 50,
+        rng.uniform(-448, 448, 20000),
+        rng.standard_normal(5000) * 1e-2,
+        mids, -mids, pos, -pos,
+        np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+        np.nextafter(mids.astype(np.float32), np.float32(-np.inf)),
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), ref)
+
+
+def test_e4m3_encode_ties_and_saturation():
+    # ties go to the even code
+    assert O.e4m3_encode(np.float32(1.0625)) == 0x38          # between 1.0 (0x38) and 1.125 (0x39)
+    assert O.e4m3_encode(np.float32(1.1875)) == 0x3A          # between 1.125 and 1.25 (0x3A)
+    # half of the smallest subnormal rounds to zero, just above rounds up
+    assert O.e4m3_encode(np.float32(2.0**-10)) == 0x00
+    assert O.e4m3_encode(np.nextafter(np.float32(2.0**-10), np.float32(1))) == 0x01
+    # saturation instead of NaN
+    for v, c in [(448.0, 0x7E), (460.0, 0x7E), (470.0, 0x7E), (1e6, 0x7E), (-1e30, 0xFE)]:
+        assert O.e4m3_encode(np.float32(v)) == c
+    # round trip of every finite code
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_value(codes).astype(np.float32)), codes)
+
+
+def test_fp8_quantize_row_properties():
+    rng = np.random.default_rng(3)
+    x = MI.to_bf16_bits(rng.standard_normal(576).astype(np.float32) * 3)
+    codes, s = O.fp8_quantize_row(x)
+    xf = O.bf16_bits_to_f64(x)
+    # the largest magnitude lands on 448 exactly
+    assert np.max(np.abs(O.e4m3_value(codes))) == 448.0
+    assert s == np.float32(np.float32(np.max(np.abs(xf))) / np.float32(448))
+    # dequantized error within half a 3-bit-mantissa ulp (relative 2^-4), or the subnormal step
+    deq = O.e4m3_value(codes) * np.float64(s)
+    bound = np.maximum(np.abs(xf) * 2.0**-4, float(s) * 2.0**-10) * (1 + 1e-6)
+    assert np.all(np.abs(deq - xf) <= bound)
+    # an all-zero row uses scale 1 and code 0
+    z_codes, z_s = O.fp8_quantize_row(np.zeros(576, np.uint16))
+    assert z_s == 1.0 and np.all(z_codes == 0)
+
+
+# ----------------------------------------------------------------------------
+# cache write
+# ----------------------------------------------------------------------------
+def test_cache_write_bf16_is_bit_copy_and_touches_only_its_slots():
+    rng = np.random.default_rng(4)
+    pool = rng.integers(0, 256, size=(5, 64, 1152), dtype=np.uint8)
+    kv = MI.to_bf16_bits(rng.standard_normal((4, 512)).astype(np.float32))
+    pe = MI.to_bf16_bits(rng.standard_normal((4, 64)).astype(np.float32))
+    slots = np.array([3 * 64 + 7, -1, 0, 4 * 64 + 63])
+    out = O.cache_write(pool, kv, pe, slots, O.KV_BF16)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        row = out[s // 64, s % 64].view("<u2")
+        assert np.array_equal(row[:512], kv[t]) and np.array_equal(row[512:], pe[t])
+    touched = np.zeros((5, 64), bool)
+    touched[3, 7] = touched[0, 0] = touched[4, 63] = True
+    assert np.array_equal(out[~touched], pool[~touched])
+
+
+def test_cache_write_fp8_layout():
+    rng = np.random.default_rng(5)
+    pool = np.zeros((2, 64, 584), dtype=np.uint8)
+    kv = MI.to_bf16_bits(rng.standard_normal((1, 512)).astype(np.float32))
+    pe = MI.to_bf16_bits(rng.standard_normal((1, 64)).astype(np.float32))
+    out = O.cache_write(pool, kv, pe, np.array([70]), O.KV_FP8)
+    row = out[1, 6]
+    codes, s = O.fp8_quantize_row(np.concatenate([kv[0], pe[0]]))
+    assert np.array_equal(row[:576], codes)
+    assert row[576:580].view("<f4")[0] == s and row[580:584].view("<f4")[0] == s
+    K, Vv = O.row_views(row[None], O.KV_FP8)
+    assert K.shape == (1, 576) and Vv.shape == (1, 512)
+
+
+# ----------------------------------------------------------------------------
+# attention: closed forms and invariants
+# ----------------------------------------------------------------------------
+def _pool_from_rows(rows_bits):
+    """bf16 pool whose page p holds rows_bits[p*64 : p*64+64] (pure byte packing)."""
+    n = rows_bits.shape[0]
+    pages = (n + 63) // 64
+    buf = np.zeros((pages * 64, rows_bits.shape[1]), np.uint16)
+    buf[:n] = rows_bits
+    return buf.astype("<u2").view(np.uint8).reshape(pages, 64, -1)
+
+
+def _rand_bits(rng, shape, std=1.0):
+    return MI.to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def test_single_token_context_returns_v_exactly():
+    rng = np.random.default_rng(6)
+    rows = _rand_bits(rng, (1, 576))
+    pool = _pool_from_rows(rows)
+    q = O.bf16_bits_to_f64(_rand_bits(rng, (1, 1, 8, 576)))
+    o, lse = O.decode(q, pool, O.KV_BF16, np.array([[0]]), np.array([1]), O.default_scale())
+    v0 = O.bf16_bits_to_f64(rows[0, :512])
+    assert np.array_equal(o[0, 0], np.broadcast_to(v0, (8, 512)))
+    k0 = O.bf16_bits_to_f64(rows[0])
+    assert np.allclose(lse[0, 0], O.default_scale() * (q[0, 0] @ k0), rtol=0, atol=1e-12)
+
+
+def test_zero_query_gives_uniform_softmax():
+    rng = np.random.default_rng(7)
+    n = 150
+    rows = _rand_bits(rng, (n, 576))
+    pool = _pool_from_rows(rows)
+    bt = np.arange(pool.shape[0])[None]
+    q = np.zeros((1, 1, 4, 576))
+    o, lse = O.decode(q, pool, O.KV_BF16, bt, np.array([n]), O.default_scale())
+    V = O.bf16_bits_to_f64(rows[:, :512])
+    assert np.allclose(lse, math.log(n), atol=1e-12)
+    assert np.allclose(o[0, 0], V.mean(0)[None], atol=1e-12)
+
+
+def test_identical_keys_give_that_value():
+    rng = np.random.default_rng(8)
+    n = 77
+    row = _rand_bits(rng, (1, 576))
+    pool = _pool_from_rows(np.repeat(row, n, axis=0))
+    q = O.bf16_bits_to_f64(_rand_bits(rng, (1, 1, 3, 576)))
+    o, lse = O.decode(q, pool, O.KV_BF16, np.arange(2)[None], np.array([n]), 0.1)
+    s = 0.1 * (q[0, 0] @ O.bf16_bits_to_f64(row[0]))
+    assert np.allclose(lse[0, 0], s + math.log(n), atol=1e-11)
+    assert np.allclose(o[0, 0], O.bf16_bits_to_f64(row[0, :512])[None], atol=1e-12)
+
+
+def test_decode_matches_torch_sdpa_and_logsumexp():
+    """The decode oracle equals torch's float64 SDPA over the gathered rows (MQA broadcast)."""
+    w = MI.make_workload("t", 3, 1, 8, [5, 64, 130], 8, MI.KV_BF16, False, 11)
+    pool = O.cache_write(np.zeros((w.num_pages, 64, 1152), np.uint8),
+                         w.kv_rows.reshape(-1, 576)[:, :512], w.kv_rows.reshape(-1, 576)[:, 512:],
+                         np.arange(w.num_pages * 64), O.KV_BF16)
+    q = O.bf16_bits_to_f64(w.q)
+    sc = O.default_scale()
+    o, lse = O.decode(q, pool, O.KV_BF16, w.block_table, w.seq_lens, sc)
+    for b in range(w.B):
+        n = int(w.seq_lens[b])
+        j = np.arange(n)
+        rows = w.kv_rows[w.block_table[b, j // 64], j % 64]
+        K = torch.from_numpy(O.bf16_bits_to_f64(rows))
+        qt = torch.from_numpy(q[b, 0])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[None, :, None, :], K[None, None].expand(1, w.N, n, 576),
+            K[None, None, :, :512].expand(1, w.N, n, 512), scale=sc)[0, :, 0]
+        assert np.allclose(o[b, 0], ref.numpy(), rtol=1e-12, atol=1e-13)
+        ref_lse = torch.logsumexp(sc * qt @ K.T, dim=-1).numpy()
+        assert np.allclose(lse[b, 0], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_probabilities_sum_to_one():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((5, 576))
+    K = rng.standard_normal((40, 576))
+    _, lse = O.attend(q, K, K[:, :512], 0.07)
+    assert np.allclose(np.exp(0.07 * q @ K.T - lse[:, None]).sum(1), 1.0, atol=1e-13)
+
+
+def test_empty_context_row():
+    q = np.ones((1, 2, 2, 576))
+    pool = np.zeros((1, 64, 1152), np.uint8)
+    o, lse = O.decode(q, pool, O.KV_BF16, np.array([[0]]), np.array([1]), 0.1)
+    # q_len 2 with seq_len 1: row 0 sees 0 tokens, row 1 sees 1
+    assert np.all(o[0, 0] == 0) and np.all(np.isneginf(lse[0, 0]))
+    assert np.all(np.isfinite(lse[0, 1]))
+
+
+def test_merge_of_any_partition_equals_unsplit():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((6, 576))
+    K = rng.standard_normal((300, 576)) * 2
+    o_all, lse_all = O.attend(q, K, K[:, :512], O.default_scale())
+    for cuts in ([0, 300], [0, 1, 300], [0, 64, 128, 200, 300], [0, 0, 150, 150, 300]):
+        parts = [O.attend(q, K[a:b], K[a:b, :512], O.default_scale()) for a, b in zip(cuts, cuts[1:])]
+        o, lse = O.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        assert np.allclose(o, o_all, atol=1e-12) and np.allclose(lse, lse_all, atol=1e-12)
+    o, lse = O.merge(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_causal_rows_equal_single_token_decodes():
+    w = MI.make_workload("t", 2, 2, 4, [70, 129], 8, MI.KV_BF16, False, 12)
+    pool = O.cache_write(np.zeros((w.num_pages, 64, 1152), np.uint8),
+                         w.kv_rows.reshape(-1, 576)[:, :512], w.kv_rows.reshape(-1, 576)[:, 512:],
+                         np.arange(w.num_pages * 64), O.KV_BF16)
+    q = O.bf16_bits_to_f64(w.q)
+    o2, lse2 = O.decode(q, pool, O.KV_BF16, w.block_table, w.seq_lens, 0.1)
+    for t in range(2):
+        o1, lse1 = O.decode(q[:, t:t + 1], pool, O.KV_BF16, w.block_table,
+                            w.seq_lens - 1 + t, 0.1)
+        assert np.array_equal(o1[:, 0], o2[:, t]) and np.array_equal(lse1[:, 0], lse2[:, t])
+    # row 0 really sees one token fewer than row 1
+    assert not np.allclose(lse2[:, 0], lse2[:, 1])
+
+
+def test_page_permutation_invariance():
+    w = MI.make_workload("t", 2, 1, 4, [100, 65], 6, MI.KV_BF16, False, 13)
+    pool = O.cache_write(np.zeros((w.num_pages, 64, 1152), np.uint8),
+                         w.kv_rows.reshape(-1, 576)[:, :512], w.kv_rows.reshape(-1, 576)[:, 512:],
+                         np.arange(w.num_pages * 64), O.KV_BF16)
+    q = O.bf16_bits_to_f64(w.q)
+    o, lse = O.decode(q, pool, O.KV_BF16, w.block_table, w.seq_lens, 0.1)
+    perm = np.random.default_rng(0).permutation(w.num_pages)      # new page id -> old page id
+    inv = np.argsort(perm)
+    bt2 = np.where(w.block_table >= 0, inv[np.maximum(w.block_table, 0)], -1)
+    o2, lse2 = O.decode(q, pool[perm], O.KV_BF16, bt2, w.seq_lens, 0.1)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_head_permutation_permutes_outputs():
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((7, 576))
+    K = rng.standard_normal((50, 576))
+    o, lse = O.attend(q, K, K[:, :512], 0.1)
+    p = rng.permutation(7)
+    o2, lse2 = O.attend(q[p], K, K[:, :512], 0.1)
+    # BLAS blocking may change the last bits with row order; values must agree to rounding
+    assert np.allclose(o2, o[p], rtol=1e-13, atol=1e-14) and np.allclose(lse2, lse[p], rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# absorption identity: brute force in pure Python loops, tiny dims
+# ----------------------------------------------------------------------------
+def _brute_unabsorbed(qn, qp, C, KPE, WK, WV, scale):
+    """Pure-Python MLA for one query row: up-project every latent, then softmax."""
+    H, P = len(qn), len(qn[0])
+    n, Lr = len(C), len(C[0])
+    Vd = len(WV[0][0])
+    ys, lses = [], []
+    for h in range(H):
+        scores = []
+        vs = []
+        for j in range(n):
+            k_nope = [sum(WK[h][p][l] * C[j][l] for l in range(Lr)) for p in range(P)]
+            s = sum(qn[h][p] * k_nope[p] for p in range(P)) + sum(qp[h][r] * KPE[j][r] for r in range(len(qp[h])))
+            scores.append(scale * s)
+            vs.append([sum(C[j][l] * WV[h][l][v] for l in range(Lr)) for v in range(Vd)])
+        m = max(scores)
+        z = sum(math.exp(s - m) for s in scores)
+        lse = m + math.log(z)
+        y = [sum(math.exp(scores[j] - lse) * vs[j][v] for j in range(n)) for v in range(Vd)]
+        ys.append(y)
+        lses.append(lse)
+    return ys, lses
+
+
+@pytest.mark.parametrize("n", [1, 3, 7])
+def test_absorption_identity_brute_force(n):
+    """up_v(decode(absorb(q))) == un-absorbed MLA, tiny dims, fp64."""
+    rng = np.random.default_rng(100 + n)
+    Ld, Rd, Pd, Vd, H = 8, 2, 4, 4, 3
+    C = rng.standard_normal((n, Ld))
+    KPE = rng.standard_normal((n, Rd))
+    WK = rng.standard_normal((H, Pd, Ld))       # W_UK_T[h] : [P, L]
+    WV = rng.standard_normal((H, Ld, Vd))       # W_UV[h]   : [L, V]
+    qn = rng.standard_normal((H, Pd))
+    qp = rng.standard_normal((H, Rd))
+    scale = (Pd + Rd) ** -0.5
+    y_ref, lse_ref = _brute_unabsorbed(qn.tolist(), qp.tolist(), C.tolist(), KPE.tolist(),
+                                       WK.tolist(), WV.tolist(), scale)
+    # oracle route: absorb -> decode over float64 rows -> up_v
+    qf = O.absorb(qn[None], qp[None], WK)[0]                  # [H, L+R]
+    rows = np.concatenate([C, KPE], axis=1)
+    o, lse = O.attend(qf, rows, rows[:, :Ld], scale)
+    y = O.up_v(o[None], WV)[0]
+    assert np.allclose(y, np.array(y_ref), rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, np.array(lse_ref), rtol=1e-12, atol=1e-12)
+    # the 576-wide (here L+R-wide) scale breaks the identity
+    o_bad, lse_bad = O.attend(qf, rows, rows[:, :Ld], (Ld + Rd) ** -0.5)
+    if n > 1:
+        assert not np.allclose(O.up_v(o_bad[None], WV)[0], np.array(y_ref), rtol=1e-6)
+    assert not np.allclose(lse_bad, np.array(lse_ref), rtol=1e-6)
+
+
+def test_absorption_identity_tiny_config_full_dims():
+    """Same identity at the tiny workload's real dims, via the vectorised un-absorbed oracle."""
+    w = MI.tiny()
+    pool = O.cache_write(np.zeros((w.num_pages, 64, 1152), np.uint8),
+                         w.kv_rows.reshape(-1, 576)[:, :512], w.kv_rows.reshape(-1, 576)[:, 512:],
+                         np.arange(w.num_pages * 64), O.KV_BF16)
+    qn = O.bf16_bits_to_f64(w.q_nope)
+    qp = O.bf16_bits_to_f64(w.q_pe)
+    wk = O.bf16_bits_to_f64(w.w_uk_t)
+    wv = O.bf16_bits_to_f64(w.w_uv)
+    sc = O.default_scale()
+    y_ref, lse_ref = O.mla_unabsorbed(qn, qp, pool, O.KV_BF16, w.block_table, w.seq_lens, wk, wv, sc)
+    qf = O.absorb(qn.reshape(-1, w.N, 128), qp.reshape(-1, w.N, 64), wk).reshape(w.B, w.q_len, w.N, 576)
+    o, lse = O.decode(qf, pool, O.KV_BF16, w.block_table, w.seq_lens, sc)
+    y = O.up_v(o.reshape(-1, w.N, 512), wv).reshape(w.B, w.q_len, w.N, 128)
+    assert np.allclose(y, y_ref, rtol=1e-9, atol=1e-12)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-10)
+    # dropping the rope term of the key would be caught here
+    y_norope, _ = O.mla_unabsorbed(qn, np.zeros_like(qp), pool, O.KV_BF16, w.block_table,
+                                   w.seq_lens, wk, wv, sc)
+    assert not np.allclose(y_norope, y_ref, rtol=1e-3)
+
+
+def test_fp8_views_use_their_own_scales():
+    """With k_scale != v_scale the un-absorbed and absorbed routes still agree,
+    and swapping the scales changes the result."""
+    rng = np.random.default_rng(15)
+    rows = MI.random_fp8_rows(rng, 64, max_code_exp=7)
+    pool = rows.reshape(1, 64, 584)
+    N = 2
+    qn = rng.standard_normal((1, 1, N, 128))
+    qp = rng.standard_normal((1, 1, N, 64))
+    wk = rng.standard_normal((N, 128, 512)) / 22
+    wv = rng.standard_normal((N, 512, 128)) / 22
+    sc = O.default_scale()
+    y_ref, lse_ref = O.mla_unabsorbed(qn, qp, pool, O.KV_FP8, np.array([[0]]), np.array([50]), wk, wv, sc)
+    qf = O.absorb(qn[0], qp[0], wk)[None]
+    o, lse = O.decode(qf, pool, O.KV_FP8, np.array([[0]]), np.array([50]), sc)
+    y = O.up_v(o[0], wv)[None]
+    assert np.allclose(y, y_ref, rtol=1e-9, atol=1e-12) and np.allclose(lse, lse_ref, atol=1e-10)
+    swapped = rows.copy()
+    swapped[:, 576:580], swapped[:, 580:584] = rows[:, 580:584], rows[:, 576:580]
+    o2, _ = O.decode(qf, swapped.reshape(1, 64, 584), O.KV_FP8, np.array([[0]]), np.array([50]), sc)
+    assert not np.allclose(o2, o, rtol=1e-3)
+
+
+def test_absorb_and_up_v_against_loops():
+    rng = np.random.default_rng(16)
+    qn = rng.standard_normal((2, 3, 4))
+    qp = rng.standard_normal((2, 3, 2))
+    wk = rng.standard_normal((3, 4, 5))
+    out = O.absorb(qn, qp, wk)
+    for t in range(2):
+        for h in range(3):
+            for l in range(5):
+                assert out[t, h, l] == pytest.approx(sum(qn[t, h, p] * wk[h, p, l] for p in range(4)), rel=1e-13)
+            assert np.array_equal(out[t, h, 5:], qp[t, h])
+    ol = rng.standard_normal((2, 3, 5))
+    wv = rng.standard_normal((3, 5, 4))
+    y = O.up_v(ol, wv)
+    for t in range(2):
+        for h in range(3):
+            for v in range(4):
+                assert y[t, h, v] == pytest.approx(sum(ol[t, h, l] * wv[h, l, v] for l in range(5)), rel=1e-13)
