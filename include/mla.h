@@ -1,0 +1,198 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA paged-latent decode library.
+ *
+ * Multi-head Latent Attention decode, run as absorbed multi-query attention
+ * over a paged cache in which every token stores ONE 576-element row
+ * [kv_c (512, RMS-normed latent) | k_pe (64, decoupled-RoPE key)].  Every query
+ * head scores against all 576 elements and the 512-element latent doubles as V.
+ *
+ * Source pages cited below (by title and section):
+ *   [vLLM-MLA]   "vLLM 源码完全拆解(三十七):MLA 注意力后端——矩阵吸收之后,576 维
+ *                latent KV 如何被四种内核读走"
+ *   [TRTLLM-TP]  "TensorRT-LLM 源码完全拆解(十二):注意力层的张量并行"
+ *   [Triton-MLA] "Triton und MLA: portable Attention und Latent-Space-Attention"
+ *
+ * General rules for every call
+ * ----------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates or frees memory inside a call.  Scratch space for
+ *   mla_decode is a caller-provided workspace sized by
+ *   mla_decode_workspace_size().
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on that stream and returns without synchronising, so the
+ *   calls can be captured into a HIP graph.  Callers order mla_cache_write
+ *   before mla_decode on the same stream (write-before-read, [vLLM-MLA]
+ *   §写缓存: the cache update runs before attention in the same step).
+ * - bf16 tensors are IEEE bfloat16; all strides are in ELEMENTS of the
+ *   tensor's own type.
+ * - Host-checkable violations return a status synchronously and enqueue
+ *   nothing; nothing falls back silently ([vLLM-MLA] §Cutlass MLA and
+ *   [Triton-MLA] §Grenzen und Fehler: unsupported shapes are rejected).
+ *   Launch failures return MLA_ERR_HIP.  Device-side preconditions (slot and
+ *   page ids in range, unique slots, seq_lens within the block table) are not
+ *   checked on the host; an out-of-range id is clamped so that no access
+ *   leaves the caller's buffers, and the affected outputs are then undefined.
+ * - Only gfx950 is supported; on another device the calls return
+ *   MLA_ERR_DEVICE.
+ */
+#ifndef MLA_PAGED_LATENT_MLA_H
+#define MLA_PAGED_LATENT_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,     /* a size is outside the supported range */
+  MLA_ERR_DTYPE = 3,     /* unknown kv_dtype */
+  MLA_ERR_ALIGN = 4,     /* a pointer or stride is not 16-byte aligned */
+  MLA_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  MLA_ERR_HIP = 6,       /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_DEVICE = 7     /* the current device is not gfx950 */
+} mla_status_t;
+
+/* Cache row formats ([vLLM-MLA] §缓存的形状).
+ *   MLA_KV_BF16     : 576 bf16 values, 1152 bytes per row.
+ *   MLA_KV_FP8_E4M3 : 576 OCP e4m3fn codes, then float32 k_scale, then float32
+ *                     v_scale; 584 bytes per row.  K = code * k_scale (all 576),
+ *                     V = code * v_scale (first 512). */
+enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 };
+
+#define MLA_KV_LORA_RANK 512   /* L  */
+#define MLA_ROPE_DIM 64        /* R  */
+#define MLA_ROW_ELEMS 576      /* L + R */
+#define MLA_QK_NOPE_DIM 128    /* P  */
+#define MLA_V_HEAD_DIM 128     /* V  */
+#define MLA_PAGE_TOKENS 64     /* tokens per cache page ([vLLM-MLA] §FlashMLA: 64 only) */
+#define MLA_MAX_HEADS 128      /* query heads per call ([vLLM-MLA] §Cutlass MLA: MAX_HEADS) */
+#define MLA_ROW_BYTES_BF16 1152
+#define MLA_ROW_BYTES_FP8 584
+
+/* Upper bound on (request, split) pairs the automatic split planner creates
+ * beyond one per request; it bounds the workspace of num_splits == 0. */
+#define MLA_AUTO_MAX_EXTRA_PAIRS 1024
+
+/*
+ * mla_cache_write -- concat-and-cache scatter ([vLLM-MLA] §写缓存: latent and
+ * k_pe of a token are written into one cache row by one kernel, at
+ * slot_mapping[t]).
+ *
+ *   kv_c          bf16 [T, 512], row stride kv_c_stride_t (>= 512, multiple of 8)
+ *   k_pe          bf16 [T, 64],  row stride k_pe_stride_t (>= 64, multiple of 8)
+ *   slot_mapping  int64 [T] (device): slot = page * 64 + offset; slot < 0 skips
+ *                 the token (padding).  Slots must be unique.
+ *   kv_cache      pool [num_pages, 64, row] of kv_dtype rows (1152 or 584 bytes)
+ *
+ * bf16: the row is a bit copy of [kv_c | k_pe].  fp8: per token, amax over the
+ * 576 values, s = amax / 448 (IEEE float32 division; s = 1 if amax == 0),
+ * code_i = e4m3fn(x_i / s) rounded to nearest-even with saturation to +-448,
+ * and s is stored in both scale slots.  Pointers 16-byte aligned.  T may be 0.
+ */
+mla_status_t mla_cache_write(const void* kv_c, int64_t kv_c_stride_t,
+                             const void* k_pe, int64_t k_pe_stride_t,
+                             const int64_t* slot_mapping, int64_t T,
+                             void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                             void* stream);
+
+/*
+ * mla_absorb_q -- query absorption ([vLLM-MLA] §权重准备 and §两套算法:
+ * q_l = q_nope . W_UK_T per head with W_UK_T laid out [N, P, L]; [TRTLLM-TP]
+ * §吸收: the product is written straight into a [T, N, L + R] fused query whose
+ * tail holds q_pe).
+ *
+ *   q_nope  bf16 [T, N, 128], strides (qn_stride_t, qn_stride_h)
+ *   q_pe    bf16 [T, N, 64],  strides (qp_stride_t, qp_stride_h); may be NULL,
+ *           then only the first 512 elements of each q_fused row are written
+ *   w_uk_t  bf16 [N, 128, 512], contiguous
+ *   q_fused bf16 [T, N, 576], strides (qf_stride_t, qf_stride_h)
+ *
+ * q_fused[t,h,0:512] = bf16_rne(sum_p q_nope[t,h,p] * W_UK_T[h,p,:]) with
+ * float32 accumulation; q_fused[t,h,512:576] = q_pe[t,h,:].
+ * 1 <= N <= 128, T >= 0.  Pointers 16-byte aligned, strides multiples of 8.
+ */
+mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+                          const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+                          const void* w_uk_t, int64_t T, int32_t N,
+                          void* q_fused, int64_t qf_stride_t, int64_t qf_stride_h,
+                          void* stream);
+
+/*
+ * mla_decode_workspace_size -- bytes of workspace mla_decode needs for this
+ * batch shape and split mode (see num_splits below).  Returns 0 for shapes
+ * mla_decode would reject.  Pure host arithmetic; no device call.
+ */
+size_t mla_decode_workspace_size(int32_t B, int32_t q_len, int32_t N, int32_t num_splits);
+
+/*
+ * mla_decode -- paged split-KV absorbed-MQA decode with an LSE split merge
+ * ([vLLM-MLA] §两套算法 data-movement-friendly form, §FlashMLA, §Triton MLA;
+ * [Triton-MLA] §Datenfluss).
+ *
+ *   q            bf16 [B, q_len, N, 576] absorbed query, strides
+ *                (q_stride_b, q_stride_t, q_stride_h); last dim contiguous
+ *   kv_cache     pool [num_pages, 64, row] (kv_dtype rows)
+ *   block_table  int32 [B, max_pages_per_seq], row stride bt_stride_b: logical
+ *                page j of request b is physical page block_table[b][j];
+ *                entries past ceil(seq_lens[b] / 64) are never read
+ *   seq_lens     int32 [B] (device): cached tokens of request b INCLUDING the
+ *                q_len new ones; query row t sees tokens
+ *                [0, seq_lens[b] - q_len + 1 + t) (causal within the q_len
+ *                block, [vLLM-MLA] §Triton MLA); a row that sees no token gets
+ *                o = 0 and lse = -inf
+ *   softmax_scale  applied to q.k (pass 1/sqrt(192) for DeepSeek-V3: the scale
+ *                keeps the un-absorbed 192-wide value, [vLLM-MLA] §两套算法)
+ *   num_splits   0 = automatic plan from seq_lens and the device's compute
+ *                units; 1 = one split per request (batch-invariant reduction
+ *                order, [vLLM-MLA] §FlashMLA batch-invariance); k > 1 = each
+ *                request split into up to k page-aligned pieces (k <= 4096)
+ *   workspace    device scratch of at least mla_decode_workspace_size() bytes,
+ *                256-byte aligned; its contents need no initialisation
+ *   out          bf16 [B, q_len, N, 512], strides (o_stride_b, o_stride_t,
+ *                o_stride_h); last dim contiguous
+ *   lse          float32 [B, q_len, N] contiguous: natural-log log-sum-exp of
+ *                the scaled scores ([Triton-MLA] §Entwurfsmotivation)
+ *
+ * Limits: 1 <= B, q_len in {1, 2}, 1 <= N <= 128.  q, out, kv_cache and
+ * workspace 16-byte aligned (workspace 256), strides multiples of 8.  The
+ * result is deterministic for fixed inputs and num_splits; across different
+ * batch compositions only num_splits == 1 keeps bit-identical per-request
+ * results.  No host synchronisation, no allocation.
+ */
+mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_t, int64_t q_stride_h,
+                        const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                        const int32_t* block_table, int64_t bt_stride_b, int32_t max_pages_per_seq,
+                        const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t N,
+                        float softmax_scale, int32_t num_splits,
+                        void* workspace, size_t workspace_bytes,
+                        void* out, int64_t o_stride_b, int64_t o_stride_t, int64_t o_stride_h,
+                        float* lse, void* stream);
+
+/*
+ * mla_up_v -- per-head V up-projection of the latent attention output
+ * ([vLLM-MLA] §两套算法, _v_up_proj: [N, T, L] @ W_UV[N, L, V] written through a
+ * transposed view into a token-major [T, N * V] buffer).
+ *
+ *   o_lat  bf16 [T, N, 512], strides (ol_stride_t, ol_stride_h)
+ *   w_uv   bf16 [N, 512, 128], contiguous
+ *   out    bf16 [T, N * 128]: head h of token t at out + t*out_stride_t + h*128
+ *
+ * out[t, h*128 + v] = bf16_rne(sum_l o_lat[t,h,l] * W_UV[h,l,v]), float32
+ * accumulation.  1 <= N <= 128, T >= 0.  16-byte alignment as above.
+ */
+mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t ol_stride_h,
+                      const void* w_uv, int64_t T, int32_t N,
+                      void* out, int64_t out_stride_t, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_str(mla_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_LATENT_MLA_H */

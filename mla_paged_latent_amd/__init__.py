@@ -1,0 +1,168 @@
+"""MI355X (gfx950) MLA paged-latent decode: thin Python binding over the C ABI.
+
+Every step of the path runs in the HIP library ``libmla_paged_latent.so`` built
+from ``mla_paged_latent_amd/csrc``; this module only marshals torch tensors into
+pointers, strides and the current HIP stream, and allocates outputs/workspace
+when the caller does not pass them.  There is no CPU fallback: if the library is
+missing, :func:`lib` raises.
+
+The four calls mirror ``include/mla.h``: :func:`cache_write`, :func:`absorb_q`,
+:func:`decode` and :func:`up_v`, plus :func:`decode_workspace_size`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_paged_latent.so")
+
+KV_BF16 = 0
+KV_FP8 = 1
+KV_LORA_RANK = 512
+ROPE_DIM = 64
+ROW_ELEMS = 576
+PAGE_TOKENS = 64
+ROW_BYTES = {KV_BF16: 1152, KV_FP8: 584}
+DEFAULT_SCALE = 192 ** -0.5
+
+_STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",
+           4: "MLA_ERR_ALIGN", 5: "MLA_ERR_WORKSPACE", 6: "MLA_ERR_HIP", 7: "MLA_ERR_DEVICE"}
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} failed: {_STATUS.get(status, status)} ({lib().mla_status_str(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m mla_paged_latent_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    L.mla_cache_write.argtypes = [vp, i64, vp, i64, vp, i64, vp, i32, i64, vp]
+    L.mla_cache_write.restype = i32
+    L.mla_absorb_q.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i32, vp, i64, i64, vp]
+    L.mla_absorb_q.restype = i32
+    L.mla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.mla_decode_workspace_size.restype = ctypes.c_size_t
+    L.mla_decode.argtypes = [vp, i64, i64, i64, vp, i32, i64, vp, i64, i32, vp, i32, i32, i32,
+                             ctypes.c_float, i32, vp, ctypes.c_size_t, vp, i64, i64, i64, vp, vp]
+    L.mla_decode.restype = i32
+    L.mla_up_v.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, vp]
+    L.mla_up_v.restype = i32
+    L.mla_status_str.argtypes = [i32]
+    L.mla_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(call: str, status: int):
+    if status != 0:
+        raise MLAError(call, status)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def cache_write(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
+                kv_cache: torch.Tensor, kv_dtype: int, stream=None) -> None:
+    """Scatter rows ``[kv_c | k_pe]`` into ``kv_cache`` at ``slot_mapping`` (see mla.h).
+
+    ``kv_c`` bf16 ``[T, 512]``, ``k_pe`` bf16 ``[T, 64]`` or ``[T, 1, 64]``,
+    ``slot_mapping`` int64 ``[T]``, ``kv_cache`` the page pool (any dtype; its
+    byte size gives the page count).
+    """
+    k_pe = k_pe.reshape(k_pe.shape[0], -1)
+    assert kv_c.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16
+    assert slot_mapping.dtype == torch.int64 and kv_c.stride(-1) == 1 and k_pe.stride(-1) == 1
+    T = kv_c.shape[0]
+    num_pages = kv_cache.numel() * kv_cache.element_size() // (PAGE_TOKENS * ROW_BYTES[kv_dtype])
+    _check("mla_cache_write", lib().mla_cache_write(
+        _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(slot_mapping), T,
+        _ptr(kv_cache), kv_dtype, num_pages, _stream(stream)))
+
+
+def absorb_q(q_nope: torch.Tensor, q_pe: torch.Tensor | None, w_uk_t: torch.Tensor,
+             q_fused: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """``q_fused[t,h] = [q_nope[t,h] . W_UK_T[h] | q_pe[t,h]]`` (bf16 ``[T, N, 576]``)."""
+    T, N, P = q_nope.shape
+    assert P == 128 and q_nope.dtype == torch.bfloat16 and w_uk_t.is_contiguous()
+    assert w_uk_t.shape == (N, 128, KV_LORA_RANK) and w_uk_t.dtype == torch.bfloat16
+    width = ROW_ELEMS if q_pe is not None else KV_LORA_RANK
+    if q_fused is None:
+        q_fused = torch.empty((T, N, width), dtype=torch.bfloat16, device=q_nope.device)
+    qp_st = q_pe.stride(0) if q_pe is not None else 0
+    qp_sh = q_pe.stride(1) if q_pe is not None else 0
+    _check("mla_absorb_q", lib().mla_absorb_q(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), qp_st, qp_sh,
+        _ptr(w_uk_t), T, N, _ptr(q_fused), q_fused.stride(0), q_fused.stride(1), _stream(stream)))
+    return q_fused
+
+
+def decode_workspace_size(B: int, q_len: int, N: int, num_splits: int = 0) -> int:
+    return int(lib().mla_decode_workspace_size(B, q_len, N, num_splits))
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_dtype: int, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, softmax_scale: float = DEFAULT_SCALE, num_splits: int = 0,
+           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Absorbed-MQA decode over the paged cache.
+
+    ``q`` bf16 ``[B, q_len, N, 576]``; ``block_table`` int32 ``[B, max_pages]``;
+    ``seq_lens`` int32 ``[B]``.  Returns ``out`` bf16 ``[B, q_len, N, 512]`` and
+    ``lse`` float32 ``[B, q_len, N]``.
+    """
+    B, q_len, N, D = q.shape
+    assert D == ROW_ELEMS and q.dtype == torch.bfloat16 and q.stride(-1) == 1
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.stride(-1) == 1
+    num_pages = kv_cache.numel() * kv_cache.element_size() // (PAGE_TOKENS * ROW_BYTES[kv_dtype])
+    if out is None:
+        out = torch.empty((B, q_len, N, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, q_len, N), dtype=torch.float32, device=q.device)
+    need = decode_workspace_size(B, q_len, N, num_splits)
+    if need == 0:
+        raise MLAError("mla_decode_workspace_size", 2)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("mla_decode", lib().mla_decode(
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2), _ptr(kv_cache), kv_dtype, num_pages,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1], _ptr(seq_lens),
+        B, q_len, N, float(softmax_scale), num_splits, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0), out.stride(1),
+        out.stride(2), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def up_v(o_lat: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """``out[t, h*128:(h+1)*128] = o_lat[t,h] . W_UV[h]`` (bf16 ``[T, N*128]``)."""
+    T, N, Lr = o_lat.shape
+    assert Lr == KV_LORA_RANK and o_lat.dtype == torch.bfloat16 and o_lat.stride(-1) == 1
+    assert w_uv.shape == (N, KV_LORA_RANK, 128) and w_uv.is_contiguous()
+    if out is None:
+        out = torch.empty((T, N * 128), dtype=torch.bfloat16, device=o_lat.device)
+    _check("mla_up_v", lib().mla_up_v(
+        _ptr(o_lat), o_lat.stride(0), o_lat.stride(1), _ptr(w_uv), T, N, _ptr(out),
+        out.stride(0), _stream(stream)))
+    return out

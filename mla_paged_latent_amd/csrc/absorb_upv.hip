@@ -1,0 +1,174 @@
+// Per-head batched contractions around the decode kernel:
+//   mla_absorb_q : q_fused[t,h,0:512] = q_nope[t,h,:] . W_UK_T[h]   (K = 128, N = 512)
+//                  q_fused[t,h,512:576] = q_pe[t,h,:]
+//   mla_up_v     : out[t, h*128 : h*128+128] = o_lat[t,h,:] . W_UV[h] (K = 512, N = 128)
+// Source: "vLLM 源码完全拆解(三十七):MLA 注意力后端", §权重准备 (W_UK_T is [N, P, L],
+// W_UV is [N, L, V], one batched GEMM over heads) and §两套算法 (absorption into the
+// query; _v_up_proj writing token-major through a transposed view); "TensorRT-LLM
+// 源码完全拆解(十二)", §吸收 (the absorbed query is written into the front of a
+// [T, N, L + R] buffer whose tail holds q_pe).
+//
+// Both weights are stored [K][N] with N contiguous while the MFMA wants K contiguous
+// per lane, so a workgroup stages its head's [K x NT] weight tile in LDS and reads it
+// with ds_read_b64_tr_b16 (a 4-row x 16-column transpose per 16 lanes).  The product
+// is formed transposed, D^T[n][t] = W^T[n][k] . A^T[k][t], on 32x32x16 bf16 MFMAs:
+// W^T is the A operand (rows n), activation rows come straight from HBM as the B
+// operand (16 contiguous bytes of one token row per lane), and each lane of the
+// accumulator holds 4 consecutive n of one token, stored as 8 contiguous bytes.
+#include "mla_common.h"
+#include "mla_host.h"
+
+namespace mla {
+
+template <int KK, int NN, int NT, int KSPLIT>
+struct GemmCfg {
+  static constexpr int kNB = NT / 32;                 // 32-wide n blocks per tile
+  static_assert(kNB * KSPLIT == 4, "4 waves per workgroup");
+  static constexpr int kKPerWave = KK / KSPLIT;
+  static constexpr int kKSteps = kKPerWave / 16;
+  static constexpr int kRowBytes = NT * 2 + 32;       // padded LDS row: 4 rows hit disjoint banks
+  static constexpr int kTileBytes = KK * kRowBytes;
+  static constexpr int kRedBytes = (KSPLIT > 1) ? (kNB * 32 * 32 * 4) : 0;
+  static constexpr int kLdsBytes = kTileBytes + kRedBytes;
+};
+
+// grid = (NN / NT, N heads); block = 256 threads.
+template <int KK, int NN, int NT, int KSPLIT, bool COPY_PE>
+__global__ __launch_bounds__(256) void head_gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // [T, N, KK]
+    const uint16_t* __restrict__ W,                                   // [N, KK, NN]
+    uint16_t* __restrict__ C, int64_t c_st, int64_t c_sh,            // [T, N, NN]
+    const uint16_t* __restrict__ pe, int64_t pe_st, int64_t pe_sh,   // [T, N, 64] (COPY_PE)
+    int64_t T) {
+  using Cfg = GemmCfg<KK, NN, NT, KSPLIT>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+
+  const int h = blockIdx.y;
+  const int n0 = blockIdx.x * NT;
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+
+  // stage W[h][0:KK][n0:n0+NT] into LDS (row-padded)
+  const uint16_t* wh = W + (int64_t)h * KK * NN + n0;
+  constexpr int kChunksPerRow = NT / 8;
+  for (int i = tid; i < KK * kChunksPerRow; i += 256) {
+    const int k = i / kChunksPerRow, c = i % kChunksPerRow;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)k * NN + c * 8);
+    *reinterpret_cast<MLA_LDS u32x4_t*>(lds + k * Cfg::kRowBytes + c * 16) = v;
+  }
+  if (COPY_PE && blockIdx.x == 0) {
+    for (int64_t i = tid; i < T * 8; i += 256) {
+      const int64_t t = i >> 3;
+      const int c = (int)(i & 7);
+      const uint4 v = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + c * 8);
+      *reinterpret_cast<uint4*>(C + t * c_st + h * c_sh + NN + c * 8) = v;
+    }
+  }
+  lds_barrier();
+
+  const int nb = w % Cfg::kNB;          // n block of this wave
+  const int kh = w / Cfg::kNB;          // K slice of this wave
+  const int g = l >> 4, lg = l & 15;
+  // transpose-read address pieces: 16-lane group g covers n = 16*(g&1) + [0,16) and
+  // k rows 8*(g>>1) + 4*r + (lg>>2) for read r; lane supplies column 4*(lg&3).
+  const uint32_t tr_col = (uint32_t)((nb * 32 + 16 * (g & 1) + 4 * (lg & 3)) * 2);
+  const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
+
+  for (int64_t tb = 0; tb < T; tb += 32) {
+    const int64_t trow = tb + (l & 31);
+    const bool t_ok = trow < T;
+    const uint16_t* arow = A + (t_ok ? trow : 0) * a_st + h * a_sh;
+    f32x16_t acc = {};
+#pragma unroll 4
+    for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
+      const int k0 = kh * Cfg::kKPerWave + ks * 16;
+      bf16x8_t b = {};
+      if (t_ok) b = *reinterpret_cast<const bf16x8_t*>(arow + k0 + 8 * (l >> 5));
+      const uint32_t r0 = (uint32_t)((k0 + tr_row0) * Cfg::kRowBytes) + tr_col;
+      const bf16x4_t lo = lds_read_tr16(lds, r0);
+      const bf16x4_t hi = lds_read_tr16(lds, r0 + 4 * Cfg::kRowBytes);
+      const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    if constexpr (KSPLIT > 1) {
+      // waves with kh > 0 hand their partial tile to the kh == 0 wave of the same n block
+      MLA_LDS float* red = reinterpret_cast<MLA_LDS float*>(lds + Cfg::kTileBytes);
+      if (kh == 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[(nb * 16 + i) * 64 + l] = acc[i];
+      }
+      lds_barrier();
+      if (kh == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += red[(nb * 16 + i) * 64 + l];
+      }
+      lds_barrier();
+    }
+    if (kh == 0 && t_ok) {
+      uint16_t* crow = C + trow * c_st + h * c_sh + n0 + nb * 32 + 4 * (l >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x4_t v = {(__bf16)acc[4 * i], (__bf16)acc[4 * i + 1], (__bf16)acc[4 * i + 2],
+                            (__bf16)acc[4 * i + 3]};
+        *reinterpret_cast<bf16x4_t*>(crow + 8 * i) = v;
+      }
+    }
+  }
+}
+
+}  // namespace mla
+
+extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+                                     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+                                     const void* w_uk_t, int64_t T, int32_t N, void* q_fused,
+                                     int64_t qf_stride_t, int64_t qf_stride_h, void* stream) {
+  using namespace mla;
+  if (T < 0 || N < 1 || N > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!q_nope || !w_uk_t || !q_fused) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk_t) || !aligned16(q_fused) || !mult8(qn_stride_t) ||
+      !mult8(qn_stride_h) || !mult8(qf_stride_t) || !mult8(qf_stride_h))
+    return MLA_ERR_ALIGN;
+  if (q_pe && (!aligned16(q_pe) || !mult8(qp_stride_t) || !mult8(qp_stride_h))) return MLA_ERR_ALIGN;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid(MLA_KV_LORA_RANK / 128, N);
+  if (q_pe)
+    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, true>), grid, dim3(256), 0, s,
+                       (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
+                       (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)q_pe,
+                       qp_stride_t, qp_stride_h, T);
+  else
+    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, false>), grid, dim3(256), 0, s,
+                       (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
+                       (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)nullptr,
+                       (int64_t)0, (int64_t)0, T);
+  return launch_status();
+}
+
+extern "C" mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t ol_stride_h,
+                                 const void* w_uv, int64_t T, int32_t N, void* out,
+                                 int64_t out_stride_t, void* stream) {
+  using namespace mla;
+  if (T < 0 || N < 1 || N > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (out_stride_t < (int64_t)N * MLA_V_HEAD_DIM) return MLA_ERR_SHAPE;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out) || !mult8(ol_stride_t) ||
+      !mult8(ol_stride_h) || !mult8(out_stride_t))
+    return MLA_ERR_ALIGN;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid(MLA_V_HEAD_DIM / 64, N);
+  hipLaunchKernelGGL((head_gemm_kernel<512, 128, 64, 2, false>), grid, dim3(256), 0, s,
+                     (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv,
+                     (uint16_t*)out, out_stride_t, (int64_t)MLA_V_HEAD_DIM,
+                     (const uint16_t*)nullptr, (int64_t)0, (int64_t)0, T);
+  return launch_status();
+}

@@ -1,0 +1,129 @@
+// Shared device helpers for the gfx950 MLA kernels: vector types, bf16 and
+// e4m3fn conversions, LDS primitives, and the swizzled LDS layout of a cache page.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace mla {
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kRow = 576;
+constexpr int kPage = 64;
+constexpr int kRowBytesBf16 = 1152;
+constexpr int kRowBytesFp8 = 584;
+constexpr int kChunksPerRow = 72;                     // 16-byte chunks in a bf16 row
+constexpr int kPageBytesBf16 = kPage * kRowBytesBf16; // 73728
+constexpr int kPageBytesFp8 = kPage * kRowBytesFp8;   // 37376
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Wave / workgroup primitives
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// Workgroup barrier without a memory fence: waits for this wave's LDS ops, then
+// s_barrier.  Global->LDS DMA completion is handled separately with vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// ---------------------------------------------------------------------------
+// LDS access with explicit address space
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8_t lds_read_b128(const MLA_LDS char* base, uint32_t byte_off) {
+  return *reinterpret_cast<const MLA_LDS bf16x8_t*>(base + byte_off);
+}
+
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const MLA_LDS char* base, uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      reinterpret_cast<MLA_LDS bf16x4_t*>(const_cast<MLA_LDS char*>(base) + byte_off));
+}
+
+__device__ __forceinline__ void dma_16B(const void* src, MLA_LDS char* dst_wave_base) {
+  // Each lane's 16 bytes land at dst_wave_base + 16 * lane.
+  __builtin_amdgcn_global_load_lds(src, reinterpret_cast<MLA_LDS void*>(dst_wave_base), 16, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Page layout in LDS.  A bf16 page is 64 token rows x 72 chunks of 16 B (8 bf16).
+// It is stored column-group major: group G = c >> 3 (128 B of every row) holds the
+// 64 tokens x 8 chunks, and inside a group chunk c of token t sits at position
+// t*8 + ((c & 7) ^ s(t)) with s(t) = ((t & 3) << 1) | ((t >> 2) & 1):
+//     slot(t, c) = (c >> 3) * 512 + t * 8 + ((c & 7) ^ s(t)),  byte = 16 * slot.
+// s is a bijection on t mod 8, so a ds_read_b128 by 8 consecutive tokens at one
+// chunk hits 8 distinct 16-byte bank groups, and a transpose read of 4 consecutive
+// tokens x 2 adjacent chunks (c even, c + 1) does too (s(t) >> 1 differs across
+// the 4).  A 1 KiB DMA instruction k fills group k >> 3, tokens 8*(k & 7) .. +7,
+// so each lane's global offset is a per-lane constant plus a wave-uniform term.
+// ---------------------------------------------------------------------------
+constexpr int kGroupSlots = 512;                      // 64 tokens x 8 chunks
+constexpr int kGroupBytes = kGroupSlots * 16;         // 8192
+
+__device__ __forceinline__ int page_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+__device__ __forceinline__ int page_slot(int t, int c) {
+  return (c >> 3) * kGroupSlots + t * 8 + ((c & 7) ^ page_swz(t));
+}
+
+// ---------------------------------------------------------------------------
+// Number formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// OCP e4m3fn encode of a finite float: round to nearest, ties to even; magnitudes
+// beyond the largest finite value saturate to +-448; the sign bit is kept.
+// Codes are monotonic in magnitude, so rounding into the next binade or from the
+// subnormal range into the smallest normal falls out of the integer arithmetic.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  uint32_t bits = __float_as_uint(x);
+  uint32_t sign = (bits >> 24) & 0x80u;
+  float a = __uint_as_float(bits & 0x7fffffffu);
+  uint32_t code;
+  if (a >= 0.015625f) {                                  // 2^-6: normal range
+    int e = (int)((bits >> 23) & 0xffu) - 127;           // floor(log2 a), a is normal in fp32
+    if (e > 8) {
+      code = 0x7eu;
+    } else {
+      float m = __builtin_ldexpf(a, 3 - e);              // in [8, 16), exact scaling
+      uint32_t r = (uint32_t)__builtin_rintf(m);         // ties to even; 8..16
+      code = ((uint32_t)(e + 7) << 3) + (r - 8u);
+      code = code > 0x7eu ? 0x7eu : code;
+    }
+  } else {
+    float m = a * 512.0f;                                // units of 2^-9, exact
+    code = (uint32_t)__builtin_rintf(m);                 // 0..8 (8 == smallest normal)
+  }
+  return sign | code;
+}
+
+}  // namespace mla

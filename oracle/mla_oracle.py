@@ -82,6 +82,19 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of float64 values, returned as float64.
+
+    Used where the pages' pipeline stores an intermediate as a bf16 tensor (the
+    absorbed query and the latent attention output are bf16 in the decode step,
+    [vLLM-MLA] §一次 decode step 的完整走查).  Finite inputs only.
+    """
+    v = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(v)                          # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.round(m * 256.0) / 256.0             # 8 significant bits, ties to even
+    return np.ldexp(q, e)
+
+
 def e4m3_value(code: np.ndarray) -> np.ndarray:
     """Value of OCP e4m3fn codes from the format definition.
 
@@ -171,6 +184,29 @@ def cache_write(pool: np.ndarray, kv_c_bits: np.ndarray, k_pe_bits: np.ndarray,
             out[page, off, n:n + 4] = np.array([s], "<f4").view(np.uint8)
             out[page, off, n + 4:n + 8] = np.array([s], "<f4").view(np.uint8)
             assert rb == n + 8
+    return out
+
+
+def encode_rows(rows_bits: np.ndarray, kv_dtype: int) -> np.ndarray:
+    """Cache-row bytes for many token rows at once: ``[n, 576]`` bf16 bits ->
+    ``[n, row_bytes]`` uint8.  The same definition as :func:`cache_write` applies
+    per row (bit copy for bf16; per-row amax scale and e4m3fn codes for fp8),
+    written with whole-array NumPy operations so full pools build quickly.
+    """
+    rows_bits = np.ascontiguousarray(rows_bits, dtype=np.uint16)
+    n, e = rows_bits.shape
+    if kv_dtype == KV_BF16:
+        return rows_bits.astype("<u2").view(np.uint8).reshape(n, 2 * e)
+    xf = bf16_bits_to_f64(rows_bits).astype(np.float32)
+    amax = np.max(np.abs(xf), axis=1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    q = (xf / s[:, None]).astype(np.float32)
+    out = np.empty((n, e + 8), dtype=np.uint8)
+    out[:, :e] = e4m3_encode(q)
+    sb = s.astype("<f4").view(np.uint8).reshape(n, 4)
+    out[:, e:e + 4] = sb
+    out[:, e + 4:e + 8] = sb
     return out
 
 

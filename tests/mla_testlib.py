@@ -1,0 +1,126 @@
+"""Helpers shared by the GPU parity tests: moving seeded workloads onto the
+device through the C ABI, building the oracle's view of the same inputs, and the
+tolerance checks.  Not collected by pytest (no test_ prefix)."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import mla_inputs as MI
+import mla_paged_latent_amd as M
+from oracle import mla_oracle as O
+
+# Output gate: max |o_gpu - o_ref| <= OUT_TOL * RMS(o_ref) over the whole output
+# of a call; LSE gate: max |lse_gpu - lse_ref| <= LSE_TOL (absolute, natural log).
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 tensor on cuda:0 (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def gpu_pool(w: MI.Workload, kv_dtype: int | None = None) -> torch.Tensor:
+    """The workload's whole pool written on the GPU by mla_cache_write (one call)."""
+    kd = w.kv_dtype if kv_dtype is None else kv_dtype
+    rb = M.ROW_BYTES[kd]
+    pool = torch.zeros((w.num_pages, 64, rb), dtype=torch.uint8, device="cuda")
+    rows = dev_bf16(w.kv_rows.reshape(-1, 576))
+    slots = torch.arange(w.num_pages * 64, dtype=torch.int64, device="cuda")
+    M.cache_write(rows[:, :512], rows[:, 512:], slots, pool, kd)
+    return pool
+
+
+def oracle_pool(w: MI.Workload, kv_dtype: int | None = None) -> np.ndarray:
+    kd = w.kv_dtype if kv_dtype is None else kv_dtype
+    return O.encode_rows(w.kv_rows.reshape(-1, 576), kd).reshape(w.num_pages, 64, -1)
+
+
+def step_write_new_tokens_gpu(w: MI.Workload, pool: torch.Tensor, kd: int) -> None:
+    rows = dev_bf16(w.new_rows)
+    M.cache_write(rows[:, :512], rows[:, 512:], torch.from_numpy(w.new_slots).cuda(), pool, kd)
+
+
+def step_write_new_tokens_oracle(w: MI.Workload, pool: np.ndarray, kd: int) -> np.ndarray:
+    return O.cache_write(pool, w.new_rows[:, :512], w.new_rows[:, 512:], w.new_slots, kd)
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bfloat16 ulp at |x| (8 significant bits): 2^(floor(log2|x|) - 8); 0 at 0."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 0.0)
+
+
+def check_out(o_gpu: np.ndarray, o_ref: np.ndarray, name: str, tol: float = OUT_TOL) -> float:
+    """Gate, per request b (axis 0): max(|o_gpu - o_ref| - half_ulp_bf16) <= tol * RMS(o_ref[b]).
+
+    Two readings of "max-abs error 2e-2 relative to output RMS" are fixed here:
+    * The output is a bf16 tensor, so even the exactly rounded result is off by up to
+      half a bf16 ulp of the value; on flat-softmax workloads max|o| reaches ~9 x RMS,
+      where that half ulp alone exceeds 2e-2 * RMS.  The tolerance bounds the error
+      beyond the output format's own rounding (half ulp at the larger of the two
+      magnitudes, which also covers a rounding flip at a midpoint).
+    * The RMS is that of each request's own output block: requests in a decode batch
+      are independent, and a batch-wide RMS would make a short request's verdict
+      depend on the lengths of the other requests it happens to share a call with.
+    Requests whose reference output is all zero (no visible token) must match exactly.
+    The raw max error and the whole-call ratio are reported too.
+    """
+    o_gpu = np.asarray(o_gpu, np.float64)
+    assert np.all(np.isfinite(o_gpu)), f"{name}: non-finite output"
+    diff = np.abs(o_gpu - o_ref)
+    excess_el = diff - bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(o_gpu)))
+    B = o_ref.shape[0]
+    worst = 0.0
+    for b in range(B):
+        rms_b = math.sqrt(float(np.mean(o_ref[b] ** 2)))
+        ex_b = float(np.max(excess_el[b]))
+        if rms_b == 0.0:
+            assert np.all(o_gpu[b] == 0.0), f"{name}: request {b} must be exactly zero"
+            continue
+        worst = max(worst, ex_b / rms_b)
+        assert ex_b <= tol * rms_b, f"{name}: request {b}: error beyond output rounding {ex_b} > {tol} * rms {rms_b}"
+    rms = math.sqrt(float(np.mean(o_ref ** 2)))
+    say(f"  [{name}] out max|err| = {float(np.max(diff)):.3e}; beyond bf16 half-ulp: worst request "
+        f"{worst:.3e} x its rms, whole call {float(np.max(excess_el)) / max(rms, 1e-30):.3e} x rms")
+    return worst
+
+
+def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, name: str, tol: float = LSE_TOL) -> float:
+    l_gpu = np.asarray(l_gpu, np.float64)
+    inf_ref = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l_gpu), inf_ref), f"{name}: -inf pattern differs"
+    fin = ~inf_ref
+    err = float(np.max(np.abs(l_gpu[fin] - l_ref[fin]))) if fin.any() else 0.0
+    say(f"  [{name}] lse max|err| = {err:.3e}")
+    assert err <= tol, f"{name}: lse err {err} > {tol}"
+    return err
+
+
+def gpu_decode(w: MI.Workload, pool: torch.Tensor, q_bits: np.ndarray, num_splits: int = 0,
+               seq_lens: np.ndarray | None = None, block_table: np.ndarray | None = None):
+    q = dev_bf16(q_bits)
+    bt = torch.from_numpy(w.block_table if block_table is None else block_table).cuda()
+    sl = torch.from_numpy((w.seq_lens if seq_lens is None else seq_lens).astype(np.int32)).cuda()
+    out, lse = M.decode(q, pool, w.kv_dtype, bt, sl, O.default_scale(), num_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)

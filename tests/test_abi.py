@@ -1,0 +1,107 @@
+"""The C-ABI library on the CPU: it loads, exports every call include/mla.h
+declares, sizes workspaces by pure host arithmetic, and rejects bad arguments
+with a status before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_paged_latent_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH),
+                                reason="HIP library not built (python -m mla_paged_latent_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    fns = declared_functions()
+    for f in ("mla_cache_write", "mla_absorb_q", "mla_decode", "mla_up_v",
+              "mla_decode_workspace_size", "mla_status_str"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    for f in declared_functions():
+        assert hasattr(L, f), f
+
+
+def test_status_strings():
+    L = M.lib()
+    for code in range(8):
+        assert L.mla_status_str(code).startswith(b"MLA_")
+    assert b"unknown" in L.mla_status_str(99)
+
+
+def test_workspace_size_arithmetic():
+    ws = M.decode_workspace_size
+    # invalid shapes give 0
+    assert ws(0, 1, 16, 0) == 0 and ws(4, 3, 16, 0) == 0 and ws(4, 1, 0, 0) == 0
+    assert ws(4, 1, 129, 0) == 0 and ws(4, 1, 16, -1) == 0 and ws(4, 1, 16, 5000) == 0
+    # partials dominate: pairs x head groups x rows x (512 + 1) floats
+    one = ws(32, 1, 128, 1)
+    assert one >= (32 + 8) * 1 * 128 * 513 * 4
+    assert ws(32, 1, 128, 8) > one
+    assert ws(32, 1, 128, 0) >= (32 + 1024 + 8) * 128 * 513 * 4
+    # q_len 2 with 128 heads needs two head groups of 128 rows
+    assert ws(8, 2, 128, 1) >= (8 + 8) * 2 * 128 * 513 * 4
+    assert ws(64, 1, 16, 1) >= (64 + 8) * 16 * 513 * 4
+    assert ws(64, 1, 16, 1) % 256 == 0
+
+
+def _decode_args(**over):
+    vp = ctypes.c_void_p
+    a = dict(q=vp(256), qsb=576, qst=576, qsh=576, kv=vp(256), kvd=0, pages=4, bt=vp(256),
+             btsb=4, maxp=4, seq=vp(256), B=1, ql=1, N=16, scale=0.07, ns=0, ws=vp(256),
+             wsb=1 << 30, out=vp(256), osb=512, ost=512, osh=512, lse=vp(256), stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+def test_decode_rejects_bad_arguments_before_any_device_call():
+    L = M.lib()
+    assert L.mla_decode(*_decode_args(kvd=7)) == 3                 # MLA_ERR_DTYPE
+    assert L.mla_decode(*_decode_args(ql=3)) == 2                  # MLA_ERR_SHAPE
+    assert L.mla_decode(*_decode_args(N=200)) == 2
+    assert L.mla_decode(*_decode_args(B=0)) == 2
+    assert L.mla_decode(*_decode_args(scale=0.0)) == 2
+    assert L.mla_decode(*_decode_args(scale=float("nan"))) == 2
+    assert L.mla_decode(*_decode_args(btsb=2)) == 2                # row stride < max pages
+    assert L.mla_decode(*_decode_args(q=None)) == 1                # MLA_ERR_NULL
+    assert L.mla_decode(*_decode_args(lse=None)) == 1
+    assert L.mla_decode(*_decode_args(ws=None)) == 5               # MLA_ERR_WORKSPACE
+    assert L.mla_decode(*_decode_args(wsb=100)) == 5
+    assert L.mla_decode(*_decode_args(q=ctypes.c_void_p(258))) == 4   # MLA_ERR_ALIGN
+    assert L.mla_decode(*_decode_args(qsh=577)) == 4
+    assert L.mla_decode(*_decode_args(ws=ctypes.c_void_p(272))) == 4  # workspace needs 256 B
+
+
+def test_other_calls_reject_bad_arguments():
+    L = M.lib()
+    vp = ctypes.c_void_p
+    p = vp(256)
+    # cache write
+    assert L.mla_cache_write(p, 512, p, 64, p, 4, p, 9, 4, None) == 3
+    assert L.mla_cache_write(p, 512, p, 64, p, 0, p, 0, 4, None) == 0      # T == 0 is a no-op
+    assert L.mla_cache_write(None, 512, p, 64, p, 4, p, 0, 4, None) == 1
+    assert L.mla_cache_write(p, 500, p, 64, p, 4, p, 0, 4, None) == 2
+    assert L.mla_cache_write(p, 520, p, 64, vp(260), 4, p, 0, 4, None) == 4
+    # absorb
+    assert L.mla_absorb_q(p, 128, 128, p, 64, 64, p, 4, 0, p, 576, 576, None) == 2
+    assert L.mla_absorb_q(p, 128, 128, None, 0, 0, p, 0, 16, p, 576, 576, None) == 0
+    assert L.mla_absorb_q(None, 128, 128, None, 0, 0, p, 4, 16, p, 576, 576, None) == 1
+    assert L.mla_absorb_q(p, 130, 128, None, 0, 0, p, 4, 16, p, 576, 576, None) == 4
+    # up_v
+    assert L.mla_up_v(p, 512, 512, p, 4, 129, p, 128 * 129, None) == 2
+    assert L.mla_up_v(p, 512, 512, p, 4, 16, p, 1024, None) == 2           # out row too short
+    assert L.mla_up_v(p, 512, 512, None, 4, 16, p, 2048, None) == 1

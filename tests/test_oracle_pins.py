@@ -427,3 +427,30 @@ def test_absorb_and_up_v_against_loops():
         for h in range(3):
             for v in range(4):
                 assert y[t, h, v] == pytest.approx(sum(ol[t, h, l] * wv[h, l, v] for l in range(5)), rel=1e-13)
+
+
+def test_encode_rows_matches_per_token_cache_write():
+    rng = np.random.default_rng(17)
+    rows = MI.to_bf16_bits((rng.standard_normal((128, 576)) * rng.uniform(0.01, 100, (128, 1))).astype(np.float32))
+    rows[5] = 0                                        # an all-zero row
+    for dt, rb in ((O.KV_BF16, 1152), (O.KV_FP8, 584)):
+        pool = O.cache_write(np.zeros((2, 64, rb), np.uint8), rows[:, :512], rows[:, 512:],
+                             np.arange(128), dt)
+        assert np.array_equal(pool.reshape(128, rb), O.encode_rows(rows, dt))
+
+
+def test_round_to_bf16_matches_torch():
+    rng = np.random.default_rng(18)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000),
+                        (rng.integers(-2**15, 2**15, 4000) + 0.5) * 2.0 ** -7])   # exact ties
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.round_to_bf16(x), ref)
+
+
+def test_bf16_half_ulp_helper():
+    from tests.mla_testlib import bf16_half_ulp
+    x = np.array([1.0, 1.99, 0.5, -3.0, 2.0 ** -20, 0.0])
+    assert np.array_equal(bf16_half_ulp(x), [2.0 ** -8, 2.0 ** -8, 2.0 ** -9, 2.0 ** -7, 2.0 ** -28, 0.0])
+    # the exactly rounded value is always within half an ulp
+    v = np.random.default_rng(0).standard_normal(10000)
+    assert np.all(np.abs(O.round_to_bf16(v) - v) <= bf16_half_ulp(v))
