@@ -1,0 +1,263 @@
+#!/usr/bin/env python
+"""Throughput of one MLA paged-latent decode step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic decode input, all in
+the HIP library: the new tokens' cache write, query absorption, paged split-KV
+decode (plan, split kernel, LSE merge) and the V up-projection.  Inputs are
+resident in HBM before timing starts.  The KV pool is replicated R times and the
+steps rotate over the copies so that the 256 MB Infinity Cache cannot serve one
+step's pages to the next.
+
+Prints ONE JSON line (stdout).  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mla_inputs as MI  # noqa: E402
+
+METRIC = "MLA decode tokens/s + achieved HBM TB/s (% roofline), 128 heads, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, published
+MALL_BYTES = 256 * 2**20
+DECODE_SRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc", "decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w: MI.Workload) -> tuple[int, float, int]:
+    """Bytes and flops a decode launch must move/compute, and the KV bytes alone.
+
+    Every cached row is read once and shared by all heads and query rows; the
+    query, output, LSE, block table and seq_lens are read/written once.  Flops:
+    N * (2*576 + 2*512) per visible (query row, token) pair.  Split partials,
+    LDS traffic and re-reads are implementation overhead and are not counted.
+    """
+    row = 1152 if w.kv_dtype == MI.KV_BF16 else 584
+    kv = int(w.seq_lens.astype(np.int64).sum()) * row
+    rows = w.B * w.q_len * w.N
+    io = rows * 576 * 2 + rows * 512 * 2 + rows * 4
+    pages = int(((w.seq_lens.astype(np.int64) + 63) // 64).sum())
+    meta = pages * 4 + w.B * 4
+    vis = 0
+    for b in range(w.B):
+        for t in range(w.q_len):
+            vis += max(0, int(w.seq_lens[b]) - w.q_len + 1 + t)
+    flops = float(vis) * w.N * (2 * 576 + 2 * 512)
+    return kv + io + meta, flops, kv
+
+
+def traffic_record(workload: str):
+    """HBM bytes per decode launch measured with rocprofv3 PMC counters, if the
+    committed record matches the current decode kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("decode_hip_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: MI.Workload, budget_s: float = 12.0) -> dict:
+    """The oracle (float64 NumPy) running the same step on this host's cores."""
+    from oracle import mla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    cores = min(len(os.sched_getaffinity(0)), blas)
+    kd = w.kv_dtype
+    pool = O.encode_rows(w.kv_rows.reshape(-1, 576), kd).reshape(w.num_pages, 64, -1)
+    T = w.B * w.q_len
+    sc = O.default_scale()
+
+    def step():
+        p = O.cache_write(pool, w.new_rows[:, :512], w.new_rows[:, 512:], w.new_slots, kd)
+        if w.q is None:
+            q = O.round_to_bf16(O.absorb(O.bf16_bits_to_f64(w.q_nope.reshape(T, w.N, 128)),
+                                         O.bf16_bits_to_f64(w.q_pe.reshape(T, w.N, 64)),
+                                         O.bf16_bits_to_f64(w.w_uk_t))).reshape(w.B, w.q_len, w.N, 576)
+        else:
+            q = O.bf16_bits_to_f64(w.q)
+        o, _ = O.decode(q, p, kd, w.block_table, w.seq_lens, sc)
+        if w.w_uv is not None:
+            O.up_v(O.round_to_bf16(o).reshape(T, w.N, 512), O.bf16_bits_to_f64(w.w_uv))
+
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all >= budget_s or len(times) >= 20:
+            break
+    mean = sum(times) / len(times)
+    return {"value": T / mean, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full {w.name} batch ({w.B} requests x q_len {w.q_len}) through the "
+                      f"float64 oracle step (cache write, absorb, decode, up-projection), "
+                      f"{len(times)} repetition(s), mean {mean:.3f} s"}
+
+
+def run(args) -> dict:
+    import torch
+    import mla_paged_latent_amd as M
+
+    w = MI.CONFIGS[args.workload]()
+    kd = w.kv_dtype
+    dev = torch.device("cuda:0")
+    T = w.B * w.q_len
+    bytes_alg, flops_alg, kv_bytes = algorithmic_work(w)
+    row = M.ROW_BYTES[kd]
+    # enough pool copies that consecutive reuse of one copy is >= 3 MALL capacities apart
+    R = min(8, max(2, math.ceil(3 * MALL_BYTES / max(kv_bytes, 1))))
+    log(f"[bench] workload {w.name}: B={w.B} q_len={w.q_len} N={w.N} kv={'bf16' if kd == 0 else 'fp8'} "
+        f"pages={w.num_pages} KV bytes/step={kv_bytes / 1e6:.1f} MB, pool copies={R}")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    rows = bf16(w.kv_rows.reshape(-1, 576))
+    slots = torch.arange(w.num_pages * 64, dtype=torch.int64, device=dev)
+    pools = []
+    for _ in range(R):
+        pool = torch.empty((w.num_pages, 64, row), dtype=torch.uint8, device=dev)
+        M.cache_write(rows[:, :512], rows[:, 512:], slots, pool, kd)
+        pools.append(pool)
+    del rows, slots
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    new = bf16(w.new_rows)
+    new_slots = torch.from_numpy(w.new_slots).to(dev)
+    with_w = w.w_uk_t is not None
+    if with_w:
+        q_nope = bf16(w.q_nope.reshape(T, w.N, 128))
+        q_pe = bf16(w.q_pe.reshape(T, w.N, 64))
+        w_uk_t = bf16(w.w_uk_t)
+        w_uv = bf16(w.w_uv)
+        qf = torch.empty((T, w.N, 576), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T, w.N * 128), dtype=torch.bfloat16, device=dev)
+    else:
+        qf = bf16(w.q.reshape(T, w.N, 576))
+    out = torch.empty((w.B, w.q_len, w.N, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.q_len, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.decode_workspace_size(w.B, w.q_len, w.N, args.num_splits), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i: int, timed: bool):
+        pool = pools[i % R]
+        M.cache_write(new[:, :512], new[:, 512:], new_slots, pool, kd)
+        if with_w:
+            M.absorb_q(q_nope, q_pe, w_uk_t, q_fused=qf)
+        if timed:
+            ev[i][0].record()
+        M.decode(qf.view(w.B, w.q_len, w.N, 576), pool, kd, bt, sl, M.DEFAULT_SCALE, args.num_splits,
+                 workspace=ws, out=out, lse=lse)
+        if timed:
+            ev[i][1].record()
+        if with_w:
+            M.up_v(out.view(T, w.N, 512), w_uv, out=y)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i, True)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_mean = sum(dec_ms) / len(dec_ms)
+    dec_med = sorted(dec_ms)[len(dec_ms) // 2]
+    log(f"[bench] step {ms_step * 1e3:.1f} us, mla_decode mean {dec_mean * 1e3:.1f} us "
+        f"(median {dec_med * 1e3:.1f}, min {min(dec_ms) * 1e3:.1f}, max {max(dec_ms) * 1e3:.1f})")
+
+    achieved = bytes_alg / (dec_mean * 1e-3) / 1e9
+    tflops = flops_alg / (dec_mean * 1e-3) / 1e12
+    t_hbm = bytes_alg / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_alg / (MFMA_BF16_PEAK_TFS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4)}
+    roof["traffic"] = traffic_record(args.workload)
+    roof["kernel"] = "mla_decode (plan + split-KV decode + LSE merge)"
+    roof["algorithmic_bytes"] = bytes_alg
+    roof["algorithmic_flops"] = flops_alg
+    roof["mean_launch_us"] = round(dec_mean * 1e3, 2)
+    roof["mfma_frac_bf16"] = round(tflops / MFMA_BF16_PEAK_TFS, 4)
+    roof["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if kd == MI.KV_BF16 else "fp8-e4m3 cache, bf16 mfma",
+        "data": "synthetic (seeded N(0,1) latents/queries, N(0,1/512) weights; random page placement)",
+        "config": {"workload": f"{w.name}: B={w.B}, q_len={w.q_len}, heads={w.N}, "
+                               f"seq_lens={'all ' + str(int(w.seq_lens[0])) if len(set(w.seq_lens.tolist())) == 1 else 'mixed'}, "
+                               f"kv={'bf16' if kd == 0 else 'fp8'} 576-d rows, 64-token pages, "
+                               f"absorb + decode + up-proj",
+                   "batch": w.B, "q_len": w.q_len, "heads": w.N, "kv_tokens": w.tokens,
+                   "num_splits": args.num_splits, "pool_copies": R},
+        "decode_latent_kv_tbs": round(kv_bytes / (dec_mean * 1e-3) / 1e12, 3),
+        "roofline": roof,
+    }
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="full_head", choices=sorted(MI.CONFIGS))
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode path shards by "
+                                   "request (attention-DP) or heads (TP) with no exchange inside the "
+                                   "path, so only --gpus 1 is measured"}), flush=True)
+        sys.exit(2)
+    res = run(args)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(MI.CONFIGS[args.workload]())
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

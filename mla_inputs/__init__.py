@@ -39,9 +39,13 @@ KV_BF16, KV_FP8 = 0, 1
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 draws to bfloat16 bit patterns (nearest, ties to even)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
-    return u.astype(np.uint16)
+    # finite inputs only: u + 0x8000 cannot wrap for any finite float32 pattern
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 @dataclasses.dataclass
