@@ -177,9 +177,27 @@ __device__ __forceinline__ void issue_page_fp8(const char* page, MLA_LDS char* d
   }
 }
 
-__device__ __forceinline__ const char* page_ptr(const DecodeParams& p, int b, int pg, bool fp8) {
-  int id = p.block_table[(int64_t)b * p.bt_sb + pg];
-  id = (id < 0 || id >= p.num_pages) ? 0 : id;          // out-of-contract id: clamp, never fault
+// Physical page ids of a unit, 64 at a time: lane j of every wave holds the id of
+// logical page base + j in one VGPR and the id of page pg is read with readlane, so a
+// page's DMA never waits on a block-table load (the ids are fetched up to 64 pages
+// ahead; the reload every 64 pages is the only exposed table access).
+struct PageIds {
+  int base;   // logical page held by lane 0
+  int vec;    // this lane's id (clamped into [0, num_pages))
+};
+
+__device__ __forceinline__ void load_page_ids(PageIds& ids, const DecodeParams& p, int b, int base,
+                                              int pg_end, int l) {
+  ids.base = base;
+  int id = 0;
+  if (base + l < pg_end) id = p.block_table[(int64_t)b * p.bt_sb + base + l];
+  ids.vec = (id < 0 || id >= p.num_pages) ? 0 : id;     // out-of-contract id: clamp, never fault
+}
+
+__device__ __forceinline__ const char* page_ptr(PageIds& ids, const DecodeParams& p, int b, int pg,
+                                                int pg_end, int l, bool fp8) {
+  if (pg - ids.base >= 64) load_page_ids(ids, p, b, pg, pg_end, l);   // uniform branch
+  const int id = __builtin_amdgcn_readlane(ids.vec, pg - ids.base);
   return p.kv + (int64_t)id * (fp8 ? kPageBytesFp8 : kPageBytesBf16);
 }
 
@@ -293,12 +311,25 @@ __device__ __forceinline__ void wide_page(const MLA_LDS char* pg, const MLA_LDS 
   // The page is processed as two 32-token halves, each a full online-softmax step.
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    // S^T = K . Q^T over 576 features in 36 steps of 16
+    // S^T = K . Q^T over 576 features in 36 steps of 16.  K fragments are read
+    // kPrefK steps ahead of their MFMA (a rolling register buffer) so the LDS latency
+    // hides behind the MFMA pipeline; the scheduler is told to alternate one LDS read
+    // with one MFMA.
+    constexpr int kPrefK = 4;
+    const uint32_t kofs = tb * (32 * 8 * 16);
+    bf16x8_t kbuf[kPrefK];
+#pragma unroll
+    for (int d = 0; d < kPrefK; ++d) kbuf[d] = lds_read_b128(pg, kbase[d & 3] + (d >> 2) * kGroupBytes + kofs);
+    __builtin_amdgcn_sched_group_barrier(0x100, kPrefK, 0);               // prologue reads first
     f32x16_t sc = {};
 #pragma unroll
     for (int kk = 0; kk < 36; ++kk) {
-      const bf16x8_t a = lds_read_b128(pg, kbase[kk & 3] + (kk >> 2) * kGroupBytes + tb * (32 * 8 * 16));
+      const bf16x8_t a = kbuf[kk % kPrefK];
+      const int nk = kk + kPrefK;
+      if (nk < 36) kbuf[kk % kPrefK] = lds_read_b128(pg, kbase[nk & 3] + (nk >> 2) * kGroupBytes + kofs);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sc, 0, 0, 0);
+      if (nk < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
     }
     // scores -> log2 domain, mask, tile max.  Element i = 4a + j is token
     // 32*tb + 8a + 4*h32 + j of the page.  For fp8 the per-token factors (k_scale *
@@ -358,15 +389,32 @@ __device__ __forceinline__ void wide_page(const MLA_LDS char* pg, const MLA_LDS 
           lrsum += FP8 ? (float)r * ivf[j] : (float)r;
         }
       }
-      // O^T += V^T . P^T for token step u = 2*tb + jj (tokens 16u .. 16u+15)
+      // O^T += V^T . P^T for token step u = 2*tb + jj (tokens 16u .. 16u+15); the two
+      // transpose reads of each V^T fragment are issued kPrefV MFMAs ahead.
       const int u = 2 * tb + jj;
+      constexpr int kPrefV = 3;
+      const uint32_t uofs = (uint32_t)(16 * u * 8 * 16);
+      bf16x4_t vlo[kPrefV], vhi[kPrefV];
+#pragma unroll
+      for (int d = 0; d < kPrefV; ++d) {
+        const uint32_t off = vbase[d & 1] + (d >> 1) * kGroupBytes + uofs;
+        vlo[d] = lds_read_tr16(pg, off);
+        vhi[d] = lds_read_tr16(pg, off + 8 * 8 * 16);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefV, 0);         // prologue reads first
 #pragma unroll
       for (int fb = 0; fb < 16; ++fb) {
-        const uint32_t off = vbase[fb & 1] + (fb >> 1) * kGroupBytes + (uint32_t)(16 * u * 8 * 16);
-        const bf16x4_t v0 = lds_read_tr16(pg, off);
-        const bf16x4_t v1 = lds_read_tr16(pg, off + 8 * 8 * 16);
+        const bf16x4_t v0 = vlo[fb % kPrefV], v1 = vhi[fb % kPrefV];
+        const int nf = fb + kPrefV;
+        if (nf < 16) {
+          const uint32_t off = vbase[nf & 1] + (nf >> 1) * kGroupBytes + uofs;
+          vlo[fb % kPrefV] = lds_read_tr16(pg, off);
+          vhi[fb % kPrefV] = lds_read_tr16(pg, off + 8 * 8 * 16);
+        }
         const bf16x8_t va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         st.o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, st.o[fb], 0, 0, 0);
+        if (nf < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // 2 DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
       }
     }
     st.l += lsum;
@@ -483,9 +531,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     // stage the unit's first page before loading the query fragments
     MLA_LDS char* buf0 = smem + (FP8 ? kFp8Raw0 : 0);
     MLA_LDS char* buf1 = smem + (FP8 ? kFp8Raw1 : kPageBytesBf16);
+    PageIds ids;
+    load_page_ids(ids, p, b, pg0, pg1, l);
     if (pg1 > pg0) {
-      if constexpr (FP8) issue_page_fp8(page_ptr(p, b, pg0, true), buf0, w, l);
-      else issue_page_bf16(page_ptr(p, b, pg0, false), buf0, w, l);
+      if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
+      else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
     }
 
     // query fragments (B operand): row r, features 16*kk + 8*(l>>5) (wide) or
@@ -529,8 +579,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       if (tid == 0) *ovf = 0;
       lds_barrier();
       if (attempt > 0 && pg1 > pg0) {
-        if constexpr (FP8) issue_page_fp8(page_ptr(p, b, pg0, true), buf0, w, l);
-        else issue_page_bf16(page_ptr(p, b, pg0, false), buf0, w, l);
+        load_page_ids(ids, p, b, pg0, pg1, l);
+        if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
+        else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
       }
 
       for (int pg = pg0; pg < pg1; ++pg) {
@@ -539,11 +590,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         MLA_LDS char* nxt = odd ? buf0 : buf1;
         if (pg + 1 < pg1) {
           if constexpr (FP8) {
-            issue_page_fp8(page_ptr(p, b, pg + 1, true), nxt, w, l);
+            issue_page_fp8(page_ptr(ids, p, b, pg + 1, pg1, l, true), nxt, w, l);
             if (w == 0) wait_vmcnt<10>();
             else wait_vmcnt<9>();
           } else {
-            issue_page_bf16(page_ptr(p, b, pg + 1, false), nxt, w, l);
+            issue_page_bf16(page_ptr(ids, p, b, pg + 1, pg1, l, false), nxt, w, l);
             wait_vmcnt<18>();
           }
         } else {
@@ -586,36 +637,65 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     // ---- epilogue ----
     const size_t slot = (size_t)pi * p.n_hg + hg;
     if constexpr (WIDE) {
+      // Each lane holds O^T for one row (l & 31) and features 32*fb + 8*a + 4*h32 + [0,4).
+      // The rows are staged through this wave's own LDS region (rows padded to
+      // 1040 B so that 32 lanes writing 32 rows hit distinct banks) and written back
+      // row by row, 64 lanes x 16 B = 1 KiB contiguous per store instruction.
       const int h32 = l >> 5;
+      const int rl = l & 31;
       const float l_tot = ws.l + shfl_xor_f(ws.l, 32);
       const float lr_tot = ws.lr + shfl_xor_f(ws.lr, 32);
       const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
       const float lse_v = l_tot > 0.f ? (ws.m + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-      if (row_ok) {
-        if (nsplit == 1) {
-          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq * p.o_st + (int64_t)head * p.o_sh;
+      constexpr int kRowPad = 1040;
+      MLA_LDS char* stage = smem + w * (32 * kRowPad);
+      const bool single = nsplit == 1;
+      // 32 rows of this wave: row r0 + i maps to (head, q row) like the lanes' own rows
+      const int nhalf = single ? 1 : 2;               // bf16: 512 x 2 B per row; fp32: two halves of 256
+      for (int hf = 0; hf < nhalf; ++hf) {
+        if (single) {
 #pragma unroll
           for (int fb = 0; fb < 16; ++fb)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
               const bf16x4_t v = {(__bf16)(ws.o[fb][4 * a] * inv), (__bf16)(ws.o[fb][4 * a + 1] * inv),
                                   (__bf16)(ws.o[fb][4 * a + 2] * inv), (__bf16)(ws.o[fb][4 * a + 3] * inv)};
-              *reinterpret_cast<bf16x4_t*>(orow + 32 * fb + 8 * a + 4 * h32) = v;
+              *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + rl * kRowPad + (32 * fb + 8 * a + 4 * h32) * 2) = v;
             }
-          if (h32 == 0) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = lse_v;
         } else {
-          float* prow = p.part_o + (slot * p.m_wg + r) * kLatent;
 #pragma unroll
-          for (int fb = 0; fb < 16; ++fb)
+          for (int fb = 0; fb < 16; ++fb) {
+            if ((fb >> 3) != hf) continue;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-              const f32x4_t v = {ws.o[fb][4 * a] * inv, ws.o[fb][4 * a + 1] * inv,
-                                 ws.o[fb][4 * a + 2] * inv, ws.o[fb][4 * a + 3] * inv};
-              *reinterpret_cast<f32x4_t*>(prow + 32 * fb + 8 * a + 4 * h32) = v;
+              const f32x4_t v = {ws.o[fb][4 * a] * inv, ws.o[fb][4 * a + 1] * inv, ws.o[fb][4 * a + 2] * inv,
+                                 ws.o[fb][4 * a + 3] * inv};
+              *reinterpret_cast<MLA_LDS f32x4_t*>(stage + rl * kRowPad + (32 * (fb & 7) + 8 * a + 4 * h32) * 4) = v;
             }
-          if (h32 == 0) p.part_lse[slot * p.m_wg + r] = lse_v;
+          }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's stage is written
+        for (int i = 0; i < 32; ++i) {
+          const int rr = 32 * w + i;
+          const int hl_i = rr / p.q_len, tq_i = rr - hl_i * p.q_len;
+          const int head_i = hg * p.hg_heads + hl_i;
+          if (head_i >= p.N) continue;                        // uniform
+          const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + i * kRowPad + l * 16);
+          if (single) {
+            uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_i * p.o_st + (int64_t)head_i * p.o_sh;
+            *reinterpret_cast<u32x4_t*>(orow + 8 * l) = v;
+          } else {
+            float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 256 * hf;
+            *reinterpret_cast<u32x4_t*>(prow + 4 * l) = v;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the stage is reused
       }
+      if (row_ok && h32 == 0) {
+        if (single) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = lse_v;
+        else p.part_lse[slot * p.m_wg + r] = lse_v;
+      }
+      lds_barrier();                                          // stages free before the next unit's DMA
     } else {
       // combine the four token-slices of the waves through LDS
       float l_w = ns.l + shfl_xor_f(ns.l, 16);
@@ -635,7 +715,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       }
       lds_barrier();
       const int rr = tid >> 4;                 // row 0..15
-      const int f0 = (tid & 15) * 32;          // 32 features per thread
+      const int fp = tid & 15;                 // features 64*j + 4*fp + [0,4), j = 0..7:
+                                               // 16 lanes of a row store 256 contiguous bytes
       float mw[4], lw[4], lrw[4];
       float M = -INFINITY;
 #pragma unroll
@@ -658,33 +739,29 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       const int rhl = rr / p.q_len, rtq = rr - rhl * p.q_len;
       const int rhead = hg * p.hg_heads + rhl;
       if (rhead < p.N) {
-        float acc[32];
+        f32x4_t acc[8];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + f0;
+          const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + 4 * fp;
 #pragma unroll
-          for (int j = 0; j < 32; ++j) acc[j] += wgt[k] * src[j];
+          for (int j = 0; j < 8; ++j) acc[j] += wgt[k] * *reinterpret_cast<const MLA_LDS f32x4_t*>(src + 64 * j);
         }
         if (nsplit == 1) {
-          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + f0;
+          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + 4 * fp;
 #pragma unroll
-          for (int j = 0; j < 32; j += 8) {
-            const bf16x8_t v = {(__bf16)(acc[j] * inv), (__bf16)(acc[j + 1] * inv), (__bf16)(acc[j + 2] * inv),
-                                (__bf16)(acc[j + 3] * inv), (__bf16)(acc[j + 4] * inv), (__bf16)(acc[j + 5] * inv),
-                                (__bf16)(acc[j + 6] * inv), (__bf16)(acc[j + 7] * inv)};
-            *reinterpret_cast<bf16x8_t*>(orow + j) = v;
+          for (int j = 0; j < 8; ++j) {
+            const bf16x4_t v = {(__bf16)(acc[j][0] * inv), (__bf16)(acc[j][1] * inv), (__bf16)(acc[j][2] * inv),
+                                (__bf16)(acc[j][3] * inv)};
+            *reinterpret_cast<bf16x4_t*>(orow + 64 * j) = v;
           }
-          if ((tid & 15) == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
+          if (fp == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
         } else {
-          float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + f0;
+          float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 4 * fp;
 #pragma unroll
-          for (int j = 0; j < 32; j += 4) {
-            const f32x4_t v = {acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv};
-            *reinterpret_cast<f32x4_t*>(prow + j) = v;
-          }
-          if ((tid & 15) == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
+          for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(prow + 64 * j) = acc[j] * inv;
+          if (fp == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
         }
       }
       lds_barrier();
@@ -697,6 +774,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 // lane 8 of the 512 latent features.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+  // grid = (B * n_hg, ceil(m_wg / 16)): each wave merges 4 rows; lane s < nsplit fetches
+  // split s's lse, so the max and the weights take one load and a wave reduction; each
+  // lane then accumulates 8 of the 512 features over the splits, 4 splits' loads in flight.
   const int b = blockIdx.x / p.n_hg;
   const int hg = blockIdx.x - b * p.n_hg;
   const int4 rq = p.req[b];
@@ -710,28 +790,50 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     const int head = hg * p.hg_heads + hl;
     if (head >= p.N) continue;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t slot = (size_t)(first + s) * p.n_hg + hg;
-      M = fmaxf(M, p.part_lse[slot * p.m_wg + r]);
+    for (int s0 = 0; s0 < nsplit; s0 += 64) {
+      const int s = s0 + l;
+      const float ls = s < nsplit ? p.part_lse[((size_t)(first + s) * p.n_hg + hg) * p.m_wg + r] : -INFINITY;
+      M = fmaxf(M, ls);
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
     const float Mb = M == -INFINITY ? 0.f : M;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x4_t a0 = {}, a1 = {};
     float wsum = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+      f32x4_t v[4][2];
+      float wt[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const size_t slot = (size_t)(first + s + k) * p.n_hg + hg;
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
+        v[k][0] = src[0];
+        v[k][1] = src[1];
+        const float ls = p.part_lse[slot * p.m_wg + r];
+        wt[k] = ls == -INFINITY ? 0.f : __expf(ls - Mb);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        wsum += wt[k];
+        a0 += wt[k] * v[k][0];
+        a1 += wt[k] * v[k][1];
+      }
+    }
+    for (; s < nsplit; ++s) {
       const size_t slot = (size_t)(first + s) * p.n_hg + hg;
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
       const float ls = p.part_lse[slot * p.m_wg + r];
       const float wt = ls == -INFINITY ? 0.f : __expf(ls - Mb);
       wsum += wt;
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
-      const f32x4_t a = src[0], c = src[1];
-      acc[0] += wt * a[0]; acc[1] += wt * a[1]; acc[2] += wt * a[2]; acc[3] += wt * a[3];
-      acc[4] += wt * c[0]; acc[5] += wt * c[1]; acc[6] += wt * c[2]; acc[7] += wt * c[3];
+      a0 += wt * src[0];
+      a1 += wt * src[1];
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq * p.o_st + (int64_t)head * p.o_sh + 8 * l;
-    const bf16x8_t v = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
-                        (__bf16)(acc[3] * inv), (__bf16)(acc[4] * inv), (__bf16)(acc[5] * inv),
-                        (__bf16)(acc[6] * inv), (__bf16)(acc[7] * inv)};
+    const bf16x8_t v = {(__bf16)(a0[0] * inv), (__bf16)(a0[1] * inv), (__bf16)(a0[2] * inv),
+                        (__bf16)(a0[3] * inv), (__bf16)(a1[0] * inv), (__bf16)(a1[1] * inv),
+                        (__bf16)(a1[2] * inv), (__bf16)(a1[3] * inv)};
     *reinterpret_cast<bf16x8_t*>(orow) = v;
     if (l == 0) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = wsum > 0.f ? Mb + __logf(wsum) : -INFINITY;
   }
