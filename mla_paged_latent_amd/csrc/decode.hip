@@ -22,6 +22,8 @@
 //                                     S^T accumulator re-packed to bf16 in place)
 //                 then writes the final output (single split) or a float32 partial
 //   merge_kernel  LSE-weighted combine of the partials of split requests
+#include <utility>
+
 #include "mla_common.h"
 #include "mla_host.h"
 
@@ -155,26 +157,42 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeParams p) {
 // (18 per wave).  Instruction k fills LDS group k >> 3 for tokens 8*(k & 7) + (lane >> 3);
 // lane j loads global chunk 8*(k >> 3) + ((j & 7) ^ s(j >> 3)) of that token (the
 // swizzle only sees t & 7 = j >> 3), i.e. page + lane_off + 9216*(k & 7) + 128*(k >> 3).
+template <int... I>
+__device__ __forceinline__ void issue_bf16_seq(std::integer_sequence<int, I...>, const char* page,
+                                               const char* half1, uint32_t voff, uint32_t lds) {
+  (dma_16B<128 * (I >> 1), 4096 * I>((I & 1) ? half1 : page, voff, lds), ...);
+}
+
 __device__ __forceinline__ void issue_page_bf16(const char* page, MLA_LDS char* dst, int w, int l) {
-  const uint32_t lane_off = (uint32_t)((l >> 3) * kRowBytesBf16 + ((l & 7) ^ page_swz(l >> 3)) * 16);
-#pragma unroll
-  for (int i = 0; i < 18; ++i) {
-    const int k = w + 4 * i;
-    const char* src = page + (8 * kRowBytesBf16 * (k & 7) + 128 * (k >> 3));
-    dma_16B(src + lane_off, dst + k * 1024);
-  }
+  // instruction k = w + 4i covers tokens 8*(k & 7) .. +7 of 128-byte column k >> 3;
+  // with w < 4 that is tokens 8w + 32*(i & 1) and column i >> 1, so the wave's part
+  // of the offset sits in voff and the rest is a compile-time constant.
+  const uint32_t voff = (uint32_t)((l >> 3) * kRowBytesBf16 + ((l & 7) ^ page_swz(l >> 3)) * 16 +
+                                   w * 8 * kRowBytesBf16);
+  const char* half1 = page + 32 * kRowBytesBf16;
+  const uint32_t lds = lds_addr(dst) + (uint32_t)w * 1024u;
+  issue_bf16_seq(std::make_integer_sequence<int, 18>{}, page, half1, voff, lds);
 }
 
 // fp8 page: the 37376 raw bytes (16-byte aligned) as 2336 flat 16-B chunks in 37
-// instructions; wave 0 issues 10 of them, waves 1..3 issue 9.
+// instructions k = w + 4i; wave 0 issues 10 of them (the last one half-masked),
+// waves 1..3 issue 9.
+template <int I>
+__device__ __forceinline__ void issue_fp8_one(const char* page, uint32_t voff, uint32_t lds, int w, int l) {
+  const int k = w + 4 * I;
+  if (k < 37 && k * 64 + l < kPageBytesFp8 / 16) dma_16B<0, 4096 * I>(page + 4096 * I, voff, lds);
+}
+
+template <int... I>
+__device__ __forceinline__ void issue_fp8_seq(std::integer_sequence<int, I...>, const char* page, uint32_t voff,
+                                              uint32_t lds, int w, int l) {
+  (issue_fp8_one<I>(page, voff, lds, w, l), ...);
+}
+
 __device__ __forceinline__ void issue_page_fp8(const char* page, MLA_LDS char* dst, int w, int l) {
-#pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const int k = w + 4 * i;
-    if (k < 37) {
-      if (k * 64 + l < kPageBytesFp8 / 16) dma_16B(page + k * 1024 + l * 16, dst + k * 1024);
-    }
-  }
+  const uint32_t voff = (uint32_t)(w * 1024 + l * 16);
+  const uint32_t lds = lds_addr(dst) + (uint32_t)w * 1024u;
+  issue_fp8_seq(std::make_integer_sequence<int, 10>{}, page, voff, lds, w, l);
 }
 
 // Physical page ids of a unit, 64 at a time: lane j of every wave holds the id of

@@ -69,9 +69,29 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const MLA_LDS char* base, uint
       reinterpret_cast<MLA_LDS bf16x4_t*>(const_cast<MLA_LDS char*>(base) + byte_off));
 }
 
-__device__ __forceinline__ void dma_16B(const void* src, MLA_LDS char* dst_wave_base) {
-  // Each lane's 16 bytes land at dst_wave_base + 16 * lane.
-  __builtin_amdgcn_global_load_lds(src, reinterpret_cast<MLA_LDS void*>(dst_wave_base), 16, 0, 0);
+// One 1 KiB global->LDS copy: lane l's 16 bytes at sbase + voff + IMM land at LDS
+// byte address lds_base + LDS_ADD + 16 * l.  sbase must be wave-uniform (SGPR pair),
+// voff a 32-bit per-lane offset, IMM < 4096.  The instruction adds its immediate to
+// the LDS address as well as to the global one, so M0 gets LDS_ADD - IMM.
+// Written as inline asm on purpose: the compiler does not see the LDS write, so it
+// inserts no vmcnt(0) drain in front of later LDS reads of other buffers (it cannot
+// prove they do not alias) and keeps no per-copy constants live.  Completion is the
+// caller's business: each call is one vector-memory instruction for vmcnt.  M0 is
+// set inside the statement; nothing else in these kernels keeps a value in M0.
+template <int IMM, int LDS_ADD>
+__device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  static_assert(IMM >= 0 && IMM < 4096, "immediate offset range");
+  asm volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 offset:%4"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base), "i"(LDS_ADD - IMM), "i"(IMM)
+      : "memory", "scc");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) {
+  return (uint32_t)(uintptr_t)p;
 }
 
 // ---------------------------------------------------------------------------
