@@ -11,17 +11,21 @@
 // "Triton und MLA", §Datenfluss and §Entwurfsmotivation (natural-log LSE returned).
 //
 // Structure (all on the caller's stream, no host synchronisation):
-//   plan_kernel   one workgroup: per-request split count and page-aligned token
-//                 ranges -> (request, split) pair table in the workspace
-//   decode_kernel persistent grid: one work unit = (pair, head group); the unit's
-//                 pages stream through LDS (double-buffered global->LDS DMA), every
-//                 query head of the group scores against each staged page:
-//                   S^T = K . Q^T  (MFMA; Q lives in registers as the B operand)
-//                   online softmax in the log2 domain, per head = per lane
-//                   O^T += V^T . P^T (MFMA; V^T via LDS transpose reads, P^T is the
-//                                     S^T accumulator re-packed to bf16 in place)
-//                 then writes the final output (single split) or a float32 partial
-//   merge_kernel  LSE-weighted combine of the partials of split requests
+//   plan_kernel          one workgroup: per-request split count and page-aligned token
+//                        ranges -> (request, split) pair table in the workspace
+//   decode_wide_kernel   q_len * N > 16: persistent grid, one work unit = (pair, head
+//                        group of 64 query rows); the unit's cache rows stream through
+//                        LDS in 32-token blocks (global->LDS DMA ring) and every query
+//                        row of the group scores against each staged block:
+//                          S^T = K . Q^T   (MFMA; wave w: 32 rows x 16 tokens, Q in
+//                                           registers)
+//                          softmax in the log2 domain against a fixed reference max
+//                          O^T += V^T . P^T (MFMA; wave w's 128 latent features of all
+//                                            rows, V^T via LDS transpose reads, P via LDS)
+//   decode_narrow_kernel q_len * N <= 16 (16-head decode): 16 rows per unit, whole
+//                        pages double-buffered, the 4 waves split each page's tokens
+//   Both write the final output (single split) or float32 partials; then
+//   merge_kernel         LSE-weighted combine of the partials of split requests
 #include <utility>
 
 #include "mla_common.h"
@@ -167,7 +171,7 @@ __device__ __forceinline__ void issue_page_bf16(const char* page, MLA_LDS char* 
   // instruction k = w + 4i covers tokens 8*(k & 7) .. +7 of 128-byte column k >> 3;
   // with w < 4 that is tokens 8w + 32*(i & 1) and column i >> 1, so the wave's part
   // of the offset sits in voff and the rest is a compile-time constant.
-  const uint32_t voff = (uint32_t)((l >> 3) * kRowBytesBf16 + ((l & 7) ^ page_swz(l >> 3)) * 16 +
+  const uint32_t voff = (uint32_t)((l >> 3) * kRowBytesBf16 + ((l & 7) ^ page_swz(8 * (w & 1) + (l >> 3))) * 16 +
                                    w * 8 * kRowBytesBf16);
   const char* half1 = page + 32 * kRowBytesBf16;
   const uint32_t lds = lds_addr(dst) + (uint32_t)w * 1024u;
@@ -282,7 +286,7 @@ __device__ __forceinline__ void zero_tail_rows(MLA_LDS char* page, int valid, in
 }
 
 // ---------------------------------------------------------------------------
-// Per-unit compute: wide variant (128 query rows, 32 per wave, 32x32x16 MFMA)
+// Softmax reference max
 // ---------------------------------------------------------------------------
 // Softmax bookkeeping without rescaling the accumulators.  Each row's reference
 // max m is fixed from the first 32-token block of the unit (exact for that block);
@@ -293,160 +297,12 @@ __device__ __forceinline__ void zero_tail_rows(MLA_LDS char* page, int valid, in
 // reference.  O never needs a VALU rescale inside the page loop.
 constexpr float kRefSlack = 64.0f;
 
-struct WideState {
-  f32x16_t o[16];     // O^T: 16 blocks of 32 latent features x 32 rows (lane = row)
-  float m;            // reference max (log2 domain), -inf until set
-  float l;            // sum of p over this lane's half of the tokens (for the LSE)
-  float lr;           // same sum over the bf16-rounded weights (normalises O)
-  float m_seen;       // largest visible score seen (for a restart)
-};
-
-template <bool FP8>
-__device__ __forceinline__ void wide_page(const MLA_LDS char* pg, const MLA_LDS float* ks,
-                                          const MLA_LDS float* vs, const MLA_LDS float* ivs,
-                                          const bf16x8_t (&qf)[36],
-                                          WideState& st, int tok0, int nvis, bool need_mask,
-                                          float scale_log2, int l, bool first,
-                                          MLA_LDS int* overflow) {
-  const int h32 = l >> 5, c32 = l & 31;
-  const int g = l >> 4, lg = l & 15;
-  // K chunk c = 2*kk + h32 of token 32*tb + c32: group kk >> 2, in-group chunk
-  // 2*(kk & 3) + h32, swizzle s(c32) (the swizzle sees t & 7 only).
-  uint32_t kbase[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) kbase[m] = (uint32_t)(c32 * 8 + ((2 * m + h32) ^ page_swz(c32))) * 16;
-  // Transpose reads: the 16-lane group g reads tokens 16u + 8r + 4*h32 + e (e = 0..3,
-  // read r = 0/1) at features 32*fb + 16*(g & 1) + [0, 16); lane lg supplies token row
-  // lg >> 2 and column 4*(lg & 3).  Chunk c = 4*fb + cpart lies in group fb >> 1 at
-  // in-group chunk 4*(fb & 1) + cpart and the swizzle sees t & 7 = 4*h32 + (lg >> 2).
-  const int vt = 4 * h32 + (lg >> 2);
-  const int cpart = 2 * (g & 1) + ((lg & 3) >> 1);
-  uint32_t vbase[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    vbase[m] = (uint32_t)(vt * 8 + ((4 * m + cpart) ^ page_swz(vt))) * 16 + (uint32_t)(lg & 1) * 8;
-
-  // The page is processed as two 32-token halves, each a full online-softmax step.
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    // S^T = K . Q^T over 576 features in 36 steps of 16.  K fragments are read
-    // kPrefK steps ahead of their MFMA (a rolling register buffer) so the LDS latency
-    // hides behind the MFMA pipeline; the scheduler is told to alternate one LDS read
-    // with one MFMA.
-    constexpr int kPrefK = 4;
-    const uint32_t kofs = tb * (32 * 8 * 16);
-    bf16x8_t kbuf[kPrefK];
-#pragma unroll
-    for (int d = 0; d < kPrefK; ++d) kbuf[d] = lds_read_b128(pg, kbase[d & 3] + (d >> 2) * kGroupBytes + kofs);
-    __builtin_amdgcn_sched_group_barrier(0x100, kPrefK, 0);               // prologue reads first
-    f32x16_t sc = {};
-#pragma unroll
-    for (int kk = 0; kk < 36; ++kk) {
-      const bf16x8_t a = kbuf[kk % kPrefK];
-      const int nk = kk + kPrefK;
-      if (nk < 36) kbuf[kk % kPrefK] = lds_read_b128(pg, kbase[nk & 3] + (nk >> 2) * kGroupBytes + kofs);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sc, 0, 0, 0);
-      if (nk < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-    }
-    // scores -> log2 domain, mask, tile max.  Element i = 4a + j is token
-    // 32*tb + 8a + 4*h32 + j of the page.  For fp8 the per-token factors (k_scale *
-    // softmax scale, v_scale, 1/v_scale) of the 4 tokens of group a are read as one
-    // 16-byte vector each; a compiler fence between groups keeps only one group's
-    // factors live (the query fragments stay in registers).
-    f32x4_t kf[4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t0 = 32 * tb + 8 * a + 4 * h32;
-      if constexpr (FP8) {
-        asm volatile("" ::: "memory");
-        kf[a] = *reinterpret_cast<const MLA_LDS f32x4_t*>(ks + t0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * a + j;
-        float x = FP8 ? sc[i] * kf[a][j] : sc[i] * scale_log2;
-        if (need_mask) x = (tok0 + t0 + j < nvis) ? x : -INFINITY;
-        sc[i] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    if (first) st.m = (tb == 0) ? mt : st.m;          // reference from the unit's first block
-    st.m_seen = fmaxf(st.m_seen, mt);
-    const float base = st.m == -INFINITY ? 0.f : st.m;
-    if (mt > base + kRefSlack) *overflow = 1;
-    // For each 16-token k-step jj (elements 8jj .. 8jj+7 of this lane) the weights are
-    // exponentiated, packed to bf16 and consumed by that step's 16 PV MFMAs right
-    // away, so only one step's weights and per-token factors are live at a time.
-    // The row sum accumulates the bf16-rounded weights the MFMA actually uses, so the
-    // output is an exact convex combination of the V rows: the rounding of a dominant
-    // weight then largely cancels instead of scaling the output.
-    float lsum = 0.f, lrsum = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      bf16x8_t pb;
-#pragma unroll
-      for (int ah = 0; ah < 2; ++ah) {
-        const int a = 2 * jj + ah;
-        const int t0 = 32 * tb + 8 * a + 4 * h32;
-        f32x4_t vf, ivf;
-        if constexpr (FP8) {
-          asm volatile("" ::: "memory");
-          vf = *reinterpret_cast<const MLA_LDS f32x4_t*>(vs + t0);
-          ivf = *reinterpret_cast<const MLA_LDS f32x4_t*>(ivs + t0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pr = __builtin_amdgcn_exp2f(sc[4 * a + j] - base);
-          const float v = FP8 ? pr * vf[j] : pr;
-          const __bf16 r = (__bf16)v;
-          pb[4 * ah + j] = r;
-          lsum += pr;
-          lrsum += FP8 ? (float)r * ivf[j] : (float)r;
-        }
-      }
-      // O^T += V^T . P^T for token step u = 2*tb + jj (tokens 16u .. 16u+15); the two
-      // transpose reads of each V^T fragment are issued kPrefV MFMAs ahead.
-      const int u = 2 * tb + jj;
-      constexpr int kPrefV = 3;
-      const uint32_t uofs = (uint32_t)(16 * u * 8 * 16);
-      bf16x4_t vlo[kPrefV], vhi[kPrefV];
-#pragma unroll
-      for (int d = 0; d < kPrefV; ++d) {
-        const uint32_t off = vbase[d & 1] + (d >> 1) * kGroupBytes + uofs;
-        vlo[d] = lds_read_tr16(pg, off);
-        vhi[d] = lds_read_tr16(pg, off + 8 * 8 * 16);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefV, 0);         // prologue reads first
-#pragma unroll
-      for (int fb = 0; fb < 16; ++fb) {
-        const bf16x4_t v0 = vlo[fb % kPrefV], v1 = vhi[fb % kPrefV];
-        const int nf = fb + kPrefV;
-        if (nf < 16) {
-          const uint32_t off = vbase[nf & 1] + (nf >> 1) * kGroupBytes + uofs;
-          vlo[fb % kPrefV] = lds_read_tr16(pg, off);
-          vhi[fb % kPrefV] = lds_read_tr16(pg, off + 8 * 8 * 16);
-        }
-        const bf16x8_t va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        st.o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, st.o[fb], 0, 0, 0);
-        if (nf < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // 2 DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
-      }
-    }
-    st.l += lsum;
-    st.lr += lrsum;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Per-unit compute: narrow variant (16 query rows; wave w takes tokens
-// 16w..16w+15 of every page; 16x16x32 MFMA for scores, 16x16x16 for PV)
+// Narrow variant: 16 query rows per unit, 16x16 MFMA, waves split the page's tokens
 // ---------------------------------------------------------------------------
 struct NarrowState {
   f32x4_t o[32];      // O^T: 32 blocks of 16 latent features x 16 rows (lane%16 = row)
-  float m, l, lr, m_seen;   // as in WideState
+  float m, l, lr, m_seen;   // as in RowState
 };
 
 template <bool FP8>
@@ -484,7 +340,8 @@ __device__ __forceinline__ void narrow_page(const MLA_LDS char* pg, const MLA_LD
   st.m_seen = fmaxf(st.m_seen, mt);
   const float base = st.m == -INFINITY ? 0.f : st.m;
   if (mt > base + kRefSlack) *overflow = 1;
-  // row sum of the bf16-rounded weights (see wide_page)
+  // row sum of the bf16-rounded weights: O becomes an exact convex combination of the V
+  // rows the MFMA saw, so the rounding of a dominant weight cancels
   float lsum = 0.f, lrsum = 0.f;
   bf16x4_t pb;
 #pragma unroll
@@ -517,8 +374,8 @@ __device__ __forceinline__ void narrow_page(const MLA_LDS char* pg, const MLA_LD
 // ---------------------------------------------------------------------------
 // The persistent decode kernel
 // ---------------------------------------------------------------------------
-template <bool FP8, bool WIDE>
-__global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
   MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
   const int tid = threadIdx.x;
@@ -540,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     const int first_nvis = seq - p.q_len + 1;          // visible tokens of query row 0
 
     // the row this lane owns in the S^T / O^T accumulators
-    const int r = WIDE ? (32 * w + (l & 31)) : (l & 15);
+    const int r = l & 15;
     const int hl = r / p.q_len, tq = r - hl * p.q_len;
     const int head = hg * p.hg_heads + hl;
     const bool row_ok = head < p.N;
@@ -556,42 +413,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
     }
 
-    // query fragments (B operand): row r, features 16*kk + 8*(l>>5) (wide) or
-    // 32*kk + 8*(l>>4) (narrow)
-    constexpr int NQ = WIDE ? 36 : 18;
+    // query fragments (B operand): row r, features 32*kk + 8*(l>>4)
+    constexpr int NQ = 18;
     bf16x8_t qf[NQ];
     {
       // padding rows (head >= N) load head 0 and are zeroed: no divergent loads
       const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
-      const int off = WIDE ? 8 * (l >> 5) : 8 * (l >> 4);
+      const int off = 8 * (l >> 4);
 #pragma unroll
-      for (int kk = 0; kk < NQ; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + (WIDE ? 16 : 32) * kk + off);
+      for (int kk = 0; kk < NQ; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + off);
       if (!row_ok) {
 #pragma unroll
         for (int kk = 0; kk < NQ; ++kk) qf[kk] = bf16x8_t{};
       }
     }
 
-    WideState ws;
     NarrowState ns;
     MLA_LDS int* ovf = reinterpret_cast<MLA_LDS int*>(smem + kLdsFlag);
     float m_restart = -INFINITY;
     for (int attempt = 0; attempt < 2; ++attempt) {
-      if constexpr (WIDE) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ws.o[i] = f32x16_t{};
-        ws.m = m_restart;
-        ws.l = 0.f;
-        ws.lr = 0.f;
-        ws.m_seen = -INFINITY;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) ns.o[i] = f32x4_t{};
-        ns.m = m_restart;
-        ns.l = 0.f;
-        ns.lr = 0.f;
-        ns.m_seen = -INFINITY;
-      }
+      for (int i = 0; i < 32; ++i) ns.o[i] = f32x4_t{};
+      ns.m = m_restart;
+      ns.l = 0.f;
+      ns.lr = 0.f;
+      ns.m_seen = -INFINITY;
       // reset the flag and make the reset visible before any wave can read it
       // (a unit without pages reads it right after this barrier)
       if (tid == 0) *ovf = 0;
@@ -638,10 +484,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         }
         const bool need_mask = tok0 + kPage > first_nvis;
         const bool first = attempt == 0 && pg == pg0;
-        if constexpr (WIDE)
-          wide_page<FP8>(page, ksc, vsc, ivsc, qf, ws, tok0, nvis, need_mask, p.scale_log2, l, first, ovf);
-        else
-          narrow_page<FP8>(page, ksc, vsc, ivsc, qf, ns, tok0, nvis, need_mask, p.scale_log2, w, l, first, ovf);
+        narrow_page<FP8>(page, ksc, vsc, ivsc, qf, ns, tok0, nvis, need_mask, p.scale_log2, w, l, first, ovf);
         lds_barrier();
       }
       // every wave reads the flag after the last barrier; the second barrier keeps a
@@ -649,141 +492,626 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       const int redo = *ovf;
       lds_barrier();
       if (redo == 0) break;
-      m_restart = WIDE ? ws.m_seen : ns.m_seen;
+      m_restart = ns.m_seen;
     }
 
     // ---- epilogue ----
     const size_t slot = (size_t)pi * p.n_hg + hg;
-    if constexpr (WIDE) {
-      // Each lane holds O^T for one row (l & 31) and features 32*fb + 8*a + 4*h32 + [0,4).
-      // The rows are staged through this wave's own LDS region (rows padded to
-      // 1040 B so that 32 lanes writing 32 rows hit distinct banks) and written back
-      // row by row, 64 lanes x 16 B = 1 KiB contiguous per store instruction.
-      const int h32 = l >> 5;
-      const int rl = l & 31;
-      const float l_tot = ws.l + shfl_xor_f(ws.l, 32);
-      const float lr_tot = ws.lr + shfl_xor_f(ws.lr, 32);
-      const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
-      const float lse_v = l_tot > 0.f ? (ws.m + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-      constexpr int kRowPad = 1040;
-      MLA_LDS char* stage = smem + w * (32 * kRowPad);
-      const bool single = nsplit == 1;
-      // 32 rows of this wave: row r0 + i maps to (head, q row) like the lanes' own rows
-      const int nhalf = single ? 1 : 2;               // bf16: 512 x 2 B per row; fp32: two halves of 256
-      for (int hf = 0; hf < nhalf; ++hf) {
-        if (single) {
+    // combine the four token-slices of the waves through LDS
+    float l_w = ns.l + shfl_xor_f(ns.l, 16);
+    l_w += shfl_xor_f(l_w, 32);
+    float lr_w = ns.lr + shfl_xor_f(ns.lr, 16);
+    lr_w += shfl_xor_f(lr_w, 32);
+    MLA_LDS float* obuf = reinterpret_cast<MLA_LDS float*>(smem);
+    MLA_LDS float* stat = reinterpret_cast<MLA_LDS float*>(smem + 4 * 16 * kLatent * 4);
+    const int g = l >> 4;
 #pragma unroll
-          for (int fb = 0; fb < 16; ++fb)
+    for (int fb = 0; fb < 32; ++fb)
+      *reinterpret_cast<MLA_LDS f32x4_t*>(obuf + (w * 16 + r) * kLatent + 16 * fb + 4 * g) = ns.o[fb];
+    if (l < 16) {
+      stat[(w * 16 + r) * 4] = ns.m;
+      stat[(w * 16 + r) * 4 + 1] = l_w;
+      stat[(w * 16 + r) * 4 + 2] = lr_w;
+    }
+    lds_barrier();
+    const int rr = tid >> 4;                 // row 0..15
+    const int fp = tid & 15;                 // features 64*j + 4*fp + [0,4), j = 0..7:
+                                             // 16 lanes of a row store 256 contiguous bytes
+    float mw[4], lw[4], lrw[4];
+    float M = -INFINITY;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const bf16x4_t v = {(__bf16)(ws.o[fb][4 * a] * inv), (__bf16)(ws.o[fb][4 * a + 1] * inv),
-                                  (__bf16)(ws.o[fb][4 * a + 2] * inv), (__bf16)(ws.o[fb][4 * a + 3] * inv)};
-              *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + rl * kRowPad + (32 * fb + 8 * a + 4 * h32) * 2) = v;
-            }
-        } else {
+    for (int k = 0; k < 4; ++k) {
+      mw[k] = stat[(k * 16 + rr) * 4];
+      lw[k] = stat[(k * 16 + rr) * 4 + 1];
+      lrw[k] = stat[(k * 16 + rr) * 4 + 2];
+      M = fmaxf(M, mw[k]);
+    }
+    const float Mb = M == -INFINITY ? 0.f : M;
+    float wgt[4], L = 0.f, LR = 0.f;
 #pragma unroll
-          for (int fb = 0; fb < 16; ++fb) {
-            if ((fb >> 3) != hf) continue;
+    for (int k = 0; k < 4; ++k) {
+      wgt[k] = __builtin_amdgcn_exp2f(mw[k] - Mb);
+      L += wgt[k] * lw[k];
+      LR += wgt[k] * lrw[k];
+    }
+    const float inv = LR > 0.f ? 1.0f / LR : 0.f;
+    const float lse_v = L > 0.f ? (Mb + __builtin_log2f(L)) * kLn2 : -INFINITY;
+    const int rhl = rr / p.q_len, rtq = rr - rhl * p.q_len;
+    const int rhead = hg * p.hg_heads + rhl;
+    if (rhead < p.N) {
+      f32x4_t acc[8];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const f32x4_t v = {ws.o[fb][4 * a] * inv, ws.o[fb][4 * a + 1] * inv, ws.o[fb][4 * a + 2] * inv,
-                                 ws.o[fb][4 * a + 3] * inv};
-              *reinterpret_cast<MLA_LDS f32x4_t*>(stage + rl * kRowPad + (32 * (fb & 7) + 8 * a + 4 * h32) * 4) = v;
-            }
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's stage is written
-        for (int i = 0; i < 32; ++i) {
-          const int rr = 32 * w + i;
-          const int hl_i = rr / p.q_len, tq_i = rr - hl_i * p.q_len;
-          const int head_i = hg * p.hg_heads + hl_i;
-          if (head_i >= p.N) continue;                        // uniform
-          const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + i * kRowPad + l * 16);
-          if (single) {
-            uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_i * p.o_st + (int64_t)head_i * p.o_sh;
-            *reinterpret_cast<u32x4_t*>(orow + 8 * l) = v;
-          } else {
-            float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 256 * hf;
-            *reinterpret_cast<u32x4_t*>(prow + 4 * l) = v;
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the stage is reused
+      for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + 4 * fp;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += wgt[k] * *reinterpret_cast<const MLA_LDS f32x4_t*>(src + 64 * j);
       }
-      if (row_ok && h32 == 0) {
-        if (single) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = lse_v;
-        else p.part_lse[slot * p.m_wg + r] = lse_v;
-      }
-      lds_barrier();                                          // stages free before the next unit's DMA
-    } else {
-      // combine the four token-slices of the waves through LDS
-      float l_w = ns.l + shfl_xor_f(ns.l, 16);
-      l_w += shfl_xor_f(l_w, 32);
-      float lr_w = ns.lr + shfl_xor_f(ns.lr, 16);
-      lr_w += shfl_xor_f(lr_w, 32);
-      MLA_LDS float* obuf = reinterpret_cast<MLA_LDS float*>(smem);
-      MLA_LDS float* stat = reinterpret_cast<MLA_LDS float*>(smem + 4 * 16 * kLatent * 4);
-      const int g = l >> 4;
+      if (nsplit == 1) {
+        uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + 4 * fp;
 #pragma unroll
-      for (int fb = 0; fb < 32; ++fb)
-        *reinterpret_cast<MLA_LDS f32x4_t*>(obuf + (w * 16 + r) * kLatent + 16 * fb + 4 * g) = ns.o[fb];
-      if (l < 16) {
-        stat[(w * 16 + r) * 4] = ns.m;
-        stat[(w * 16 + r) * 4 + 1] = l_w;
-        stat[(w * 16 + r) * 4 + 2] = lr_w;
+        for (int j = 0; j < 8; ++j) {
+          const bf16x4_t v = {(__bf16)(acc[j][0] * inv), (__bf16)(acc[j][1] * inv), (__bf16)(acc[j][2] * inv),
+                              (__bf16)(acc[j][3] * inv)};
+          *reinterpret_cast<bf16x4_t*>(orow + 64 * j) = v;
+        }
+        if (fp == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
+      } else {
+        float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 4 * fp;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(prow + 64 * j) = acc[j] * inv;
+        if (fp == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide variant: 64 query rows per unit, 4 waves, 32-token blocks
+// ---------------------------------------------------------------------------
+// Division of labour inside a workgroup (w = wave):
+//  * scores: wave w owns query rows 32*(w >> 1) .. +31 and tokens 16*(w & 1) .. +15 of
+//    each block.  S^T = K . Q^T runs on 16x16x32 MFMA: one K fragment (16 tokens x 32
+//    features, from LDS) feeds two MFMAs (row halves), the wave's query rows stay in
+//    registers (B operand).  The bf16 weights P go to LDS.
+//  * values: wave w owns latent features 128w .. 128w+127 of all 64 rows.
+//    O^T += V^T . P^T runs on 32x32x16 MFMA, V^T from LDS transpose reads of the same
+//    staged rows (the latent is V), P^T read back from LDS.
+// With this split every staged K and V byte is read by one wave only, and a wave holds
+// 128 accumulator registers (its O) plus its query fragments.
+// Pipeline over the blocks of a unit (a block = 32 token rows = half a page):
+//    QK(j) -> [softmax(j) interleaved with PV(j-1)] -> P(j) to LDS -> wait for own
+//    DMA of block j+1 -> barrier Y(j) -> DMA of block j+3
+// so the softmax VALU work of one block overlaps the PV MFMAs of the previous one
+// and a block needs one barrier; blocks j+2 and j+3 are in flight while block j+1 is
+// computed.  bf16 blocks land straight in a 4-slot ring; fp8 blocks land raw in a
+// 4-slot ring and are converted into 2 bf16 slots right after Y(j) (one more barrier
+// Z(j+1) before QK(j+1) reads them).
+constexpr int kBlk = 32;
+constexpr int kBlkBytesBf16 = kBlk * kRowBytesBf16;    // 36864
+constexpr int kBlkBytesFp8 = kBlk * kRowBytesFp8;      // 18688
+constexpr int kBlkGroupBytes = kBlk * 128;             // 4096: one 128-byte column of the block
+constexpr int kBlkChunksFp8 = kBlkBytesFp8 / 16;       // 1168
+constexpr int kWRows = 64;                             // query rows per wide unit
+
+// LDS plan of the wide kernel
+constexpr int kWRing = 4;                              // DMA ring depth (blocks)
+constexpr int kWSlot = kBlkBytesBf16;                  // bf16 block slots at 0, 36864, ...
+constexpr int kWRaw = 2 * kWSlot;                      // fp8: 2 converted slots, then 4 raw blocks
+constexpr int kWFac = kWRaw + kWRing * kBlkBytesFp8;   // fp8 per-token factors, 2 x [3][32] f32
+constexpr int kWFacBytes = 3 * kBlk * 4;
+constexpr int kWP = 149504;                            // P: 2 buffers x 64 rows x 64 B
+constexpr int kWPBytes = kWRows * 64;
+constexpr int kWStats = kWP + 2 * kWPBytes;            // per token half and row {m, l, lr, -}
+constexpr int kWFlag = kWStats + 2 * kWRows * 16;      // overflow flag of the reference max
+constexpr int kWLdsBytes = kWFlag + 16;
+constexpr int kWStagePitch32 = 528;                    // epilogue staging: 512 B fp32 row + pad
+constexpr int kWStagePitch16 = 272;                    // 256 B bf16 row + pad
+static_assert(kWRing * kWSlot <= kWP && kWFac + 2 * kWFacBytes <= kWP, "wide LDS plan");
+static_assert(4 * 32 * kWStagePitch32 <= 2 * kWSlot, "epilogue staging fits the block slots");
+static_assert(kWLdsBytes <= 160 * 1024, "LDS budget");
+
+// bf16 block: 36 DMA instructions of 64 x 16 B; wave w loads tokens 8w .. 8w+7 of
+// every 128-byte column i (instruction i = 0..8): lane j takes token t = 8w + (j >> 3),
+// chunk 8i + ((j & 7) ^ s(t)), so the global offset is voff + 128 i and the LDS
+// destination 1024 w + 4096 i.
+template <int... I>
+__device__ __forceinline__ void issue_blk_bf16_seq(std::integer_sequence<int, I...>, const char* blk,
+                                                   uint32_t voff, uint32_t lds) {
+  (dma_16B<128 * I, kBlkGroupBytes * I>(blk, voff, lds), ...);
+}
+
+__device__ __forceinline__ void issue_blk_bf16(const char* blk, MLA_LDS char* dst, int w, int l) {
+  const int t = 8 * w + (l >> 3);
+  const uint32_t voff = (uint32_t)(t * kRowBytesBf16 + ((l & 7) ^ page_swz(t)) * 16);
+  issue_blk_bf16_seq(std::make_integer_sequence<int, 9>{}, blk, voff, lds_addr(dst) + 1024u * (uint32_t)w);
+}
+
+// fp8 block: the 18688 raw bytes as 1168 flat 16-byte chunks, instructions
+// k = w + 4i (i = 0..4) while k * 64 + lane < 1168.
+template <int I>
+__device__ __forceinline__ void issue_blk_fp8_one(const char* blk, uint32_t voff, uint32_t lds, int w, int l) {
+  if ((w + 4 * I) * 64 + l < kBlkChunksFp8) dma_16B<0, 4096 * I>(blk + 4096 * I, voff, lds);
+}
+
+template <int... I>
+__device__ __forceinline__ void issue_blk_fp8_seq(std::integer_sequence<int, I...>, const char* blk,
+                                                  uint32_t voff, uint32_t lds, int w, int l) {
+  (issue_blk_fp8_one<I>(blk, voff, lds, w, l), ...);
+}
+
+__device__ __forceinline__ void issue_blk_fp8(const char* blk, MLA_LDS char* dst, int w, int l) {
+  issue_blk_fp8_seq(std::make_integer_sequence<int, 5>{}, blk, (uint32_t)(1024 * w + 16 * l),
+                    lds_addr(dst) + 1024u * (uint32_t)w, w, l);
+}
+
+// Rows >= valid of this wave's own DMA share (tokens 8w .. 8w+7 of every column)
+// become zero: cache bytes past the end of a sequence may hold anything, and a
+// NaN there times a zero weight would still reach O.
+__device__ __forceinline__ void zero_own_tail(MLA_LDS char* blk, int valid, int w, int l) {
+  if (8 * w + 8 > valid && 8 * w + (l >> 3) >= valid) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      *reinterpret_cast<MLA_LDS u32x4_t*>(blk + kBlkGroupBytes * i + 1024 * w + 16 * l) = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// fp8 raw block -> swizzled bf16 block (exact) plus the per-token factors
+// {k_scale * softmax scale * log2 e, v_scale, 1 / v_scale}; rows >= valid become 0.
+__device__ __forceinline__ void convert_fp8_blk(const MLA_LDS char* raw, MLA_LDS char* conv,
+                                                MLA_LDS float* fac, int valid, int tid, float scale_log2) {
+#pragma unroll 1
+  for (int s = tid; s < kBlk * kChunksPerRow; s += 256) {
+    const int t = (s >> 3) & (kBlk - 1);
+    const int c = (s >> 8) * 8 + ((s & 7) ^ page_swz(t));
+    bf16x8_t v = {};
+    if (t < valid) {
+      const u32x2_t code = *reinterpret_cast<const MLA_LDS u32x2_t*>(raw + t * kRowBytesFp8 + c * 8);
+      const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[0], 1.0f, false);
+      const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[0], 1.0f, true);
+      const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[1], 1.0f, false);
+      const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[1], 1.0f, true);
+      v = bf16x8_t{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+    }
+    *reinterpret_cast<MLA_LDS bf16x8_t*>(conv + s * 16) = v;
+  }
+  if (tid < kBlk) {
+    float k = 0.f, v = 0.f;
+    if (tid < valid) {
+      const f32x2_t sc = *reinterpret_cast<const MLA_LDS f32x2_t*>(raw + tid * kRowBytesFp8 + kRow);
+      k = sc[0];
+      v = sc[1];
+    }
+    fac[tid] = k * scale_log2;
+    fac[kBlk + tid] = v;
+    fac[2 * kBlk + tid] = v != 0.f ? 1.0f / v : 0.f;
+  }
+}
+
+// S^T = K . Q^T of this wave's 16 tokens of a block for its 32 rows: 18 steps of 32
+// features, each one K fragment read (kPrefK steps ahead, a rolling register buffer)
+// and two 16x16x32 MFMAs (row halves rs = 0, 1).
+__device__ __forceinline__ void wide_scores(const MLA_LDS char* blk, const bf16x8_t (&qf)[2][18],
+                                            const uint32_t (&kbase)[2], f32x4_t (&sc)[2]) {
+  constexpr int kPrefK = 4;
+  uint32_t ka[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) ka[m] = opaque(lds_addr(blk) + kbase[m]);
+  bf16x8_t kbuf[kPrefK];
+#pragma unroll
+  for (int d = 0; d < kPrefK; ++d) kbuf[d] = lds_read_b128_at(ka[d & 1] + (d >> 1) * kBlkGroupBytes);
+  __builtin_amdgcn_sched_group_barrier(0x100, kPrefK, 0);
+  sc[0] = f32x4_t{};
+  sc[1] = f32x4_t{};
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) {
+    const bf16x8_t a = kbuf[kk % kPrefK];
+    const int nk = kk + kPrefK;
+    if (nk < 18) kbuf[kk % kPrefK] = lds_read_b128_at(ka[nk & 1] + (nk >> 1) * kBlkGroupBytes);
+    sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][kk], sc[0], 0, 0, 0);
+    sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][kk], sc[1], 0, 0, 0);
+    if (nk < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
+// O^T[this wave's 128 features][64 rows] += V^T . P^T over one block (2 steps of 16
+// tokens).  Step s: V^T fragment of feature block fb = two transpose reads (tokens
+// 16s + 8hh + 4r + 0..3, r = 0/1, hh = lane >> 5), P^T fragment of row block rb = one
+// 16-byte read of tokens 16s + 8hh .. +7 of row 32rb + (lane & 31).
+__device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS char* pbuf,
+                                        f32x16_t (&o)[4][2], const uint32_t (&vbase)[2][2],
+                                        const uint32_t (&pbase)[2]) {
+  uint32_t va_addr[2][2], pa[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int f1 = 0; f1 < 2; ++f1) va_addr[r][f1] = opaque(lds_addr(blk) + vbase[r][f1]);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) pa[s] = opaque(lds_addr(pbuf) + pbase[s]);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) pb[rb] = lds_read_b128_at(pa[s] + rb * 2048);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const uint32_t off = (uint32_t)((fb >> 1) * kBlkGroupBytes + s * 2048);
+      const bf16x4_t lo = lds_read_tr16_at(va_addr[0][fb & 1] + off);
+      const bf16x4_t hi = lds_read_tr16_at(va_addr[1][fb & 1] + off);
+      const bf16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[rb], o[fb][rb], 0, 0, 0);
+    }
+  }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kWLdsBytes];
+  MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  const int rg = w >> 1, th = w & 1;            // score phase: row group, token half
+  const int l16 = l & 15, g4 = l >> 4;
+  const int P = p.hdr[0];
+  const int U = p.hdr[1];
+  MLA_LDS int* ovf_flag = reinterpret_cast<MLA_LDS int*>(smem + kWFlag);
+  MLA_LDS f32x4_t* stats = reinterpret_cast<MLA_LDS f32x4_t*>(smem + kWStats);   // [2][64]
+
+  // Per-lane LDS offsets, fixed for the whole kernel.
+  // K fragment of step kk: token 16*th + l16, chunk 4kk + g4 (group kk >> 1, in-group
+  // chunk 4(kk & 1) + g4).
+  uint32_t kbase[2];
+  {
+    const int t = 16 * th + l16;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) kbase[m] = (uint32_t)(t * 8 + ((4 * m + g4) ^ page_swz(t))) * 16;
+  }
+  // V^T transpose reads: the 16-lane group g4 reads tokens 16s + 8*(l >> 5) + 4r + (l16 >> 2)
+  // at features 128w + 32fb + 16(g4 & 1) + 4(l16 & 3); chunk 16w + 4fb + 2(g4 & 1) +
+  // ((l16 >> 1) & 1) lies in group 2w + (fb >> 1) at in-group chunk
+  // 4(fb & 1) + 2(g4 & 1) + ((l16 >> 1) & 1).  s and fb >> 1 only add offsets.
+  uint32_t vbase[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int f1 = 0; f1 < 2; ++f1) {
+      const int t = 8 * (l >> 5) + 4 * r + (l16 >> 2);
+      const int cin = 4 * f1 + 2 * (g4 & 1) + ((l16 >> 1) & 1);
+      vbase[r][f1] = (uint32_t)(2 * w * kBlkGroupBytes + (t * 8 + (cin ^ page_swz(t))) * 16 + 8 * (l16 & 1));
+    }
+  // P rows: 64 B = 4 chunks of 8 tokens; chunk a of row R sits at position a ^ ((R >> 2) & 3)
+  // so that 16 consecutive rows reading one chunk hit 16 distinct bank groups.
+  uint32_t pbase[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int R = l & 31;
+    pbase[s] = (uint32_t)(R * 64 + (((2 * s + (l >> 5)) ^ ((R >> 2) & 3)) * 16));
+  }
+
+  for (int u = blockIdx.x; u < U; u += gridDim.x) {
+    int pi, hg;
+    unit_to_pair(u, p.n_hg, &pi, &hg);
+    if (pi >= P) continue;
+    const int4 pr = p.pairs[pi];
+    const int b = pr.x, t_begin = pr.z, t_end = pr.w;
+    const int4 rq = p.req[b];
+    const int nsplit = rq.y, seq = rq.w;
+    const int nblk = t_end > t_begin ? (t_end - t_begin + kBlk - 1) / kBlk : 0;
+    const int pg0 = t_begin / kPage;
+    const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
+
+    // the two query rows this lane owns in the score phase: 32rg + 16rs + l16
+    int nvis[2];
+    bool row_ok[2];
+    int qhead[2], qtq[2];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const int r = 32 * rg + 16 * rs + l16;
+      const int hl = r / p.q_len, tq = r - hl * p.q_len;
+      qhead[rs] = hg * p.hg_heads + hl;
+      qtq[rs] = tq;
+      row_ok[rs] = qhead[rs] < p.N;
+      nvis[rs] = seq - p.q_len + 1 + tq;
+    }
+
+    PageIds ids;
+    load_page_ids(ids, p, b, pg0, pg1, l);
+    // DMA destination of block j: ring slot j % 4 (bf16 slot, or fp8 raw slot)
+    auto issue = [&](int j) {
+      const char* pg = page_ptr(ids, p, b, pg0 + (j >> 1), pg1, l, FP8);
+      if constexpr (FP8)
+        issue_blk_fp8(pg + (j & 1) * kBlkBytesFp8, smem + kWRaw + (j & (kWRing - 1)) * kBlkBytesFp8, w, l);
+      else
+        issue_blk_bf16(pg + (j & 1) * kBlkBytesBf16, smem + (j & (kWRing - 1)) * kWSlot, w, l);
+    };
+    auto valid_of = [&](int j) {
+      const int v = t_end - (t_begin + kBlk * j);
+      return v < kBlk ? v : kBlk;
+    };
+    if (nblk > 0) issue(0);
+
+    // query fragments (B operand of the 16x16x32 MFMA): row 32rg + 16rs + l16, features
+    // 32kk + 8*g4 .. +7.  Padding rows (head >= N) load head 0 and are zeroed.
+    bf16x8_t qf[2][18];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qtq[rs] * p.q_st +
+                             (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
+      if (!row_ok[rs]) {
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = bf16x8_t{};
+      }
+    }
+    // Wait for the query here: the compiler would otherwise wait at its first use,
+    // after block 1's DMA is in flight, and so wait for that DMA as well.
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
+
+    f32x16_t o[4][2];
+    float m[2], lsum[2], lrsum[2], m_seen[2];
+    int ovf = 0;
+    float m_restart[2] = {-INFINITY, -INFINITY};
+    for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[fb][rb] = f32x16_t{};
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        m[rs] = m_restart[rs];
+        lsum[rs] = 0.f;
+        lrsum[rs] = 0.f;
+        m_seen[rs] = -INFINITY;
+      }
+      ovf = 0;
+      if (tid == 0) *ovf_flag = 0;
+      if (attempt > 0 && nblk > 0) {
+        load_page_ids(ids, p, b, pg0, pg1, l);
+        issue(0);
+      }
+      // block 0 has landed (the query too); the barrier also publishes the flag reset
+      wait_vmcnt<0>();
+      if constexpr (!FP8) {
+        if (nblk == 1) zero_own_tail(smem, valid_of(0), w, l);
       }
       lds_barrier();
-      const int rr = tid >> 4;                 // row 0..15
-      const int fp = tid & 15;                 // features 64*j + 4*fp + [0,4), j = 0..7:
-                                               // 16 lanes of a row store 256 contiguous bytes
-      float mw[4], lw[4], lrw[4];
-      float M = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mw[k] = stat[(k * 16 + rr) * 4];
-        lw[k] = stat[(k * 16 + rr) * 4 + 1];
-        lrw[k] = stat[(k * 16 + rr) * 4 + 2];
-        M = fmaxf(M, mw[k]);
+      if constexpr (FP8) {
+        if (nblk > 0)
+          convert_fp8_blk(smem + kWRaw, smem, reinterpret_cast<MLA_LDS float*>(smem + kWFac), valid_of(0), tid,
+                          p.scale_log2);
       }
-      const float Mb = M == -INFINITY ? 0.f : M;
-      float wgt[4], L = 0.f, LR = 0.f;
+      if (nblk > 1) issue(1);
+      if (nblk > 2) issue(2);
+      if constexpr (FP8) lds_barrier();
+
+      // One loop pass per block plus a final pass that only runs the last block's PV
+      // (a single PV call site keeps the accumulators in one place).
+      for (int j = 0; j <= nblk; ++j) {
+        const bool has = j < nblk;
+        const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kWRing - 1))) * kWSlot;
+        const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kWFac + (j & 1) * kWFacBytes);
+        const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
+
+        f32x4_t sc[2] = {};
+        if (has) wide_scores(cur, qf, kbase, sc);
+
+        // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
+        // Element i of row half rs is token tok0 + i.
+        float mt[2];
+        {
+          f32x4_t kf;
+          if constexpr (FP8) kf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 16 * th + 4 * g4);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        wgt[k] = __builtin_amdgcn_exp2f(mw[k] - Mb);
-        L += wgt[k] * lw[k];
-        LR += wgt[k] * lrw[k];
-      }
-      const float inv = LR > 0.f ? 1.0f / LR : 0.f;
-      const float lse_v = L > 0.f ? (Mb + __builtin_log2f(L)) * kLn2 : -INFINITY;
-      const int rhl = rr / p.q_len, rtq = rr - rhl * p.q_len;
-      const int rhead = hg * p.hg_heads + rhl;
-      if (rhead < p.N) {
-        f32x4_t acc[8];
+          for (int rs = 0; rs < 2; ++rs) {
+            mt[rs] = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + 4 * fp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += wgt[k] * *reinterpret_cast<const MLA_LDS f32x4_t*>(src + 64 * j);
-        }
-        if (nsplit == 1) {
-          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + 4 * fp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bf16x4_t v = {(__bf16)(acc[j][0] * inv), (__bf16)(acc[j][1] * inv), (__bf16)(acc[j][2] * inv),
-                                (__bf16)(acc[j][3] * inv)};
-            *reinterpret_cast<bf16x4_t*>(orow + 64 * j) = v;
+            for (int i = 0; i < 4; ++i) {
+              float x = sc[rs][i] * (FP8 ? kf[i] : p.scale_log2);
+              x = (tok0 + i < nvis[rs]) ? x : -INFINITY;
+              sc[rs][i] = x;
+              mt[rs] = fmaxf(mt[rs], x);
+            }
+            mt[rs] = fmaxf(mt[rs], shfl_xor_f(mt[rs], 16));
+            mt[rs] = fmaxf(mt[rs], shfl_xor_f(mt[rs], 32));
+            mt[rs] = has ? mt[rs] : -INFINITY;        // the final pass has no block
           }
-          if (fp == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
-        } else {
-          float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 4 * fp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(prow + 64 * j) = acc[j] * inv;
-          if (fp == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
         }
+        if (has && attempt == 0 && j == 0) {
+          // reference max of each row from the unit's first block: the two token halves
+          // of a row live in two waves, so their maxima meet in LDS
+          if (g4 == 0) {
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = mt[rs];
+          }
+          lds_barrier();
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs) {
+            const int R = 32 * rg + 16 * rs + l16;
+            m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+          }
+        }
+        float base[2];
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          m_seen[rs] = fmaxf(m_seen[rs], mt[rs]);
+          base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
+          ovf |= (mt[rs] > base[rs] + kRefSlack) ? 1 : 0;
+        }
+
+        // PV of the previous block overlaps this block's exponentials
+        if (j > 0) {
+          const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kWRing - 1))) * kWSlot;
+          wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
+        }
+        if (!has) break;
+
+        // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
+        // the sums keep both the exact weights (LSE) and the rounded ones (O).
+        {
+          f32x4_t vf, ivf;
+          if constexpr (FP8) {
+            vf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + kBlk + 16 * th + 4 * g4);
+            ivf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 2 * kBlk + 16 * th + 4 * g4);
+          }
+          MLA_LDS char* pw = smem + kWP + (j & 1) * kWPBytes;
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs) {
+            bf16x4_t pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pr = __builtin_amdgcn_exp2f(sc[rs][i] - base[rs]);
+              const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
+              pk[i] = rr;
+              lsum[rs] += pr;
+              lrsum[rs] += FP8 ? (float)rr * ivf[i] : (float)rr;
+            }
+            // row R, tokens 16th + 4g4 .. +3: chunk 2th + (g4 >> 1), half g4 & 1
+            const int R = 32 * rg + 16 * rs + l16;
+            const int a = 2 * th + (g4 >> 1);
+            *reinterpret_cast<MLA_LDS bf16x4_t*>(pw + R * 64 + ((a ^ ((R >> 2) & 3)) * 16) + 8 * (g4 & 1)) = pk;
+          }
+        }
+
+        if (j + 1 < nblk) {
+          // this wave's share of block j+1 has landed when at most block j+2's
+          // instructions are still outstanding (9 per wave for bf16; 5, 5, 5, 4 for fp8)
+          if (j + 2 < nblk) {
+            if constexpr (FP8) {
+              if (w == 3) wait_vmcnt<4>();
+              else wait_vmcnt<5>();
+            } else {
+              wait_vmcnt<9>();
+            }
+          } else {
+            wait_vmcnt<0>();
+          }
+          if constexpr (!FP8) {
+            if (j + 2 == nblk) zero_own_tail(smem + ((j + 1) & (kWRing - 1)) * kWSlot, valid_of(j + 1), w, l);
+          }
+        }
+        lds_barrier();                              // Y(j)
+        if (j + 3 < nblk) issue(j + 3);
+        if constexpr (FP8) {
+          if (j + 1 < nblk)
+            convert_fp8_blk(smem + kWRaw + ((j + 1) & (kWRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kWSlot,
+                            reinterpret_cast<MLA_LDS float*>(smem + kWFac + ((j + 1) & 1) * kWFacBytes),
+                            valid_of(j + 1), tid, p.scale_log2);
+          lds_barrier();                            // Z(j+1)
+        }
+      }
+      // any row over the reference slack: the whole workgroup redoes the unit
+      if (ovf) *ovf_flag = 1;
+      lds_barrier();
+      const int redo = *ovf_flag;
+      lds_barrier();
+      if (redo == 0) break;
+      // restart with the largest score seen in either token half of each row
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const float ms = fmaxf(m_seen[rs], shfl_xor_f(m_seen[rs], 16));
+        m_seen[rs] = fmaxf(ms, shfl_xor_f(ms, 32));
+      }
+      if (g4 == 0) {
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = m_seen[rs];
+      }
+      lds_barrier();
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const int R = 32 * rg + 16 * rs + l16;
+        m_restart[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
       }
       lds_barrier();
     }
+
+    // ---- epilogue ----
+    const size_t slot = (size_t)pi * p.n_hg + hg;
+    const bool single = nsplit == 1;
+    // row sums: over the 4 lane groups of this wave, then over the two token halves
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      float a = lsum[rs] + shfl_xor_f(lsum[rs], 16);
+      a += shfl_xor_f(a, 32);
+      float c = lrsum[rs] + shfl_xor_f(lrsum[rs], 16);
+      c += shfl_xor_f(c, 32);
+      if (g4 == 0) stats[th * kWRows + 32 * rg + 16 * rs + l16] = f32x4_t{m[rs], a, c, 0.f};
+    }
+    lds_barrier();
+    if (th == 0 && g4 == 0) {
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const int R = 32 * rg + 16 * rs + l16;
+        const float lt = stats[R][1] + stats[kWRows + R][1];
+        const float lse_v = lt > 0.f ? (m[rs] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
+        if (row_ok[rs]) {
+          if (single) p.lse[((int64_t)b * p.q_len + qtq[rs]) * p.N + qhead[rs]] = lse_v;
+          else p.part_lse[slot * p.m_wg + R] = lse_v;
+        }
+      }
+    }
+    // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5) + jj.
+    // Each row block is staged through this wave's own LDS region and written back
+    // row-contiguously (512 B fp32 or 256 B bf16 per row and wave).
+    MLA_LDS char* stage = smem + w * (32 * kWStagePitch32);
+    const int c32 = l & 31, h32 = l >> 5;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int R = 32 * rb + c32;
+      const float lr_row = stats[R][2] + stats[kWRows + R][2];
+      const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
+      if (single) {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x4_t v = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
+                                (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
+            *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fb + 8 * i + 4 * h32) * 2) = v;
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int row = 4 * k + (l >> 4);
+          const int Rr = 32 * rb + row;
+          const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
+          const int head_r = hg * p.hg_heads + hl_r;
+          const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + l16 * 16);
+          if (head_r < p.N) {
+            uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
+            *reinterpret_cast<u32x4_t*>(orow + 128 * w + 8 * l16) = v;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4_t v = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
+                               o[fb][rb][4 * i + 3] * inv};
+            *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fb + 8 * i + 4 * h32) * 4) = v;
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int row = 2 * k + h32;
+          const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch32 + c32 * 16);
+          float* prow = p.part_o + (slot * p.m_wg + 32 * rb + row) * kLatent + 128 * w + 4 * c32;
+          *reinterpret_cast<u32x4_t*>(prow) = v;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
+    }
+    lds_barrier();                                          // LDS free before the next unit's DMA
   }
 }
 
@@ -869,7 +1197,7 @@ inline bool decode_shape(int32_t B, int32_t q_len, int32_t N, int32_t num_splits
   if (B < 1 || (q_len != 1 && q_len != 2) || N < 1 || N > MLA_MAX_HEADS) return false;
   if (num_splits < 0 || num_splits > 4096) return false;
   s->wide = q_len * N > 16;
-  s->m_wg = s->wide ? 128 : 16;
+  s->m_wg = s->wide ? kWRows : 16;
   s->hg_heads = s->m_wg / q_len;
   s->n_hg = (N + s->hg_heads - 1) / s->hg_heads;
   int64_t mp;
@@ -990,11 +1318,11 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   if (grid > max_units) grid = (max_units + 7) / 8 * 8;
   if (grid < 8) grid = 8;
   if (kv_dtype == MLA_KV_BF16) {
-    if (s.wide) hipLaunchKernelGGL((decode_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0, hs, p);
-    else hipLaunchKernelGGL((decode_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
+    if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
+    else hipLaunchKernelGGL((decode_narrow_kernel<false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
   } else {
-    if (s.wide) hipLaunchKernelGGL((decode_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0, hs, p);
-    else hipLaunchKernelGGL((decode_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
+    if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true>), dim3((unsigned)grid), dim3(256), 0, hs, p);
+    else hipLaunchKernelGGL((decode_narrow_kernel<true>), dim3((unsigned)grid), dim3(256), 0, hs, p);
   }
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   if (num_splits != 1) {

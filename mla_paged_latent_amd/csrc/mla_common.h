@@ -69,6 +69,23 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const MLA_LDS char* base, uint
       reinterpret_cast<MLA_LDS bf16x4_t*>(const_cast<MLA_LDS char*>(base) + byte_off));
 }
 
+// LDS reads at a 32-bit LDS byte address (a base the caller made opaque, plus a
+// compile-time offset that lands in the instruction's offset field).
+__device__ __forceinline__ bf16x8_t lds_read_b128_at(uint32_t addr) {
+  return *reinterpret_cast<const MLA_LDS bf16x8_t*>((uintptr_t)addr);
+}
+
+__device__ __forceinline__ bf16x4_t lds_read_tr16_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<MLA_LDS bf16x4_t*>((uintptr_t)addr));
+}
+
+// Hides a value from the optimiser: address arithmetic done on the result is not
+// hoisted out of loops (where it would hold one register per unrolled access).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // One 1 KiB global->LDS copy: lane l's 16 bytes at sbase + voff + IMM land at LDS
 // byte address lds_base + LDS_ADD + 16 * l.  sbase must be wave-uniform (SGPR pair),
 // voff a 32-bit per-lane offset, IMM < 4096.  The instruction adds its immediate to
@@ -95,21 +112,30 @@ __device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Page layout in LDS.  A bf16 page is 64 token rows x 72 chunks of 16 B (8 bf16).
-// It is stored column-group major: group G = c >> 3 (128 B of every row) holds the
-// 64 tokens x 8 chunks, and inside a group chunk c of token t sits at position
-// t*8 + ((c & 7) ^ s(t)) with s(t) = ((t & 3) << 1) | ((t >> 2) & 1):
-//     slot(t, c) = (c >> 3) * 512 + t * 8 + ((c & 7) ^ s(t)),  byte = 16 * slot.
-// s is a bijection on t mod 8, so a ds_read_b128 by 8 consecutive tokens at one
-// chunk hits 8 distinct 16-byte bank groups, and a transpose read of 4 consecutive
-// tokens x 2 adjacent chunks (c even, c + 1) does too (s(t) >> 1 differs across
-// the 4).  A 1 KiB DMA instruction k fills group k >> 3, tokens 8*(k & 7) .. +7,
-// so each lane's global offset is a per-lane constant plus a wave-uniform term.
+// Layout of cache rows in LDS.  A block of T token rows (T = 64 for a page, 32 for
+// a half page) x 72 chunks of 16 B (8 bf16) is stored column-group major: group
+// G = c >> 3 (128 B of every row) holds the T tokens x 8 chunks, and inside a group
+// chunk c of token t sits at position t*8 + ((c & 7) ^ s(t)):
+//     slot(t, c) = (c >> 3) * 8T + t * 8 + ((c & 7) ^ s(t)),  byte = 16 * slot,
+// with s(t) the 3-bit reversal of (t >> 1) & 7.  gfx950 LDS serves 256 B (64 banks)
+// per clock, i.e. 16 slots; a slot's bank group is slot & 15 = 8*(t & 1) + position.
+//  * ds_read_b128 of one chunk by 16 consecutive tokens: for each parity of t the 8
+//    tokens have distinct (t >> 1) & 7, hence distinct s(t): 16 distinct groups.
+//  * transpose reads of 4 consecutive tokens (t0 = 0 mod 4) x 4 chunks (one 4-aligned
+//    chunk quad, 32 lanes): tokens t0 and t0 + 2 differ in bit 0 of (t >> 1), i.e. in
+//    bit 2 of s, so their chunk quads land in different halves of the 8 positions.
+//  * transpose reads of 8 consecutive tokens x 2 chunks: s(t) >> 1 takes 4 distinct
+//    values over the 4 tokens of each parity.
+// A 1 KiB DMA instruction fills 8 consecutive tokens of one group; the swizzle only
+// permutes 16-byte chunks inside each token's 128 B, so each lane's global offset
+// is a per-lane constant plus a wave-uniform term.
 // ---------------------------------------------------------------------------
-constexpr int kGroupSlots = 512;                      // 64 tokens x 8 chunks
+constexpr int kGroupSlots = 512;                      // page: 64 tokens x 8 chunks
 constexpr int kGroupBytes = kGroupSlots * 16;         // 8192
 
-__device__ __forceinline__ int page_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+__device__ __forceinline__ int page_swz(int t) {
+  return (((t >> 1) & 1) << 2) | ((t >> 1) & 2) | ((t >> 3) & 1);
+}
 
 __device__ __forceinline__ int page_slot(int t, int c) {
   return (c >> 3) * kGroupSlots + t * 8 + ((c & 7) ^ page_swz(t));
