@@ -50,13 +50,48 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   const int w = wave_id();
   const int l = lane_id();
 
-  // stage W[h][0:KK][n0:n0+NT] into LDS (row-padded)
+  // W[h][0:KK][n0:n0+NT] and the first token block's activation fragments are all
+  // requested before anything waits, so a workgroup keeps its whole tile in flight.
   const uint16_t* wh = W + (int64_t)h * KK * NN + n0;
   constexpr int kChunksPerRow = NT / 8;
-  for (int i = tid; i < KK * kChunksPerRow; i += 256) {
+  constexpr int kTileChunks = KK * kChunksPerRow;
+  static_assert(kTileChunks % 256 == 0, "tile chunks per thread");
+  constexpr int kPerThread = kTileChunks / 256;
+  u32x4_t wv[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int i = tid + 256 * j;
     const int k = i / kChunksPerRow, c = i % kChunksPerRow;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)k * NN + c * 8);
-    *reinterpret_cast<MLA_LDS u32x4_t*>(lds + k * Cfg::kRowBytes + c * 16) = v;
+    wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)k * NN + c * 8);
+  }
+
+  const int nb = w % Cfg::kNB;          // n block of this wave
+  const int kh = w / Cfg::kNB;          // K slice of this wave
+  const int g = l >> 4, lg = l & 15;
+  // transpose-read address pieces: 16-lane group g covers n = 16*(g&1) + [0,16) and
+  // k rows 8*(g>>1) + 4*r + (lg>>2) for read r; lane supplies column 4*(lg&3).
+  const uint32_t tr_col = (uint32_t)((nb * 32 + 16 * (g & 1) + 4 * (lg & 3)) * 2);
+  const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
+
+  bf16x8_t bfrag[Cfg::kKSteps];
+  auto load_act = [&](int64_t tb) {
+    const int64_t trow = tb + (l & 31);
+    const bool t_ok = trow < T;
+    const uint16_t* arow = A + (t_ok ? trow : 0) * a_st + h * a_sh;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
+      const int k0 = kh * Cfg::kKPerWave + ks * 16;
+      bfrag[ks] = *reinterpret_cast<const bf16x8_t*>(arow + k0 + 8 * (l >> 5));
+      if (!t_ok) bfrag[ks] = bf16x8_t{};
+    }
+  };
+  load_act(0);
+
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int i = tid + 256 * j;
+    const int k = i / kChunksPerRow, c = i % kChunksPerRow;
+    *reinterpret_cast<MLA_LDS u32x4_t*>(lds + k * Cfg::kRowBytes + c * 16) = wv[j];
   }
   if (COPY_PE && blockIdx.x == 0) {
     for (int64_t i = tid; i < T * 8; i += 256) {
@@ -68,29 +103,19 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   }
   lds_barrier();
 
-  const int nb = w % Cfg::kNB;          // n block of this wave
-  const int kh = w / Cfg::kNB;          // K slice of this wave
-  const int g = l >> 4, lg = l & 15;
-  // transpose-read address pieces: 16-lane group g covers n = 16*(g&1) + [0,16) and
-  // k rows 8*(g>>1) + 4*r + (lg>>2) for read r; lane supplies column 4*(lg&3).
-  const uint32_t tr_col = (uint32_t)((nb * 32 + 16 * (g & 1) + 4 * (lg & 3)) * 2);
-  const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
-
   for (int64_t tb = 0; tb < T; tb += 32) {
     const int64_t trow = tb + (l & 31);
     const bool t_ok = trow < T;
-    const uint16_t* arow = A + (t_ok ? trow : 0) * a_st + h * a_sh;
+    if (tb > 0) load_act(tb);
     f32x16_t acc = {};
-#pragma unroll 4
+#pragma unroll
     for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
       const int k0 = kh * Cfg::kKPerWave + ks * 16;
-      bf16x8_t b = {};
-      if (t_ok) b = *reinterpret_cast<const bf16x8_t*>(arow + k0 + 8 * (l >> 5));
       const uint32_t r0 = (uint32_t)((k0 + tr_row0) * Cfg::kRowBytes) + tr_col;
       const bf16x4_t lo = lds_read_tr16(lds, r0);
       const bf16x4_t hi = lds_read_tr16(lds, r0 + 4 * Cfg::kRowBytes);
       const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[ks], acc, 0, 0, 0);
     }
     if constexpr (KSPLIT > 1) {
       // waves with kh > 0 hand their partial tile to the kh == 0 wave of the same n block

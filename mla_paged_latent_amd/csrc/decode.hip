@@ -26,6 +26,7 @@
 //                        pages double-buffered, the 4 waves split each page's tokens
 //   Both write the final output (single split) or float32 partials; then
 //   merge_kernel         LSE-weighted combine of the partials of split requests
+#include <type_traits>
 #include <utility>
 
 #include "mla_common.h"
@@ -894,16 +895,17 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       if (nblk > 2) issue(2);
       if constexpr (FP8) lds_barrier();
 
-      // One loop pass per block plus a final pass that only runs the last block's PV
-      // (a single PV call site keeps the accumulators in one place).
-      for (int j = 0; j <= nblk; ++j) {
-        const bool has = j < nblk;
+      // Block step: scores of block j, their weights into P(j), interleaved (WITH_PV)
+      // with the PV MFMAs of block j-1, then the hand-over to block j+1.  Block 0 runs
+      // without PV (peeled) so that the steady-state body is one straight-line region.
+      auto step = [&](int j, auto with_pv) {
+        constexpr bool WITH_PV = decltype(with_pv)::value;
         const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kWRing - 1))) * kWSlot;
         const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kWFac + (j & 1) * kWFacBytes);
         const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
 
-        f32x4_t sc[2] = {};
-        if (has) wide_scores(cur, qf, kbase, sc);
+        f32x4_t sc[2];
+        wide_scores(cur, qf, kbase, sc);
 
         // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
         // Element i of row half rs is token tok0 + i.
@@ -923,21 +925,22 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
             }
             mt[rs] = fmaxf(mt[rs], shfl_xor_f(mt[rs], 16));
             mt[rs] = fmaxf(mt[rs], shfl_xor_f(mt[rs], 32));
-            mt[rs] = has ? mt[rs] : -INFINITY;        // the final pass has no block
           }
         }
-        if (has && attempt == 0 && j == 0) {
-          // reference max of each row from the unit's first block: the two token halves
-          // of a row live in two waves, so their maxima meet in LDS
-          if (g4 == 0) {
+        if constexpr (!WITH_PV) {
+          if (attempt == 0) {
+            // reference max of each row from the unit's first block: the two token halves
+            // of a row live in two waves, so their maxima meet in LDS
+            if (g4 == 0) {
 #pragma unroll
-            for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = mt[rs];
-          }
-          lds_barrier();
+              for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = mt[rs];
+            }
+            lds_barrier();
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs) {
-            const int R = 32 * rg + 16 * rs + l16;
-            m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+            for (int rs = 0; rs < 2; ++rs) {
+              const int R = 32 * rg + 16 * rs + l16;
+              m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+            }
           }
         }
         float base[2];
@@ -949,11 +952,10 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         }
 
         // PV of the previous block overlaps this block's exponentials
-        if (j > 0) {
+        if constexpr (WITH_PV) {
           const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kWRing - 1))) * kWSlot;
           wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
         }
-        if (!has) break;
 
         // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
         // the sums keep both the exact weights (LSE) and the rounded ones (O).
@@ -1008,6 +1010,13 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
                             valid_of(j + 1), tid, p.scale_log2);
           lds_barrier();                            // Z(j+1)
         }
+      };
+      if (nblk > 0) {
+        step(0, std::false_type{});
+        for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
+        const int jl = nblk - 1;
+        wide_pv(smem + (FP8 ? (jl & 1) : (jl & (kWRing - 1))) * kWSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase,
+                pbase);
       }
       // any row over the reference slack: the whole workgroup redoes the unit
       if (ovf) *ovf_flag = 1;
@@ -1116,73 +1125,66 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: grid = (B * n_hg, ceil(m_wg / 16)); each wave merges 4 rows, each
-// lane 8 of the 512 latent features.
+// Split merge ([vLLM-MLA] §Prefill merge of partial states; §Triton MLA second stage):
+// o = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max_s lse_s), lse = max + ln sum w.
+// grid = (B * n_hg, m_wg / 4), 4 waves: one query row per wave, 8 features per lane;
+// the partial rows and LSEs of up to 8 splits are in flight together.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  // grid = (B * n_hg, ceil(m_wg / 16)): each wave merges 4 rows; lane s < nsplit fetches
-  // split s's lse, so the max and the weights take one load and a wave reduction; each
-  // lane then accumulates 8 of the 512 features over the splits, 4 splits' loads in flight.
   const int b = blockIdx.x / p.n_hg;
   const int hg = blockIdx.x - b * p.n_hg;
   const int4 rq = p.req[b];
   const int first = rq.x, nsplit = rq.y;
   if (nsplit <= 1) return;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  for (int j = 0; j < 4; ++j) {
-    const int r = blockIdx.y * 16 + w * 4 + j;
-    if (r >= p.m_wg) break;
-    const int hl = r / p.q_len, tq = r - hl * p.q_len;
-    const int head = hg * p.hg_heads + hl;
-    if (head >= p.N) continue;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < nsplit; s0 += 64) {
-      const int s = s0 + l;
-      const float ls = s < nsplit ? p.part_lse[((size_t)(first + s) * p.n_hg + hg) * p.m_wg + r] : -INFINITY;
-      M = fmaxf(M, ls);
-    }
+  const int r = blockIdx.y * 4 + w;
+  if (r >= p.m_wg) return;
+  const int hl = r / p.q_len, tq = r - hl * p.q_len;
+  const int head = hg * p.hg_heads + hl;
+  if (head >= p.N) return;
+  // Splits are taken 8 at a time: the 8 partial rows and their LSEs are loaded
+  // together (every lane reads the same LSE values), then folded into a running
+  // (max, weight sum, weighted sum) with the usual rescale when the max grows.
+  float M = -INFINITY;
+  f32x4_t a0 = {}, a1 = {};
+  float wsum = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    f32x4_t v[8][2];
+    float ls[8];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
-    const float Mb = M == -INFINITY ? 0.f : M;
-    f32x4_t a0 = {}, a1 = {};
-    float wsum = 0.f;
-    int s = 0;
-    for (; s + 4 <= nsplit; s += 4) {
-      f32x4_t v[4][2];
-      float wt[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const size_t slot = (size_t)(first + s + k) * p.n_hg + hg;
-        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
-        v[k][0] = src[0];
-        v[k][1] = src[1];
-        const float ls = p.part_lse[slot * p.m_wg + r];
-        wt[k] = ls == -INFINITY ? 0.f : __expf(ls - Mb);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        wsum += wt[k];
-        a0 += wt[k] * v[k][0];
-        a1 += wt[k] * v[k][1];
-      }
-    }
-    for (; s < nsplit; ++s) {
+    for (int k = 0; k < 8; ++k) {
+      const int s = s0 + k < nsplit ? s0 + k : nsplit - 1;          // clamp: in bounds, weight 0 below
       const size_t slot = (size_t)(first + s) * p.n_hg + hg;
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
-      const float ls = p.part_lse[slot * p.m_wg + r];
-      const float wt = ls == -INFINITY ? 0.f : __expf(ls - Mb);
-      wsum += wt;
-      a0 += wt * src[0];
-      a1 += wt * src[1];
+      v[k][0] = src[0];
+      v[k][1] = src[1];
+      ls[k] = s0 + k < nsplit ? p.part_lse[slot * p.m_wg + r] : -INFINITY;
     }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq * p.o_st + (int64_t)head * p.o_sh + 8 * l;
-    const bf16x8_t v = {(__bf16)(a0[0] * inv), (__bf16)(a0[1] * inv), (__bf16)(a0[2] * inv),
-                        (__bf16)(a0[3] * inv), (__bf16)(a1[0] * inv), (__bf16)(a1[1] * inv),
-                        (__bf16)(a1[2] * inv), (__bf16)(a1[3] * inv)};
-    *reinterpret_cast<bf16x8_t*>(orow) = v;
-    if (l == 0) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = wsum > 0.f ? Mb + __logf(wsum) : -INFINITY;
+    float mc = M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mc = fmaxf(mc, ls[k]);
+    if (mc == -INFINITY) continue;                                   // all splits so far empty
+    const float resc = M == -INFINITY ? 0.f : __expf(M - mc);
+    wsum *= resc;
+    a0 *= resc;
+    a1 *= resc;
+    M = mc;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wt = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - M);
+      wsum += wt;
+      a0 += wt * v[k][0];
+      a1 += wt * v[k][1];
+    }
   }
+  const float Mb = M == -INFINITY ? 0.f : M;
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq * p.o_st + (int64_t)head * p.o_sh + 8 * l;
+  const bf16x8_t v = {(__bf16)(a0[0] * inv), (__bf16)(a0[1] * inv), (__bf16)(a0[2] * inv),
+                      (__bf16)(a0[3] * inv), (__bf16)(a1[0] * inv), (__bf16)(a1[1] * inv),
+                      (__bf16)(a1[2] * inv), (__bf16)(a1[3] * inv)};
+  *reinterpret_cast<bf16x8_t*>(orow) = v;
+  if (l == 0) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = wsum > 0.f ? Mb + __logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1326,7 +1328,7 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   }
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   if (num_splits != 1) {
-    dim3 mg((unsigned)(B * s.n_hg), (unsigned)((s.m_wg + 15) / 16));
+    dim3 mg((unsigned)(B * s.n_hg), (unsigned)((s.m_wg + 3) / 4));
     hipLaunchKernelGGL(merge_kernel, mg, dim3(256), 0, hs, p);
   }
   return launch_status();
