@@ -335,8 +335,7 @@ __device__ __forceinline__ void narrow_page(const MLA_LDS char* pg, const MLA_LD
     s[i] = x;
     mt = fmaxf(mt, x);
   }
-  mt = fmaxf(mt, shfl_xor_f(mt, 16));
-  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+  mt = max_xor32(max_xor16(mt));
   if (first) st.m = mt;                                // reference from the unit's first page
   st.m_seen = fmaxf(st.m_seen, mt);
   const float base = st.m == -INFINITY ? 0.f : st.m;
@@ -499,10 +498,8 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
     // ---- epilogue ----
     const size_t slot = (size_t)pi * p.n_hg + hg;
     // combine the four token-slices of the waves through LDS
-    float l_w = ns.l + shfl_xor_f(ns.l, 16);
-    l_w += shfl_xor_f(l_w, 32);
-    float lr_w = ns.lr + shfl_xor_f(ns.lr, 16);
-    lr_w += shfl_xor_f(lr_w, 32);
+    const float l_w = sum_xor32(sum_xor16(ns.l));
+    const float lr_w = sum_xor32(sum_xor16(ns.lr));
     MLA_LDS float* obuf = reinterpret_cast<MLA_LDS float*>(smem);
     MLA_LDS float* stat = reinterpret_cast<MLA_LDS float*>(smem + 4 * 16 * kLatent * 4);
     const int g = l >> 4;
@@ -923,8 +920,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
               sc[rs][i] = x;
               mt[rs] = fmaxf(mt[rs], x);
             }
-            mt[rs] = fmaxf(mt[rs], shfl_xor_f(mt[rs], 16));
-            mt[rs] = fmaxf(mt[rs], shfl_xor_f(mt[rs], 32));
+            mt[rs] = max_xor32(max_xor16(mt[rs]));
           }
         }
         if constexpr (!WITH_PV) {
@@ -1027,8 +1023,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       // restart with the largest score seen in either token half of each row
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        const float ms = fmaxf(m_seen[rs], shfl_xor_f(m_seen[rs], 16));
-        m_seen[rs] = fmaxf(ms, shfl_xor_f(ms, 32));
+        m_seen[rs] = max_xor32(max_xor16(m_seen[rs]));
       }
       if (g4 == 0) {
 #pragma unroll
@@ -1049,10 +1044,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     // row sums: over the 4 lane groups of this wave, then over the two token halves
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
-      float a = lsum[rs] + shfl_xor_f(lsum[rs], 16);
-      a += shfl_xor_f(a, 32);
-      float c = lrsum[rs] + shfl_xor_f(lrsum[rs], 16);
-      c += shfl_xor_f(c, 32);
+      const float a = sum_xor32(sum_xor16(lsum[rs]));
+      const float c = sum_xor32(sum_xor16(lrsum[rs]));
       if (g4 == 0) stats[th * kWRows + 32 * rg + 16 * rs + l16] = f32x4_t{m[rs], a, c, 0.f};
     }
     lds_barrier();
