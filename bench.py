@@ -160,6 +160,15 @@ def run(args) -> dict:
     lse = torch.empty((w.B, w.q_len, w.N), dtype=torch.float32, device=dev)
     ws = torch.empty(M.decode_workspace_size(w.B, w.q_len, w.N, args.num_splits), dtype=torch.uint8,
                      device=dev)
+    if args.copy_calibration_mb > 0:
+        # one device-to-device copy of a known size: under a --pmc run its FETCH_SIZE /
+        # WRITE_SIZE give the counters' scale (see --traffic-record)
+        nb = args.copy_calibration_mb * 2**20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -238,6 +247,46 @@ def run(args) -> dict:
     return res
 
 
+DECODE_KERNELS = ("plan_kernel", "decode_wide_kernel", "decode_narrow_kernel", "merge_kernel")
+COPY_KERNEL = "copyBuffer"
+
+
+def _counter_rows(d: str, counter: str):
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], int(r.get("Dispatch_Id", 0) or 0), float(r["Counter_Value"])))
+    return out
+
+
+def traffic_record_from_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mb: int, command: str) -> dict:
+    """HBM bytes per mla_decode call from two rocprofv3 --pmc runs of this script
+    (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by what the
+    same counter reads for the calibration copy of copy_mb MiB in that run."""
+    res = {"workload": workload, "command": command, "copy_calibration_bytes": copy_mb * 2**20}
+    per_call = 0.0
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, name)
+        copies = [v for k, _, v in rows if COPY_KERNEL in k]
+        if not copies:
+            raise SystemExit(f"no calibration copy found in {d}")
+        scale = copy_mb * 2**20 / (max(copies) * 1024.0)
+        kern = {}
+        for k, _, v in rows:
+            for kn in DECODE_KERNELS:
+                if kn in k:
+                    kern.setdefault(kn, []).append(v * 1024.0 * scale)
+        med = {kn: sorted(v)[len(v) // 2] for kn, v in kern.items()}
+        res[name] = {"scale": round(scale, 4), "bytes_per_dispatch": {k: round(v) for k, v in med.items()}}
+        per_call += sum(med.values())
+    res["hbm_bytes_per_launch"] = round(per_call)
+    res["decode_hip_sha256"] = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +295,21 @@ def main():
     ap.add_argument("--workload", default="full_head", choices=sorted(MI.CONFIGS))
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run one device copy of this many MiB before the steps (counter calibration)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/decode_traffic_<workload>.json from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of this script made with --copy-calibration-mb; no GPU")
+    ap.add_argument("--traffic-command", default="", help="the profiling command, stored in the record")
     args = ap.parse_args()
+    if args.traffic_record:
+        rec = traffic_record_from_pmc(args.traffic_record[0], args.traffic_record[1], args.workload,
+                                      args.copy_calibration_mb, args.traffic_command)
+        path = os.path.join(ROOT, "profiles", f"decode_traffic_{args.workload}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the decode path shards by "
                                    "request (attention-DP) or heads (TP) with no exchange inside the "
