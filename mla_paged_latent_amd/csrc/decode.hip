@@ -11,10 +11,11 @@
 // "Triton und MLA", §Datenfluss and §Entwurfsmotivation (natural-log LSE returned).
 //
 // Structure (all on the caller's stream, no host synchronisation):
-//   plan_kernel          one workgroup: per-request split count and page-aligned token
-//                        ranges -> (request, split) pair table in the workspace
-//   decode_wide_kernel   q_len * N > 16: persistent grid, one work unit = (pair, head
-//                        group of 64 query rows); the unit's cache rows stream through
+//   split plan           computed inside the decode kernels from seq_lens: the batch is
+//                        cut into equal-cost streams of (request, token range) pieces,
+//                        one per workgroup and head group
+//   decode_wide_kernel   q_len * N > 16: one work unit = (stream, head group of 64
+//                        query rows); each piece's cache rows stream through
 //                        LDS in 32-token blocks (global->LDS DMA ring) and every query
 //                        row of the group scores against each staged block:
 //                          S^T = K . Q^T   (MFMA; wave w: 32 rows x 16 tokens, Q in
@@ -45,115 +46,212 @@ struct DecodeParams {
   const int32_t* seq_lens;
   int32_t B, q_len, N;
   int32_t n_hg;        // head groups per request
-  int32_t m_wg;        // query rows per work unit (16 narrow, 128 wide)
+  int32_t m_wg;        // query rows per work unit (16 narrow, 64 wide)
   int32_t hg_heads;    // heads per head group = m_wg / q_len
   float scale_log2;    // softmax_scale * log2(e)
   uint16_t* out;
   int64_t o_sb, o_st, o_sh;
   float* lse;
   // workspace views
-  int32_t* hdr;        // [0] pairs, [1] units
-  int4* req;           // per request: {first pair, splits, chunk, clamped seq_len}
-  int4* pairs;         // per pair: {request, split, token begin, token end}
-  float* part_lse;     // [pairs * n_hg * m_wg]
-  float* part_o;       // [pairs * n_hg * m_wg * 512]
-  int32_t max_pairs;
-  int32_t num_splits;  // 0 auto, 1 single, k forced
-  int32_t target_pairs;
+  int4* req;           // per request: {first partial slot, pieces, 0, clamped seq_len}
+  float* part_lse;     // [slots * n_hg * m_wg]
+  float* part_o;       // [slots * n_hg * m_wg * 512]
+  int32_t num_splits;  // 0 automatic, k >= 1 forced
+  int32_t n_streams;   // streams of the plan
+  int32_t n_units;     // n_streams x head groups, rounded for the sibling order
 };
 
-// unit -> (pair, head group).  Sibling head groups of one pair sit 8 units apart so
-// that, with a grid that is a multiple of 8, they run at the same time on the same
-// XCD (workgroups are dispatched round-robin over the 8 XCDs) and share the pair's
+// unit -> (stream, head group).  Sibling head groups of one stream sit 8 units apart
+// so that, with a grid that is a multiple of 8, they run at the same time on the same
+// XCD (workgroups are dispatched round-robin over the 8 XCDs) and share the stream's
 // pages through that XCD's L2.
-__device__ __forceinline__ void unit_to_pair(int u, int n_hg, int* pair, int* hg) {
+__device__ __forceinline__ void unit_to_stream(int u, int n_hg, int* stream, int* hg) {
   if (n_hg == 1) {
-    *pair = u;
+    *stream = u;
     *hg = 0;
   } else {
-    *pair = (u / (8 * n_hg)) * 8 + (u & 7);
+    *stream = (u / (8 * n_hg)) * 8 + (u & 7);
     *hg = (u >> 3) % n_hg;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split planner
+// Split plan ([vLLM-MLA] §FlashMLA: the split count follows seq_len and the number
+// of compute units; single-partition mode for batch invariance)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void plan_kernel(DecodeParams p) {
-  __shared__ long long red[256];
-  __shared__ int scan[256];
-  const int tid = threadIdx.x;
-  const int seq_cap = p.max_pages * kPage;
-  long long local = 0;
-  for (int b = tid; b < p.B; b += 256) {
-    int s = p.seq_lens[b];
-    s = s < 0 ? 0 : (s > seq_cap ? seq_cap : s);
-    local += s;
-  }
-  red[tid] = local;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const long long total = red[0];
-  // automatic mode: one common page-aligned chunk so that the whole batch makes
-  // about target_pairs (request, split) pairs
-  long long auto_chunk = (total + p.target_pairs - 1) / p.target_pairs;
-  auto_chunk = ((auto_chunk + kPage - 1) / kPage) * kPage;
-  if (auto_chunk < kPage) auto_chunk = kPage;
+// A stream is the ordered list of (request, token range) pieces one unit works
+// through; a unit is (stream, head group).
+//
+// num_splits == 0 (automatic): request b occupies a stretch of kSegOverhead +
+// pages(b) cost positions on one line (the overhead stands for the fixed cost of
+// a piece: its start-up and its partial row); the line is cut into n_streams
+// streams of T = ceil(total / n_streams) positions, one unit per workgroup and head
+// group, so that every workgroup gets the same amount of work whatever the length
+// mix.  The pages of b inside stream s form one piece; b is split when its pages
+// straddle a cut.  The piece of b in stream s writes partial slot b + s: the slots
+// of b + 1 all lie above those of b, so B + n_streams slots suffice.  Every
+// workgroup derives the plan from seq_lens itself (one prefix sum over the batch),
+// so there is no planning launch and no host synchronisation.
+//
+// num_splits == k >= 1: stream s is split s % k of request s / k, over page-aligned
+// chunks of ceil(seq / k) tokens; its partial slot is s.  k == 1 keeps one piece
+// per request (bit-identical results whatever the rest of the batch).
+//
+// The piece that holds a request's first page (head group 0) records
+// {first slot, number of pieces} in req[b] for the merge.
+constexpr int kSegOverhead = 2;                         // in pages
 
-  int base = 0;
-  for (int b0 = 0; b0 < p.B; b0 += 256) {
-    const int b = b0 + tid;
-    int ns = 0, chunk = kPage, s = 0;
-    if (b < p.B) {
-      s = p.seq_lens[b];
-      s = s < 0 ? 0 : (s > seq_cap ? seq_cap : s);
-      long long c;
-      if (p.num_splits == 0)
-        c = auto_chunk;
-      else if (p.num_splits == 1)
-        c = s > 0 ? s : 1;
-      else
-        c = (s + p.num_splits - 1) / p.num_splits;
-      c = ((c + kPage - 1) / kPage) * kPage;
-      if (c < kPage) c = kPage;
-      chunk = (int)c;
-      ns = s > 0 ? (int)((s + c - 1) / c) : 1;
+__device__ __forceinline__ int clamp_seq(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
+__device__ __forceinline__ int pages_of(int s) { return (s + kPage - 1) / kPage; }
+
+// LDS scratch of the planner: 256 exclusive prefixes, 4 wave totals, a 2-value result
+constexpr int kPlanLdsBytes = (256 + 4 + 2) * 8;
+
+// a workgroup-uniform 64-bit value read from LDS, moved to scalar registers
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+struct PlanTotals {
+  long long total;    // cost positions of the whole batch
+  long long T;        // positions per stream
+};
+
+// Thread tid sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
+// pre[tid] receives the exclusive prefix of those sums.
+__device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS long long* pre, int tid) {
+  const int cap = p.max_pages * kPage;
+  const int K = (p.B + 255) >> 8;
+  const int b0 = tid * K;
+  const int b1 = b0 + K < p.B ? b0 + K : p.B;
+  long long local = 0;
+  for (int b = b0; b < b1; ++b) local += kSegOverhead + pages_of(clamp_seq(p.seq_lens[b], cap));
+  const int l = tid & 63;
+  long long incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long v = __shfl_up(incl, d, 64);
+    if (l >= d) incl += v;
+  }
+  MLA_LDS long long* wtot = pre + 256;
+  if (l == 63) wtot[tid >> 6] = incl;
+  lds_barrier();
+  long long off = 0;
+  for (int k = 0; k < (tid >> 6); ++k) off += wtot[k];
+  pre[tid] = off + incl - local;
+  PlanTotals r;
+  r.total = uniform64(wtot[0] + wtot[1] + wtot[2] + wtot[3]);
+  r.T = (r.total + p.n_streams - 1) / p.n_streams;
+  lds_barrier();
+  return r;
+}
+
+// The request holding cost position X (< total) and the position where it starts.
+__device__ __forceinline__ void plan_find(const DecodeParams& p, MLA_LDS long long* pre, long long X, long long total, int tid,
+                          int* b_out, long long* c_out) {
+  MLA_LDS long long* sel = pre + 260;
+  const int cap = p.max_pages * kPage;
+  const int K = (p.B + 255) >> 8;
+  const int b0 = tid * K;
+  const int b1 = b0 + K < p.B ? b0 + K : p.B;
+  const long long e0 = pre[tid];
+  const long long e1 = tid < 255 ? pre[tid + 1] : total;
+  if (b0 < b1 && e0 <= X && X < e1) {
+    long long c = e0;
+    int b = b0;
+    for (; b < b1 - 1; ++b) {
+      const long long cb = kSegOverhead + pages_of(clamp_seq(p.seq_lens[b], cap));
+      if (X < c + cb) break;
+      c += cb;
     }
-    // exclusive scan of ns over the 256 requests of this block
-    scan[tid] = ns;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const int v = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
+    sel[0] = b;
+    sel[1] = c;
+  }
+  lds_barrier();
+  *b_out = __builtin_amdgcn_readfirstlane((int)sel[0]);
+  *c_out = uniform64(sel[1]);
+  lds_barrier();                                        // sel is rewritten by the next search
+}
+
+// One piece of a stream: request b, tokens [t_begin, t_end) of its seq (clamped)
+// tokens, the number of pieces of b and this piece's partial slot.
+struct Piece {
+  int b, t_begin, t_end, seq, nsplit, slot;
+};
+
+// Walks the pieces of stream s in order; every value is workgroup-uniform.  pre / tot
+// come from plan_prefix (automatic mode only).
+struct PieceIter {
+  long long lo, hi, c, T;
+  int b, s;
+  bool done;
+
+  __device__ __forceinline__ void init(const DecodeParams& p, MLA_LDS long long* pre, const PlanTotals& tot, int stream,
+                       int tid) {
+    s = stream;
+    done = false;
+    if (p.num_splits > 0) return;
+    T = tot.T;
+    lo = (long long)s * tot.T;
+    hi = lo + tot.T < tot.total ? lo + tot.T : tot.total;
+    if (lo >= tot.total) {
+      done = true;
+      return;
     }
-    const int incl = scan[tid];
-    const int block_total = scan[255];
-    if (b < p.B) {
-      const int first = base + incl - ns;
-      p.req[b] = make_int4(first, ns, chunk, s);
-      for (int k = 0; k < ns; ++k) {
-        const int pi = first + k;
-        if (pi < p.max_pairs) {
-          const int t0 = k * chunk;
-          const int t1 = (k + 1) * chunk < s ? (k + 1) * chunk : s;
-          p.pairs[pi] = make_int4(b, k, t0, t1 > t0 ? t1 : t0);
+    plan_find(p, pre, lo, tot.total, tid, &b, &c);
+  }
+
+  __device__ __forceinline__ bool next(const DecodeParams& p, int hg, int tid, Piece& pc) {
+    if (done) return false;
+    const int cap = p.max_pages * kPage;
+    if (p.num_splits > 0) {
+      done = true;
+      const int k = p.num_splits;
+      const int rb = s / k, sp = s - rb * k;
+      const int seq = clamp_seq(p.seq_lens[rb], cap);
+      int chunk = pages_of((seq + k - 1) / k) * kPage;
+      if (chunk < kPage) chunk = kPage;
+      const int ns = seq > 0 ? (seq + chunk - 1) / chunk : 1;
+      if (sp == 0 && hg == 0 && tid == 0) p.req[rb] = make_int4(rb * k, ns, 0, seq);
+      if (sp >= ns) return false;
+      const int t0 = sp * chunk;
+      const int t1 = t0 + chunk < seq ? t0 + chunk : seq;
+      pc = Piece{rb, t0, t1 > t0 ? t1 : t0, seq, ns, s};
+      return true;
+    }
+    while (b < p.B && c < hi) {
+      const int seq = clamp_seq(p.seq_lens[b], cap);
+      const int np = pages_of(seq);
+      const long long p0 = c + kSegOverhead;            // position of page 0
+      bool have = false;
+      if (np == 0) {
+        if (c >= lo) {
+          if (hg == 0 && tid == 0) p.req[b] = make_int4(0, 1, 0, 0);
+          pc = Piece{b, 0, 0, 0, 1, b + s};
+          have = true;
+        }
+      } else {
+        const long long a = lo > p0 ? lo : p0;
+        const long long e = hi < p0 + np ? hi : p0 + np;
+        if (a < e) {
+          const int sf = (int)(p0 / T), sl = (int)((p0 + np - 1) / T);
+          if (s == sf && hg == 0 && tid == 0) p.req[b] = make_int4(b + sf, sl - sf + 1, 0, seq);
+          const int t1 = (int)(e - p0) * kPage;
+          pc = Piece{b, (int)(a - p0) * kPage, t1 < seq ? t1 : seq, seq, sl - sf + 1, b + s};
+          have = true;
         }
       }
+      c = p0 + np;
+      ++b;
+      if (have) return true;
     }
-    base += block_total;
-    __syncthreads();
+    done = true;
+    return false;
   }
-  if (tid == 0) {
-    const int P = base < p.max_pairs ? base : p.max_pairs;
-    p.hdr[0] = P;
-    p.hdr[1] = p.n_hg == 1 ? P : ((P + 7) / 8) * 8 * p.n_hg;
-  }
-}
+};
 
 // ---------------------------------------------------------------------------
 // Page staging
@@ -239,7 +337,8 @@ constexpr int kFp8IVScale = kFp8VScale + 256;
 constexpr int kLdsFp8 = kFp8IVScale + 256;
 constexpr int kLdsPages = kLdsBf16 > kLdsFp8 ? kLdsBf16 : kLdsFp8;
 constexpr int kLdsFlag = kLdsPages;                    // overflow flag of the reference max
-constexpr int kLdsBytes = kLdsPages + 16;
+constexpr int kLdsPlan = kLdsFlag + 16;                // split-plan scratch
+constexpr int kLdsBytes = kLdsPlan + kPlanLdsBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 // fp8 raw page -> swizzled bf16 page (exact: every e4m3fn value is a bf16 value);
@@ -381,188 +480,192 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
-  const int P = p.hdr[0];
-  const int U = p.hdr[1];
 
-  for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    int pi, hg;
-    unit_to_pair(u, p.n_hg, &pi, &hg);
-    if (pi >= P) continue;
-    const int4 pr = p.pairs[pi];
-    const int b = pr.x, t_begin = pr.z, t_end = pr.w;
-    const int4 rq = p.req[b];
-    const int nsplit = rq.y, seq = rq.w;
-    const int pg0 = t_begin / kPage;
-    const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
-    const int first_nvis = seq - p.q_len + 1;          // visible tokens of query row 0
+  MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kLdsPlan);
+  PlanTotals tot{0, 1};
+  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
+  for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
+    int sid, hg;
+    unit_to_stream(u, p.n_hg, &sid, &hg);
+    if (sid >= p.n_streams) continue;
+    PieceIter it;
+    it.init(p, plan_lds, tot, sid, tid);
+    Piece pc;
+    while (it.next(p, hg, tid, pc)) {
+      const int b = pc.b, t_begin = pc.t_begin, t_end = pc.t_end, seq = pc.seq, nsplit = pc.nsplit;
+      const int pslot = pc.slot;
+      const int pg0 = t_begin / kPage;
+      const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
+      const int first_nvis = seq - p.q_len + 1;          // visible tokens of query row 0
 
-    // the row this lane owns in the S^T / O^T accumulators
-    const int r = l & 15;
-    const int hl = r / p.q_len, tq = r - hl * p.q_len;
-    const int head = hg * p.hg_heads + hl;
-    const bool row_ok = head < p.N;
-    const int nvis = seq - p.q_len + 1 + tq;
+      // the row this lane owns in the S^T / O^T accumulators
+      const int r = l & 15;
+      const int hl = r / p.q_len, tq = r - hl * p.q_len;
+      const int head = hg * p.hg_heads + hl;
+      const bool row_ok = head < p.N;
+      const int nvis = seq - p.q_len + 1 + tq;
 
-    // stage the unit's first page before loading the query fragments
-    MLA_LDS char* buf0 = smem + (FP8 ? kFp8Raw0 : 0);
-    MLA_LDS char* buf1 = smem + (FP8 ? kFp8Raw1 : kPageBytesBf16);
-    PageIds ids;
-    load_page_ids(ids, p, b, pg0, pg1, l);
-    if (pg1 > pg0) {
-      if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
-      else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
-    }
-
-    // query fragments (B operand): row r, features 32*kk + 8*(l>>4)
-    constexpr int NQ = 18;
-    bf16x8_t qf[NQ];
-    {
-      // padding rows (head >= N) load head 0 and are zeroed: no divergent loads
-      const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
-      const int off = 8 * (l >> 4);
-#pragma unroll
-      for (int kk = 0; kk < NQ; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + off);
-      if (!row_ok) {
-#pragma unroll
-        for (int kk = 0; kk < NQ; ++kk) qf[kk] = bf16x8_t{};
-      }
-    }
-
-    NarrowState ns;
-    MLA_LDS int* ovf = reinterpret_cast<MLA_LDS int*>(smem + kLdsFlag);
-    float m_restart = -INFINITY;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) ns.o[i] = f32x4_t{};
-      ns.m = m_restart;
-      ns.l = 0.f;
-      ns.lr = 0.f;
-      ns.m_seen = -INFINITY;
-      // reset the flag and make the reset visible before any wave can read it
-      // (a unit without pages reads it right after this barrier)
-      if (tid == 0) *ovf = 0;
-      lds_barrier();
-      if (attempt > 0 && pg1 > pg0) {
-        load_page_ids(ids, p, b, pg0, pg1, l);
+      // stage the unit's first page before loading the query fragments
+      MLA_LDS char* buf0 = smem + (FP8 ? kFp8Raw0 : 0);
+      MLA_LDS char* buf1 = smem + (FP8 ? kFp8Raw1 : kPageBytesBf16);
+      PageIds ids;
+      load_page_ids(ids, p, b, pg0, pg1, l);
+      if (pg1 > pg0) {
         if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
         else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
       }
 
-      for (int pg = pg0; pg < pg1; ++pg) {
-        const bool odd = ((pg - pg0) & 1) != 0;
-        MLA_LDS char* cur = odd ? buf1 : buf0;
-        MLA_LDS char* nxt = odd ? buf0 : buf1;
-        if (pg + 1 < pg1) {
-          if constexpr (FP8) {
-            issue_page_fp8(page_ptr(ids, p, b, pg + 1, pg1, l, true), nxt, w, l);
-            if (w == 0) wait_vmcnt<10>();
-            else wait_vmcnt<9>();
-          } else {
-            issue_page_bf16(page_ptr(ids, p, b, pg + 1, pg1, l, false), nxt, w, l);
-            wait_vmcnt<18>();
-          }
-        } else {
-          wait_vmcnt<0>();
+      // query fragments (B operand): row r, features 32*kk + 8*(l>>4)
+      constexpr int NQ = 18;
+      bf16x8_t qf[NQ];
+      {
+        // padding rows (head >= N) load head 0 and are zeroed: no divergent loads
+        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
+        const int off = 8 * (l >> 4);
+#pragma unroll
+        for (int kk = 0; kk < NQ; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + off);
+        if (!row_ok) {
+#pragma unroll
+          for (int kk = 0; kk < NQ; ++kk) qf[kk] = bf16x8_t{};
         }
-        lds_barrier();
-        const int tok0 = pg * kPage;
-        const int valid = seq - tok0 < kPage ? seq - tok0 : kPage;
-        const MLA_LDS char* page;
-        MLA_LDS float* ksc = reinterpret_cast<MLA_LDS float*>(smem + kFp8KScale);
-        MLA_LDS float* vsc = reinterpret_cast<MLA_LDS float*>(smem + kFp8VScale);
-        MLA_LDS float* ivsc = reinterpret_cast<MLA_LDS float*>(smem + kFp8IVScale);
-        if constexpr (FP8) {
-          convert_fp8_page(cur, smem + kFp8Conv, ksc, vsc, ivsc, valid, tid, p.scale_log2);
-          lds_barrier();
-          page = smem + kFp8Conv;
-        } else {
-          if (valid < kPage) {
-            zero_tail_rows(cur, valid, tid);
-            lds_barrier();
-          }
-          page = cur;
-        }
-        const bool need_mask = tok0 + kPage > first_nvis;
-        const bool first = attempt == 0 && pg == pg0;
-        narrow_page<FP8>(page, ksc, vsc, ivsc, qf, ns, tok0, nvis, need_mask, p.scale_log2, w, l, first, ovf);
-        lds_barrier();
       }
-      // every wave reads the flag after the last barrier; the second barrier keeps a
-      // fast wave from clearing it (next attempt or unit) before all have read it
-      const int redo = *ovf;
-      lds_barrier();
-      if (redo == 0) break;
-      m_restart = ns.m_seen;
-    }
 
-    // ---- epilogue ----
-    const size_t slot = (size_t)pi * p.n_hg + hg;
-    // combine the four token-slices of the waves through LDS
-    const float l_w = sum_xor32(sum_xor16(ns.l));
-    const float lr_w = sum_xor32(sum_xor16(ns.lr));
-    MLA_LDS float* obuf = reinterpret_cast<MLA_LDS float*>(smem);
-    MLA_LDS float* stat = reinterpret_cast<MLA_LDS float*>(smem + 4 * 16 * kLatent * 4);
-    const int g = l >> 4;
+      NarrowState ns;
+      MLA_LDS int* ovf = reinterpret_cast<MLA_LDS int*>(smem + kLdsFlag);
+      float m_restart = -INFINITY;
+      for (int attempt = 0; attempt < 2; ++attempt) {
 #pragma unroll
-    for (int fb = 0; fb < 32; ++fb)
-      *reinterpret_cast<MLA_LDS f32x4_t*>(obuf + (w * 16 + r) * kLatent + 16 * fb + 4 * g) = ns.o[fb];
-    if (l < 16) {
-      stat[(w * 16 + r) * 4] = ns.m;
-      stat[(w * 16 + r) * 4 + 1] = l_w;
-      stat[(w * 16 + r) * 4 + 2] = lr_w;
-    }
-    lds_barrier();
-    const int rr = tid >> 4;                 // row 0..15
-    const int fp = tid & 15;                 // features 64*j + 4*fp + [0,4), j = 0..7:
-                                             // 16 lanes of a row store 256 contiguous bytes
-    float mw[4], lw[4], lrw[4];
-    float M = -INFINITY;
+        for (int i = 0; i < 32; ++i) ns.o[i] = f32x4_t{};
+        ns.m = m_restart;
+        ns.l = 0.f;
+        ns.lr = 0.f;
+        ns.m_seen = -INFINITY;
+        // reset the flag and make the reset visible before any wave can read it
+        // (a unit without pages reads it right after this barrier)
+        if (tid == 0) *ovf = 0;
+        lds_barrier();
+        if (attempt > 0 && pg1 > pg0) {
+          load_page_ids(ids, p, b, pg0, pg1, l);
+          if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
+          else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
+        }
+
+        for (int pg = pg0; pg < pg1; ++pg) {
+          const bool odd = ((pg - pg0) & 1) != 0;
+          MLA_LDS char* cur = odd ? buf1 : buf0;
+          MLA_LDS char* nxt = odd ? buf0 : buf1;
+          if (pg + 1 < pg1) {
+            if constexpr (FP8) {
+              issue_page_fp8(page_ptr(ids, p, b, pg + 1, pg1, l, true), nxt, w, l);
+              if (w == 0) wait_vmcnt<10>();
+              else wait_vmcnt<9>();
+            } else {
+              issue_page_bf16(page_ptr(ids, p, b, pg + 1, pg1, l, false), nxt, w, l);
+              wait_vmcnt<18>();
+            }
+          } else {
+            wait_vmcnt<0>();
+          }
+          lds_barrier();
+          const int tok0 = pg * kPage;
+          const int valid = seq - tok0 < kPage ? seq - tok0 : kPage;
+          const MLA_LDS char* page;
+          MLA_LDS float* ksc = reinterpret_cast<MLA_LDS float*>(smem + kFp8KScale);
+          MLA_LDS float* vsc = reinterpret_cast<MLA_LDS float*>(smem + kFp8VScale);
+          MLA_LDS float* ivsc = reinterpret_cast<MLA_LDS float*>(smem + kFp8IVScale);
+          if constexpr (FP8) {
+            convert_fp8_page(cur, smem + kFp8Conv, ksc, vsc, ivsc, valid, tid, p.scale_log2);
+            lds_barrier();
+            page = smem + kFp8Conv;
+          } else {
+            if (valid < kPage) {
+              zero_tail_rows(cur, valid, tid);
+              lds_barrier();
+            }
+            page = cur;
+          }
+          const bool need_mask = tok0 + kPage > first_nvis;
+          const bool first = attempt == 0 && pg == pg0;
+          narrow_page<FP8>(page, ksc, vsc, ivsc, qf, ns, tok0, nvis, need_mask, p.scale_log2, w, l, first, ovf);
+          lds_barrier();
+        }
+        // every wave reads the flag after the last barrier; the second barrier keeps a
+        // fast wave from clearing it (next attempt or unit) before all have read it
+        const int redo = *ovf;
+        lds_barrier();
+        if (redo == 0) break;
+        m_restart = ns.m_seen;
+      }
+
+      // ---- epilogue ----
+      const size_t slot = (size_t)pslot * p.n_hg + hg;
+      // combine the four token-slices of the waves through LDS
+      const float l_w = sum_xor32(sum_xor16(ns.l));
+      const float lr_w = sum_xor32(sum_xor16(ns.lr));
+      MLA_LDS float* obuf = reinterpret_cast<MLA_LDS float*>(smem);
+      MLA_LDS float* stat = reinterpret_cast<MLA_LDS float*>(smem + 4 * 16 * kLatent * 4);
+      const int g = l >> 4;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      mw[k] = stat[(k * 16 + rr) * 4];
-      lw[k] = stat[(k * 16 + rr) * 4 + 1];
-      lrw[k] = stat[(k * 16 + rr) * 4 + 2];
-      M = fmaxf(M, mw[k]);
-    }
-    const float Mb = M == -INFINITY ? 0.f : M;
-    float wgt[4], L = 0.f, LR = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      wgt[k] = __builtin_amdgcn_exp2f(mw[k] - Mb);
-      L += wgt[k] * lw[k];
-      LR += wgt[k] * lrw[k];
-    }
-    const float inv = LR > 0.f ? 1.0f / LR : 0.f;
-    const float lse_v = L > 0.f ? (Mb + __builtin_log2f(L)) * kLn2 : -INFINITY;
-    const int rhl = rr / p.q_len, rtq = rr - rhl * p.q_len;
-    const int rhead = hg * p.hg_heads + rhl;
-    if (rhead < p.N) {
-      f32x4_t acc[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{};
+      for (int fb = 0; fb < 32; ++fb)
+        *reinterpret_cast<MLA_LDS f32x4_t*>(obuf + (w * 16 + r) * kLatent + 16 * fb + 4 * g) = ns.o[fb];
+      if (l < 16) {
+        stat[(w * 16 + r) * 4] = ns.m;
+        stat[(w * 16 + r) * 4 + 1] = l_w;
+        stat[(w * 16 + r) * 4 + 2] = lr_w;
+      }
+      lds_barrier();
+      const int rr = tid >> 4;                 // row 0..15
+      const int fp = tid & 15;                 // features 64*j + 4*fp + [0,4), j = 0..7:
+                                               // 16 lanes of a row store 256 contiguous bytes
+      float mw[4], lw[4], lrw[4];
+      float M = -INFINITY;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + 4 * fp;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += wgt[k] * *reinterpret_cast<const MLA_LDS f32x4_t*>(src + 64 * j);
+        mw[k] = stat[(k * 16 + rr) * 4];
+        lw[k] = stat[(k * 16 + rr) * 4 + 1];
+        lrw[k] = stat[(k * 16 + rr) * 4 + 2];
+        M = fmaxf(M, mw[k]);
       }
-      if (nsplit == 1) {
-        uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + 4 * fp;
+      const float Mb = M == -INFINITY ? 0.f : M;
+      float wgt[4], L = 0.f, LR = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16x4_t v = {(__bf16)(acc[j][0] * inv), (__bf16)(acc[j][1] * inv), (__bf16)(acc[j][2] * inv),
-                              (__bf16)(acc[j][3] * inv)};
-          *reinterpret_cast<bf16x4_t*>(orow + 64 * j) = v;
+      for (int k = 0; k < 4; ++k) {
+        wgt[k] = __builtin_amdgcn_exp2f(mw[k] - Mb);
+        L += wgt[k] * lw[k];
+        LR += wgt[k] * lrw[k];
+      }
+      const float inv = LR > 0.f ? 1.0f / LR : 0.f;
+      const float lse_v = L > 0.f ? (Mb + __builtin_log2f(L)) * kLn2 : -INFINITY;
+      const int rhl = rr / p.q_len, rtq = rr - rhl * p.q_len;
+      const int rhead = hg * p.hg_heads + rhl;
+      if (rhead < p.N) {
+        f32x4_t acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + 4 * fp;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] += wgt[k] * *reinterpret_cast<const MLA_LDS f32x4_t*>(src + 64 * j);
         }
-        if (fp == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
-      } else {
-        float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 4 * fp;
+        if (nsplit == 1) {
+          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + 4 * fp;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(prow + 64 * j) = acc[j] * inv;
-        if (fp == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
+          for (int j = 0; j < 8; ++j) {
+            const bf16x4_t v = {(__bf16)(acc[j][0] * inv), (__bf16)(acc[j][1] * inv), (__bf16)(acc[j][2] * inv),
+                                (__bf16)(acc[j][3] * inv)};
+            *reinterpret_cast<bf16x4_t*>(orow + 64 * j) = v;
+          }
+          if (fp == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
+        } else {
+          float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 4 * fp;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(prow + 64 * j) = acc[j] * inv;
+          if (fp == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
+        }
       }
+      lds_barrier();
     }
-    lds_barrier();
   }
 }
 
@@ -604,7 +707,8 @@ constexpr int kWP = 149504;                            // P: 2 buffers x 64 rows
 constexpr int kWPBytes = kWRows * 64;
 constexpr int kWStats = kWP + 2 * kWPBytes;            // per token half and row {m, l, lr, -}
 constexpr int kWFlag = kWStats + 2 * kWRows * 16;      // overflow flag of the reference max
-constexpr int kWLdsBytes = kWFlag + 16;
+constexpr int kWPlan = kWFlag + 16;                    // split-plan scratch
+constexpr int kWLdsBytes = kWPlan + kPlanLdsBytes;
 constexpr int kWStagePitch32 = 528;                    // epilogue staging: 512 B fp32 row + pad
 constexpr int kWStagePitch16 = 272;                    // 256 B bf16 row + pad
 static_assert(kWRing * kWSlot <= kWP && kWFac + 2 * kWFacBytes <= kWP, "wide LDS plan");
@@ -756,8 +860,6 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
   const int l = lane_id();
   const int rg = w >> 1, th = w & 1;            // score phase: row group, token half
   const int l16 = l & 15, g4 = l >> 4;
-  const int P = p.hdr[0];
-  const int U = p.hdr[1];
   MLA_LDS int* ovf_flag = reinterpret_cast<MLA_LDS int*>(smem + kWFlag);
   MLA_LDS f32x4_t* stats = reinterpret_cast<MLA_LDS f32x4_t*>(smem + kWStats);   // [2][64]
 
@@ -792,328 +894,334 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     pbase[s] = (uint32_t)(R * 64 + (((2 * s + (l >> 5)) ^ ((R >> 2) & 3)) * 16));
   }
 
-  for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    int pi, hg;
-    unit_to_pair(u, p.n_hg, &pi, &hg);
-    if (pi >= P) continue;
-    const int4 pr = p.pairs[pi];
-    const int b = pr.x, t_begin = pr.z, t_end = pr.w;
-    const int4 rq = p.req[b];
-    const int nsplit = rq.y, seq = rq.w;
-    const int nblk = t_end > t_begin ? (t_end - t_begin + kBlk - 1) / kBlk : 0;
-    const int pg0 = t_begin / kPage;
-    const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
+  MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
+  PlanTotals tot{0, 1};
+  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
+  for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
+    int sid, hg;
+    unit_to_stream(u, p.n_hg, &sid, &hg);
+    if (sid >= p.n_streams) continue;
+    PieceIter it;
+    it.init(p, plan_lds, tot, sid, tid);
+    Piece pc;
+    while (it.next(p, hg, tid, pc)) {
+      const int b = pc.b, t_begin = pc.t_begin, t_end = pc.t_end, seq = pc.seq, nsplit = pc.nsplit;
+      const int pslot = pc.slot;
+      const int nblk = t_end > t_begin ? (t_end - t_begin + kBlk - 1) / kBlk : 0;
+      const int pg0 = t_begin / kPage;
+      const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
 
-    // the two query rows this lane owns in the score phase: 32rg + 16rs + l16
-    int nvis[2];
-    bool row_ok[2];
-    int qhead[2], qtq[2];
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs) {
-      const int r = 32 * rg + 16 * rs + l16;
-      const int hl = r / p.q_len, tq = r - hl * p.q_len;
-      qhead[rs] = hg * p.hg_heads + hl;
-      qtq[rs] = tq;
-      row_ok[rs] = qhead[rs] < p.N;
-      nvis[rs] = seq - p.q_len + 1 + tq;
-    }
-
-    PageIds ids;
-    load_page_ids(ids, p, b, pg0, pg1, l);
-    // DMA destination of block j: ring slot j % 4 (bf16 slot, or fp8 raw slot)
-    auto issue = [&](int j) {
-      const char* pg = page_ptr(ids, p, b, pg0 + (j >> 1), pg1, l, FP8);
-      if constexpr (FP8)
-        issue_blk_fp8(pg + (j & 1) * kBlkBytesFp8, smem + kWRaw + (j & (kWRing - 1)) * kBlkBytesFp8, w, l);
-      else
-        issue_blk_bf16(pg + (j & 1) * kBlkBytesBf16, smem + (j & (kWRing - 1)) * kWSlot, w, l);
-    };
-    auto valid_of = [&](int j) {
-      const int v = t_end - (t_begin + kBlk * j);
-      return v < kBlk ? v : kBlk;
-    };
-    if (nblk > 0) issue(0);
-
-    // query fragments (B operand of the 16x16x32 MFMA): row 32rg + 16rs + l16, features
-    // 32kk + 8*g4 .. +7.  Padding rows (head >= N) load head 0 and are zeroed.
-    bf16x8_t qf[2][18];
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs) {
-      const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qtq[rs] * p.q_st +
-                             (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
-      if (!row_ok[rs]) {
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = bf16x8_t{};
-      }
-    }
-    // Wait for the query here: the compiler would otherwise wait at its first use,
-    // after block 1's DMA is in flight, and so wait for that DMA as well.
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
-
-    f32x16_t o[4][2];
-    float m[2], lsum[2], lrsum[2], m_seen[2];
-    int ovf = 0;
-    float m_restart[2] = {-INFINITY, -INFINITY};
-    for (int attempt = 0; attempt < 2; ++attempt) {
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) o[fb][rb] = f32x16_t{};
+      // the two query rows this lane owns in the score phase: 32rg + 16rs + l16
+      int nvis[2];
+      bool row_ok[2];
+      int qhead[2], qtq[2];
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        m[rs] = m_restart[rs];
-        lsum[rs] = 0.f;
-        lrsum[rs] = 0.f;
-        m_seen[rs] = -INFINITY;
+        const int r = 32 * rg + 16 * rs + l16;
+        const int hl = r / p.q_len, tq = r - hl * p.q_len;
+        qhead[rs] = hg * p.hg_heads + hl;
+        qtq[rs] = tq;
+        row_ok[rs] = qhead[rs] < p.N;
+        nvis[rs] = seq - p.q_len + 1 + tq;
       }
-      ovf = 0;
-      if (tid == 0) *ovf_flag = 0;
-      if (attempt > 0 && nblk > 0) {
-        load_page_ids(ids, p, b, pg0, pg1, l);
-        issue(0);
-      }
-      // block 0 has landed (the query too); the barrier also publishes the flag reset
-      wait_vmcnt<0>();
-      if constexpr (!FP8) {
-        if (nblk == 1) zero_own_tail(smem, valid_of(0), w, l);
-      }
-      lds_barrier();
-      if constexpr (FP8) {
-        if (nblk > 0)
-          convert_fp8_blk(smem + kWRaw, smem, reinterpret_cast<MLA_LDS float*>(smem + kWFac), valid_of(0), tid,
-                          p.scale_log2);
-      }
-      if (nblk > 1) issue(1);
-      if (nblk > 2) issue(2);
-      if constexpr (FP8) lds_barrier();
 
-      // Block step: scores of block j, their weights into P(j), interleaved (WITH_PV)
-      // with the PV MFMAs of block j-1, then the hand-over to block j+1.  Block 0 runs
-      // without PV (peeled) so that the steady-state body is one straight-line region.
-      auto step = [&](int j, auto with_pv) {
-        constexpr bool WITH_PV = decltype(with_pv)::value;
-        const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kWRing - 1))) * kWSlot;
-        const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kWFac + (j & 1) * kWFacBytes);
-        const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
+      PageIds ids;
+      load_page_ids(ids, p, b, pg0, pg1, l);
+      // DMA destination of block j: ring slot j % 4 (bf16 slot, or fp8 raw slot)
+      auto issue = [&](int j) {
+        const char* pg = page_ptr(ids, p, b, pg0 + (j >> 1), pg1, l, FP8);
+        if constexpr (FP8)
+          issue_blk_fp8(pg + (j & 1) * kBlkBytesFp8, smem + kWRaw + (j & (kWRing - 1)) * kBlkBytesFp8, w, l);
+        else
+          issue_blk_bf16(pg + (j & 1) * kBlkBytesBf16, smem + (j & (kWRing - 1)) * kWSlot, w, l);
+      };
+      auto valid_of = [&](int j) {
+        const int v = t_end - (t_begin + kBlk * j);
+        return v < kBlk ? v : kBlk;
+      };
+      if (nblk > 0) issue(0);
 
-        f32x4_t sc[2];
-        wide_scores(cur, qf, kbase, sc);
-
-        // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
-        // Element i of row half rs is token tok0 + i.
-        float mt[2];
-        {
-          f32x4_t kf;
-          if constexpr (FP8) kf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 16 * th + 4 * g4);
+      // query fragments (B operand of the 16x16x32 MFMA): row 32rg + 16rs + l16, features
+      // 32kk + 8*g4 .. +7.  Padding rows (head >= N) load head 0 and are zeroed.
+      bf16x8_t qf[2][18];
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs) {
-            mt[rs] = -INFINITY;
+      for (int rs = 0; rs < 2; ++rs) {
+        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qtq[rs] * p.q_st +
+                               (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float x = sc[rs][i] * (FP8 ? kf[i] : p.scale_log2);
-              x = (tok0 + i < nvis[rs]) ? x : -INFINITY;
-              sc[rs][i] = x;
-              mt[rs] = fmaxf(mt[rs], x);
-            }
-            mt[rs] = max_xor32(max_xor16(mt[rs]));
-          }
+        for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
+        if (!row_ok[rs]) {
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = bf16x8_t{};
         }
-        if constexpr (!WITH_PV) {
-          if (attempt == 0) {
-            // reference max of each row from the unit's first block: the two token halves
-            // of a row live in two waves, so their maxima meet in LDS
-            if (g4 == 0) {
+      }
+      // Wait for the query here: the compiler would otherwise wait at its first use,
+      // after block 1's DMA is in flight, and so wait for that DMA as well.
 #pragma unroll
-              for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = mt[rs];
-            }
-            lds_barrier();
+      for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
-            for (int rs = 0; rs < 2; ++rs) {
-              const int R = 32 * rg + 16 * rs + l16;
-              m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
-            }
-          }
-        }
-        float base[2];
+        for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
+
+      f32x16_t o[4][2];
+      float m[2], lsum[2], lrsum[2], m_seen[2];
+      int ovf = 0;
+      float m_restart[2] = {-INFINITY, -INFINITY};
+      for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) o[fb][rb] = f32x16_t{};
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
-          m_seen[rs] = fmaxf(m_seen[rs], mt[rs]);
-          base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
-          ovf |= (mt[rs] > base[rs] + kRefSlack) ? 1 : 0;
+          m[rs] = m_restart[rs];
+          lsum[rs] = 0.f;
+          lrsum[rs] = 0.f;
+          m_seen[rs] = -INFINITY;
         }
-
-        // PV of the previous block overlaps this block's exponentials
-        if constexpr (WITH_PV) {
-          const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kWRing - 1))) * kWSlot;
-          wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
+        ovf = 0;
+        if (tid == 0) *ovf_flag = 0;
+        if (attempt > 0 && nblk > 0) {
+          load_page_ids(ids, p, b, pg0, pg1, l);
+          issue(0);
         }
+        // block 0 has landed (the query too); the barrier also publishes the flag reset
+        wait_vmcnt<0>();
+        if constexpr (!FP8) {
+          if (nblk == 1) zero_own_tail(smem, valid_of(0), w, l);
+        }
+        lds_barrier();
+        if constexpr (FP8) {
+          if (nblk > 0)
+            convert_fp8_blk(smem + kWRaw, smem, reinterpret_cast<MLA_LDS float*>(smem + kWFac), valid_of(0), tid,
+                            p.scale_log2);
+        }
+        if (nblk > 1) issue(1);
+        if (nblk > 2) issue(2);
+        if constexpr (FP8) lds_barrier();
 
-        // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
-        // the sums keep both the exact weights (LSE) and the rounded ones (O).
-        {
-          f32x4_t vf, ivf;
-          if constexpr (FP8) {
-            vf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + kBlk + 16 * th + 4 * g4);
-            ivf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 2 * kBlk + 16 * th + 4 * g4);
+        // Block step: scores of block j, their weights into P(j), interleaved (WITH_PV)
+        // with the PV MFMAs of block j-1, then the hand-over to block j+1.  Block 0 runs
+        // without PV (peeled) so that the steady-state body is one straight-line region.
+        auto step = [&](int j, auto with_pv) {
+          constexpr bool WITH_PV = decltype(with_pv)::value;
+          const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kWRing - 1))) * kWSlot;
+          const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kWFac + (j & 1) * kWFacBytes);
+          const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
+
+          f32x4_t sc[2];
+          wide_scores(cur, qf, kbase, sc);
+
+          // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
+          // Element i of row half rs is token tok0 + i.
+          float mt[2];
+          {
+            f32x4_t kf;
+            if constexpr (FP8) kf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 16 * th + 4 * g4);
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs) {
+              mt[rs] = -INFINITY;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float x = sc[rs][i] * (FP8 ? kf[i] : p.scale_log2);
+                x = (tok0 + i < nvis[rs]) ? x : -INFINITY;
+                sc[rs][i] = x;
+                mt[rs] = fmaxf(mt[rs], x);
+              }
+              mt[rs] = max_xor32(max_xor16(mt[rs]));
+            }
           }
-          MLA_LDS char* pw = smem + kWP + (j & 1) * kWPBytes;
+          if constexpr (!WITH_PV) {
+            if (attempt == 0) {
+              // reference max of each row from the unit's first block: the two token halves
+              // of a row live in two waves, so their maxima meet in LDS
+              if (g4 == 0) {
+#pragma unroll
+                for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = mt[rs];
+              }
+              lds_barrier();
+#pragma unroll
+              for (int rs = 0; rs < 2; ++rs) {
+                const int R = 32 * rg + 16 * rs + l16;
+                m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+              }
+            }
+          }
+          float base[2];
 #pragma unroll
           for (int rs = 0; rs < 2; ++rs) {
-            bf16x4_t pk;
+            m_seen[rs] = fmaxf(m_seen[rs], mt[rs]);
+            base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
+            ovf |= (mt[rs] > base[rs] + kRefSlack) ? 1 : 0;
+          }
+
+          // PV of the previous block overlaps this block's exponentials
+          if constexpr (WITH_PV) {
+            const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kWRing - 1))) * kWSlot;
+            wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
+          }
+
+          // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
+          // the sums keep both the exact weights (LSE) and the rounded ones (O).
+          {
+            f32x4_t vf, ivf;
+            if constexpr (FP8) {
+              vf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + kBlk + 16 * th + 4 * g4);
+              ivf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 2 * kBlk + 16 * th + 4 * g4);
+            }
+            MLA_LDS char* pw = smem + kWP + (j & 1) * kWPBytes;
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs) {
+              bf16x4_t pk;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float pr = __builtin_amdgcn_exp2f(sc[rs][i] - base[rs]);
+                const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
+                pk[i] = rr;
+                lsum[rs] += pr;
+                lrsum[rs] += FP8 ? (float)rr * ivf[i] : (float)rr;
+              }
+              // row R, tokens 16th + 4g4 .. +3: chunk 2th + (g4 >> 1), half g4 & 1
+              const int R = 32 * rg + 16 * rs + l16;
+              const int a = 2 * th + (g4 >> 1);
+              *reinterpret_cast<MLA_LDS bf16x4_t*>(pw + R * 64 + ((a ^ ((R >> 2) & 3)) * 16) + 8 * (g4 & 1)) = pk;
+            }
+          }
+
+          if (j + 1 < nblk) {
+            // this wave's share of block j+1 has landed when at most block j+2's
+            // instructions are still outstanding (9 per wave for bf16; 5, 5, 5, 4 for fp8)
+            if (j + 2 < nblk) {
+              if constexpr (FP8) {
+                if (w == 3) wait_vmcnt<4>();
+                else wait_vmcnt<5>();
+              } else {
+                wait_vmcnt<9>();
+              }
+            } else {
+              wait_vmcnt<0>();
+            }
+            if constexpr (!FP8) {
+              if (j + 2 == nblk) zero_own_tail(smem + ((j + 1) & (kWRing - 1)) * kWSlot, valid_of(j + 1), w, l);
+            }
+          }
+          lds_barrier();                              // Y(j)
+          if (j + 3 < nblk) issue(j + 3);
+          if constexpr (FP8) {
+            if (j + 1 < nblk)
+              convert_fp8_blk(smem + kWRaw + ((j + 1) & (kWRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kWSlot,
+                              reinterpret_cast<MLA_LDS float*>(smem + kWFac + ((j + 1) & 1) * kWFacBytes),
+                              valid_of(j + 1), tid, p.scale_log2);
+            lds_barrier();                            // Z(j+1)
+          }
+        };
+        if (nblk > 0) {
+          step(0, std::false_type{});
+          for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
+          const int jl = nblk - 1;
+          wide_pv(smem + (FP8 ? (jl & 1) : (jl & (kWRing - 1))) * kWSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase,
+                  pbase);
+        }
+        // any row over the reference slack: the whole workgroup redoes the unit
+        if (ovf) *ovf_flag = 1;
+        lds_barrier();
+        const int redo = *ovf_flag;
+        lds_barrier();
+        if (redo == 0) break;
+        // restart with the largest score seen in either token half of each row
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          m_seen[rs] = max_xor32(max_xor16(m_seen[rs]));
+        }
+        if (g4 == 0) {
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = m_seen[rs];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          const int R = 32 * rg + 16 * rs + l16;
+          m_restart[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+        }
+        lds_barrier();
+      }
+
+      // ---- epilogue ----
+      const size_t slot = (size_t)pslot * p.n_hg + hg;
+      const bool single = nsplit == 1;
+      // row sums: over the 4 lane groups of this wave, then over the two token halves
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const float a = sum_xor32(sum_xor16(lsum[rs]));
+        const float c = sum_xor32(sum_xor16(lrsum[rs]));
+        if (g4 == 0) stats[th * kWRows + 32 * rg + 16 * rs + l16] = f32x4_t{m[rs], a, c, 0.f};
+      }
+      lds_barrier();
+      if (th == 0 && g4 == 0) {
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          const int R = 32 * rg + 16 * rs + l16;
+          const float lt = stats[R][1] + stats[kWRows + R][1];
+          const float lse_v = lt > 0.f ? (m[rs] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
+          if (row_ok[rs]) {
+            if (single) p.lse[((int64_t)b * p.q_len + qtq[rs]) * p.N + qhead[rs]] = lse_v;
+            else p.part_lse[slot * p.m_wg + R] = lse_v;
+          }
+        }
+      }
+      // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5) + jj.
+      // Each row block is staged through this wave's own LDS region and written back
+      // row-contiguously (512 B fp32 or 256 B bf16 per row and wave).
+      MLA_LDS char* stage = smem + w * (32 * kWStagePitch32);
+      const int c32 = l & 31, h32 = l >> 5;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int R = 32 * rb + c32;
+        const float lr_row = stats[R][2] + stats[kWRows + R][2];
+        const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
+        if (single) {
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float pr = __builtin_amdgcn_exp2f(sc[rs][i] - base[rs]);
-              const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
-              pk[i] = rr;
-              lsum[rs] += pr;
-              lrsum[rs] += FP8 ? (float)rr * ivf[i] : (float)rr;
+              const bf16x4_t v = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
+                                  (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
+              *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fb + 8 * i + 4 * h32) * 2) = v;
             }
-            // row R, tokens 16th + 4g4 .. +3: chunk 2th + (g4 >> 1), half g4 & 1
-            const int R = 32 * rg + 16 * rs + l16;
-            const int a = 2 * th + (g4 >> 1);
-            *reinterpret_cast<MLA_LDS bf16x4_t*>(pw + R * 64 + ((a ^ ((R >> 2) & 3)) * 16) + 8 * (g4 & 1)) = pk;
-          }
-        }
-
-        if (j + 1 < nblk) {
-          // this wave's share of block j+1 has landed when at most block j+2's
-          // instructions are still outstanding (9 per wave for bf16; 5, 5, 5, 4 for fp8)
-          if (j + 2 < nblk) {
-            if constexpr (FP8) {
-              if (w == 3) wait_vmcnt<4>();
-              else wait_vmcnt<5>();
-            } else {
-              wait_vmcnt<9>();
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int row = 4 * k + (l >> 4);
+            const int Rr = 32 * rb + row;
+            const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
+            const int head_r = hg * p.hg_heads + hl_r;
+            const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + l16 * 16);
+            if (head_r < p.N) {
+              uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
+              *reinterpret_cast<u32x4_t*>(orow + 128 * w + 8 * l16) = v;
             }
-          } else {
-            wait_vmcnt<0>();
           }
-          if constexpr (!FP8) {
-            if (j + 2 == nblk) zero_own_tail(smem + ((j + 1) & (kWRing - 1)) * kWSlot, valid_of(j + 1), w, l);
+        } else {
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4_t v = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
+                                 o[fb][rb][4 * i + 3] * inv};
+              *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fb + 8 * i + 4 * h32) * 4) = v;
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int row = 2 * k + h32;
+            const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch32 + c32 * 16);
+            float* prow = p.part_o + (slot * p.m_wg + 32 * rb + row) * kLatent + 128 * w + 4 * c32;
+            *reinterpret_cast<u32x4_t*>(prow) = v;
           }
         }
-        lds_barrier();                              // Y(j)
-        if (j + 3 < nblk) issue(j + 3);
-        if constexpr (FP8) {
-          if (j + 1 < nblk)
-            convert_fp8_blk(smem + kWRaw + ((j + 1) & (kWRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kWSlot,
-                            reinterpret_cast<MLA_LDS float*>(smem + kWFac + ((j + 1) & 1) * kWFacBytes),
-                            valid_of(j + 1), tid, p.scale_log2);
-          lds_barrier();                            // Z(j+1)
-        }
-      };
-      if (nblk > 0) {
-        step(0, std::false_type{});
-        for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
-        const int jl = nblk - 1;
-        wide_pv(smem + (FP8 ? (jl & 1) : (jl & (kWRing - 1))) * kWSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase,
-                pbase);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
       }
-      // any row over the reference slack: the whole workgroup redoes the unit
-      if (ovf) *ovf_flag = 1;
-      lds_barrier();
-      const int redo = *ovf_flag;
-      lds_barrier();
-      if (redo == 0) break;
-      // restart with the largest score seen in either token half of each row
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        m_seen[rs] = max_xor32(max_xor16(m_seen[rs]));
-      }
-      if (g4 == 0) {
-#pragma unroll
-        for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = m_seen[rs];
-      }
-      lds_barrier();
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const int R = 32 * rg + 16 * rs + l16;
-        m_restart[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
-      }
-      lds_barrier();
+      lds_barrier();                                          // LDS free before the next unit's DMA
     }
-
-    // ---- epilogue ----
-    const size_t slot = (size_t)pi * p.n_hg + hg;
-    const bool single = nsplit == 1;
-    // row sums: over the 4 lane groups of this wave, then over the two token halves
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs) {
-      const float a = sum_xor32(sum_xor16(lsum[rs]));
-      const float c = sum_xor32(sum_xor16(lrsum[rs]));
-      if (g4 == 0) stats[th * kWRows + 32 * rg + 16 * rs + l16] = f32x4_t{m[rs], a, c, 0.f};
-    }
-    lds_barrier();
-    if (th == 0 && g4 == 0) {
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const int R = 32 * rg + 16 * rs + l16;
-        const float lt = stats[R][1] + stats[kWRows + R][1];
-        const float lse_v = lt > 0.f ? (m[rs] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
-        if (row_ok[rs]) {
-          if (single) p.lse[((int64_t)b * p.q_len + qtq[rs]) * p.N + qhead[rs]] = lse_v;
-          else p.part_lse[slot * p.m_wg + R] = lse_v;
-        }
-      }
-    }
-    // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5) + jj.
-    // Each row block is staged through this wave's own LDS region and written back
-    // row-contiguously (512 B fp32 or 256 B bf16 per row and wave).
-    MLA_LDS char* stage = smem + w * (32 * kWStagePitch32);
-    const int c32 = l & 31, h32 = l >> 5;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int R = 32 * rb + c32;
-      const float lr_row = stats[R][2] + stats[kWRows + R][2];
-      const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
-      if (single) {
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bf16x4_t v = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
-                                (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
-            *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fb + 8 * i + 4 * h32) * 2) = v;
-          }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int row = 4 * k + (l >> 4);
-          const int Rr = 32 * rb + row;
-          const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
-          const int head_r = hg * p.hg_heads + hl_r;
-          const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + l16 * 16);
-          if (head_r < p.N) {
-            uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
-            *reinterpret_cast<u32x4_t*>(orow + 128 * w + 8 * l16) = v;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4_t v = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
-                               o[fb][rb][4 * i + 3] * inv};
-            *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fb + 8 * i + 4 * h32) * 4) = v;
-          }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int row = 2 * k + h32;
-          const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch32 + c32 * 16);
-          float* prow = p.part_o + (slot * p.m_wg + 32 * rb + row) * kLatent + 128 * w + 4 * c32;
-          *reinterpret_cast<u32x4_t*>(prow) = v;
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
-    }
-    lds_barrier();                                          // LDS free before the next unit's DMA
   }
 }
 
@@ -1185,7 +1293,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 struct Shape {
   bool wide;
-  int m_wg, hg_heads, n_hg, max_pairs;
+  int m_wg, hg_heads, n_hg, max_slots;
 };
 
 inline bool decode_shape(int32_t B, int32_t q_len, int32_t N, int32_t num_splits, Shape* s) {
@@ -1200,12 +1308,12 @@ inline bool decode_shape(int32_t B, int32_t q_len, int32_t N, int32_t num_splits
   else mp = (int64_t)B * num_splits;
   mp += 8;
   if (mp > (1 << 24)) return false;
-  s->max_pairs = (int)mp;
+  s->max_slots = (int)mp;
   return true;
 }
 
 struct WsLayout {
-  size_t hdr, req, pairs, part_lse, part_o, total;
+  size_t req, part_lse, part_o, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1213,13 +1321,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline WsLayout ws_layout(int32_t B, const Shape& s) {
   WsLayout w;
   size_t off = 0;
-  w.hdr = off;
-  off = align256(off + 16 * sizeof(int32_t));
   w.req = off;
   off = align256(off + (size_t)B * sizeof(int4));
-  w.pairs = off;
-  off = align256(off + (size_t)s.max_pairs * sizeof(int4));
-  const size_t rows = (size_t)s.max_pairs * s.n_hg * s.m_wg;
+  const size_t rows = (size_t)s.max_slots * s.n_hg * s.m_wg;
   w.part_lse = off;
   off = align256(off + rows * sizeof(float));
   w.part_o = off;
@@ -1288,30 +1392,30 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   p.o_st = o_stride_t;
   p.o_sh = o_stride_h;
   p.lse = lse;
-  p.hdr = reinterpret_cast<int32_t*>(ws + wl.hdr);
   p.req = reinterpret_cast<int4*>(ws + wl.req);
-  p.pairs = reinterpret_cast<int4*>(ws + wl.pairs);
   p.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
   p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
-  p.max_pairs = s.max_pairs;
   p.num_splits = num_splits;
-  // automatic plan: about one work unit per CU for the wide kernel (one
-  // 256-thread workgroup fills a CU) and four per CU for the short narrow units
-  int target_units = s.wide ? di.cu_count : 4 * di.cu_count;
-  int tp = target_units / s.n_hg;
-  if (tp < 1) tp = 1;
-  if (tp > MLA_AUTO_MAX_EXTRA_PAIRS) tp = MLA_AUTO_MAX_EXTRA_PAIRS;
-  p.target_pairs = tp;
+  // One workgroup (256 threads, most of the LDS) per CU.  Automatic plan: one
+  // stream per workgroup and head group, so every unit runs concurrently; with
+  // several head groups the stream count is a multiple of 8 (sibling order).
+  const int64_t cus = ((int64_t)di.cu_count + 7) / 8 * 8;
+  int64_t streams;
+  if (num_splits == 0) {
+    streams = s.n_hg == 1 ? cus : cus / (8 * s.n_hg) * 8;
+    if (streams < 8) streams = 8;
+    if (streams > MLA_AUTO_MAX_EXTRA_PAIRS) streams = MLA_AUTO_MAX_EXTRA_PAIRS;
+  } else {
+    streams = (int64_t)B * num_splits;
+  }
+  const int64_t units = s.n_hg == 1 ? streams : (streams + 7) / 8 * 8 * s.n_hg;
+  if (units > (int64_t)1 << 30) return MLA_ERR_SHAPE;
+  p.n_streams = (int32_t)streams;
+  p.n_units = (int32_t)units;
+  int64_t grid = cus < units ? cus : units;
+  if (grid < 1) grid = 1;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, hs, p);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-
-  const int64_t max_units = s.n_hg == 1 ? s.max_pairs : ((s.max_pairs + 7) / 8) * 8 * (int64_t)s.n_hg;
-  int64_t grid = (int64_t)di.cu_count;
-  grid = (grid + 7) / 8 * 8;
-  if (grid > max_units) grid = (max_units + 7) / 8 * 8;
-  if (grid < 8) grid = 8;
   if (kv_dtype == MLA_KV_BF16) {
     if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
     else hipLaunchKernelGGL((decode_narrow_kernel<false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
