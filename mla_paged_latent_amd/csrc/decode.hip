@@ -764,20 +764,24 @@ __device__ __forceinline__ void zero_own_tail(MLA_LDS char* blk, int valid, int 
 // {k_scale * softmax scale * log2 e, v_scale, 1 / v_scale}; rows >= valid become 0.
 __device__ __forceinline__ void convert_fp8_blk(const MLA_LDS char* raw, MLA_LDS char* conv,
                                                 MLA_LDS float* fac, int valid, int tid, float scale_log2) {
-#pragma unroll 1
-  for (int s = tid; s < kBlk * kChunksPerRow; s += 256) {
-    const int t = (s >> 3) & (kBlk - 1);
-    const int c = (s >> 8) * 8 + ((s & 7) ^ page_swz(t));
-    bf16x8_t v = {};
-    if (t < valid) {
-      const u32x2_t code = *reinterpret_cast<const MLA_LDS u32x2_t*>(raw + t * kRowBytesFp8 + c * 8);
-      const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[0], 1.0f, false);
-      const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[0], 1.0f, true);
-      const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[1], 1.0f, false);
-      const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[1], 1.0f, true);
-      v = bf16x8_t{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
-    }
-    *reinterpret_cast<MLA_LDS bf16x8_t*>(conv + s * 16) = v;
+  // thread tid converts chunk 8i + ((tid & 7) ^ s(t)) of token t = tid >> 3 for i = 0..8
+  // (output slot tid + 256 i); the nine 8-byte code reads are issued together so their
+  // LDS latency is paid once
+  const int t = tid >> 3;
+  const bool ok = t < valid;
+  const MLA_LDS char* src = raw + t * kRowBytesFp8 + ((tid & 7) ^ page_swz(t)) * 8;
+  u32x2_t code[kChunksPerRow / 8];
+#pragma unroll
+  for (int i = 0; i < kChunksPerRow / 8; ++i)
+    code[i] = ok ? *reinterpret_cast<const MLA_LDS u32x2_t*>(src + 64 * i) : u32x2_t{0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kChunksPerRow / 8; ++i) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[i][0], 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[i][0], 1.0f, true);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[i][1], 1.0f, false);
+    const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[i][1], 1.0f, true);
+    *reinterpret_cast<MLA_LDS bf16x8_t*>(conv + (tid + 256 * i) * 16) =
+        bf16x8_t{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
   }
   if (tid < kBlk) {
     float k = 0.f, v = 0.f;
@@ -1146,6 +1150,10 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       }
 
       // ---- epilogue ----
+      // lane-dependent addresses below derive from an opaque copy of the lane id, so
+      // the compiler cannot hoist them out of the piece loop (they would stay live,
+      // and spill, across the whole block loop)
+      const int le = (int)opaque((uint32_t)l);
       const size_t slot = (size_t)pslot * p.n_hg + hg;
       const bool single = nsplit == 1;
       // row sums: over the 4 lane groups of this wave, then over the two token halves
@@ -1172,7 +1180,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       // Each row block is staged through this wave's own LDS region and written back
       // row-contiguously (512 B fp32 or 256 B bf16 per row and wave).
       MLA_LDS char* stage = smem + w * (32 * kWStagePitch32);
-      const int c32 = l & 31, h32 = l >> 5;
+      const int c32 = le & 31, h32 = le >> 5;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int R = 32 * rb + c32;
@@ -1190,14 +1198,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const int row = 4 * k + (l >> 4);
+            const int row = 4 * k + (le >> 4);
             const int Rr = 32 * rb + row;
             const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
             const int head_r = hg * p.hg_heads + hl_r;
-            const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + l16 * 16);
+            const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + (le & 15) * 16);
             if (head_r < p.N) {
               uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
-              *reinterpret_cast<u32x4_t*>(orow + 128 * w + 8 * l16) = v;
+              *reinterpret_cast<u32x4_t*>(orow + 128 * w + 8 * (le & 15)) = v;
             }
           }
         } else {
