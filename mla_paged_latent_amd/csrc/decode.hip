@@ -254,50 +254,8 @@ struct PieceIter {
 };
 
 // ---------------------------------------------------------------------------
-// Page staging
+// Block staging
 // ---------------------------------------------------------------------------
-// bf16 page: 72 DMA instructions of 64 x 16 B; wave w issues instructions w, w+4, ...
-// (18 per wave).  Instruction k fills LDS group k >> 3 for tokens 8*(k & 7) + (lane >> 3);
-// lane j loads global chunk 8*(k >> 3) + ((j & 7) ^ s(j >> 3)) of that token (the
-// swizzle only sees t & 7 = j >> 3), i.e. page + lane_off + 9216*(k & 7) + 128*(k >> 3).
-template <int... I>
-__device__ __forceinline__ void issue_bf16_seq(std::integer_sequence<int, I...>, const char* page,
-                                               const char* half1, uint32_t voff, uint32_t lds) {
-  (dma_16B<128 * (I >> 1), 4096 * I>((I & 1) ? half1 : page, voff, lds), ...);
-}
-
-__device__ __forceinline__ void issue_page_bf16(const char* page, MLA_LDS char* dst, int w, int l) {
-  // instruction k = w + 4i covers tokens 8*(k & 7) .. +7 of 128-byte column k >> 3;
-  // with w < 4 that is tokens 8w + 32*(i & 1) and column i >> 1, so the wave's part
-  // of the offset sits in voff and the rest is a compile-time constant.
-  const uint32_t voff = (uint32_t)((l >> 3) * kRowBytesBf16 + ((l & 7) ^ page_swz(8 * (w & 1) + (l >> 3))) * 16 +
-                                   w * 8 * kRowBytesBf16);
-  const char* half1 = page + 32 * kRowBytesBf16;
-  const uint32_t lds = lds_addr(dst) + (uint32_t)w * 1024u;
-  issue_bf16_seq(std::make_integer_sequence<int, 18>{}, page, half1, voff, lds);
-}
-
-// fp8 page: the 37376 raw bytes (16-byte aligned) as 2336 flat 16-B chunks in 37
-// instructions k = w + 4i; wave 0 issues 10 of them (the last one half-masked),
-// waves 1..3 issue 9.
-template <int I>
-__device__ __forceinline__ void issue_fp8_one(const char* page, uint32_t voff, uint32_t lds, int w, int l) {
-  const int k = w + 4 * I;
-  if (k < 37 && k * 64 + l < kPageBytesFp8 / 16) dma_16B<0, 4096 * I>(page + 4096 * I, voff, lds);
-}
-
-template <int... I>
-__device__ __forceinline__ void issue_fp8_seq(std::integer_sequence<int, I...>, const char* page, uint32_t voff,
-                                              uint32_t lds, int w, int l) {
-  (issue_fp8_one<I>(page, voff, lds, w, l), ...);
-}
-
-__device__ __forceinline__ void issue_page_fp8(const char* page, MLA_LDS char* dst, int w, int l) {
-  const uint32_t voff = (uint32_t)(w * 1024 + l * 16);
-  const uint32_t lds = lds_addr(dst) + (uint32_t)w * 1024u;
-  issue_fp8_seq(std::make_integer_sequence<int, 10>{}, page, voff, lds, w, l);
-}
-
 // Physical page ids of a unit, 64 at a time: lane j of every wave holds the id of
 // logical page base + j in one VGPR and the id of page pg is read with readlane, so a
 // page's DMA never waits on a block-table load (the ids are fetched up to 64 pages
@@ -322,398 +280,24 @@ __device__ __forceinline__ const char* page_ptr(PageIds& ids, const DecodeParams
   return p.kv + (int64_t)id * (fp8 ? kPageBytesFp8 : kPageBytesBf16);
 }
 
-// ---------------------------------------------------------------------------
-// LDS plan
-// ---------------------------------------------------------------------------
-//   bf16: two swizzled pages [0, 73728) and [73728, 147456)
-//   fp8 : raw pages at 0 and 37376, converted bf16 page at 74752, k/v scales after
-constexpr int kLdsBf16 = 2 * kPageBytesBf16;
-constexpr int kFp8Raw0 = 0;
-constexpr int kFp8Raw1 = kPageBytesFp8;
-constexpr int kFp8Conv = 2 * kPageBytesFp8;
-constexpr int kFp8KScale = kFp8Conv + kPageBytesBf16;
-constexpr int kFp8VScale = kFp8KScale + 256;
-constexpr int kFp8IVScale = kFp8VScale + 256;
-constexpr int kLdsFp8 = kFp8IVScale + 256;
-constexpr int kLdsPages = kLdsBf16 > kLdsFp8 ? kLdsBf16 : kLdsFp8;
-constexpr int kLdsFlag = kLdsPages;                    // overflow flag of the reference max
-constexpr int kLdsPlan = kLdsFlag + 16;                // split-plan scratch
-constexpr int kLdsBytes = kLdsPlan + kPlanLdsBytes;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-
-// fp8 raw page -> swizzled bf16 page (exact: every e4m3fn value is a bf16 value);
-// token rows at or past `valid` become zero so stale pool bytes never reach the MFMA.
-__device__ __forceinline__ void convert_fp8_page(const MLA_LDS char* raw, MLA_LDS char* conv,
-                                                 MLA_LDS float* ks, MLA_LDS float* vs,
-                                                 MLA_LDS float* ivs, int valid, int tid,
-                                                 float scale_log2) {
-  // not unrolled: the query fragments and accumulators are live across this loop
-#pragma unroll 1
-  for (int s = tid; s < kPage * kChunksPerRow; s += 256) {
-    const int t = (s >> 3) & 63;
-    const int c = (s >> 9) * 8 + ((s & 7) ^ page_swz(t));
-    bf16x8_t v = {};
-    if (t < valid) {
-      const u32x2_t code = *reinterpret_cast<const MLA_LDS u32x2_t*>(raw + t * kRowBytesFp8 + c * 8);
-      const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[0], 1.0f, false);
-      const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[0], 1.0f, true);
-      const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[1], 1.0f, false);
-      const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)code[1], 1.0f, true);
-      v = bf16x8_t{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
-    }
-    *reinterpret_cast<MLA_LDS bf16x8_t*>(conv + s * 16) = v;
-  }
-  if (tid < kPage) {
-    float k = 0.f, v = 0.f;
-    if (tid < valid) {
-      const f32x2_t sc = *reinterpret_cast<const MLA_LDS f32x2_t*>(raw + tid * kRowBytesFp8 + kRow);
-      k = sc[0];
-      v = sc[1];
-    }
-    ks[tid] = k * scale_log2;                          // k_scale folded with the softmax scale
-    vs[tid] = v;
-    ivs[tid] = v != 0.f ? 1.0f / v : 0.f;
-  }
-}
-
-__device__ __forceinline__ void zero_tail_rows(MLA_LDS char* page, int valid, int tid) {
-  const int per_group = (kPage - valid) * 8;          // slots of rows valid..63 in one group
-  for (int s = tid; s < 9 * per_group; s += 256) {
-    const int grp = s / per_group;
-    const int slot = grp * kGroupSlots + valid * 8 + (s - grp * per_group);
-    *reinterpret_cast<MLA_LDS u32x4_t*>(page + slot * 16) = u32x4_t{0u, 0u, 0u, 0u};
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Softmax reference max
-// ---------------------------------------------------------------------------
-// Softmax bookkeeping without rescaling the accumulators.  Each row's reference
-// max m is fixed from the first 32-token block of the unit (exact for that block);
-// later scores may exceed it, so p = 2^(s - m) can be > 1, which float32
-// accumulation and bfloat16 probabilities represent without loss of relative
-// precision.  A visible score more than kRefSlack above m would risk overflow:
-// the block then raises a flag and the workgroup redoes the unit with the larger
-// reference.  O never needs a VALU rescale inside the page loop.
-constexpr float kRefSlack = 64.0f;
-
-// ---------------------------------------------------------------------------
-// Narrow variant: 16 query rows per unit, 16x16 MFMA, waves split the page's tokens
-// ---------------------------------------------------------------------------
-struct NarrowState {
-  f32x4_t o[32];      // O^T: 32 blocks of 16 latent features x 16 rows (lane%16 = row)
-  float m, l, lr, m_seen;   // as in RowState
-};
-
-template <bool FP8>
-__device__ __forceinline__ void narrow_page(const MLA_LDS char* pg, const MLA_LDS float* ks,
-                                            const MLA_LDS float* vs, const MLA_LDS float* ivs,
-                                            const bf16x8_t (&qf)[18],
-                                            NarrowState& st, int tok0, int nvis, bool need_mask,
-                                            float scale_log2, int w, int l, bool first,
-                                            MLA_LDS int* overflow) {
-  const int g = l >> 4, lg = l & 15;
-  f32x4_t s = {};
-  // K chunk c = 4*kk + g of token 16w + lg: group kk >> 1, in-group chunk 4*(kk & 1) + g
-  uint32_t kbase[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    kbase[m] = (uint32_t)((16 * w + lg) * 8 + ((4 * m + g) ^ page_swz(lg))) * 16;
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    const bf16x8_t a = lds_read_b128(pg, kbase[kk & 1] + (kk >> 1) * kGroupBytes);
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], s, 0, 0, 0);
-  }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = 16 * w + 4 * g + i;
-    // fp8: ks[] already holds k_scale * softmax scale * log2(e)
-    float x = FP8 ? s[i] * ks[t] : s[i] * scale_log2;
-    if (need_mask) x = (tok0 + t < nvis) ? x : -INFINITY;
-    s[i] = x;
-    mt = fmaxf(mt, x);
-  }
-  mt = max_xor32(max_xor16(mt));
-  if (first) st.m = mt;                                // reference from the unit's first page
-  st.m_seen = fmaxf(st.m_seen, mt);
-  const float base = st.m == -INFINITY ? 0.f : st.m;
-  if (mt > base + kRefSlack) *overflow = 1;
-  // row sum of the bf16-rounded weights: O becomes an exact convex combination of the V
-  // rows the MFMA saw, so the rounding of a dominant weight cancels
-  float lsum = 0.f, lrsum = 0.f;
-  bf16x4_t pb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = 16 * w + 4 * g + i;
-    const float pr = __builtin_amdgcn_exp2f(s[i] - base);
-    const float v = FP8 ? pr * vs[t] : pr;
-    const __bf16 r = (__bf16)v;
-    pb[i] = r;
-    lsum += pr;
-    lrsum += FP8 ? (float)r * ivs[t] : (float)r;
-  }
-  st.l += lsum;
-  st.lr += lrsum;
-  // V^T transpose reads: token 16w + 4g + (lg >> 2), chunk c = 2*fb + ((lg & 3) >> 1) in
-  // group fb >> 2 at in-group chunk 2*(fb & 3) + ((lg & 3) >> 1)
-  const int tok = 16 * w + 4 * g + (lg >> 2);
-  uint32_t vbase[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    vbase[m] = (uint32_t)(tok * 8 + ((2 * m + ((lg & 3) >> 1)) ^ page_swz(tok))) * 16 +
-               (uint32_t)(lg & 1) * 8;
-#pragma unroll
-  for (int fb = 0; fb < 32; ++fb) {
-    const bf16x4_t va = lds_read_tr16(pg, vbase[fb & 3] + (fb >> 2) * kGroupBytes);
-    st.o[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.o[fb], 0, 0, 0);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The persistent decode kernel
-// ---------------------------------------------------------------------------
-template <bool FP8>
-__global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
-  MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
-  const int tid = threadIdx.x;
-  const int w = wave_id();
-  const int l = lane_id();
-
-  MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kLdsPlan);
-  PlanTotals tot{0, 1};
-  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
-  for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
-    int sid, hg;
-    unit_to_stream(u, p.n_hg, &sid, &hg);
-    if (sid >= p.n_streams) continue;
-    PieceIter it;
-    it.init(p, plan_lds, tot, sid, tid);
-    Piece pc;
-    while (it.next(p, hg, tid, pc)) {
-      const int b = pc.b, t_begin = pc.t_begin, t_end = pc.t_end, seq = pc.seq, nsplit = pc.nsplit;
-      const int pslot = pc.slot;
-      const int pg0 = t_begin / kPage;
-      const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
-      const int first_nvis = seq - p.q_len + 1;          // visible tokens of query row 0
-
-      // the row this lane owns in the S^T / O^T accumulators
-      const int r = l & 15;
-      const int hl = r / p.q_len, tq = r - hl * p.q_len;
-      const int head = hg * p.hg_heads + hl;
-      const bool row_ok = head < p.N;
-      const int nvis = seq - p.q_len + 1 + tq;
-
-      // stage the unit's first page before loading the query fragments
-      MLA_LDS char* buf0 = smem + (FP8 ? kFp8Raw0 : 0);
-      MLA_LDS char* buf1 = smem + (FP8 ? kFp8Raw1 : kPageBytesBf16);
-      PageIds ids;
-      load_page_ids(ids, p, b, pg0, pg1, l);
-      if (pg1 > pg0) {
-        if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
-        else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
-      }
-
-      // query fragments (B operand): row r, features 32*kk + 8*(l>>4)
-      constexpr int NQ = 18;
-      bf16x8_t qf[NQ];
-      {
-        // padding rows (head >= N) load head 0 and are zeroed: no divergent loads
-        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
-        const int off = 8 * (l >> 4);
-#pragma unroll
-        for (int kk = 0; kk < NQ; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + off);
-        if (!row_ok) {
-#pragma unroll
-          for (int kk = 0; kk < NQ; ++kk) qf[kk] = bf16x8_t{};
-        }
-      }
-
-      NarrowState ns;
-      MLA_LDS int* ovf = reinterpret_cast<MLA_LDS int*>(smem + kLdsFlag);
-      float m_restart = -INFINITY;
-      for (int attempt = 0; attempt < 2; ++attempt) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) ns.o[i] = f32x4_t{};
-        ns.m = m_restart;
-        ns.l = 0.f;
-        ns.lr = 0.f;
-        ns.m_seen = -INFINITY;
-        // reset the flag and make the reset visible before any wave can read it
-        // (a unit without pages reads it right after this barrier)
-        if (tid == 0) *ovf = 0;
-        lds_barrier();
-        if (attempt > 0 && pg1 > pg0) {
-          load_page_ids(ids, p, b, pg0, pg1, l);
-          if constexpr (FP8) issue_page_fp8(page_ptr(ids, p, b, pg0, pg1, l, true), buf0, w, l);
-          else issue_page_bf16(page_ptr(ids, p, b, pg0, pg1, l, false), buf0, w, l);
-        }
-
-        for (int pg = pg0; pg < pg1; ++pg) {
-          const bool odd = ((pg - pg0) & 1) != 0;
-          MLA_LDS char* cur = odd ? buf1 : buf0;
-          MLA_LDS char* nxt = odd ? buf0 : buf1;
-          if (pg + 1 < pg1) {
-            if constexpr (FP8) {
-              issue_page_fp8(page_ptr(ids, p, b, pg + 1, pg1, l, true), nxt, w, l);
-              if (w == 0) wait_vmcnt<10>();
-              else wait_vmcnt<9>();
-            } else {
-              issue_page_bf16(page_ptr(ids, p, b, pg + 1, pg1, l, false), nxt, w, l);
-              wait_vmcnt<18>();
-            }
-          } else {
-            wait_vmcnt<0>();
-          }
-          lds_barrier();
-          const int tok0 = pg * kPage;
-          const int valid = seq - tok0 < kPage ? seq - tok0 : kPage;
-          const MLA_LDS char* page;
-          MLA_LDS float* ksc = reinterpret_cast<MLA_LDS float*>(smem + kFp8KScale);
-          MLA_LDS float* vsc = reinterpret_cast<MLA_LDS float*>(smem + kFp8VScale);
-          MLA_LDS float* ivsc = reinterpret_cast<MLA_LDS float*>(smem + kFp8IVScale);
-          if constexpr (FP8) {
-            convert_fp8_page(cur, smem + kFp8Conv, ksc, vsc, ivsc, valid, tid, p.scale_log2);
-            lds_barrier();
-            page = smem + kFp8Conv;
-          } else {
-            if (valid < kPage) {
-              zero_tail_rows(cur, valid, tid);
-              lds_barrier();
-            }
-            page = cur;
-          }
-          const bool need_mask = tok0 + kPage > first_nvis;
-          const bool first = attempt == 0 && pg == pg0;
-          narrow_page<FP8>(page, ksc, vsc, ivsc, qf, ns, tok0, nvis, need_mask, p.scale_log2, w, l, first, ovf);
-          lds_barrier();
-        }
-        // every wave reads the flag after the last barrier; the second barrier keeps a
-        // fast wave from clearing it (next attempt or unit) before all have read it
-        const int redo = *ovf;
-        lds_barrier();
-        if (redo == 0) break;
-        m_restart = ns.m_seen;
-      }
-
-      // ---- epilogue ----
-      const size_t slot = (size_t)pslot * p.n_hg + hg;
-      // combine the four token-slices of the waves through LDS
-      const float l_w = sum_xor32(sum_xor16(ns.l));
-      const float lr_w = sum_xor32(sum_xor16(ns.lr));
-      MLA_LDS float* obuf = reinterpret_cast<MLA_LDS float*>(smem);
-      MLA_LDS float* stat = reinterpret_cast<MLA_LDS float*>(smem + 4 * 16 * kLatent * 4);
-      const int g = l >> 4;
-#pragma unroll
-      for (int fb = 0; fb < 32; ++fb)
-        *reinterpret_cast<MLA_LDS f32x4_t*>(obuf + (w * 16 + r) * kLatent + 16 * fb + 4 * g) = ns.o[fb];
-      if (l < 16) {
-        stat[(w * 16 + r) * 4] = ns.m;
-        stat[(w * 16 + r) * 4 + 1] = l_w;
-        stat[(w * 16 + r) * 4 + 2] = lr_w;
-      }
-      lds_barrier();
-      const int rr = tid >> 4;                 // row 0..15
-      const int fp = tid & 15;                 // features 64*j + 4*fp + [0,4), j = 0..7:
-                                               // 16 lanes of a row store 256 contiguous bytes
-      float mw[4], lw[4], lrw[4];
-      float M = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mw[k] = stat[(k * 16 + rr) * 4];
-        lw[k] = stat[(k * 16 + rr) * 4 + 1];
-        lrw[k] = stat[(k * 16 + rr) * 4 + 2];
-        M = fmaxf(M, mw[k]);
-      }
-      const float Mb = M == -INFINITY ? 0.f : M;
-      float wgt[4], L = 0.f, LR = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        wgt[k] = __builtin_amdgcn_exp2f(mw[k] - Mb);
-        L += wgt[k] * lw[k];
-        LR += wgt[k] * lrw[k];
-      }
-      const float inv = LR > 0.f ? 1.0f / LR : 0.f;
-      const float lse_v = L > 0.f ? (Mb + __builtin_log2f(L)) * kLn2 : -INFINITY;
-      const int rhl = rr / p.q_len, rtq = rr - rhl * p.q_len;
-      const int rhead = hg * p.hg_heads + rhl;
-      if (rhead < p.N) {
-        f32x4_t acc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const MLA_LDS float* src = obuf + (k * 16 + rr) * kLatent + 4 * fp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += wgt[k] * *reinterpret_cast<const MLA_LDS f32x4_t*>(src + 64 * j);
-        }
-        if (nsplit == 1) {
-          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)rtq * p.o_st + (int64_t)rhead * p.o_sh + 4 * fp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bf16x4_t v = {(__bf16)(acc[j][0] * inv), (__bf16)(acc[j][1] * inv), (__bf16)(acc[j][2] * inv),
-                                (__bf16)(acc[j][3] * inv)};
-            *reinterpret_cast<bf16x4_t*>(orow + 64 * j) = v;
-          }
-          if (fp == 0) p.lse[((int64_t)b * p.q_len + rtq) * p.N + rhead] = lse_v;
-        } else {
-          float* prow = p.part_o + (slot * p.m_wg + rr) * kLatent + 4 * fp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(prow + 64 * j) = acc[j] * inv;
-          if (fp == 0) p.part_lse[slot * p.m_wg + rr] = lse_v;
-        }
-      }
-      lds_barrier();
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Wide variant: 64 query rows per unit, 4 waves, 32-token blocks
-// ---------------------------------------------------------------------------
-// Division of labour inside a workgroup (w = wave):
-//  * scores: wave w owns query rows 32*(w >> 1) .. +31 and tokens 16*(w & 1) .. +15 of
-//    each block.  S^T = K . Q^T runs on 16x16x32 MFMA: one K fragment (16 tokens x 32
-//    features, from LDS) feeds two MFMAs (row halves), the wave's query rows stay in
-//    registers (B operand).  The bf16 weights P go to LDS.
-//  * values: wave w owns latent features 128w .. 128w+127 of all 64 rows.
-//    O^T += V^T . P^T runs on 32x32x16 MFMA, V^T from LDS transpose reads of the same
-//    staged rows (the latent is V), P^T read back from LDS.
-// With this split every staged K and V byte is read by one wave only, and a wave holds
-// 128 accumulator registers (its O) plus its query fragments.
-// Pipeline over the blocks of a unit (a block = 32 token rows = half a page):
-//    QK(j) -> [softmax(j) interleaved with PV(j-1)] -> P(j) to LDS -> wait for own
-//    DMA of block j+1 -> barrier Y(j) -> DMA of block j+3
-// so the softmax VALU work of one block overlaps the PV MFMAs of the previous one
-// and a block needs one barrier; blocks j+2 and j+3 are in flight while block j+1 is
-// computed.  bf16 blocks land straight in a 4-slot ring; fp8 blocks land raw in a
-// 4-slot ring and are converted into 2 bf16 slots right after Y(j) (one more barrier
-// Z(j+1) before QK(j+1) reads them).
+// The cache rows of a piece stream through LDS in 32-token blocks (half a page).  A
+// block is stored column-group major: group G = c >> 3 (128 bytes of every row, 4 KB)
+// holds 32 tokens x 8 chunks of 16 B, chunk c of token t at slot
+// G * 256 + t * 8 + ((c & 7) ^ s(t)).  bf16 blocks land straight in a 4-slot ring;
+// fp8 blocks land raw in a 4-slot ring and are converted into 2 bf16 slots plus
+// per-token factors.  Ring slot of a block = its index in the unit's block stream & 3.
 constexpr int kBlk = 32;
 constexpr int kBlkBytesBf16 = kBlk * kRowBytesBf16;    // 36864
 constexpr int kBlkBytesFp8 = kBlk * kRowBytesFp8;      // 18688
 constexpr int kBlkGroupBytes = kBlk * 128;             // 4096: one 128-byte column of the block
 constexpr int kBlkChunksFp8 = kBlkBytesFp8 / 16;       // 1168
-constexpr int kWRows = 64;                             // query rows per wide unit
-
-// LDS plan of the wide kernel
-constexpr int kWRing = 4;                              // DMA ring depth (blocks)
-constexpr int kWSlot = kBlkBytesBf16;                  // bf16 block slots at 0, 36864, ...
-constexpr int kWRaw = 2 * kWSlot;                      // fp8: 2 converted slots, then 4 raw blocks
-constexpr int kWFac = kWRaw + kWRing * kBlkBytesFp8;   // fp8 per-token factors, 2 x [3][32] f32
-constexpr int kWFacBytes = 3 * kBlk * 4;
-constexpr int kWP = 149504;                            // P: 2 buffers x 64 rows x 64 B
-constexpr int kWPBytes = kWRows * 64;
-constexpr int kWStats = kWP + 2 * kWPBytes;            // per token half and row {m, l, lr, -}
-constexpr int kWFlag = kWStats + 2 * kWRows * 16;      // overflow flag of the reference max
-constexpr int kWPlan = kWFlag + 16;                    // split-plan scratch
-constexpr int kWLdsBytes = kWPlan + kPlanLdsBytes;
-constexpr int kWStagePitch32 = 528;                    // epilogue staging: 512 B fp32 row + pad
-constexpr int kWStagePitch16 = 272;                    // 256 B bf16 row + pad
-static_assert(kWRing * kWSlot <= kWP && kWFac + 2 * kWFacBytes <= kWP, "wide LDS plan");
-static_assert(4 * 32 * kWStagePitch32 <= 2 * kWSlot, "epilogue staging fits the block slots");
-static_assert(kWLdsBytes <= 160 * 1024, "LDS budget");
+constexpr int kRing = 4;                               // DMA ring depth (blocks)
+constexpr int kSlot = kBlkBytesBf16;                   // bf16 block slots at 0, 36864, ...
+constexpr int kRaw = 2 * kSlot;                        // fp8: 2 converted slots, then 4 raw blocks
+constexpr int kFac = kRaw + kRing * kBlkBytesFp8;      // fp8 per-token factors, 2 x [3][32] f32
+constexpr int kFacBytes = 3 * kBlk * 4;
+constexpr int kStageEnd = 149504;                      // end of the staging area
+static_assert(kRing * kSlot <= kStageEnd && kFac + 2 * kFacBytes <= kStageEnd, "staging LDS plan");
 
 // bf16 block: 36 DMA instructions of 64 x 16 B; wave w loads tokens 8w .. 8w+7 of
 // every 128-byte column i (instruction i = 0..8): lane j takes token t = 8w + (j >> 3),
@@ -795,6 +379,471 @@ __device__ __forceinline__ void convert_fp8_blk(const MLA_LDS char* raw, MLA_LDS
     fac[2 * kBlk + tid] = v != 0.f ? 1.0f / v : 0.f;
   }
 }
+
+// ---------------------------------------------------------------------------
+// Softmax reference max
+// ---------------------------------------------------------------------------
+// Softmax bookkeeping without rescaling the accumulators.  Each row's reference
+// max m is fixed from the first 32-token block of the unit (exact for that block);
+// later scores may exceed it, so p = 2^(s - m) can be > 1, which float32
+// accumulation and bfloat16 probabilities represent without loss of relative
+// precision.  A visible score more than kRefSlack above m would risk overflow:
+// the block then raises a flag and the workgroup redoes the unit with the larger
+// reference.  O never needs a VALU rescale inside the page loop.
+constexpr float kRefSlack = 64.0f;
+
+// ---------------------------------------------------------------------------
+// Narrow variant: 16 query rows per unit (16-head decode), 4 waves, 32-token blocks
+// ---------------------------------------------------------------------------
+// Division of labour inside a workgroup (w = wave, th = w & 1):
+//  * scores: wave w computes S^T = K . Q^T for tokens 16th .. 16th+15 of each block and
+//    all 16 rows (16x16x32 MFMA, K fragments from LDS, the query in registers).  Waves
+//    w and w ^ 2 compute the same scores: that costs LDS and MFMA time the block's HBM
+//    time covers, and keeps one barrier per block.  Waves 0 and 1 write the weights P.
+//  * values: wave w owns latent features 128w .. 128w+127 of the 16 rows,
+//    O^T += V^T . P^T on 16x16x32 MFMA over the block's 32 tokens.
+// The contraction order of the 32 tokens inside one PV MFMA is a permutation chosen so
+// that each transpose read touches 8 consecutive tokens per half-wave (conflict-free
+// with the block swizzle); P is stored in that order, so the product is unchanged.
+// The unit's pieces form one block stream: the DMA of the next piece's first blocks is
+// issued while the current piece finishes, so a piece boundary costs no page latency.
+constexpr int kNRows = 16;
+constexpr int kNP = kStageEnd;                         // P: 2 buffers x 16 rows x 64 B
+constexpr int kNPBytes = kNRows * 64;
+constexpr int kNStats = kNP + 2 * kNPBytes;            // per token half and row {m, l, lr, -}
+constexpr int kNFlag = kNStats + 2 * kNRows * 16;      // overflow flag of the reference max
+constexpr int kNPlan = kNFlag + 16;                    // split-plan scratch
+constexpr int kNLdsBytes = kNPlan + kPlanLdsBytes;
+static_assert(kNLdsBytes <= 160 * 1024, "LDS budget");
+
+// token of k-slot 4h + i (i = 0..3) of lane group g in the PV contraction
+__device__ __forceinline__ int pv_token(int g, int h) { return 16 * (g >> 1) + 8 * h + 4 * (g & 1); }
+
+// S^T of this wave's 16 tokens for the 16 rows: 18 steps of 32 features, K fragments
+// read kPrefK steps ahead.
+__device__ __forceinline__ f32x4_t narrow_scores(const MLA_LDS char* blk, const bf16x8_t (&qf)[18],
+                                                 const uint32_t (&kbase)[2]) {
+  constexpr int kPrefK = 4;
+  uint32_t ka[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) ka[m] = opaque(lds_addr(blk) + kbase[m]);
+  bf16x8_t kbuf[kPrefK];
+#pragma unroll
+  for (int d = 0; d < kPrefK; ++d) kbuf[d] = lds_read_b128_at(ka[d & 1] + (d >> 1) * kBlkGroupBytes);
+  f32x4_t sc = {};
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) {
+    const bf16x8_t a = kbuf[kk % kPrefK];
+    const int nk = kk + kPrefK;
+    if (nk < 18) kbuf[kk % kPrefK] = lds_read_b128_at(ka[nk & 1] + (nk >> 1) * kBlkGroupBytes);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sc, 0, 0, 0);
+  }
+  return sc;
+}
+
+// O^T[this wave's 128 features][16 rows] += V^T . P^T over one block: 8 feature tiles of
+// 16, each one MFMA over the 32 tokens (two transpose reads for V^T); P^T is one 16-byte
+// read per lane.
+__device__ __forceinline__ void narrow_pv(const MLA_LDS char* blk, const MLA_LDS char* pbuf, f32x4_t (&o)[8],
+                                          const uint32_t (&vbase)[2][4], uint32_t pbase) {
+  uint32_t va[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int f3 = 0; f3 < 4; ++f3) va[h][f3] = opaque(lds_addr(blk) + vbase[h][f3]);
+  const bf16x8_t pb = lds_read_b128_at(opaque(lds_addr(pbuf) + pbase));
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const uint32_t off = (uint32_t)((f >> 2) * kBlkGroupBytes);
+    const bf16x4_t lo = lds_read_tr16_at(va[0][f & 3] + off);
+    const bf16x4_t hi = lds_read_tr16_at(va[1][f & 3] + off);
+    const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    o[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[f], 0, 0, 0);
+  }
+}
+
+// A piece whose blocks are (being) staged: token range, page range and page ids.
+struct StagedPiece {
+  Piece pc;
+  int nblk, pg0, pg1;
+  PageIds ids;
+};
+
+// (the piece values are workgroup-uniform; readfirstlane states it to the compiler)
+__device__ __forceinline__ void stage_piece(StagedPiece& sp, const DecodeParams& p, int l) {
+  sp.pc.b = __builtin_amdgcn_readfirstlane(sp.pc.b);
+  sp.pc.t_begin = __builtin_amdgcn_readfirstlane(sp.pc.t_begin);
+  sp.pc.t_end = __builtin_amdgcn_readfirstlane(sp.pc.t_end);
+  sp.nblk = sp.pc.t_end > sp.pc.t_begin ? (sp.pc.t_end - sp.pc.t_begin + kBlk - 1) / kBlk : 0;
+  sp.pg0 = sp.pc.t_begin / kPage;
+  sp.pg1 = sp.nblk > 0 ? (sp.pc.t_end + kPage - 1) / kPage : sp.pg0;
+  load_page_ids(sp.ids, p, sp.pc.b, sp.pg0, sp.pg1, l);
+}
+
+template <bool FP8>
+__device__ __forceinline__ void issue_piece_block(StagedPiece& sp, const DecodeParams& p, int jb, int g,
+                                                  MLA_LDS char* smem, int w, int l) {
+  jb = __builtin_amdgcn_readfirstlane(jb);
+  g = __builtin_amdgcn_readfirstlane(g);
+  const char* pg = page_ptr(sp.ids, p, sp.pc.b, sp.pg0 + (jb >> 1), sp.pg1, l, FP8);
+  if constexpr (FP8)
+    issue_blk_fp8(pg + (jb & 1) * kBlkBytesFp8, smem + kRaw + (g & (kRing - 1)) * kBlkBytesFp8, w, l);
+  else
+    issue_blk_bf16(pg + (jb & 1) * kBlkBytesBf16, smem + (g & (kRing - 1)) * kSlot, w, l);
+}
+
+// wait until at most one block (later > 0) or nothing issued after the awaited one is
+// outstanding (per-wave instruction counts of a block: 9 bf16; 5, 5, 5, 4 fp8)
+template <bool FP8>
+__device__ __forceinline__ void wait_blocks_after(int later, int w) {
+  if (later <= 0) {
+    wait_vmcnt<0>();
+  } else if constexpr (FP8) {
+    if (w == 3) wait_vmcnt<4>();
+    else wait_vmcnt<5>();
+  } else {
+    wait_vmcnt<9>();
+  }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kNLdsBytes];
+  MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  const int th = w & 1;                          // token half of the score phase
+  const int l16 = l & 15, g4 = l >> 4;
+  MLA_LDS int* ovf_flag = reinterpret_cast<MLA_LDS int*>(smem + kNFlag);
+  MLA_LDS f32x4_t* stats = reinterpret_cast<MLA_LDS f32x4_t*>(smem + kNStats);   // [2][16]
+
+  // Per-lane LDS offsets, fixed for the whole kernel.
+  // K fragment of step kk: token 16th + l16, chunk 4kk + g4 (group kk >> 1, in-group
+  // chunk 4(kk & 1) + g4).
+  uint32_t kbase[2];
+  {
+    const int t = 16 * th + l16;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) kbase[m] = (uint32_t)(t * 8 + ((4 * m + g4) ^ page_swz(t))) * 16;
+  }
+  // V^T transpose read h of feature tile f (features 128w + 16f .. +15): the 16 lanes of
+  // group g4 read tokens pv_token(g4, h) + (l16 >> 2), features 128w + 16f + 4(l16 & 3)
+  // .. +3, i.e. chunk 16w + 2f + ((l16 & 3) >> 1) (group 2w + (f >> 2), in-group chunk
+  // 2(f & 3) + ((l16 & 3) >> 1)), byte 8(l16 & 1); f >> 2 only adds an offset.
+  uint32_t vbase[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int f3 = 0; f3 < 4; ++f3) {
+      const int t = pv_token(g4, h) + (l16 >> 2);
+      const int cin = 2 * f3 + ((l16 & 3) >> 1);
+      vbase[h][f3] = (uint32_t)(2 * w * kBlkGroupBytes + (t * 8 + (cin ^ page_swz(t))) * 16 + 8 * (l16 & 1));
+    }
+  // P rows: 64 B = 4 chunks; chunk g holds the 8 k-slots of lane group g, at position
+  // g ^ ((row >> 2) & 3).  PV reads chunk g4 of row l16.
+  const uint32_t pbase = (uint32_t)(l16 * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16));
+  // score-phase element i of this lane is token 16th + 4g4 + i = k-slot 4(g4 >> 1) + i of
+  // lane group 2th + (g4 & 1)
+  const int pg_w = 2 * th + (g4 & 1);
+  const uint32_t pwrite = (uint32_t)(l16 * 64 + ((pg_w ^ ((l16 >> 2) & 3)) * 16) + 8 * (g4 >> 1));
+
+  // query row of this lane in both phases: r = l16
+  const int hl = l16 / p.q_len, tq = l16 - hl * p.q_len;
+  const int head = hl;                            // one head group
+  const bool row_ok = head < p.N;
+
+  MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kNPlan);
+  PlanTotals tot{0, 1};
+  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
+  for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
+    int sid, hg;
+    unit_to_stream(u, p.n_hg, &sid, &hg);
+    if (sid >= p.n_streams) continue;
+    PieceIter it;
+    it.init(p, plan_lds, tot, sid, tid);
+    StagedPiece cur, nxt;
+    bool has_cur = it.next(p, hg, tid, cur.pc);
+    if (!has_cur) continue;
+    stage_piece(cur, p, l);
+    bool has_nxt = it.next(p, hg, tid, nxt.pc);
+    if (has_nxt) stage_piece(nxt, p, l);
+
+    // Block stream: the issue cursor (piece 0 = cur, 1 = nxt; block jb) runs up to 3
+    // blocks ahead of the block being computed, across the boundary into nxt.
+    int ic_piece = 0, ic_j = 0;
+    int issued = 0;                              // blocks issued in this unit
+    int g0 = 0;                                  // stream index of cur's block 0
+    auto issue_next = [&]() {
+      if (ic_piece == 0 && ic_j >= cur.nblk) {
+        if (!has_nxt) return;
+        ic_piece = 1;
+        ic_j = 0;
+      }
+      if (ic_piece == 0) {
+        issue_piece_block<FP8>(cur, p, ic_j, issued, smem, w, l);
+      } else {
+        if (ic_j >= nxt.nblk) return;
+        issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, w, l);
+      }
+      ++ic_j;
+      ++issued;
+    };
+
+    while (true) {
+      const int b = cur.pc.b, t_begin = cur.pc.t_begin, t_end = cur.pc.t_end, seq = cur.pc.seq;
+      const int nblk = cur.nblk;
+      const int nvis = seq - p.q_len + 1 + tq;
+      auto valid_of = [&](int j) {
+        const int v = t_end - (t_begin + kBlk * j);
+        return v < kBlk ? v : kBlk;
+      };
+
+      // the piece's first three blocks: in flight already (issued while the previous
+      // piece finished) or issued here, ahead of the query loads.  The stream must be
+      // three blocks ahead before step 0: each step issues only one more.
+      for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      // query fragments (B operand): row l16, features 32kk + 8g4 .. +7; padding rows
+      // load head 0 and are zeroed.  Waiting for them also waits for the blocks issued
+      // before them, block 0 among them.
+      bf16x8_t qf[18];
+      {
+        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
+        if (!row_ok) {
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) qf[kk] = bf16x8_t{};
+        }
+      }
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[kk]));
+
+      f32x4_t o[8];
+      float m = -INFINITY, lsum = 0.f, lrsum = 0.f, m_seen = -INFINITY;
+      int ovf = 0;
+      float m_restart = -INFINITY;
+      for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f) o[f] = f32x4_t{};
+        m = m_restart;
+        lsum = 0.f;
+        lrsum = 0.f;
+        m_seen = -INFINITY;
+        ovf = 0;
+        if (tid == 0) *ovf_flag = 0;
+        if (attempt > 0 && nblk > 0) {
+          // drop whatever the stream had in flight and restage this piece from block 0
+          wait_vmcnt<0>();
+          ic_piece = 0;
+          ic_j = 0;
+          g0 = issued;
+          load_page_ids(cur.ids, p, b, cur.pg0, cur.pg1, l);
+          issue_next();
+          issue_next();
+          issue_next();
+          wait_vmcnt<0>();
+        }
+        if constexpr (!FP8) {
+          if (nblk == 1) zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), w, l);
+        }
+        lds_barrier();                           // block 0 visible, flag reset published
+        if constexpr (FP8) {
+          if (nblk > 0) {
+            convert_fp8_blk(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, smem,
+                            reinterpret_cast<MLA_LDS float*>(smem + kFac), valid_of(0), tid, p.scale_log2);
+            lds_barrier();
+          }
+        }
+
+        // Block step: scores of block j and their weights into P(j), with the PV MFMAs
+        // of block j-1 between the row maxima and the exponentials (WITH_PV), then the
+        // hand-over to block j+1.
+        auto step = [&](int j, auto with_pv) {
+          constexpr bool WITH_PV = decltype(with_pv)::value;
+          const int g = g0 + j;
+          const MLA_LDS char* cb = smem + (FP8 ? (j & 1) : (g & (kRing - 1))) * kSlot;
+          const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kFac + (j & 1) * kFacBytes);
+          const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of element 0
+
+          f32x4_t sc = narrow_scores(cb, qf, kbase);
+          float mt = -INFINITY;
+          {
+            f32x4_t kf;
+            if constexpr (FP8) kf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 16 * th + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = sc[i] * (FP8 ? kf[i] : p.scale_log2);
+              x = (tok0 + i < nvis) ? x : -INFINITY;
+              sc[i] = x;
+              mt = fmaxf(mt, x);
+            }
+            mt = max_xor32(max_xor16(mt));
+          }
+          if constexpr (!WITH_PV) {
+            if (attempt == 0) {
+              // reference max of each row from the piece's first block: the two token
+              // halves meet in LDS
+              if (w < 2 && g4 == 0) stats[th * kNRows + l16][0] = mt;
+              lds_barrier();
+              m = fmaxf(stats[l16][0], stats[kNRows + l16][0]);
+            }
+          }
+          m_seen = fmaxf(m_seen, mt);
+          const float base = m == -INFINITY ? 0.f : m;
+          ovf |= (mt > base + kRefSlack) ? 1 : 0;
+
+          if constexpr (WITH_PV) {
+            const int gp = g - 1;
+            narrow_pv(smem + (FP8 ? ((j - 1) & 1) : (gp & (kRing - 1))) * kSlot, smem + kNP + ((j - 1) & 1) * kNPBytes,
+                      o, vbase, pbase);
+          }
+
+          // weights p = 2^(x - m), bf16 for the MFMA (fp8: times v_scale); the sums keep
+          // the exact weights (LSE) and the rounded ones (O)
+          {
+            f32x4_t vf, ivf;
+            if constexpr (FP8) {
+              vf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + kBlk + 16 * th + 4 * g4);
+              ivf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 2 * kBlk + 16 * th + 4 * g4);
+            }
+            bf16x4_t pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pr = __builtin_amdgcn_exp2f(sc[i] - base);
+              const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
+              pk[i] = rr;
+              lsum += pr;
+              lrsum += FP8 ? (float)rr * ivf[i] : (float)rr;
+            }
+            if (w < 2) *reinterpret_cast<MLA_LDS bf16x4_t*>(smem + kNP + (j & 1) * kNPBytes + pwrite) = pk;
+          }
+
+          if (j + 1 < nblk) {
+            // this wave's share of block j+1 has landed once only the blocks issued after
+            // it (at most block j+2) are outstanding
+            wait_blocks_after<FP8>(issued - (g + 2), w);
+            if constexpr (!FP8) {
+              if (j + 2 == nblk) zero_own_tail(smem + ((g + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
+            }
+          }
+          lds_barrier();                         // Y(j)
+          issue_next();                          // block g+3 of the stream
+          if constexpr (FP8) {
+            if (j + 1 < nblk) {
+              convert_fp8_blk(smem + kRaw + ((g + 1) & (kRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kSlot,
+                              reinterpret_cast<MLA_LDS float*>(smem + kFac + ((j + 1) & 1) * kFacBytes),
+                              valid_of(j + 1), tid, p.scale_log2);
+              lds_barrier();                     // Z(j+1)
+            }
+          }
+        };
+        if (nblk > 0) {
+          step(0, std::false_type{});
+          for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
+          const int jl = nblk - 1;
+          narrow_pv(smem + (FP8 ? (jl & 1) : ((g0 + jl) & (kRing - 1))) * kSlot, smem + kNP + (jl & 1) * kNPBytes, o,
+                    vbase, pbase);
+        }
+        // any row over the reference slack: the whole workgroup redoes the piece
+        if (ovf) *ovf_flag = 1;
+        lds_barrier();
+        const int redo = *ovf_flag;
+        lds_barrier();
+        if (redo == 0) break;
+        // restart with the largest score seen in either token half of each row
+        m_seen = max_xor32(max_xor16(m_seen));
+        if (w < 2 && g4 == 0) stats[th * kNRows + l16][0] = m_seen;
+        lds_barrier();
+        m_restart = fmaxf(stats[l16][0], stats[kNRows + l16][0]);
+        lds_barrier();
+      }
+
+      // ---- epilogue ----
+      // row sums over the 4 lane groups, then over the two token halves
+      {
+        const float a = sum_xor32(sum_xor16(lsum));
+        const float c = sum_xor32(sum_xor16(lrsum));
+        if (w < 2 && g4 == 0) stats[th * kNRows + l16] = f32x4_t{m, a, c, 0.f};
+      }
+      lds_barrier();
+      const bool single = cur.pc.nsplit == 1;
+      const size_t slot = (size_t)cur.pc.slot * p.n_hg + hg;
+      const float lt = stats[l16][1] + stats[kNRows + l16][1];
+      const float lr = stats[l16][2] + stats[kNRows + l16][2];
+      const float inv = lr > 0.f ? 1.0f / lr : 0.f;
+      if (w == 0 && g4 == 0 && row_ok) {
+        const float lse_v = lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -INFINITY;
+        if (single) p.lse[((int64_t)b * p.q_len + tq) * p.N + head] = lse_v;
+        else p.part_lse[slot * kNRows + l16] = lse_v;
+      }
+      // this lane's accumulators: row l16, features 128w + 16f + 4g4 .. +3
+      if (row_ok) {
+        if (single) {
+          uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq * p.o_st + (int64_t)head * p.o_sh + 128 * w + 4 * g4;
+#pragma unroll
+          for (int f = 0; f < 8; ++f) {
+            const bf16x4_t v = {(__bf16)(o[f][0] * inv), (__bf16)(o[f][1] * inv), (__bf16)(o[f][2] * inv),
+                                (__bf16)(o[f][3] * inv)};
+            *reinterpret_cast<bf16x4_t*>(orow + 16 * f) = v;
+          }
+        } else {
+          float* prow = p.part_o + (slot * kNRows + l16) * kLatent + 128 * w + 4 * g4;
+#pragma unroll
+          for (int f = 0; f < 8; ++f) *reinterpret_cast<f32x4_t*>(prow + 16 * f) = o[f] * inv;
+        }
+      }
+      lds_barrier();                             // stats and P free for the next piece
+
+      if (!has_nxt) break;
+      // the next piece becomes current; its blocks continue the stream
+      g0 += nblk;
+      cur = nxt;
+      if (ic_piece == 1) {
+        ic_piece = 0;                            // the cursor was already inside it
+      } else {
+        ic_j = 0;                                // nothing of it issued yet
+      }
+      has_nxt = it.next(p, hg, tid, nxt.pc);
+      if (has_nxt) stage_piece(nxt, p, l);
+    }
+    wait_vmcnt<0>();                             // nothing in flight into LDS at the unit's end
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide variant: 64 query rows per unit, 4 waves, 32-token blocks
+// ---------------------------------------------------------------------------
+// Division of labour inside a workgroup (w = wave):
+//  * scores: wave w owns query rows 32*(w >> 1) .. +31 and tokens 16*(w & 1) .. +15 of
+//    each block.  S^T = K . Q^T runs on 16x16x32 MFMA: one K fragment (16 tokens x 32
+//    features, from LDS) feeds two MFMAs (row halves), the wave's query rows stay in
+//    registers (B operand).  The bf16 weights P go to LDS.
+//  * values: wave w owns latent features 128w .. 128w+127 of all 64 rows.
+//    O^T += V^T . P^T runs on 32x32x16 MFMA, V^T from LDS transpose reads of the same
+//    staged rows (the latent is V), P^T read back from LDS.
+// With this split every staged K and V byte is read by one wave only, and a wave holds
+// 128 accumulator registers (its O) plus its query fragments.
+// Pipeline over the blocks of a unit (a block = 32 token rows = half a page):
+//    QK(j) -> [softmax(j) interleaved with PV(j-1)] -> P(j) to LDS -> wait for own
+//    DMA of block j+1 -> barrier Y(j) -> DMA of block j+3
+// so the softmax VALU work of one block overlaps the PV MFMAs of the previous one
+// and a block needs one barrier; blocks j+2 and j+3 are in flight while block j+1 is
+// computed.  bf16 blocks land straight in a 4-slot ring; fp8 blocks land raw in a
+// 4-slot ring and are converted into 2 bf16 slots right after Y(j) (one more barrier
+// Z(j+1) before QK(j+1) reads them).
+constexpr int kWRows = 64;                             // query rows per wide unit
+constexpr int kWP = kStageEnd;                         // P: 2 buffers x 64 rows x 64 B
+constexpr int kWPBytes = kWRows * 64;
+constexpr int kWStats = kWP + 2 * kWPBytes;            // per token half and row {m, l, lr, -}
+constexpr int kWFlag = kWStats + 2 * kWRows * 16;      // overflow flag of the reference max
+constexpr int kWPlan = kWFlag + 16;                    // split-plan scratch
+constexpr int kWLdsBytes = kWPlan + kPlanLdsBytes;
+constexpr int kWStagePitch32 = 528;                    // epilogue staging: 512 B fp32 row + pad
+constexpr int kWStagePitch16 = 272;                    // 256 B bf16 row + pad
+static_assert(4 * 32 * kWStagePitch32 <= 2 * kSlot, "epilogue staging fits the block slots");
+static_assert(kWLdsBytes <= 160 * 1024, "LDS budget");
 
 // S^T = K . Q^T of this wave's 16 tokens of a block for its 32 rows: 18 steps of 32
 // features, each one K fragment read (kPrefK steps ahead, a rolling register buffer)
@@ -935,9 +984,9 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       auto issue = [&](int j) {
         const char* pg = page_ptr(ids, p, b, pg0 + (j >> 1), pg1, l, FP8);
         if constexpr (FP8)
-          issue_blk_fp8(pg + (j & 1) * kBlkBytesFp8, smem + kWRaw + (j & (kWRing - 1)) * kBlkBytesFp8, w, l);
+          issue_blk_fp8(pg + (j & 1) * kBlkBytesFp8, smem + kRaw + (j & (kRing - 1)) * kBlkBytesFp8, w, l);
         else
-          issue_blk_bf16(pg + (j & 1) * kBlkBytesBf16, smem + (j & (kWRing - 1)) * kWSlot, w, l);
+          issue_blk_bf16(pg + (j & 1) * kBlkBytesBf16, smem + (j & (kRing - 1)) * kSlot, w, l);
       };
       auto valid_of = [&](int j) {
         const int v = t_end - (t_begin + kBlk * j);
@@ -996,7 +1045,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         lds_barrier();
         if constexpr (FP8) {
           if (nblk > 0)
-            convert_fp8_blk(smem + kWRaw, smem, reinterpret_cast<MLA_LDS float*>(smem + kWFac), valid_of(0), tid,
+            convert_fp8_blk(smem + kRaw, smem, reinterpret_cast<MLA_LDS float*>(smem + kFac), valid_of(0), tid,
                             p.scale_log2);
         }
         if (nblk > 1) issue(1);
@@ -1008,8 +1057,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         // without PV (peeled) so that the steady-state body is one straight-line region.
         auto step = [&](int j, auto with_pv) {
           constexpr bool WITH_PV = decltype(with_pv)::value;
-          const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kWRing - 1))) * kWSlot;
-          const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kWFac + (j & 1) * kWFacBytes);
+          const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kRing - 1))) * kSlot;
+          const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kFac + (j & 1) * kFacBytes);
           const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
 
           f32x4_t sc[2];
@@ -1060,7 +1109,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 
           // PV of the previous block overlaps this block's exponentials
           if constexpr (WITH_PV) {
-            const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kWRing - 1))) * kWSlot;
+            const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kRing - 1))) * kSlot;
             wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
           }
 
@@ -1105,15 +1154,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
               wait_vmcnt<0>();
             }
             if constexpr (!FP8) {
-              if (j + 2 == nblk) zero_own_tail(smem + ((j + 1) & (kWRing - 1)) * kWSlot, valid_of(j + 1), w, l);
+              if (j + 2 == nblk) zero_own_tail(smem + ((j + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
             }
           }
           lds_barrier();                              // Y(j)
           if (j + 3 < nblk) issue(j + 3);
           if constexpr (FP8) {
             if (j + 1 < nblk)
-              convert_fp8_blk(smem + kWRaw + ((j + 1) & (kWRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kWSlot,
-                              reinterpret_cast<MLA_LDS float*>(smem + kWFac + ((j + 1) & 1) * kWFacBytes),
+              convert_fp8_blk(smem + kRaw + ((j + 1) & (kRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kSlot,
+                              reinterpret_cast<MLA_LDS float*>(smem + kFac + ((j + 1) & 1) * kFacBytes),
                               valid_of(j + 1), tid, p.scale_log2);
             lds_barrier();                            // Z(j+1)
           }
@@ -1122,7 +1171,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           step(0, std::false_type{});
           for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
           const int jl = nblk - 1;
-          wide_pv(smem + (FP8 ? (jl & 1) : (jl & (kWRing - 1))) * kWSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase,
+          wide_pv(smem + (FP8 ? (jl & 1) : (jl & (kRing - 1))) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase,
                   pbase);
         }
         // any row over the reference slack: the whole workgroup redoes the unit

@@ -253,10 +253,11 @@ def test_fp8_rows_with_distinct_k_and_v_scales(N):
         check_lse(lse.cpu().numpy(), lse_ref, "fp8 scales")
 
 
-def test_large_score_range_triggers_reference_redo():
+@pytest.mark.parametrize("N", [16, 128])
+def test_large_score_range_triggers_reference_redo(N):
     """Scores that grow by far more than the reference slack within a unit: the
     kernel redoes the unit with a larger reference and still matches the oracle."""
-    w = _small("range", 16, 1, [640, 640], seed=83)
+    w = _small("range", N, 1, [640, 640], seed=83)
     rows = w.kv_rows.copy()
     # scale up the latents of one late page of each request by 2^7
     for b in range(2):
