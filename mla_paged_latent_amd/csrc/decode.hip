@@ -59,6 +59,7 @@ struct DecodeParams {
   int32_t num_splits;  // 0 automatic, k >= 1 forced
   int32_t n_streams;   // streams of the plan
   int32_t n_units;     // n_streams x head groups, rounded for the sibling order
+  int32_t max_slots;   // partial slots the workspace holds
 };
 
 // unit -> (stream, head group).  Sibling head groups of one stream sit 8 units apart
@@ -85,13 +86,14 @@ __device__ __forceinline__ void unit_to_stream(int u, int n_hg, int* stream, int
 // num_splits == 0 (automatic): request b occupies a stretch of kSegOverhead +
 // pages(b) cost positions on one line (the overhead stands for the fixed cost of
 // a piece: its start-up and its partial row); the line is cut into n_streams
-// streams of T = ceil(total / n_streams) positions, one unit per workgroup and head
-// group, so that every workgroup gets the same amount of work whatever the length
-// mix.  The pages of b inside stream s form one piece; b is split when its pages
-// straddle a cut.  The piece of b in stream s writes partial slot b + s: the slots
-// of b + 1 all lie above those of b, so B + n_streams slots suffice.  Every
-// workgroup derives the plan from seq_lens itself (one prefix sum over the batch),
-// so there is no planning launch and no host synchronisation.
+// streams, stream s covering [s * total / n, (s + 1) * total / n), one unit per
+// workgroup and head group, so that every workgroup gets the same amount of work
+// (within one position) whatever the length mix.  The pages of b inside stream s
+// form one piece; b is split when its pages straddle a cut.  The piece of b in
+// stream s writes partial slot b + s: the slots of b + 1 all lie above those of b,
+// so B + n_streams slots suffice.  Every workgroup derives the plan from seq_lens
+// itself (one prefix sum over the batch), so there is no planning launch and no
+// host synchronisation.
 //
 // num_splits == k >= 1: stream s is split s % k of request s / k, over page-aligned
 // chunks of ceil(seq / k) tokens; its partial slot is s.  k == 1 keeps one piece
@@ -116,8 +118,11 @@ __device__ __forceinline__ long long uniform64(long long v) {
 }
 
 struct PlanTotals {
-  long long total;    // cost positions of the whole batch
-  long long T;        // positions per stream
+  long long total;    // cost positions of the whole batch (>= 1)
+  long long n;        // streams
+  __device__ __forceinline__ long long start(long long s) const { return s * total / n; }
+  // the stream holding position X: the largest s with start(s) <= X
+  __device__ __forceinline__ int stream_of(long long X) const { return (int)(((X + 1) * n - 1) / total); }
 };
 
 // Thread tid sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
@@ -144,7 +149,9 @@ __device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS
   pre[tid] = off + incl - local;
   PlanTotals r;
   r.total = uniform64(wtot[0] + wtot[1] + wtot[2] + wtot[3]);
-  r.T = (r.total + p.n_streams - 1) / p.n_streams;
+  // no more streams than positions, so that no stream is empty (the pieces of a
+  // request then sit in consecutive streams)
+  r.n = p.n_streams < r.total ? p.n_streams : r.total;
   lds_barrier();
   return r;
 }
@@ -185,7 +192,8 @@ struct Piece {
 // Walks the pieces of stream s in order; every value is workgroup-uniform.  pre / tot
 // come from plan_prefix (automatic mode only).
 struct PieceIter {
-  long long lo, hi, c, T;
+  long long lo, hi, c;
+  PlanTotals tot;
   int b, s;
   bool done;
 
@@ -194,10 +202,10 @@ struct PieceIter {
     s = stream;
     done = false;
     if (p.num_splits > 0) return;
-    T = tot.T;
-    lo = (long long)s * tot.T;
-    hi = lo + tot.T < tot.total ? lo + tot.T : tot.total;
-    if (lo >= tot.total) {
+    this->tot = tot;
+    lo = tot.start(s);
+    hi = tot.start(s + 1);
+    if (s >= tot.n) {
       done = true;
       return;
     }
@@ -237,7 +245,7 @@ struct PieceIter {
         const long long a = lo > p0 ? lo : p0;
         const long long e = hi < p0 + np ? hi : p0 + np;
         if (a < e) {
-          const int sf = (int)(p0 / T), sl = (int)((p0 + np - 1) / T);
+          const int sf = tot.stream_of(p0), sl = tot.stream_of(p0 + np - 1);
           if (s == sf && hg == 0 && tid == 0) p.req[b] = make_int4(b + sf, sl - sf + 1, 0, seq);
           const int t1 = (int)(e - p0) * kPage;
           pc = Piece{b, (int)(a - p0) * kPage, t1 < seq ? t1 : seq, seq, sl - sf + 1, b + s};
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
   const bool row_ok = head < p.N;
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kNPlan);
-  PlanTotals tot{0, 1};
+  PlanTotals tot{1, 1};
   if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
@@ -563,11 +571,16 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
     PieceIter it;
     it.init(p, plan_lds, tot, sid, tid);
     StagedPiece cur, nxt;
-    bool has_cur = it.next(p, hg, tid, cur.pc);
-    if (!has_cur) continue;
+    if (!it.next(p, hg, tid, cur.pc)) continue;
     stage_piece(cur, p, l);
-    bool has_nxt = it.next(p, hg, tid, nxt.pc);
-    if (has_nxt) stage_piece(nxt, p, l);
+    // the following piece is looked up once the current one's first blocks are in flight
+    bool nxt_known = false, has_nxt = false;
+    auto fetch_nxt = [&]() {
+      if (nxt_known) return;
+      nxt_known = true;
+      has_nxt = it.next(p, hg, tid, nxt.pc);
+      if (has_nxt) stage_piece(nxt, p, l);
+    };
 
     // Block stream: the issue cursor (piece 0 = cur, 1 = nxt; block jb) runs up to 3
     // blocks ahead of the block being computed, across the boundary into nxt.
@@ -576,7 +589,7 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
     int g0 = 0;                                  // stream index of cur's block 0
     auto issue_next = [&]() {
       if (ic_piece == 0 && ic_j >= cur.nblk) {
-        if (!has_nxt) return;
+        if (!nxt_known || !has_nxt) return;
         ic_piece = 1;
         ic_j = 0;
       }
@@ -603,6 +616,7 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       // piece finished) or issued here, ahead of the query loads.  The stream must be
       // three blocks ahead before step 0: each step issues only one more.
       for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      const bool topped = issued >= g0 + 3;
       // query fragments (B operand): row l16, features 32kk + 8g4 .. +7; padding rows
       // load head 0 and are zeroed.  Waiting for them also waits for the blocks issued
       // before them, block 0 among them.
@@ -615,6 +629,10 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
 #pragma unroll
           for (int kk = 0; kk < 18; ++kk) qf[kk] = bf16x8_t{};
         }
+      }
+      fetch_nxt();
+      if (!topped) {
+        for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       }
       wait_vmcnt<0>();
 #pragma unroll
@@ -796,17 +814,17 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       }
       lds_barrier();                             // stats and P free for the next piece
 
+      fetch_nxt();
       if (!has_nxt) break;
       // the next piece becomes current; its blocks continue the stream
       g0 += nblk;
       cur = nxt;
+      nxt_known = false;
       if (ic_piece == 1) {
         ic_piece = 0;                            // the cursor was already inside it
       } else {
         ic_j = 0;                                // nothing of it issued yet
       }
-      has_nxt = it.next(p, hg, tid, nxt.pc);
-      if (has_nxt) stage_piece(nxt, p, l);
     }
     wait_vmcnt<0>();                             // nothing in flight into LDS at the unit's end
   }
@@ -948,7 +966,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
   }
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
-  PlanTotals tot{0, 1};
+  PlanTotals tot{1, 1};
   if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
@@ -1294,6 +1312,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int4 rq = p.req[b];
   const int first = rq.x, nsplit = rq.y;
   if (nsplit <= 1) return;
+  // the decode kernel writes req[b] with slots inside the workspace; checked anyway so
+  // that no read can leave it
+  if (first < 0 || nsplit > p.max_slots || first > p.max_slots - nsplit) return;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = blockIdx.y * 4 + w;
   if (r >= p.m_wg) return;
@@ -1453,6 +1474,7 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   p.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
   p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   p.num_splits = num_splits;
+  p.max_slots = s.max_slots;
   // One workgroup (256 threads, most of the LDS) per CU.  Automatic plan: one
   // stream per workgroup and head group, so every unit runs concurrently; with
   // several head groups the stream count is a multiple of 8 (sibling order).
