@@ -618,17 +618,13 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       const bool topped = issued >= g0 + 3;
       // query fragments (B operand): row l16, features 32kk + 8g4 .. +7; padding rows
-      // load head 0 and are zeroed.  Waiting for them also waits for the blocks issued
-      // before them, block 0 among them.
+      // compute with head 0's query and are never stored.  Waiting for them also waits
+      // for the blocks issued before them, block 0 among them.
       bf16x8_t qf[18];
       {
         const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
-        if (!row_ok) {
-#pragma unroll
-          for (int kk = 0; kk < 18; ++kk) qf[kk] = bf16x8_t{};
-        }
       }
       fetch_nxt();
       if (!topped) {
@@ -858,9 +854,10 @@ constexpr int kWStats = kWP + 2 * kWPBytes;            // per token half and row
 constexpr int kWFlag = kWStats + 2 * kWRows * 16;      // overflow flag of the reference max
 constexpr int kWPlan = kWFlag + 16;                    // split-plan scratch
 constexpr int kWLdsBytes = kWPlan + kPlanLdsBytes;
-constexpr int kWStagePitch32 = 528;                    // epilogue staging: 512 B fp32 row + pad
-constexpr int kWStagePitch16 = 272;                    // 256 B bf16 row + pad
-static_assert(4 * 32 * kWStagePitch32 <= 2 * kSlot, "epilogue staging fits the block slots");
+constexpr int kWStagePitch32 = 272;                    // epilogue staging: 64 fp32 of a row + pad
+constexpr int kWStagePitch16 = 144;                    // 64 bf16 of a row + pad
+constexpr int kWStageBytes = 32 * kWStagePitch32;      // per wave
+static_assert(4 * kWStageBytes <= kSlot, "epilogue staging fits one block slot");
 static_assert(kWLdsBytes <= 160 * 1024, "LDS budget");
 
 // S^T = K . Q^T of this wave's 16 tokens of a block for its 32 rows: 18 steps of 32
@@ -974,60 +971,102 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     if (sid >= p.n_streams) continue;
     PieceIter it;
     it.init(p, plan_lds, tot, sid, tid);
-    Piece pc;
-    while (it.next(p, hg, tid, pc)) {
-      const int b = pc.b, t_begin = pc.t_begin, t_end = pc.t_end, seq = pc.seq, nsplit = pc.nsplit;
-      const int pslot = pc.slot;
-      const int nblk = t_end > t_begin ? (t_end - t_begin + kBlk - 1) / kBlk : 0;
-      const int pg0 = t_begin / kPage;
-      const int pg1 = t_end > t_begin ? (t_end + kPage - 1) / kPage : pg0;
+    StagedPiece cur, nxt;
+    if (!it.next(p, hg, tid, cur.pc)) continue;
+    stage_piece(cur, p, l);
+    // the following piece is looked up once the current one's first blocks are in flight
+    bool nxt_known = false, has_nxt = false;
+    auto fetch_nxt = [&]() {
+      if (nxt_known) return;
+      nxt_known = true;
+      has_nxt = it.next(p, hg, tid, nxt.pc);
+      if (has_nxt) stage_piece(nxt, p, l);
+    };
+    // Block stream (as in the narrow variant): the issue cursor (piece 0 = cur, 1 = nxt;
+    // block jb) runs up to 3 blocks ahead of the block being computed, across the
+    // boundary into nxt.
+    int ic_piece = 0, ic_j = 0;
+    int issued = 0;                              // blocks issued in this unit
+    int g0 = 0;                                  // stream index of cur's block 0
+    auto issue_next = [&]() {
+      if (ic_piece == 0 && ic_j >= cur.nblk) {
+        if (!nxt_known || !has_nxt) return;
+        ic_piece = 1;
+        ic_j = 0;
+      }
+      if (ic_piece == 0) {
+        issue_piece_block<FP8>(cur, p, ic_j, issued, smem, w, l);
+      } else {
+        if (ic_j >= nxt.nblk) return;
+        issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, w, l);
+      }
+      ++ic_j;
+      ++issued;
+    };
 
-      // the two query rows this lane owns in the score phase: 32rg + 16rs + l16
-      int nvis[2];
-      bool row_ok[2];
-      int qhead[2], qtq[2];
+    // the two query rows this lane owns in the score phase: 32rg + 16rs + l16
+    bool row_ok[2];
+    int qhead[2], qtq[2];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const int r = 32 * rg + 16 * rs + l16;
+      const int hl = r / p.q_len, tq = r - hl * p.q_len;
+      qhead[rs] = hg * p.hg_heads + hl;
+      qtq[rs] = tq;
+      row_ok[rs] = qhead[rs] < p.N;
+    }
+    // every row of the head group is a real head: then the epilogue issues a fixed
+    // number of stores per wave
+    const bool group_full = (hg + 1) * p.hg_heads <= p.N;
+    // query fragments (B operand of the 16x16x32 MFMA): row 32rg + 16rs + l16, features
+    // 32kk + 8*g4 .. +7.  Padding rows (head >= N) compute with head 0's query; their
+    // results are never stored.  (Nothing may read the loaded registers before they are
+    // needed: a select on them would make the compiler wait for the loads right here.)
+    bf16x8_t qf[2][18];
+    auto load_q = [&](int bq) {
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
-        const int r = 32 * rg + 16 * rs + l16;
-        const int hl = r / p.q_len, tq = r - hl * p.q_len;
-        qhead[rs] = hg * p.hg_heads + hl;
-        qtq[rs] = tq;
-        row_ok[rs] = qhead[rs] < p.N;
-        nvis[rs] = seq - p.q_len + 1 + tq;
+        const uint16_t* qrow = p.q + (int64_t)bq * p.q_sb + (int64_t)qtq[rs] * p.q_st +
+                               (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
       }
+    };
+    // the next piece's query is loaded at the end of the current piece, before its output
+    // stores, so that waiting for it does not wait for those stores (vmcnt is in order)
+    bool q_ready = false;
+    int stores_after_q = 0;
 
-      PageIds ids;
-      load_page_ids(ids, p, b, pg0, pg1, l);
-      // DMA destination of block j: ring slot j % 4 (bf16 slot, or fp8 raw slot)
-      auto issue = [&](int j) {
-        const char* pg = page_ptr(ids, p, b, pg0 + (j >> 1), pg1, l, FP8);
-        if constexpr (FP8)
-          issue_blk_fp8(pg + (j & 1) * kBlkBytesFp8, smem + kRaw + (j & (kRing - 1)) * kBlkBytesFp8, w, l);
-        else
-          issue_blk_bf16(pg + (j & 1) * kBlkBytesBf16, smem + (j & (kRing - 1)) * kSlot, w, l);
-      };
+    while (true) {
+      const int b = cur.pc.b, t_begin = cur.pc.t_begin, t_end = cur.pc.t_end, seq = cur.pc.seq;
+      const int nsplit = cur.pc.nsplit, pslot = cur.pc.slot;
+      const int nblk = cur.nblk;
+      int nvis[2];
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) nvis[rs] = seq - p.q_len + 1 + qtq[rs];
+
       auto valid_of = [&](int j) {
         const int v = t_end - (t_begin + kBlk * j);
         return v < kBlk ? v : kBlk;
       };
-      if (nblk > 0) issue(0);
+      // the piece's first three blocks: in flight already (issued while the previous
+      // piece finished) or issued here, ahead of the query loads
+      const int issued_at_start = issued;
+      for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      const bool topped = issued >= g0 + 3;
 
-      // query fragments (B operand of the 16x16x32 MFMA): row 32rg + 16rs + l16, features
-      // 32kk + 8*g4 .. +7.  Padding rows (head >= N) load head 0 and are zeroed.
-      bf16x8_t qf[2][18];
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qtq[rs] * p.q_st +
-                               (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
-        if (!row_ok[rs]) {
-#pragma unroll
-          for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = bf16x8_t{};
-        }
+      if (!q_ready) load_q(b);
+      fetch_nxt();
+      if (!topped) {
+        for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       }
-      // Wait for the query here: the compiler would otherwise wait at its first use,
-      // after block 1's DMA is in flight, and so wait for that DMA as well.
+      // The query and the blocks issued before it (block 0 among them) have landed once
+      // at most the vector-memory operations issued after the query are outstanding.
+      // With the query loaded at the end of the previous piece these are at least that
+      // piece's output stores.
+      if (!q_ready || issued != issued_at_start || stores_after_q == 0) wait_vmcnt<0>();
+      else if (stores_after_q == 16) wait_vmcnt<16>();
+      else wait_vmcnt<32>();
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
@@ -1052,35 +1091,41 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         ovf = 0;
         if (tid == 0) *ovf_flag = 0;
         if (attempt > 0 && nblk > 0) {
-          load_page_ids(ids, p, b, pg0, pg1, l);
-          issue(0);
+          // drop whatever the stream had in flight and restage this piece from block 0
+          wait_vmcnt<0>();
+          ic_piece = 0;
+          ic_j = 0;
+          g0 = issued;
+          load_page_ids(cur.ids, p, b, cur.pg0, cur.pg1, l);
+          issue_next();
+          issue_next();
+          issue_next();
+          wait_vmcnt<0>();
         }
-        // block 0 has landed (the query too); the barrier also publishes the flag reset
-        wait_vmcnt<0>();
         if constexpr (!FP8) {
-          if (nblk == 1) zero_own_tail(smem, valid_of(0), w, l);
+          if (nblk == 1) zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), w, l);
         }
-        lds_barrier();
+        lds_barrier();                           // block 0 visible, flag reset published
         if constexpr (FP8) {
-          if (nblk > 0)
-            convert_fp8_blk(smem + kRaw, smem, reinterpret_cast<MLA_LDS float*>(smem + kFac), valid_of(0), tid,
-                            p.scale_log2);
+          if (nblk > 0) {
+            convert_fp8_blk(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, smem,
+                            reinterpret_cast<MLA_LDS float*>(smem + kFac), valid_of(0), tid, p.scale_log2);
+            lds_barrier();
+          }
         }
-        if (nblk > 1) issue(1);
-        if (nblk > 2) issue(2);
-        if constexpr (FP8) lds_barrier();
 
         // Block step: scores of block j, their weights into P(j), interleaved (WITH_PV)
         // with the PV MFMAs of block j-1, then the hand-over to block j+1.  Block 0 runs
         // without PV (peeled) so that the steady-state body is one straight-line region.
         auto step = [&](int j, auto with_pv) {
           constexpr bool WITH_PV = decltype(with_pv)::value;
-          const MLA_LDS char* cur = smem + (FP8 ? (j & 1) : (j & (kRing - 1))) * kSlot;
+          const int g = g0 + j;
+          const MLA_LDS char* cb = smem + (FP8 ? (j & 1) : (g & (kRing - 1))) * kSlot;
           const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kFac + (j & 1) * kFacBytes);
           const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
 
           f32x4_t sc[2];
-          wide_scores(cur, qf, kbase, sc);
+          wide_scores(cb, qf, kbase, sc);
 
           // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
           // Element i of row half rs is token tok0 + i.
@@ -1127,7 +1172,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 
           // PV of the previous block overlaps this block's exponentials
           if constexpr (WITH_PV) {
-            const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((j - 1) & (kRing - 1))) * kSlot;
+            const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((g - 1) & (kRing - 1))) * kSlot;
             wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
           }
 
@@ -1159,38 +1204,30 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           }
 
           if (j + 1 < nblk) {
-            // this wave's share of block j+1 has landed when at most block j+2's
-            // instructions are still outstanding (9 per wave for bf16; 5, 5, 5, 4 for fp8)
-            if (j + 2 < nblk) {
-              if constexpr (FP8) {
-                if (w == 3) wait_vmcnt<4>();
-                else wait_vmcnt<5>();
-              } else {
-                wait_vmcnt<9>();
-              }
-            } else {
-              wait_vmcnt<0>();
-            }
+            // this wave's share of block j+1 has landed once only the blocks issued after
+            // it (at most block j+2) are outstanding
+            wait_blocks_after<FP8>(issued - (g + 2), w);
             if constexpr (!FP8) {
-              if (j + 2 == nblk) zero_own_tail(smem + ((j + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
+              if (j + 2 == nblk) zero_own_tail(smem + ((g + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
             }
           }
           lds_barrier();                              // Y(j)
-          if (j + 3 < nblk) issue(j + 3);
+          issue_next();                               // block g+3 of the stream
           if constexpr (FP8) {
-            if (j + 1 < nblk)
-              convert_fp8_blk(smem + kRaw + ((j + 1) & (kRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kSlot,
+            if (j + 1 < nblk) {
+              convert_fp8_blk(smem + kRaw + ((g + 1) & (kRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kSlot,
                               reinterpret_cast<MLA_LDS float*>(smem + kFac + ((j + 1) & 1) * kFacBytes),
                               valid_of(j + 1), tid, p.scale_log2);
-            lds_barrier();                            // Z(j+1)
+              lds_barrier();                          // Z(j+1)
+            }
           }
         };
         if (nblk > 0) {
           step(0, std::false_type{});
           for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
           const int jl = nblk - 1;
-          wide_pv(smem + (FP8 ? (jl & 1) : (jl & (kRing - 1))) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase,
-                  pbase);
+          wide_pv(smem + (FP8 ? (jl & 1) : ((g0 + jl) & (kRing - 1))) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o,
+                  vbase, pbase);
         }
         // any row over the reference slack: the whole workgroup redoes the unit
         if (ovf) *ovf_flag = 1;
@@ -1243,62 +1280,89 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           }
         }
       }
-      // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5) + jj.
-      // Each row block is staged through this wave's own LDS region and written back
-      // row-contiguously (512 B fp32 or 256 B bf16 per row and wave).
-      MLA_LDS char* stage = smem + w * (32 * kWStagePitch32);
+      // next piece's query: its loads go out before this piece's output stores
+      q_ready = has_nxt;
+      if (has_nxt) load_q(nxt.pc.b);
+      // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5)
+      // + 0..3.  They are staged, half a row block at a time, through this wave's part of
+      // the one ring slot the next piece's blocks leave free (the slot of this piece's
+      // last block; fp8: the first converted slot) and stored as whole row segments
+      // (256 B fp32, 128 B bf16 per row and wave).
+      MLA_LDS char* stage = smem + (FP8 ? 0 : ((g0 + nblk + 3) & (kRing - 1)) * kSlot) + w * kWStageBytes;
       const int c32 = le & 31, h32 = le >> 5;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int R = 32 * rb + c32;
         const float lr_row = stats[R][2] + stats[kWRows + R][2];
         const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
-        if (single) {
 #pragma unroll
-          for (int fb = 0; fb < 4; ++fb)
+        for (int fh = 0; fh < 2; ++fh) {
+          if (single) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bf16x4_t v = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
-                                  (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
-              *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fb + 8 * i + 4 * h32) * 2) = v;
+            for (int fl = 0; fl < 2; ++fl)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int fb = 2 * fh + fl;
+                const bf16x4_t v = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
+                                    (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
+                *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fl + 8 * i + 4 * h32) * 2) = v;
+              }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int row = 8 * k + (le >> 3);
+              const int Rr = 32 * rb + row;
+              const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
+              const int head_r = hg * p.hg_heads + hl_r;
+              const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + (le & 7) * 16);
+              if (head_r < p.N) {
+                uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
+                *reinterpret_cast<u32x4_t*>(orow + 128 * w + 64 * fh + 8 * (le & 7)) = v;
+              }
             }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          } else {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int row = 4 * k + (le >> 4);
-            const int Rr = 32 * rb + row;
-            const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
-            const int head_r = hg * p.hg_heads + hl_r;
-            const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + (le & 15) * 16);
-            if (head_r < p.N) {
-              uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
-              *reinterpret_cast<u32x4_t*>(orow + 128 * w + 8 * (le & 15)) = v;
+            for (int fl = 0; fl < 2; ++fl)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int fb = 2 * fh + fl;
+                const f32x4_t v = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
+                                   o[fb][rb][4 * i + 3] * inv};
+                *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fl + 8 * i + 4 * h32) * 4) = v;
+              }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int row = 4 * k + (le >> 4);
+              const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch32 + (le & 15) * 16);
+              float* prow = p.part_o + (slot * p.m_wg + 32 * rb + row) * kLatent + 128 * w + 64 * fh + 4 * (le & 15);
+              *reinterpret_cast<u32x4_t*>(prow) = v;
             }
           }
-        } else {
-#pragma unroll
-          for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const f32x4_t v = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
-                                 o[fb][rb][4 * i + 3] * inv};
-              *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fb + 8 * i + 4 * h32) * 4) = v;
-            }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int row = 2 * k + h32;
-            const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch32 + c32 * 16);
-            float* prow = p.part_o + (slot * p.m_wg + 32 * rb + row) * kLatent + 128 * w + 4 * c32;
-            *reinterpret_cast<u32x4_t*>(prow) = v;
-          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
       }
-      lds_barrier();                                          // LDS free before the next unit's DMA
+      // output stores issued after the next query (per wave): 2 x 2 x 4 bf16 row segments,
+      // all issued only when no row of the group is padding; 2 x 2 x 8 fp32
+      stores_after_q = single ? (group_full ? 16 : 0) : 32;
+      lds_barrier();                             // stats and P free for the next piece
+
+      fetch_nxt();
+      if (!has_nxt) break;
+      // the next piece becomes current; its blocks continue the stream
+      g0 += nblk;
+      cur = nxt;
+      nxt_known = false;
+      if (ic_piece == 1) {
+        ic_piece = 0;                            // the cursor was already inside it
+      } else {
+        ic_j = 0;                                // nothing of it issued yet
+      }
     }
+    wait_vmcnt<0>();                             // nothing in flight into LDS at the unit's end
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // Split merge ([vLLM-MLA] §Prefill merge of partial states; §Triton MLA second stage):
