@@ -919,6 +919,90 @@ __device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS c
   }
 }
 
+// ---- fp8 rows read in place (wide variant) ----
+// The raw block keeps the cache's row layout: token t at t * 584 (576 e4m3 codes, then
+// k_scale and v_scale).  Fragments are converted to bf16 in registers (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(u32x2_t c) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], 1.0f, true);
+  const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], 1.0f, false);
+  const bf16x2_t f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], e[0], e[1], f[0], f[1]};
+}
+
+__device__ __forceinline__ u32x2_t lds_read_b64_at(uint32_t addr) {
+  return *reinterpret_cast<const MLA_LDS u32x2_t*>((uintptr_t)addr);
+}
+
+// Transpose read of 8-bit data: the 16 lanes of a group each give 8 bytes; lane pair
+// (2k, 2k+1) forms row k of an 8 x 16 byte matrix and lane i receives column i.
+__device__ __forceinline__ u32x2_t lds_read_tr8_at(uint32_t addr) {
+  const v2i32_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<MLA_LDS v2i32_t*>((uintptr_t)addr));
+  return u32x2_t{(uint32_t)r[0], (uint32_t)r[1]};
+}
+
+// S^T of this wave's 16 tokens for its 32 rows from raw fp8 codes: 18 steps of 32
+// features, each one 8-byte code read (kPrefK steps ahead) converted to bf16.
+__device__ __forceinline__ void wide_scores_fp8(const MLA_LDS char* blk, const bf16x8_t (&qf)[2][18], uint32_t kbase8,
+                                                f32x4_t (&sc)[2]) {
+  constexpr int kPrefK = 6;
+  const uint32_t ka = opaque(lds_addr(blk) + kbase8);
+  u32x2_t kbuf[kPrefK];
+#pragma unroll
+  for (int d = 0; d < kPrefK; ++d) kbuf[d] = lds_read_b64_at(ka + 32 * d);
+  sc[0] = f32x4_t{};
+  sc[1] = f32x4_t{};
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) {
+    const bf16x8_t a = fp8x8_to_bf16(kbuf[kk % kPrefK]);
+    const int nk = kk + kPrefK;
+    if (nk < 18) kbuf[kk % kPrefK] = lds_read_b64_at(ka + 32 * nk);
+    sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][kk], sc[0], 0, 0, 0);
+    sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][kk], sc[1], 0, 0, 0);
+  }
+}
+
+// O^T += V^T . P^T over one raw fp8 block: per step of 16 tokens and feature block fb,
+// one 8-bit transpose read gives each lane its feature's 8 tokens.
+__device__ __forceinline__ void wide_pv_fp8(const MLA_LDS char* blk, const MLA_LDS char* pbuf, f32x16_t (&o)[4][2],
+                                            uint32_t vbase8, const uint32_t (&pbase)[2]) {
+  const uint32_t va = opaque(lds_addr(blk) + vbase8);
+  uint32_t pa[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) pa[s] = opaque(lds_addr(pbuf) + pbase[s]);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) pb[rb] = lds_read_b128_at(pa[s] + rb * 2048);
+    u32x2_t vc[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) vc[fb] = lds_read_tr8_at(va + s * 16 * kRowBytesFp8 + 32 * fb);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const bf16x8_t a = fp8x8_to_bf16(vc[fb]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb], o[fb][rb], 0, 0, 0);
+    }
+  }
+}
+
+// Bytes of rows >= valid inside this wave's share of a raw fp8 block (flat 16-byte
+// chunks 64k + lane, k = w + 4i) become zero: codes and scales past the end of a
+// sequence may hold NaN patterns.  Row ends are multiples of 8 bytes.
+__device__ __forceinline__ void zero_own_tail_fp8(MLA_LDS char* blk, int valid, int w, int l) {
+  const int end = valid * kRowBytesFp8;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int o = 16 * (64 * (w + 4 * i) + l);
+    if (o + 16 <= kBlkBytesFp8 && o + 16 > end) {
+      if (o >= end) *reinterpret_cast<MLA_LDS u32x4_t*>(blk + o) = u32x4_t{0u, 0u, 0u, 0u};
+      else *reinterpret_cast<MLA_LDS u32x2_t*>(blk + o + 8) = u32x2_t{0u, 0u};
+    }
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kWLdsBytes];
@@ -955,6 +1039,12 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     }
   // P rows: 64 B = 4 chunks of 8 tokens; chunk a of row R sits at position a ^ ((R >> 2) & 3)
   // so that 16 consecutive rows reading one chunk hit 16 distinct bank groups.
+  // fp8 (raw rows): K codes of token 16th + l16 at features 32kk + 8g4; the 8-bit
+  // transpose read of step s and feature block fb: lane pair (2k, 2k+1) of group g4 gives
+  // token 16s + 8(g4 >> 1) + k, features 128w + 32fb + 16(g4 & 1) + 8(l16 & 1) .. +7.
+  const uint32_t kbase8 = (uint32_t)((16 * th + l16) * kRowBytesFp8 + 8 * g4);
+  const uint32_t vbase8 =
+      (uint32_t)((8 * (g4 >> 1) + (l16 >> 1)) * kRowBytesFp8 + 128 * w + 16 * (g4 & 1) + 8 * (l16 & 1));
   uint32_t pbase[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -1102,17 +1192,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           issue_next();
           wait_vmcnt<0>();
         }
-        if constexpr (!FP8) {
-          if (nblk == 1) zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), w, l);
+        if (nblk == 1) {
+          if constexpr (FP8) zero_own_tail_fp8(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, valid_of(0), w, l);
+          else zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), w, l);
         }
         lds_barrier();                           // block 0 visible, flag reset published
-        if constexpr (FP8) {
-          if (nblk > 0) {
-            convert_fp8_blk(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, smem,
-                            reinterpret_cast<MLA_LDS float*>(smem + kFac), valid_of(0), tid, p.scale_log2);
-            lds_barrier();
-          }
-        }
 
         // Block step: scores of block j, their weights into P(j), interleaved (WITH_PV)
         // with the PV MFMAs of block j-1, then the hand-over to block j+1.  Block 0 runs
@@ -1120,25 +1204,31 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         auto step = [&](int j, auto with_pv) {
           constexpr bool WITH_PV = decltype(with_pv)::value;
           const int g = g0 + j;
-          const MLA_LDS char* cb = smem + (FP8 ? (j & 1) : (g & (kRing - 1))) * kSlot;
-          const MLA_LDS float* fac = reinterpret_cast<const MLA_LDS float*>(smem + kFac + (j & 1) * kFacBytes);
+          const MLA_LDS char* cb = FP8 ? smem + kRaw + (g & (kRing - 1)) * kBlkBytesFp8 : smem + (g & (kRing - 1)) * kSlot;
           const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
 
           f32x4_t sc[2];
-          wide_scores(cb, qf, kbase, sc);
+          // fp8: {k_scale, v_scale} of this lane's 4 tokens, read from the raw rows
+          f32x2_t kv[4];
+          if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              kv[i] = *reinterpret_cast<const MLA_LDS f32x2_t*>(cb + (16 * th + 4 * g4 + i) * kRowBytesFp8 + kRow);
+            wide_scores_fp8(cb, qf, kbase8, sc);
+          } else {
+            wide_scores(cb, qf, kbase, sc);
+          }
 
           // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
           // Element i of row half rs is token tok0 + i.
           float mt[2];
           {
-            f32x4_t kf;
-            if constexpr (FP8) kf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 16 * th + 4 * g4);
 #pragma unroll
             for (int rs = 0; rs < 2; ++rs) {
               mt[rs] = -INFINITY;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                float x = sc[rs][i] * (FP8 ? kf[i] : p.scale_log2);
+                float x = sc[rs][i] * (FP8 ? kv[i][0] * p.scale_log2 : p.scale_log2);
                 x = (tok0 + i < nvis[rs]) ? x : -INFINITY;
                 sc[rs][i] = x;
                 mt[rs] = fmaxf(mt[rs], x);
@@ -1172,8 +1262,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 
           // PV of the previous block overlaps this block's exponentials
           if constexpr (WITH_PV) {
-            const MLA_LDS char* prev = smem + (FP8 ? ((j - 1) & 1) : ((g - 1) & (kRing - 1))) * kSlot;
-            wide_pv(prev, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
+            if constexpr (FP8)
+              wide_pv_fp8(smem + kRaw + ((g - 1) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + ((j - 1) & 1) * kWPBytes, o,
+                          vbase8, pbase);
+            else
+              wide_pv(smem + ((g - 1) & (kRing - 1)) * kSlot, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
           }
 
           // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
@@ -1181,8 +1274,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           {
             f32x4_t vf, ivf;
             if constexpr (FP8) {
-              vf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + kBlk + 16 * th + 4 * g4);
-              ivf = *reinterpret_cast<const MLA_LDS f32x4_t*>(fac + 2 * kBlk + 16 * th + 4 * g4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                vf[i] = kv[i][1];
+                ivf[i] = kv[i][1] != 0.f ? 1.0f / kv[i][1] : 0.f;
+              }
             }
             MLA_LDS char* pw = smem + kWP + (j & 1) * kWPBytes;
 #pragma unroll
@@ -1207,27 +1303,25 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
             // this wave's share of block j+1 has landed once only the blocks issued after
             // it (at most block j+2) are outstanding
             wait_blocks_after<FP8>(issued - (g + 2), w);
-            if constexpr (!FP8) {
-              if (j + 2 == nblk) zero_own_tail(smem + ((g + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
+            if (j + 2 == nblk) {
+              if constexpr (FP8)
+                zero_own_tail_fp8(smem + kRaw + ((g + 1) & (kRing - 1)) * kBlkBytesFp8, valid_of(j + 1), w, l);
+              else
+                zero_own_tail(smem + ((g + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
             }
           }
           lds_barrier();                              // Y(j)
           issue_next();                               // block g+3 of the stream
-          if constexpr (FP8) {
-            if (j + 1 < nblk) {
-              convert_fp8_blk(smem + kRaw + ((g + 1) & (kRing - 1)) * kBlkBytesFp8, smem + ((j + 1) & 1) * kSlot,
-                              reinterpret_cast<MLA_LDS float*>(smem + kFac + ((j + 1) & 1) * kFacBytes),
-                              valid_of(j + 1), tid, p.scale_log2);
-              lds_barrier();                          // Z(j+1)
-            }
-          }
         };
         if (nblk > 0) {
           step(0, std::false_type{});
           for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
           const int jl = nblk - 1;
-          wide_pv(smem + (FP8 ? (jl & 1) : ((g0 + jl) & (kRing - 1))) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o,
-                  vbase, pbase);
+          if constexpr (FP8)
+            wide_pv_fp8(smem + kRaw + ((g0 + jl) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + (jl & 1) * kWPBytes, o,
+                        vbase8, pbase);
+          else
+            wide_pv(smem + ((g0 + jl) & (kRing - 1)) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase, pbase);
         }
         // any row over the reference slack: the whole workgroup redoes the unit
         if (ovf) *ovf_flag = 1;
