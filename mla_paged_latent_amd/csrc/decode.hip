@@ -106,8 +106,8 @@ constexpr int kSegOverhead = 2;                         // in pages
 __device__ __forceinline__ int clamp_seq(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
 __device__ __forceinline__ int pages_of(int s) { return (s + kPage - 1) / kPage; }
 
-// LDS scratch of the planner: 256 exclusive prefixes, 4 wave totals, a 2-value result
-constexpr int kPlanLdsBytes = (256 + 4 + 2) * 8;
+// LDS scratch of the planner: 256 exclusive prefixes, 4 wave totals, a 3-value result
+constexpr int kPlanLdsBytes = (256 + 4 + 4) * 8;
 
 // a workgroup-uniform 64-bit value read from LDS, moved to scalar registers
 __device__ __forceinline__ long long uniform64(long long v) {
@@ -127,13 +127,19 @@ struct PlanTotals {
 
 // Thread tid sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
 // pre[tid] receives the exclusive prefix of those sums.
-__device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS long long* pre, int tid) {
+// *seq0 receives the clamped seq_len of request tid * K (0 if there is none).
+__device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS long long* pre, int tid, int* seq0) {
   const int cap = p.max_pages * kPage;
   const int K = (p.B + 255) >> 8;
   const int b0 = tid * K;
   const int b1 = b0 + K < p.B ? b0 + K : p.B;
   long long local = 0;
-  for (int b = b0; b < b1; ++b) local += kSegOverhead + pages_of(clamp_seq(p.seq_lens[b], cap));
+  *seq0 = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int s = clamp_seq(p.seq_lens[b], cap);
+    if (b == b0) *seq0 = s;
+    local += kSegOverhead + pages_of(s);
+  }
   const int l = tid & 63;
   long long incl = local;
 #pragma unroll
@@ -156,9 +162,10 @@ __device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS
   return r;
 }
 
-// The request holding cost position X (< total) and the position where it starts.
-__device__ __forceinline__ void plan_find(const DecodeParams& p, MLA_LDS long long* pre, long long X, long long total, int tid,
-                          int* b_out, long long* c_out) {
+// The request holding cost position X (< total), the position where it starts and its
+// clamped seq_len (seq0: this thread's value from plan_prefix).
+__device__ __forceinline__ void plan_find(const DecodeParams& p, MLA_LDS long long* pre, long long X, long long total,
+                                          int tid, int seq0, int* b_out, long long* c_out, int* seq_out) {
   MLA_LDS long long* sel = pre + 260;
   const int cap = p.max_pages * kPage;
   const int K = (p.B + 255) >> 8;
@@ -168,18 +175,21 @@ __device__ __forceinline__ void plan_find(const DecodeParams& p, MLA_LDS long lo
   const long long e1 = tid < 255 ? pre[tid + 1] : total;
   if (b0 < b1 && e0 <= X && X < e1) {
     long long c = e0;
-    int b = b0;
+    int b = b0, sq = seq0;
     for (; b < b1 - 1; ++b) {
-      const long long cb = kSegOverhead + pages_of(clamp_seq(p.seq_lens[b], cap));
+      const long long cb = kSegOverhead + pages_of(sq);
       if (X < c + cb) break;
       c += cb;
+      sq = clamp_seq(p.seq_lens[b + 1], cap);
     }
     sel[0] = b;
     sel[1] = c;
+    sel[2] = sq;
   }
   lds_barrier();
   *b_out = __builtin_amdgcn_readfirstlane((int)sel[0]);
   *c_out = uniform64(sel[1]);
+  *seq_out = __builtin_amdgcn_readfirstlane((int)sel[2]);
   lds_barrier();                                        // sel is rewritten by the next search
 }
 
@@ -195,12 +205,14 @@ struct PieceIter {
   long long lo, hi, c;
   PlanTotals tot;
   int b, s;
+  int seq_b;          // clamped seq_len of request b as found by plan_find (-1: unknown)
   bool done;
 
   __device__ __forceinline__ void init(const DecodeParams& p, MLA_LDS long long* pre, const PlanTotals& tot, int stream,
-                       int tid) {
+                                       int tid, int seq0) {
     s = stream;
     done = false;
+    seq_b = -1;
     if (p.num_splits > 0) return;
     this->tot = tot;
     lo = tot.start(s);
@@ -209,7 +221,7 @@ struct PieceIter {
       done = true;
       return;
     }
-    plan_find(p, pre, lo, tot.total, tid, &b, &c);
+    plan_find(p, pre, lo, tot.total, tid, seq0, &b, &c, &seq_b);
   }
 
   __device__ __forceinline__ bool next(const DecodeParams& p, int hg, int tid, Piece& pc) {
@@ -231,7 +243,8 @@ struct PieceIter {
       return true;
     }
     while (b < p.B && c < hi) {
-      const int seq = clamp_seq(p.seq_lens[b], cap);
+      const int seq = seq_b >= 0 ? seq_b : clamp_seq(p.seq_lens[b], cap);
+      seq_b = -1;
       const int np = pages_of(seq);
       const long long p0 = c + kSegOverhead;            // position of page 0
       bool have = false;
@@ -563,13 +576,14 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kNPlan);
   PlanTotals tot{1, 1};
-  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
+  int seq0 = 0;
+  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid, &seq0);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
     unit_to_stream(u, p.n_hg, &sid, &hg);
     if (sid >= p.n_streams) continue;
     PieceIter it;
-    it.init(p, plan_lds, tot, sid, tid);
+    it.init(p, plan_lds, tot, sid, tid, seq0);
     StagedPiece cur, nxt;
     if (!it.next(p, hg, tid, cur.pc)) continue;
     stage_piece(cur, p, l);
@@ -1054,13 +1068,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
   PlanTotals tot{1, 1};
-  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid);
+  int seq0 = 0;
+  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid, &seq0);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
     unit_to_stream(u, p.n_hg, &sid, &hg);
     if (sid >= p.n_streams) continue;
     PieceIter it;
-    it.init(p, plan_lds, tot, sid, tid);
+    it.init(p, plan_lds, tot, sid, tid, seq0);
     StagedPiece cur, nxt;
     if (!it.next(p, hg, tid, cur.pc)) continue;
     stage_piece(cur, p, l);
@@ -1182,6 +1197,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         if (tid == 0) *ovf_flag = 0;
         if (attempt > 0 && nblk > 0) {
           // drop whatever the stream had in flight and restage this piece from block 0
+          load_q(b);
           wait_vmcnt<0>();
           ic_piece = 0;
           ic_j = 0;
@@ -1316,6 +1332,12 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         if (nblk > 0) {
           step(0, std::false_type{});
           for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
+        }
+        // This piece's scores are done: the next piece's query loads go out now, ahead of
+        // the last PV and the output stores (a redo reloads this piece's query).
+        q_ready = has_nxt;
+        if (has_nxt) load_q(nxt.pc.b);
+        if (nblk > 0) {
           const int jl = nblk - 1;
           if constexpr (FP8)
             wide_pv_fp8(smem + kRaw + ((g0 + jl) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + (jl & 1) * kWPBytes, o,
@@ -1374,9 +1396,6 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           }
         }
       }
-      // next piece's query: its loads go out before this piece's output stores
-      q_ready = has_nxt;
-      if (has_nxt) load_q(nxt.pc.b);
       // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5)
       // + 0..3.  They are staged, half a row block at a time, through this wave's part of
       // the one ring slot the next piece's blocks leave free (the slot of this piece's
@@ -1402,16 +1421,20 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
                 *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fl + 8 * i + 4 * h32) * 2) = v;
               }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // all reads first: the global stores may alias LDS as far as the compiler knows,
+            // so interleaving would serialise every read behind the previous store
+            u32x4_t v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              v[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (8 * k + (le >> 3)) * kWStagePitch16 + (le & 7) * 16);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              const int row = 8 * k + (le >> 3);
-              const int Rr = 32 * rb + row;
+              const int Rr = 32 * rb + 8 * k + (le >> 3);
               const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
               const int head_r = hg * p.hg_heads + hl_r;
-              const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch16 + (le & 7) * 16);
               if (head_r < p.N) {
                 uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
-                *reinterpret_cast<u32x4_t*>(orow + 128 * w + 64 * fh + 8 * (le & 7)) = v;
+                *reinterpret_cast<u32x4_t*>(orow + 128 * w + 64 * fh + 8 * (le & 7)) = v[k];
               }
             }
           } else {
@@ -1425,12 +1448,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
                 *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fl + 8 * i + 4 * h32) * 4) = v;
               }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            u32x4_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              v[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (4 * k + (le >> 4)) * kWStagePitch32 + (le & 15) * 16);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              const int row = 4 * k + (le >> 4);
-              const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + row * kWStagePitch32 + (le & 15) * 16);
-              float* prow = p.part_o + (slot * p.m_wg + 32 * rb + row) * kLatent + 128 * w + 64 * fh + 4 * (le & 15);
-              *reinterpret_cast<u32x4_t*>(prow) = v;
+              float* prow = p.part_o + (slot * p.m_wg + 32 * rb + 4 * k + (le >> 4)) * kLatent + 128 * w + 64 * fh +
+                            4 * (le & 15);
+              *reinterpret_cast<u32x4_t*>(prow) = v[k];
             }
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
