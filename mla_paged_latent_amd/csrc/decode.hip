@@ -120,9 +120,18 @@ __device__ __forceinline__ long long uniform64(long long v) {
 struct PlanTotals {
   long long total;    // cost positions of the whole batch (>= 1)
   long long n;        // streams
-  __device__ __forceinline__ long long start(long long s) const { return s * total / n; }
+  // 64-bit division is a long software sequence on the GPU: when every product below
+  // fits in 32 bits (any realistic batch), 32-bit unsigned division is used instead
+  __device__ __forceinline__ bool small() const { return total <= (long long)(0xFFFFFFFFu / (uint32_t)(n + 1)); }
+  __device__ __forceinline__ long long start(long long s) const {
+    if (small()) return (long long)((uint32_t)s * (uint32_t)total / (uint32_t)n);
+    return s * total / n;
+  }
   // the stream holding position X: the largest s with start(s) <= X
-  __device__ __forceinline__ int stream_of(long long X) const { return (int)(((X + 1) * n - 1) / total); }
+  __device__ __forceinline__ int stream_of(long long X) const {
+    if (small()) return (int)((((uint32_t)X + 1u) * (uint32_t)n - 1u) / (uint32_t)total);
+    return (int)(((X + 1) * n - 1) / total);
+  }
 };
 
 // Thread tid sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
@@ -617,6 +626,18 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       ++issued;
     };
 
+    // query fragments (B operand): row l16, features 32kk + 8g4 .. +7; padding rows
+    // compute with head 0's query and are never stored.  The next piece's query is
+    // loaded while the current piece finishes, before its output stores, so that
+    // waiting for it does not wait for those stores (vmcnt is in order).
+    bf16x8_t qf[18];
+    auto load_q = [&](int bq) {
+      const uint16_t* qrow = p.q + (int64_t)bq * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
+    };
+    bool q_ready = false;
+
     while (true) {
       const int b = cur.pc.b, t_begin = cur.pc.t_begin, t_end = cur.pc.t_end, seq = cur.pc.seq;
       const int nblk = cur.nblk;
@@ -629,22 +650,19 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       // the piece's first three blocks: in flight already (issued while the previous
       // piece finished) or issued here, ahead of the query loads.  The stream must be
       // three blocks ahead before step 0: each step issues only one more.
+      const int issued_at_start = issued;
       for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       const bool topped = issued >= g0 + 3;
-      // query fragments (B operand): row l16, features 32kk + 8g4 .. +7; padding rows
-      // compute with head 0's query and are never stored.  Waiting for them also waits
-      // for the blocks issued before them, block 0 among them.
-      bf16x8_t qf[18];
-      {
-        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)(row_ok ? head : 0) * p.q_sh;
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
-      }
+      if (!q_ready) load_q(b);
       fetch_nxt();
       if (!topped) {
         for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       }
-      wait_vmcnt<0>();
+      // the query and the blocks issued before it (block 0 among them) have landed once
+      // at most the operations issued after the query are outstanding: with the query
+      // loaded at the end of the previous piece, at least its 8 output stores per wave
+      if (!q_ready || issued != issued_at_start) wait_vmcnt<0>();
+      else wait_vmcnt<8>();
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[kk]));
 
@@ -663,6 +681,7 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
         if (tid == 0) *ovf_flag = 0;
         if (attempt > 0 && nblk > 0) {
           // drop whatever the stream had in flight and restage this piece from block 0
+          load_q(b);
           wait_vmcnt<0>();
           ic_piece = 0;
           ic_j = 0;
@@ -770,6 +789,12 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
         if (nblk > 0) {
           step(0, std::false_type{});
           for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
+        }
+        // this piece's scores are done: the next piece's query loads go out now (a redo
+        // reloads this piece's query)
+        q_ready = has_nxt;
+        if (has_nxt) load_q(nxt.pc.b);
+        if (nblk > 0) {
           const int jl = nblk - 1;
           narrow_pv(smem + (FP8 ? (jl & 1) : ((g0 + jl) & (kRing - 1))) * kSlot, smem + kNP + (jl & 1) * kNPBytes, o,
                     vbase, pbase);
@@ -1293,7 +1318,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 vf[i] = kv[i][1];
-                ivf[i] = kv[i][1] != 0.f ? 1.0f / kv[i][1] : 0.f;
+                // hardware reciprocal (1 ulp): only normalises the weight sum
+                ivf[i] = kv[i][1] != 0.f ? __builtin_amdgcn_rcpf(kv[i][1]) : 0.f;
               }
             }
             MLA_LDS char* pw = smem + kWP + (j & 1) * kWPBytes;
