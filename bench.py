@@ -215,7 +215,7 @@ def run(args) -> dict:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = traffic_record(args.workload)
-    roof["kernel"] = "mla_decode (plan + split-KV decode + LSE merge)"
+    roof["kernel"] = "mla_decode (split-KV decode with in-kernel split plan + LSE merge)"
     roof["algorithmic_bytes"] = bytes_alg
     roof["algorithmic_flops"] = flops_alg
     roof["mean_launch_us"] = round(dec_mean * 1e3, 2)
