@@ -223,11 +223,15 @@ def test_stale_nan_rows_past_the_end_are_ignored():
         check_lse(lse.cpu().numpy(), lse_ref, "nan tails")
 
 
-def test_many_requests_plan_scan():
-    """More than 256 requests: the planner's scan runs over several blocks."""
-    rng = np.random.default_rng(82)
-    seq = rng.integers(0, 300, size=600)
-    w = MI.make_workload("many", 600, 1, 16, seq, None, MI.KV_BF16, False, 82)
+@pytest.mark.parametrize("N,q_len,kd", [(16, 1, MI.KV_BF16), (128, 1, MI.KV_BF16), (64, 2, MI.KV_BF16),
+                                         (128, 1, MI.KV_FP8)])
+def test_many_requests_plan_scan(N, q_len, kd):
+    """More than 256 requests, many of them short or empty: the planner's scan spans
+    several entries per thread and every stream runs through many pieces, so blocks of
+    the next piece are prefetched across piece boundaries (both kernel variants)."""
+    rng = np.random.default_rng(82 + N + q_len)
+    seq = rng.integers(0, 300, size=600) * (rng.random(600) > 0.1)
+    w = MI.make_workload("many", 600, q_len, N, seq, None, kd, False, 82)
     pool = gpu_pool(w)
     o_ref, lse_ref = O.decode(O.bf16_bits_to_f64(w.q), oracle_pool(w), w.kv_dtype, w.block_table,
                               w.seq_lens, SC)
