@@ -296,7 +296,7 @@ def run(args) -> dict:
     return res
 
 
-DECODE_KERNELS = ("plan_kernel", "decode_wide_kernel", "decode_narrow_kernel", "merge_kernel")
+DECODE_KERNELS = ("decode_wide_kernel", "decode_narrow_kernel", "merge_kernel")
 COPY_KERNEL = "copyBuffer"
 
 
