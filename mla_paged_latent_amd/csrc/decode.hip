@@ -1537,35 +1537,41 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   float M = -INFINITY;
   f32x4_t a0 = {}, a1 = {};
   float wsum = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    f32x4_t v[8][2];
-    float ls[8];
+  // KS splits per round (4 when a request has at most 4: no clamped duplicate loads)
+  auto fold = [&](auto ks_c) {
+    constexpr int KS = decltype(ks_c)::value;
+    for (int s0 = 0; s0 < nsplit; s0 += KS) {
+      f32x4_t v[KS][2];
+      float ls[KS];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = s0 + k < nsplit ? s0 + k : nsplit - 1;          // clamp: in bounds, weight 0 below
-      const size_t slot = (size_t)(first + s) * p.n_hg + hg;
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
-      v[k][0] = src[0];
-      v[k][1] = src[1];
-      ls[k] = s0 + k < nsplit ? p.part_lse[slot * p.m_wg + r] : -INFINITY;
+      for (int k = 0; k < KS; ++k) {
+        const int s = s0 + k < nsplit ? s0 + k : nsplit - 1;        // clamp: in bounds, weight 0 below
+        const size_t slot = (size_t)(first + s) * p.n_hg + hg;
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
+        v[k][0] = src[0];
+        v[k][1] = src[1];
+        ls[k] = s0 + k < nsplit ? p.part_lse[slot * p.m_wg + r] : -INFINITY;
+      }
+      float mc = M;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) mc = fmaxf(mc, ls[k]);
+      if (mc == -INFINITY) continue;                                 // all splits so far empty
+      const float resc = M == -INFINITY ? 0.f : __expf(M - mc);
+      wsum *= resc;
+      a0 *= resc;
+      a1 *= resc;
+      M = mc;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const float wt = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - M);
+        wsum += wt;
+        a0 += wt * v[k][0];
+        a1 += wt * v[k][1];
+      }
     }
-    float mc = M;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mc = fmaxf(mc, ls[k]);
-    if (mc == -INFINITY) continue;                                   // all splits so far empty
-    const float resc = M == -INFINITY ? 0.f : __expf(M - mc);
-    wsum *= resc;
-    a0 *= resc;
-    a1 *= resc;
-    M = mc;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float wt = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - M);
-      wsum += wt;
-      a0 += wt * v[k][0];
-      a1 += wt * v[k][1];
-    }
-  }
+  };
+  if (nsplit <= 4) fold(std::integral_constant<int, 4>{});
+  else fold(std::integral_constant<int, 8>{});
   const float Mb = M == -INFINITY ? 0.f : M;
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq * p.o_st + (int64_t)head * p.o_sh + 8 * l;
