@@ -101,7 +101,7 @@ __device__ __forceinline__ void unit_to_stream(int u, int n_hg, int* stream, int
 //
 // The piece that holds a request's first page (head group 0) records
 // {first slot, number of pieces} in req[b] for the merge.
-constexpr int kSegOverhead = 2;                         // in pages
+constexpr int kSegOverhead = 4;                         // in pages
 
 __device__ __forceinline__ int clamp_seq(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
 __device__ __forceinline__ int pages_of(int s) { return (s + kPage - 1) / kPage; }
