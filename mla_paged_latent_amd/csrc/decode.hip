@@ -984,7 +984,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr8_at(uint32_t addr) {
 // features, each one 8-byte code read (kPrefK steps ahead) converted to bf16.
 __device__ __forceinline__ void wide_scores_fp8(const MLA_LDS char* blk, const bf16x8_t (&qf)[2][18], uint32_t kbase8,
                                                 f32x4_t (&sc)[2]) {
-  constexpr int kPrefK = 6;
+  constexpr int kPrefK = 3;                              // timed against 2, 4, 6, 9
   const uint32_t ka = opaque(lds_addr(blk) + kbase8);
   u32x2_t kbuf[kPrefK];
 #pragma unroll
