@@ -14,7 +14,8 @@
 // is formed transposed, D^T[n][t] = W^T[n][k] . A^T[k][t], on 32x32x16 bf16 MFMAs:
 // W^T is the A operand (rows n), activation rows come straight from HBM as the B
 // operand (16 contiguous bytes of one token row per lane), and each lane of the
-// accumulator holds 4 consecutive n of one token, stored as 8 contiguous bytes.
+// accumulator holds 4 consecutive n of one token; the 32-token tile is staged in LDS
+// and leaves as contiguous row segments.
 #include "mla_common.h"
 #include "mla_host.h"
 
@@ -29,7 +30,9 @@ struct GemmCfg {
   static constexpr int kRowBytes = NT * 2 + 32;       // padded LDS row: 4 rows hit disjoint banks
   static constexpr int kTileBytes = KK * kRowBytes;
   static constexpr int kRedBytes = (KSPLIT > 1) ? (kNB * 32 * 32 * 4) : 0;
-  static constexpr int kLdsBytes = kTileBytes + kRedBytes;
+  static constexpr int kOutPitch = NT * 2 + 16;       // output staging row (32 tokens x NT)
+  static constexpr int kOutBytes = 32 * kOutPitch;
+  static constexpr int kLdsBytes = kTileBytes + kRedBytes + kOutBytes;
 };
 
 // grid = (NN / NT, N heads); block = 256 threads.
@@ -50,8 +53,13 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   const int w = wave_id();
   const int l = lane_id();
 
-  // W[h][0:KK][n0:n0+NT] and the first token block's activation fragments are all
-  // requested before anything waits, so a workgroup keeps its whole tile in flight.
+  // The first 32 tokens' q_pe chunks (COPY_PE, n-tile 0), W[h][0:KK][n0:n0+NT] and the
+  // first token block's activation fragments are all requested before anything waits,
+  // so a workgroup keeps its whole tile in flight.
+  const bool copy_pe = COPY_PE && blockIdx.x == 0;
+  uint4 pe_v;
+  const bool pe_first = copy_pe && tid < T * 8;
+  if (pe_first) pe_v = *reinterpret_cast<const uint4*>(pe + (tid >> 3) * pe_st + h * pe_sh + (tid & 7) * 8);
   const uint16_t* wh = W + (int64_t)h * KK * NN + n0;
   constexpr int kChunksPerRow = NT / 8;
   constexpr int kTileChunks = KK * kChunksPerRow;
@@ -93,8 +101,9 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
     const int k = i / kChunksPerRow, c = i % kChunksPerRow;
     *reinterpret_cast<MLA_LDS u32x4_t*>(lds + k * Cfg::kRowBytes + c * 16) = wv[j];
   }
-  if (COPY_PE && blockIdx.x == 0) {
-    for (int64_t i = tid; i < T * 8; i += 256) {
+  if (pe_first) *reinterpret_cast<uint4*>(C + (tid >> 3) * c_st + h * c_sh + NN + (tid & 7) * 8) = pe_v;
+  if (copy_pe) {
+    for (int64_t i = tid + 256; i < T * 8; i += 256) {
       const int64_t t = i >> 3;
       const int c = (int)(i & 7);
       const uint4 v = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + c * 8);
@@ -104,8 +113,6 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   lds_barrier();
 
   for (int64_t tb = 0; tb < T; tb += 32) {
-    const int64_t trow = tb + (l & 31);
-    const bool t_ok = trow < T;
     if (tb > 0) load_act(tb);
     f32x16_t acc = {};
 #pragma unroll
@@ -131,15 +138,29 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
       }
       lds_barrier();
     }
-    if (kh == 0 && t_ok) {
-      uint16_t* crow = C + trow * c_st + h * c_sh + n0 + nb * 32 + 4 * (l >> 5);
+    // The tile goes out through LDS so that every token's NT outputs leave as whole
+    // contiguous row segments (16 B per lane) rather than as 8-byte pieces of 32 rows.
+    MLA_LDS char* ostage = lds + Cfg::kTileBytes + Cfg::kRedBytes;
+    if (kh == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x4_t v = {(__bf16)acc[4 * i], (__bf16)acc[4 * i + 1], (__bf16)acc[4 * i + 2],
                             (__bf16)acc[4 * i + 3]};
-        *reinterpret_cast<bf16x4_t*>(crow + 8 * i) = v;
+        *reinterpret_cast<MLA_LDS bf16x4_t*>(ostage + (l & 31) * Cfg::kOutPitch +
+                                             (nb * 32 + 8 * i + 4 * (l >> 5)) * 2) = v;
       }
     }
+    lds_barrier();
+    constexpr int kRowChunks = NT / 8;
+#pragma unroll
+    for (int c = tid; c < 32 * kRowChunks; c += 256) {
+      const int r = c / kRowChunks, cc = c % kRowChunks;
+      if (tb + r < T) {
+        const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * Cfg::kOutPitch + cc * 16);
+        *reinterpret_cast<u32x4_t*>(C + (tb + r) * c_st + h * c_sh + n0 + cc * 8) = v;
+      }
+    }
+    lds_barrier();                                      // staging free for the next token block
   }
 }
 
