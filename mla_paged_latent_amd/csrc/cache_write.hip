@@ -17,14 +17,15 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane_id();
   if (t >= T) return;
+  // the slot and the row are read together (no load waits for another): lanes 8..63
+  // re-read one of the 8 rope chunks and drop it
   const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_pages * kPage) return;   // padding or out of range: skip
-
   const uint4* src_c = reinterpret_cast<const uint4*>(kv_c + t * kv_stride);
   const uint4* src_p = reinterpret_cast<const uint4*>(k_pe + t * pe_stride);
   const uint4 vc = src_c[l];                      // latent elements 8l .. 8l+7
-  uint4 vp = make_uint4(0, 0, 0, 0);
-  if (l < 8) vp = src_p[l];                       // rope elements 8l .. 8l+7
+  const uint4 vp_any = src_p[l & 7];
+  const uint4 vp = l < 8 ? vp_any : make_uint4(0, 0, 0, 0);   // rope elements 8l .. 8l+7
+  if (slot < 0 || slot >= num_pages * kPage) return;   // padding or out of range: skip
 
   if constexpr (!FP8) {
     uint4* dst = reinterpret_cast<uint4*>(pool + slot * kRowBytesBf16);
