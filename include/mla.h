@@ -138,7 +138,8 @@ size_t mla_decode_workspace_size(int32_t B, int32_t q_len, int32_t N, int32_t nu
  *   kv_cache     pool [num_pages, 64, row] (kv_dtype rows)
  *   block_table  int32 [B, max_pages_per_seq], row stride bt_stride_b: logical
  *                page j of request b is physical page block_table[b][j];
- *                entries past ceil(seq_lens[b] / 64) are never read
+ *                entries past ceil(seq_lens[b] / 64) are never read (nor
+ *                past 2^25 - 1 pages: no int32 seq_len reaches further)
  *   seq_lens     int32 [B] (device): cached tokens of request b INCLUDING the
  *                q_len new ones; query row t sees tokens
  *                [0, seq_lens[b] - q_len + 1 + t) (causal within the q_len

@@ -88,8 +88,8 @@ __device__ __forceinline__ void unit_to_stream(int u, int n_hg, int* stream, int
 // a piece: its start-up and its partial row); the line is cut into n_streams
 // streams, stream s covering [s * total / n, (s + 1) * total / n), one unit per
 // workgroup and head group, so that every workgroup gets the same amount of work
-// (within one position) whatever the length mix.  The pages of b inside stream s
-// form one piece; b is split when its pages straddle a cut.  The piece of b in
+// (within one position) whatever the length mix.  The pages of b that fall in stream
+// s form one piece; b is split when its stretch straddles a cut.  The piece of b in
 // stream s writes partial slot b + s: the slots of b + 1 all lie above those of b,
 // so B + n_streams slots suffice.  Every workgroup derives the plan from seq_lens
 // itself (one prefix sum over the batch), so there is no planning launch and no
@@ -102,6 +102,7 @@ __device__ __forceinline__ void unit_to_stream(int u, int n_hg, int* stream, int
 // The piece that holds a request's first page (head group 0) records
 // {first slot, number of pieces} in req[b] for the merge.
 constexpr int kSegOverhead = 4;                         // in pages
+constexpr int32_t kMaxPagesPerSeq = 0x7fffffff / kPage;  // block-table entries a request can reach
 
 __device__ __forceinline__ int clamp_seq(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
 __device__ __forceinline__ int pages_of(int s) { return (s + kPage - 1) / kPage; }
@@ -117,27 +118,49 @@ __device__ __forceinline__ long long uniform64(long long v) {
   return (long long)(((uint64_t)hi << 32) | lo);
 }
 
+// 64-bit division for the rare plans whose products overflow 32 bits, as a compact
+// bit-serial loop: the plan divides at several places, and the usual inlined 64-bit
+// sequence at each of them would bloat the kernels' code.  Only the kernels built for
+// such batches (P64) contain it; the host picks them when a bound on the plan's
+// products (batch size, block-table width and stream count) exceeds 32 bits.
+__device__ __forceinline__ uint64_t udiv64_slow(uint64_t a, uint64_t b) {
+  uint64_t q = 0, r = 0;
+#pragma unroll 1
+  for (int i = 63; i >= 0; --i) {
+    r = (r << 1) | ((a >> i) & 1u);
+    if (r >= b) {
+      r -= b;
+      q |= 1ull << i;
+    }
+  }
+  return q;
+}
+
+template <bool P64>
 struct PlanTotals {
   long long total;    // cost positions of the whole batch (>= 1)
   long long n;        // streams
   // 64-bit division is a long software sequence on the GPU: when every product below
   // fits in 32 bits (any realistic batch), 32-bit unsigned division is used instead
-  __device__ __forceinline__ bool small() const { return total <= (long long)(0xFFFFFFFFu / (uint32_t)(n + 1)); }
+  __device__ __forceinline__ bool small() const {
+    return !P64 || total <= (long long)(0xFFFFFFFFu / (uint32_t)(n + 1));
+  }
   __device__ __forceinline__ long long start(long long s) const {
     if (small()) return (long long)((uint32_t)s * (uint32_t)total / (uint32_t)n);
-    return s * total / n;
+    return (long long)udiv64_slow((uint64_t)(s * total), (uint64_t)n);
   }
   // the stream holding position X: the largest s with start(s) <= X
   __device__ __forceinline__ int stream_of(long long X) const {
     if (small()) return (int)((((uint32_t)X + 1u) * (uint32_t)n - 1u) / (uint32_t)total);
-    return (int)(((X + 1) * n - 1) / total);
+    return (int)udiv64_slow((uint64_t)((X + 1) * n - 1), (uint64_t)total);
   }
 };
 
 // Thread tid sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
 // pre[tid] receives the exclusive prefix of those sums.
 // *seq0 receives the clamped seq_len of request tid * K (0 if there is none).
-__device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS long long* pre, int tid, int* seq0) {
+template <bool P64>
+__device__ __forceinline__ PlanTotals<P64> plan_prefix(const DecodeParams& p, MLA_LDS long long* pre, int tid, int* seq0) {
   const int cap = p.max_pages * kPage;
   const int K = (p.B + 255) >> 8;
   const int b0 = tid * K;
@@ -162,7 +185,7 @@ __device__ __forceinline__ PlanTotals plan_prefix(const DecodeParams& p, MLA_LDS
   long long off = 0;
   for (int k = 0; k < (tid >> 6); ++k) off += wtot[k];
   pre[tid] = off + incl - local;
-  PlanTotals r;
+  PlanTotals<P64> r;
   r.total = uniform64(wtot[0] + wtot[1] + wtot[2] + wtot[3]);
   // no more streams than positions, so that no stream is empty (the pieces of a
   // request then sit in consecutive streams)
@@ -202,6 +225,14 @@ __device__ __forceinline__ void plan_find(const DecodeParams& p, MLA_LDS long lo
   lds_barrier();                                        // sel is rewritten by the next search
 }
 
+// floor(x * np / len) for 0 <= x <= len (32-bit arithmetic when the product fits)
+template <bool P64>
+__device__ __forceinline__ int scale_floor(int x, int np, int len) {
+  if (!P64 || (uint64_t)(uint32_t)len * (uint32_t)np <= 0xFFFFFFFFull)
+    return (int)((uint32_t)x * (uint32_t)np / (uint32_t)len);
+  return (int)udiv64_slow((uint64_t)x * (uint64_t)np, (uint64_t)len);
+}
+
 // One piece of a stream: request b, tokens [t_begin, t_end) of its seq (clamped)
 // tokens, the number of pieces of b and this piece's partial slot.
 struct Piece {
@@ -210,14 +241,15 @@ struct Piece {
 
 // Walks the pieces of stream s in order; every value is workgroup-uniform.  pre / tot
 // come from plan_prefix (automatic mode only).
+template <bool P64>
 struct PieceIter {
   long long lo, hi, c;
-  PlanTotals tot;
+  PlanTotals<P64> tot;
   int b, s;
   int seq_b;          // clamped seq_len of request b as found by plan_find (-1: unknown)
   bool done;
 
-  __device__ __forceinline__ void init(const DecodeParams& p, MLA_LDS long long* pre, const PlanTotals& tot, int stream,
+  __device__ __forceinline__ void init(const DecodeParams& p, MLA_LDS long long* pre, const PlanTotals<P64>& tot, int stream,
                                        int tid, int seq0) {
     s = stream;
     done = false;
@@ -255,7 +287,7 @@ struct PieceIter {
       const int seq = seq_b >= 0 ? seq_b : clamp_seq(p.seq_lens[b], cap);
       seq_b = -1;
       const int np = pages_of(seq);
-      const long long p0 = c + kSegOverhead;            // position of page 0
+      const int len = kSegOverhead + np;                // b's stretch: [c, c + len)
       bool have = false;
       if (np == 0) {
         if (c >= lo) {
@@ -264,17 +296,32 @@ struct PieceIter {
           have = true;
         }
       } else {
-        const long long a = lo > p0 ? lo : p0;
-        const long long e = hi < p0 + np ? hi : p0 + np;
-        if (a < e) {
-          const int sf = tot.stream_of(p0), sl = tot.stream_of(p0 + np - 1);
+        // Where the stretch maps onto the pages.  Usually b starts inside a stream that
+        // also holds the end of an earlier request: that stream pays b's extra piece, so
+        // the overhead stands at the front and relative position x ends page x - O.  When
+        // a cut falls exactly on b's start, no stream pays an extra piece for b, and the
+        // stretch maps in proportion instead (x ends page floor(x * np / len)), so that a
+        // request cut into k streams gives each the same share of its pages.  Page 0 lies
+        // in stream sf, page np - 1 in stream sl.  A stream strictly between them with no
+        // page of b (only possible in proportion, for streams shorter than len / np
+        // positions) still takes an empty piece, a partial of weight zero, so that b has
+        // a partial in every slot it uses.
+        const bool prop = tot.start(tot.stream_of(c)) == c;
+        const int first_end = prop ? (len + np - 1) / np : kSegOverhead + 1;
+        const int sf = tot.stream_of(c + first_end - 1), sl = tot.stream_of(c + len - 1);
+        if (s >= sf && s <= sl) {
+          const int xa = lo > c ? (int)(lo - c) : 0;
+          const int xe = hi < c + len ? (int)(hi - c) : len;
+          const int pa = prop ? scale_floor<P64>(xa, np, len) : (xa > kSegOverhead ? xa - kSegOverhead : 0);
+          const int pe = prop ? scale_floor<P64>(xe, np, len) : (xe > kSegOverhead ? xe - kSegOverhead : 0);
           if (s == sf && hg == 0 && tid == 0) p.req[b] = make_int4(b + sf, sl - sf + 1, 0, seq);
-          const int t1 = (int)(e - p0) * kPage;
-          pc = Piece{b, (int)(a - p0) * kPage, t1 < seq ? t1 : seq, seq, sl - sf + 1, b + s};
+          const int t0 = pa * kPage < seq ? pa * kPage : seq;
+          const int t1 = pe * kPage < seq ? pe * kPage : seq;
+          pc = Piece{b, t0, t1, seq, sl - sf + 1, b + s};
           have = true;
         }
       }
-      c = p0 + np;
+      c += len;
       ++b;
       if (have) return true;
     }
@@ -536,7 +583,7 @@ __device__ __forceinline__ void wait_blocks_after(int later, int w) {
   }
 }
 
-template <bool FP8>
+template <bool FP8, bool P64>
 __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kNLdsBytes];
   MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
@@ -584,14 +631,14 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
   const bool row_ok = head < p.N;
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kNPlan);
-  PlanTotals tot{1, 1};
+  PlanTotals<P64> tot{1, 1};
   int seq0 = 0;
-  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid, &seq0);
+  if (p.num_splits == 0) tot = plan_prefix<P64>(p, plan_lds, tid, &seq0);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
     unit_to_stream(u, p.n_hg, &sid, &hg);
     if (sid >= p.n_streams) continue;
-    PieceIter it;
+    PieceIter<P64> it;
     it.init(p, plan_lds, tot, sid, tid, seq0);
     StagedPiece cur, nxt;
     if (!it.next(p, hg, tid, cur.pc)) continue;
@@ -1042,7 +1089,7 @@ __device__ __forceinline__ void zero_own_tail_fp8(MLA_LDS char* blk, int valid, 
   }
 }
 
-template <bool FP8>
+template <bool FP8, bool P64>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kWLdsBytes];
   MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
@@ -1092,14 +1139,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
   }
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
-  PlanTotals tot{1, 1};
+  PlanTotals<P64> tot{1, 1};
   int seq0 = 0;
-  if (p.num_splits == 0) tot = plan_prefix(p, plan_lds, tid, &seq0);
+  if (p.num_splits == 0) tot = plan_prefix<P64>(p, plan_lds, tid, &seq0);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
     unit_to_stream(u, p.n_hg, &sid, &hg);
     if (sid >= p.n_streams) continue;
-    PieceIter it;
+    PieceIter<P64> it;
     it.init(p, plan_lds, tot, sid, tid, seq0);
     StagedPiece cur, nxt;
     if (!it.next(p, hg, tid, cur.pc)) continue;
@@ -1474,15 +1521,19 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
                 *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fl + 8 * i + 4 * h32) * 4) = v;
               }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            u32x4_t v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-              v[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (4 * k + (le >> 4)) * kWStagePitch32 + (le & 15) * 16);
+            for (int kb = 0; kb < 2; ++kb) {
+              u32x4_t v[4];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              float* prow = p.part_o + (slot * p.m_wg + 32 * rb + 4 * k + (le >> 4)) * kLatent + 128 * w + 64 * fh +
-                            4 * (le & 15);
-              *reinterpret_cast<u32x4_t*>(prow) = v[k];
+              for (int k = 0; k < 4; ++k)
+                v[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (4 * (4 * kb + k) + (le >> 4)) * kWStagePitch32 +
+                                                                 (le & 15) * 16);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                float* prow = p.part_o + (slot * p.m_wg + 32 * rb + 4 * (4 * kb + k) + (le >> 4)) * kLatent + 128 * w +
+                              64 * fh + 4 * (le & 15);
+                *reinterpret_cast<u32x4_t*>(prow) = v[k];
+              }
             }
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
@@ -1672,6 +1723,9 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   p.num_pages = num_pages;
   p.block_table = block_table;
   p.bt_sb = bt_stride_b;
+  // a seq_len is an int32, so no request reaches past page 2^25 - 1: wider tables are
+  // read only that far (this also keeps the kernels' page * 64 arithmetic in 32 bits)
+  if (max_pages_per_seq > kMaxPagesPerSeq) max_pages_per_seq = kMaxPagesPerSeq;
   p.max_pages = max_pages_per_seq;
   p.seq_lens = seq_lens;
   p.B = B;
@@ -1710,13 +1764,30 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   int64_t grid = cus < units ? cus : units;
   if (grid < 1) grid = 1;
 
+  // The automatic plan's products fit in 32 bits when total * (streams + 1) and
+  // len * pages do (total <= B * (overhead + block-table width), len <= overhead + width);
+  // only batches beyond that bound run the kernels with 64-bit plan arithmetic.
+  const uint64_t stretch = (uint64_t)kSegOverhead + (uint64_t)max_pages_per_seq;
+  const bool p64 = num_splits == 0 && ((uint64_t)B * stretch > 0xFFFFFFFFull / (uint64_t)(streams + 1) ||
+                                       stretch * (uint64_t)max_pages_per_seq > 0xFFFFFFFFull);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const dim3 g((unsigned)grid), blk(256);
   if (kv_dtype == MLA_KV_BF16) {
-    if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
-    else hipLaunchKernelGGL((decode_narrow_kernel<false>), dim3((unsigned)grid), dim3(256), 0, hs, p);
+    if (p64) {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, true>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<false, true>), g, blk, 0, hs, p);
+    } else {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, false>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<false, false>), g, blk, 0, hs, p);
+    }
   } else {
-    if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true>), dim3((unsigned)grid), dim3(256), 0, hs, p);
-    else hipLaunchKernelGGL((decode_narrow_kernel<true>), dim3((unsigned)grid), dim3(256), 0, hs, p);
+    if (p64) {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true, true>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<true, true>), g, blk, 0, hs, p);
+    } else {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true, false>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<true, false>), g, blk, 0, hs, p);
+    }
   }
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   if (num_splits != 1) {

@@ -241,6 +241,26 @@ def test_many_requests_plan_scan(N, q_len, kd):
         check_lse(lse.cpu().numpy(), lse_ref, "many")
 
 
+@pytest.mark.parametrize("N,kd", [(16, MI.KV_BF16), (128, MI.KV_BF16), (128, MI.KV_FP8)])
+def test_wide_block_table_takes_the_64bit_plan_kernels(N, kd):
+    """A block table 70000 pages wide puts a bound on the plan's products past 32 bits,
+    so the kernels built with 64-bit plan arithmetic run (their 32-bit path, as these
+    lengths are small): same bits as the kernels a narrow table selects, and parity."""
+    w = _small("wide-bt", N, 1, [300, 1000, 4100, 64], kd=kd, seed=95)
+    pool = gpu_pool(w)
+    o_ref, lse_ref = O.decode(O.bf16_bits_to_f64(w.q), oracle_pool(w), w.kv_dtype, w.block_table,
+                              w.seq_lens, SC)
+    wide = np.full((w.B, 70000), -1, dtype=np.int32)
+    wide[:, :w.block_table.shape[1]] = w.block_table
+    for ns in (0, 3):
+        say(f"wide block table N={N} kd={kd} ns={ns}")
+        o_n, l_n = gpu_decode(w, pool, w.q, ns)
+        o_w, l_w = gpu_decode(w, pool, w.q, ns, block_table=wide)
+        assert torch.equal(o_n, o_w) and torch.equal(l_n, l_w)
+        check_out(to_f64(o_w), o_ref, "wide block table")
+        check_lse(l_w.cpu().numpy(), lse_ref, "wide block table")
+
+
 @pytest.mark.parametrize("N", [128, 16])
 def test_fp8_rows_with_distinct_k_and_v_scales(N):
     """fp8 rows whose K and V scales differ: each scale must be applied to its view."""
