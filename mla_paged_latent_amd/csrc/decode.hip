@@ -987,20 +987,37 @@ __device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS c
     for (int f1 = 0; f1 < 2; ++f1) va_addr[r][f1] = opaque(lds_addr(blk) + vbase[r][f1]);
 #pragma unroll
   for (int s = 0; s < 2; ++s) pa[s] = opaque(lds_addr(pbuf) + pbase[s]);
+  // all operands of a token half are requested before its MFMAs, the second half's
+  // while the first half's MFMAs run
+  bf16x8_t pb[2][2];
+  bf16x4_t lo[2][4], hi[2][4];
+  auto load = [&](int s) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) pb[rb] = lds_read_b128_at(pa[s] + rb * 2048);
+    for (int rb = 0; rb < 2; ++rb) pb[s][rb] = lds_read_b128_at(pa[s] + rb * 2048);
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       const uint32_t off = (uint32_t)((fb >> 1) * kBlkGroupBytes + s * 2048);
-      const bf16x4_t lo = lds_read_tr16_at(va_addr[0][fb & 1] + off);
-      const bf16x4_t hi = lds_read_tr16_at(va_addr[1][fb & 1] + off);
-      const bf16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      lo[s][fb] = lds_read_tr16_at(va_addr[0][fb & 1] + off);
+      hi[s][fb] = lds_read_tr16_at(va_addr[1][fb & 1] + off);
+    }
+  };
+  load(0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+  load(1);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[rb], o[fb][rb], 0, 0, 0);
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const bf16x8_t va = {lo[s][fb][0], lo[s][fb][1], lo[s][fb][2], lo[s][fb][3],
+                           hi[s][fb][0], hi[s][fb][1], hi[s][fb][2], hi[s][fb][3]};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s][rb], o[fb][rb], 0, 0, 0);
+        if (s == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (fb * 2 + rb < 5) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
     }
   }
 }
