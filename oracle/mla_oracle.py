@@ -341,6 +341,74 @@ def up_v(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
                      np.asarray(w_uv, np.float64))
 
 
+# --- next to decode: context gather and the two-part state merge ------------
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of float64 values, rounded to nearest, ties to even.
+
+    bfloat16 is the top half of an IEEE float32: 8 significant bits down to
+    2^-126, then subnormals spaced 2^-133; values that round past the largest
+    finite one become infinity; NaN becomes the quiet NaN 0x7FC0 (with the
+    input's sign).  The rounding is done on the exact float64 input.
+    """
+    v = np.asarray(x, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(np.where(np.isfinite(a) & (a > 0), a, 1.0))
+    quantum = np.ldexp(1.0, np.maximum(e, -125) - 8)        # 2^(e-8), 2^-133 below 2^-126
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = np.round(a / quantum) * quantum                  # round half to even
+        bits = (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(np.isnan(a), np.uint16(0x7FC0), bits)
+    bits = np.where(np.isinf(a), np.uint16(0x7F80), bits)
+    return (bits | np.where(np.signbit(v), np.uint16(0x8000), np.uint16(0))).astype(np.uint16)
+
+
+def gather_cache(pool: np.ndarray, kv_dtype: int, block_table: np.ndarray, cu_seq_lens: np.ndarray,
+                 token_to_seq: np.ndarray, seq_starts: np.ndarray | None = None,
+                 row_elems: int = ROW_ELEMS) -> np.ndarray:
+    """Gather context rows from the paged cache into a contiguous bf16 workspace.
+
+    [vLLM-MLA] §Prefill (chunked context): the context rows a chunk needs are
+    collected from the paged cache by ``block_table``, ``cu_seq_lens`` and
+    ``token_to_seq`` into a contiguous workspace so that ``kv_b_proj`` can run
+    as one GEMM; fp8 rows are upconverted to bf16 while gathering; a chunk may
+    start part-way into a request, on a page boundary (``seq_starts``).
+
+    Output row ``r`` belongs to request ``b = token_to_seq[r]`` and is that
+    request's logical token ``seq_starts[b] + r - cu_seq_lens[b]``.  bf16 rows are
+    copied bit for bit; an fp8 row becomes ``code * k_scale`` for all of its
+    elements (the row's K view), rounded once to bf16.  Returns uint16 bf16 bit
+    patterns ``[len(token_to_seq), row_elems]``.
+    """
+    pool = np.asarray(pool, dtype=np.uint8)
+    total = len(token_to_seq)
+    out = np.zeros((total, row_elems), dtype=np.uint16)
+    for r in range(total):
+        b = int(token_to_seq[r])
+        start = 0 if seq_starts is None else int(seq_starts[b])
+        j = start + r - int(cu_seq_lens[b])
+        raw = pool[int(block_table[b][j // PAGE_TOKENS]), j % PAGE_TOKENS]
+        if kv_dtype == KV_BF16:
+            out[r] = raw[:2 * row_elems].view("<u2")
+        else:
+            k_scale = float(raw[row_elems:row_elems + 4].copy().view("<f4")[0])
+            out[r] = f64_to_bf16_bits(e4m3_value(raw[:row_elems]) * k_scale)
+    return out
+
+
+def merge_attn_states(prefix_o: np.ndarray, prefix_lse: np.ndarray, suffix_o: np.ndarray,
+                      suffix_lse: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Merge two attention states of the same query rows over disjoint key sets.
+
+    [vLLM-MLA] §Prefill (merge_attn_states): the context-chunk result (prefix)
+    and the new-token result (suffix) are re-weighted by ``exp(lse - max_lse)``
+    per head and query row; a state with no keys (``o = 0``, ``lse = -inf``)
+    weighs zero.  ``o[..., D]`` and ``lse[...]`` share their leading shape;
+    returns float64 ``(o, lse)``.  This is :func:`merge` with two parts.
+    """
+    return merge(np.stack([np.asarray(prefix_o, np.float64), np.asarray(suffix_o, np.float64)]),
+                 np.stack([np.asarray(prefix_lse, np.float64), np.asarray(suffix_lse, np.float64)]))
+
+
 # --- the un-absorbed oracle --------------------------------------------------
 def mla_unabsorbed(q_nope: np.ndarray, q_pe: np.ndarray, pool: np.ndarray, kv_dtype: int,
                    block_table: np.ndarray, seq_lens: np.ndarray, w_uk_t: np.ndarray,

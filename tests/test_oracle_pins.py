@@ -454,3 +454,108 @@ def test_bf16_half_ulp_helper():
     # the exactly rounded value is always within half an ulp
     v = np.random.default_rng(0).standard_normal(10000)
     assert np.all(np.abs(O.round_to_bf16(v) - v) <= bf16_half_ulp(v))
+
+
+# ----------------------------------------------------------------------------
+# context gather and the two-part merge (the steps either side of decode)
+# ----------------------------------------------------------------------------
+def test_f64_to_bf16_bits_hand_values():
+    x = np.array([1.0, -2.0, 1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-30, 2**-133, 2**-134,
+                  3 * 2**-134, 2**-126, np.nan, np.inf, -np.inf, 3.5e38, 0.0, -0.0, 448.0 * 0.5])
+    want = [0x3F80, 0xC000, 0x3F80, 0x3F82, 0x3F81, 0x0001, 0x0000, 0x0002, 0x0080, 0x7FC0, 0x7F80,
+            0xFF80, 0x7F80, 0x0000, 0x8000, 0x4360]
+    assert [int(v) for v in O.f64_to_bf16_bits(x)] == want
+
+
+def test_f64_to_bf16_bits_matches_torch_on_float32_inputs():
+    rng = np.random.default_rng(30)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000),
+                        rng.standard_normal(2000) * 1e-39]).astype(np.float32)
+    ours = O.f64_to_bf16_bits(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def _position_pool(num_pages):
+    """bf16 pool whose every element encodes (page, offset, element)."""
+    pg, off, el = np.meshgrid(np.arange(num_pages), np.arange(64), np.arange(576), indexing="ij")
+    return ((pg * 64 + off) * 7 + el).astype(np.uint16).view(np.uint8).reshape(num_pages, 64, 1152)
+
+
+def test_gather_cache_bf16_rows_come_from_their_logical_tokens():
+    rng = np.random.default_rng(31)
+    num_pages = 40
+    pool = _position_pool(num_pages)
+    seqs = [130, 64, 1, 200]                       # context lengths of the chunk's requests
+    starts = [64, 0, 0, 128]                      # page-aligned chunk starts inside the requests
+    bt = np.full((4, 6), -1, np.int32)
+    perm = rng.permutation(num_pages)
+    k = 0
+    for b, (n, s0) in enumerate(zip(seqs, starts)):
+        for p in range((s0 + n + 63) // 64):
+            bt[b, p] = perm[k]
+            k += 1
+    cu = np.concatenate([[0], np.cumsum(seqs)]).astype(np.int32)
+    t2s = np.repeat(np.arange(4), seqs).astype(np.int32)
+    out = O.gather_cache(pool, O.KV_BF16, bt, cu, t2s, np.array(starts, np.int32))
+    for r in range(len(t2s)):
+        b = t2s[r]
+        j = starts[b] + r - cu[b]
+        page, offset = bt[b, j // 64], j % 64
+        assert np.array_equal(out[r], ((page * 64 + offset) * 7 + np.arange(576)).astype(np.uint16))
+
+
+def test_gather_cache_fp8_dequant_hand_values():
+    """code x k_scale, rounded once to bf16 (v_scale is not used by the K view)."""
+    cases = [  # (code, k_scale, expected bf16 bits)
+        (0x38, 2.0, 0x4000),             # 1.0 x 2
+        (0x7E, 0.5, 0x4360),             # 448 x 0.5 = 224
+        (0xFE, 0.5, 0xC360),             # -224
+        (0x01, 4.0, 0x3C00),             # subnormal 2^-9 x 4 = 2^-7
+        (0x00, 3.0, 0x0000),
+        (0x38, 1 + 2**-8, 0x3F80),       # exact tie 1 + 2^-8 -> even (1.0)
+        (0x38, 1 + 3 * 2**-8, 0x3F82),   # exact tie -> even (1 + 2^-6)
+        (0x3F, 1 + 2**-10, 0x3FF0),      # 1.875 (1 + 2^-10) = 1.87683... -> 1.875
+        (0x3C, 1 + 2**-8, 0x3FC1),       # 1.5 (1 + 2^-8) = 1.505859375 -> 1.5078125
+    ]
+    n = len(cases)
+    pool = np.zeros((1, 64, 584), np.uint8)
+    for i, (code, ks, _) in enumerate(cases):
+        pool[0, i, :576] = code
+        pool[0, i, 576:580] = np.array([ks], "<f4").view(np.uint8)
+        pool[0, i, 580:584] = np.array([1000.0], "<f4").view(np.uint8)   # v_scale: unused here
+    out = O.gather_cache(pool, O.KV_FP8, np.zeros((1, 1), np.int32), np.array([0, n], np.int32),
+                         np.zeros(n, np.int32))
+    for i, (_, _, want) in enumerate(cases):
+        assert np.all(out[i] == want), (i, hex(int(out[i, 0])), hex(want))
+
+
+def test_merge_attn_states_closed_forms():
+    rng = np.random.default_rng(32)
+    o1, o2 = rng.standard_normal((2, 5, 3, 16))
+    l1, l2 = rng.standard_normal((2, 5, 3))
+    # an empty state weighs nothing
+    o, lse = O.merge_attn_states(o1, l1, np.zeros_like(o2), np.full_like(l2, -np.inf))
+    assert np.array_equal(o, o1) and np.array_equal(lse, l1)
+    o, lse = O.merge_attn_states(np.zeros_like(o1), np.full_like(l1, -np.inf), o2, l2)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # both empty: o = 0, lse = -inf
+    o, lse = O.merge_attn_states(np.zeros_like(o1), np.full_like(l1, -np.inf), np.zeros_like(o2),
+                                 np.full_like(l2, -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # equal LSE: the plain average, LSE + ln 2
+    o, lse = O.merge_attn_states(o1, l1, o2, l1)
+    assert np.allclose(o, (o1 + o2) / 2, atol=1e-15) and np.allclose(lse, l1 + math.log(2), atol=1e-15)
+
+
+def test_merge_attn_states_of_a_key_split_equals_attention_over_all_keys():
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((8, 192))
+    K = rng.standard_normal((90, 192)) * 1.5
+    V = rng.standard_normal((90, 128))
+    o_all, l_all = O.attend(q, K, V, O.default_scale())
+    for cut in (0, 1, 37, 89, 90):
+        op, lp = O.attend(q, K[:cut], V[:cut], O.default_scale())
+        os_, ls = O.attend(q, K[cut:], V[cut:], O.default_scale())
+        o, lse = O.merge_attn_states(op, lp, os_, ls)
+        assert np.allclose(o, o_all, atol=1e-12) and np.allclose(lse, l_all, atol=1e-12)
