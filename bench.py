@@ -10,6 +10,7 @@ step's pages to the next.
 
 Prints ONE JSON line (stdout).  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
+    python bench.py --op gather_fp8|gather_bf16|merge_states   (the calls either side of decode)
 """
 
 from __future__ import annotations
@@ -336,6 +337,136 @@ def traffic_record_from_pmc(fetch_dir: str, write_dir: str, workload: str, copy_
     return res
 
 
+CONTEXT_OPS = {
+    # the chunked-prefill workspace at its cap (64 x 1024 rows) gathered from 16
+    # requests' 4096-token context chunks, fp8 cache upconverted to bf16
+    "gather_fp8": dict(kind="gather", kv=MI.KV_FP8, requests=16, chunk=4096),
+    "gather_bf16": dict(kind="gather", kv=MI.KV_BF16, requests=16, chunk=4096),
+    # merging the context and new-token states of an 8192-token prefill, 128 heads,
+    # v_head_dim 128
+    "merge_states": dict(kind="merge", T=8192, N=128, D=128),
+}
+
+
+def run_context_op(args) -> dict:
+    """One launch of mla_gather_cache or mla_merge_attn_states, timed back to back.
+
+    Algorithmic bytes: gather reads each source row (1152 or 584 B) and writes a
+    1152 B bf16 row, plus 4 B of token_to_seq per row, 4 B per block-table entry
+    and 12 B per request; merge reads two bf16 states and two LSEs and writes one
+    of each.  The bound is HBM (no arithmetic to speak of).
+    """
+    import ctypes
+    import torch
+    import mla_paged_latent_amd as M
+    op = CONTEXT_OPS[args.op]
+    dev = "cuda"
+    L = M.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    if op["kind"] == "gather":
+        kd, nreq, chunk = op["kv"], op["requests"], op["chunk"]
+        total = nreq * chunk
+        pages = total // 64
+        rb = M.ROW_BYTES[kd]
+        # replicated pools, rotated per call, so the 256 MB cache cannot hold the rows
+        R = max(2, math.ceil(3 * MALL_BYTES / (pages * 64 * rb)))
+        chunks = [MI.make_context_chunk([chunk] * nreq, [0] * nreq, pages, seed=500 + i) for i in range(R)]
+        w = MI.make_workload("gather-pool", 1, 1, 16, [64], pages, kd, False, 501)
+        rows = torch.from_numpy(np.ascontiguousarray(w.kv_rows.reshape(-1, 576)).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        slots = torch.arange(pages * 64, device=dev)
+        pools = []
+        for _ in range(R):
+            pl = torch.empty((pages, 64, rb), dtype=torch.uint8, device=dev)
+            M.cache_write(rows[:, :512], rows[:, 512:], slots, pl, kd)
+            pools.append(pl)
+        del rows
+        out = torch.empty((total, 576), dtype=torch.bfloat16, device=dev)
+        meta = [tuple(torch.from_numpy(a).to(dev) for a in (c.block_table, c.cu_seq_lens, c.token_to_seq))
+                for c in chunks]
+        calls = [(pools[i].data_ptr(), kd, pages, meta[i][0].data_ptr(), meta[i][0].stride(0),
+                  meta[i][0].shape[1], meta[i][1].data_ptr(), None, meta[i][2].data_ptr(), nreq, total,
+                  out.data_ptr(), out.stride(0), stream) for i in range(R)]
+        f = L.mla_gather_cache
+        bytes_alg = total * (rb + 1152 + 4) + pages * 4 + nreq * 12
+        desc = (f"{args.op}: {total} rows (the 64x1024-row prefill workspace cap) from {nreq} requests' "
+                f"{chunk}-token context chunks, {'fp8 rows upconverted' if kd == MI.KV_FP8 else 'bf16 rows'} "
+                f"to bf16, random page placement, {R} rotating pool copies")
+        metric = "context gather GB/s (% of HBM roofline), 1 MI355X"
+        dtype = "fp8->bf16" if kd == MI.KV_FP8 else "bf16"
+    else:
+        T, N, D = op["T"], op["N"], op["D"]
+        po, pl, so, sl = MI.random_attn_states(T, N, D, seed=510)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        tpo, tso = bf(po), bf(so)
+        tpl, tsl = torch.from_numpy(pl).to(dev), torch.from_numpy(sl).to(dev)
+        out = torch.empty_like(tpo)
+        olse = torch.empty_like(tpl)
+        calls = [(tpo.data_ptr(), tpl.data_ptr(), tso.data_ptr(), tsl.data_ptr(), T, N, D, tpo.stride(0),
+                  tpo.stride(1), tpl.stride(0), tpl.stride(1), out.data_ptr(), olse.data_ptr(), stream)]
+        f = L.mla_merge_attn_states
+        bytes_alg = T * N * (3 * D * 2 + 3 * 4)
+        desc = f"{args.op}: T={T} query rows x {N} heads x D={D} (bf16 states, fp32 LSE, ~10% empty rows)"
+        metric = "attention-state merge GB/s (% of HBM roofline), 1 MI355X"
+        dtype = "bf16"
+    for i in range(max(args.warmup, 3)):
+        if f(*calls[i % len(calls)]) != 0:
+            raise RuntimeError(f"{args.op} failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        f(*calls[i % len(calls)])
+    e1.record()
+    torch.cuda.synchronize()
+    mean_ms = e0.elapsed_time(e1) / args.steps
+    gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
+    log(f"[bench] {args.op}: {mean_ms * 1e3:.1f} us per call, {gbs:.0f} GB/s")
+    res = {"metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": {"workload": desc},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": args.op,
+                        "algorithmic_bytes": bytes_alg, "mean_launch_us": round(mean_ms * 1e3, 2)}}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_context(args.op)
+    return res
+
+
+def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
+    """The oracle's gather / merge on a bounded sample of the same workload."""
+    from oracle import mla_oracle as O
+    op = CONTEXT_OPS[name]
+    times, n_items = [], 0
+    t_all = time.perf_counter()
+    if op["kind"] == "gather":
+        c = MI.make_context_chunk([256] * 8, [0] * 8, 32, seed=520)
+        w = MI.make_workload("gather-pool", 1, 1, 16, [64], 32, op["kv"], False, 521)
+        pool = O.encode_rows(w.kv_rows.reshape(-1, 576), op["kv"]).reshape(32, 64, -1)
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            O.gather_cache(pool, op["kv"], c.block_table, c.cu_seq_lens, c.token_to_seq)
+            times.append(time.perf_counter() - t0)
+        n_items = c.total
+        rb = 1152 if op["kv"] == MI.KV_BF16 else 584
+        per_item = rb + 1152 + 4
+        sample = f"{c.total} rows (8 requests x 256 tokens) through the oracle gather"
+    else:
+        T, N, D = 256, op["N"], op["D"]
+        po, pl, so, sl = MI.random_attn_states(T, N, D, seed=522)
+        pof, sof = O.bf16_bits_to_f64(po), O.bf16_bits_to_f64(so)
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            O.merge_attn_states(pof, pl, sof, sl)
+            times.append(time.perf_counter() - t0)
+        n_items = T * N
+        per_item = 3 * D * 2 + 3 * 4
+        sample = f"{T} query rows x {N} heads x D={D} through the oracle merge"
+    mean = sum(times) / len(times)
+    return {"value": round(n_items * per_item / mean / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}, {len(times)} repetition(s), mean {mean:.3f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +474,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="full_head", choices=sorted(MI.CONFIGS))
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--op", default="step", choices=["step"] + sorted(CONTEXT_OPS),
+                    help="step: the decode step (default); the others time one of the two calls either "
+                         "side of decode (context gather, state merge) on their own workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
@@ -364,6 +498,9 @@ def main():
                                    "request (attention-DP) or heads (TP) with no exchange inside the "
                                    "path, so only --gpus 1 is measured"}), flush=True)
         sys.exit(2)
+    if args.op != "step":
+        print(json.dumps(run_context_op(args)), flush=True)
+        return
     res = run(args)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -189,6 +189,59 @@ mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t ol_stride_
                       const void* w_uv, int64_t T, int32_t N,
                       void* out, int64_t out_stride_t, void* stream);
 
+/*
+ * mla_gather_cache -- gather context rows of the paged cache into a contiguous
+ * bf16 workspace ([vLLM-MLA] §Prefill, chunked context: the rows a chunk needs
+ * are collected by block_table, cu_seq_lens and token_to_seq so that kv_b_proj
+ * runs as one GEMM; fp8 rows are upconverted to bf16 while gathering; a chunk
+ * starts on a page boundary of its request).
+ *
+ *   kv_cache      pool [num_pages, 64, row] (kv_dtype rows), read only
+ *   block_table   int32 [B, max_pages_per_seq], row stride bt_stride_b
+ *   cu_seq_lens   int32 [B + 1] (device): rows of request b go to output rows
+ *                 [cu_seq_lens[b], cu_seq_lens[b + 1])
+ *   seq_starts    int32 [B] (device) or NULL (all 0): the request's first token
+ *                 in this chunk
+ *   token_to_seq  int32 [total_rows] (device): the request of each output row
+ *   out           bf16 [total_rows, 576], row stride out_stride (elements)
+ *
+ * Output row r of request b = token_to_seq[r] is logical token
+ * j = seq_starts[b] + r - cu_seq_lens[b] of b, at page block_table[b][j / 64],
+ * offset j % 64.  bf16 rows are copied bit for bit; an fp8 row becomes
+ * bf16_rne(code * k_scale) for all 576 elements (its K view; rounded once from
+ * the exact product).  A row whose request, token or page id is out of range
+ * is written as zeros.  Only the output is written.  kv_cache and out 16-byte
+ * aligned, out_stride a multiple of 8.
+ */
+mla_status_t mla_gather_cache(const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride_b,
+                              int32_t max_pages_per_seq, const int32_t* cu_seq_lens,
+                              const int32_t* seq_starts, const int32_t* token_to_seq, int32_t B,
+                              int64_t total_rows, void* out, int64_t out_stride, void* stream);
+
+/*
+ * mla_merge_attn_states -- merge two attention states of the same query rows
+ * over disjoint key sets ([vLLM-MLA] §Prefill, merge_attn_states: the context
+ * result and the new-token result are re-weighted by exp(lse - max_lse) per
+ * head and row; a state with no keys, o = 0 and lse = -inf, weighs zero).
+ *
+ *   prefix_out, suffix_out, out   bf16 [T, N, D], element strides
+ *                                 (o_stride_t, o_stride_h), last dim contiguous
+ *   prefix_lse, suffix_lse, out_lse  float32 [T, N], element strides
+ *                                 (lse_stride_t, lse_stride_h); out_lse may be NULL
+ *
+ * With w_x = exp(lse_x - m), m = max(lse_p, lse_s):
+ * out = bf16_rne((w_p o_p + w_s o_s) / (w_p + w_s)), out_lse = m + ln(w_p + w_s)
+ * (float32); both states empty gives out = 0, out_lse = -inf.  1 <= N,
+ * 8 <= D <= 4096 with D a multiple of 8; tensors 16-byte aligned, o strides
+ * multiples of 8.  out may alias neither input.
+ */
+mla_status_t mla_merge_attn_states(const void* prefix_out, const float* prefix_lse,
+                                   const void* suffix_out, const float* suffix_lse, int64_t T,
+                                   int32_t N, int32_t D, int64_t o_stride_t, int64_t o_stride_h,
+                                   int64_t lse_stride_t, int64_t lse_stride_h, void* out,
+                                   float* out_lse, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* mla_status_str(mla_status_t status);
 

@@ -180,3 +180,55 @@ def random_fp8_rows(rng: np.random.Generator, n_rows: int, max_code_exp: int = 8
     rows[:, ROW:ROW + 4] = ks.view(np.uint8).reshape(n_rows, 4)
     rows[:, ROW + 4:] = vs.view(np.uint8).reshape(n_rows, 4)
     return rows
+
+
+@dataclasses.dataclass
+class ContextChunk:
+    """One chunk of prefill context to gather: which tokens of which requests."""
+    block_table: np.ndarray       # int32 [B, max_pages], -1 past the used pages
+    cu_seq_lens: np.ndarray       # int32 [B + 1]: output row offsets
+    seq_starts: np.ndarray        # int32 [B]: first token of each request in the chunk (page-aligned)
+    token_to_seq: np.ndarray      # int32 [total]
+    num_pages: int
+
+    @property
+    def total(self) -> int:
+        return int(self.cu_seq_lens[-1])
+
+
+def make_context_chunk(chunk_lens, chunk_starts, num_pages: int, seed: int) -> ContextChunk:
+    """A chunk of context rows: request b contributes ``chunk_lens[b]`` tokens
+    starting at its token ``chunk_starts[b]`` (a multiple of 64).  The requests'
+    pages (enough to cover start + length) are dealt from a random permutation of
+    the pool, as in :func:`make_workload`."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.asarray(chunk_lens, dtype=np.int64)
+    starts = np.asarray(chunk_starts, dtype=np.int64)
+    assert np.all(starts % PAGE == 0)
+    pages_per = (starts + lens + PAGE - 1) // PAGE
+    assert int(pages_per.sum()) <= num_pages, "pool too small"
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((len(lens), max(1, int(pages_per.max()))), -1, dtype=np.int32)
+    cur = 0
+    for b, n in enumerate(pages_per):
+        bt[b, :n] = perm[cur:cur + n]
+        cur += int(n)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    t2s = np.repeat(np.arange(len(lens)), lens).astype(np.int32)
+    return ContextChunk(bt, cu, starts.astype(np.int32), t2s, num_pages)
+
+
+def random_attn_states(T: int, N: int, D: int, seed: int, empty_frac: float = 0.1):
+    """Two attention states (prefix, suffix) of the same ``T x N`` query rows:
+    outputs bf16 bits ``[T, N, D]`` ~ N(0, 1), LSEs float32 ~ N(0, 3^2); a fraction
+    of rows is empty on one side or both (``o = 0``, ``lse = -inf``)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    po = _normal_bf16(rng, (T, N, D))
+    so = _normal_bf16(rng, (T, N, D))
+    pl = (rng.standard_normal((T, N)) * 3.0).astype(np.float32)
+    sl = (rng.standard_normal((T, N)) * 3.0).astype(np.float32)
+    for o, l in ((po, pl), (so, sl)):
+        empty = rng.random((T, N)) < empty_frac
+        o[empty] = 0
+        l[empty] = -np.inf
+    return po, pl, so, sl

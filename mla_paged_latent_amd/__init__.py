@@ -6,8 +6,10 @@ pointers, strides and the current HIP stream, and allocates outputs/workspace
 when the caller does not pass them.  There is no CPU fallback: if the library is
 missing, :func:`lib` raises.
 
-The four calls mirror ``include/mla.h``: :func:`cache_write`, :func:`absorb_q`,
-:func:`decode` and :func:`up_v`, plus :func:`decode_workspace_size`.
+The calls mirror ``include/mla.h``: :func:`cache_write`, :func:`absorb_q`,
+:func:`decode` and :func:`up_v`, plus :func:`decode_workspace_size`, and the two
+steps either side of decode in chunked prefill, :func:`gather_cache` and
+:func:`merge_attn_states`.
 """
 
 from __future__ import annotations
@@ -61,6 +63,10 @@ def lib() -> ctypes.CDLL:
     L.mla_decode.restype = i32
     L.mla_up_v.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.mla_up_v.restype = i32
+    L.mla_gather_cache.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp, i32, i64, vp, i64, vp]
+    L.mla_gather_cache.restype = i32
+    L.mla_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, i32, i64, i64, i64, i64, vp, vp, vp]
+    L.mla_merge_attn_states.restype = i32
     L.mla_status_str.argtypes = [i32]
     L.mla_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -166,3 +172,50 @@ def up_v(o_lat: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor | None = Non
         _ptr(o_lat), o_lat.stride(0), o_lat.stride(1), _ptr(w_uv), T, N, _ptr(out),
         out.stride(0), _stream(stream)))
     return out
+
+
+def gather_cache(kv_cache: torch.Tensor, kv_dtype: int, block_table: torch.Tensor,
+                 cu_seq_lens: torch.Tensor, token_to_seq: torch.Tensor,
+                 seq_starts: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Context rows of the paged cache as a contiguous bf16 ``[total, 576]`` workspace.
+
+    ``block_table`` int32 ``[B, max_pages]``, ``cu_seq_lens`` int32 ``[B + 1]``,
+    ``token_to_seq`` int32 ``[total]``, ``seq_starts`` int32 ``[B]`` or None.
+    """
+    assert block_table.dtype == torch.int32 and block_table.stride(-1) == 1
+    assert cu_seq_lens.dtype == torch.int32 and token_to_seq.dtype == torch.int32
+    assert seq_starts is None or seq_starts.dtype == torch.int32
+    B = block_table.shape[0]
+    total = token_to_seq.numel()
+    num_pages = kv_cache.numel() * kv_cache.element_size() // (PAGE_TOKENS * ROW_BYTES[kv_dtype])
+    if out is None:
+        out = torch.empty((total, ROW_ELEMS), dtype=torch.bfloat16, device=kv_cache.device)
+    assert out.dtype == torch.bfloat16 and out.stride(-1) == 1
+    _check("mla_gather_cache", lib().mla_gather_cache(
+        _ptr(kv_cache), kv_dtype, num_pages, _ptr(block_table), block_table.stride(0),
+        block_table.shape[1], _ptr(cu_seq_lens), _ptr(seq_starts), _ptr(token_to_seq), B, total,
+        _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def merge_attn_states(prefix_out: torch.Tensor, prefix_lse: torch.Tensor, suffix_out: torch.Tensor,
+                      suffix_lse: torch.Tensor, out: torch.Tensor | None = None,
+                      out_lse: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Merge two attention states ``(o [T, N, D] bf16, lse [T, N] fp32)`` of the same rows."""
+    T, N, D = prefix_out.shape
+    assert prefix_out.dtype == torch.bfloat16 and suffix_out.dtype == torch.bfloat16
+    assert suffix_out.stride() == prefix_out.stride() and prefix_out.stride(-1) == 1
+    assert prefix_lse.dtype == torch.float32 and suffix_lse.stride() == prefix_lse.stride()
+    if out is None:
+        out = torch.empty_strided(prefix_out.shape, prefix_out.stride(), dtype=torch.bfloat16,
+                                  device=prefix_out.device)
+    if out_lse is None:
+        out_lse = torch.empty_strided(prefix_lse.shape, prefix_lse.stride(), dtype=torch.float32,
+                                      device=prefix_lse.device)
+    assert out.stride() == prefix_out.stride() and out_lse.stride() == prefix_lse.stride()
+    _check("mla_merge_attn_states", lib().mla_merge_attn_states(
+        _ptr(prefix_out), _ptr(prefix_lse), _ptr(suffix_out), _ptr(suffix_lse), T, N, D,
+        prefix_out.stride(0), prefix_out.stride(1), prefix_lse.stride(0), prefix_lse.stride(1),
+        _ptr(out), _ptr(out_lse), _stream(stream)))
+    return out, out_lse

@@ -105,3 +105,25 @@ def test_other_calls_reject_bad_arguments():
     assert L.mla_up_v(p, 512, 512, p, 4, 129, p, 128 * 129, None) == 2
     assert L.mla_up_v(p, 512, 512, p, 4, 16, p, 1024, None) == 2           # out row too short
     assert L.mla_up_v(p, 512, 512, None, 4, 16, p, 2048, None) == 1
+
+
+def test_context_calls_reject_bad_arguments_without_a_gpu():
+    """Host-side checks of the gather and merge calls return before touching the device."""
+    L = M.lib()
+    vp = ctypes.c_void_p
+    ok = vp(256)
+    g = lambda **o: L.mla_gather_cache(*[o.get(k, v) for k, v in dict(
+        kv=ok, kd=0, pages=4, bt=ok, btsb=4, maxp=4, cu=ok, ss=None, t2s=ok, B=1, total=10,
+        out=ok, ostride=576, stream=None).items()])
+    assert g(kd=7) == 3                          # MLA_ERR_DTYPE
+    assert g(total=-1) == 2 and g(B=0) == 2 and g(btsb=3) == 2 and g(ostride=8) == 2
+    assert g(total=0) == 0                       # nothing to do
+    assert g(kv=None) == 1 and g(t2s=None) == 1
+    assert g(out=vp(264)) == 4 and g(ostride=580) == 4 and g(t2s=vp(258)) == 4
+    m = lambda **o: L.mla_merge_attn_states(*[o.get(k, v) for k, v in dict(
+        po=ok, pl=ok, so=ok, sl=ok, T=4, N=2, D=64, ost=128, osh=64, lst=2, lsh=1, out=ok,
+        ol=None, stream=None).items()])
+    assert m(D=12) == 2 and m(D=0) == 2 and m(N=0) == 2 and m(T=-1) == 2 and m(D=8192) == 2
+    assert m(T=0) == 0
+    assert m(po=None) == 1 and m(out=None) == 1
+    assert m(so=vp(264)) == 4 and m(osh=60) == 4 and m(pl=vp(258)) == 4
