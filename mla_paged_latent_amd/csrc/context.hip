@@ -19,16 +19,6 @@ namespace mla {
 
 constexpr int kGatherChunks = kRow * 2 / 16;            // 72 output chunks of 8 bf16 per row
 
-// Value of an OCP e4m3fn code (exact in float32): exponent field 0 is subnormal,
-// S.1111.111 is NaN, bias 7.
-__device__ __forceinline__ float e4m3_value_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  float mag = e == 0 ? (float)m * 0.001953125f                        // m * 2^-9
-                     : __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
-  if (e == 15u && m == 7u) mag = __uint_as_float(0x7FC00000u);
-  return (c & 0x80u) ? -mag : mag;
-}
-
 // bfloat16 bits of the exact product v * s, rounded once (nearest, ties to even).
 // v has at most 4 significant bits, so v * s has at most 28: p = fl(v * s) holds the
 // top 24 and fma(v, s, -p) the exact rest.  Rounding p to bf16 is right unless p sits
@@ -48,80 +38,140 @@ __device__ __forceinline__ uint32_t bf16_of_product(float v, float s) {
   return r & 0xFFFFu;
 }
 
+// Two adjacent codes (low 16 bits of `two`) times k_scale as a bf16 pair: the
+// hardware conversions (e4m3fn -> f32 is exact; f32 -> bf16 rounds to nearest even)
+// give the right bits unless a float32 product lies exactly on a bf16 tie, which is
+// rare; such a pair is redone with the exact rule above.
+__device__ __forceinline__ uint32_t bf16x2_of_products(uint32_t two, float ks) {
+#pragma clang fp contract(off)
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
+  const float p0 = v[0] * ks, p1 = v[1] * ks;
+  const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+  if (((b0 & 0xFFFFu) == 0x8000u) | ((b1 & 0xFFFFu) == 0x8000u))
+    return bf16_of_product(v[0], ks) | (bf16_of_product(v[1], ks) << 16);
+  const bf16x2_t r = {(__bf16)p0, (__bf16)p1};
+  return *reinterpret_cast<const uint32_t*>(&r);
+}
+
+// Chunk i of the grid is output row i / 72, bytes 16 (i % 72) .. +15.  Each thread
+// takes kGatherUnroll chunks 256 apart per round and runs their dependent loads
+// (row -> request -> page id -> data) side by side, so that several chains are in
+// flight per thread.
+constexpr int kGatherUnroll = 4;
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void gather_cache_kernel(
     const char* __restrict__ pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     int64_t bt_sb, int32_t max_pages, const int32_t* __restrict__ cu_seq_lens,
     const int32_t* __restrict__ seq_starts, const int32_t* __restrict__ token_to_seq, int32_t B,
     int64_t total, uint16_t* __restrict__ out, int64_t out_stride) {
+  constexpr int U = kGatherUnroll;
   const int64_t n = total * kGatherChunks;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / kGatherChunks;
-    const int c = (int)(i - r * kGatherChunks);
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    // request, logical token and physical page of this row; anything out of range
-    // leaves the row's chunk zero (no access outside the caller's buffers)
-    const int b = token_to_seq[r];
-    if (b >= 0 && b < B) {
-      const int64_t j = (int64_t)(seq_starts ? seq_starts[b] : 0) + (r - cu_seq_lens[b]);
-      if (j >= 0 && j < (int64_t)max_pages * kPage) {
-        const int id = block_table[(int64_t)b * bt_sb + (j >> 6)];
-        if (id >= 0 && id < num_pages) {
-          const int64_t slot = (int64_t)id * kPage + (j & (kPage - 1));
-          if constexpr (!FP8) {
-            v = *reinterpret_cast<const u32x4_t*>(pool + slot * kRowBytesBf16 + c * 16);
-          } else {
-            const char* row = pool + slot * kRowBytesFp8;
-            const u32x2_t codes = *reinterpret_cast<const u32x2_t*>(row + c * 8);
-            const float ks = *reinterpret_cast<const float*>(row + kRow);
+  const int64_t step = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n; base += step) {
+    int64_t r[U], slot[U];
+    int c[U], b[U];
+    bool ok[U];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t w = codes[k >> 1] >> (16 * (k & 1));
-              v[k] = bf16_of_product(e4m3_value_f32(w & 0xFFu), ks) |
-                     (bf16_of_product(e4m3_value_f32((w >> 8) & 0xFFu), ks) << 16);
-            }
-          }
-        }
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + 256 * u;
+      ok[u] = i < n;
+      r[u] = ok[u] ? i / kGatherChunks : 0;
+      c[u] = (int)((ok[u] ? i : 0) - r[u] * kGatherChunks);
+      b[u] = ok[u] ? token_to_seq[r[u]] : -1;
+    }
+    // request, logical token and physical page of each row; anything out of range
+    // leaves that chunk zero (no access outside the caller's buffers)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      slot[u] = -1;
+      if (b[u] >= 0 && b[u] < B) {
+        const int64_t j = (int64_t)(seq_starts ? seq_starts[b[u]] : 0) + (r[u] - cu_seq_lens[b[u]]);
+        if (j >= 0 && j < (int64_t)max_pages * kPage) slot[u] = j;
       }
     }
-    *reinterpret_cast<u32x4_t*>(out + r * out_stride + c * 8) = v;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (slot[u] >= 0) {
+        const int id = block_table[(int64_t)b[u] * bt_sb + (slot[u] >> 6)];
+        slot[u] = (id >= 0 && id < num_pages) ? (int64_t)id * kPage + (slot[u] & (kPage - 1)) : -1;
+      }
+    }
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (slot[u] < 0) continue;
+      if constexpr (!FP8) {
+        v[u] = *reinterpret_cast<const u32x4_t*>(pool + slot[u] * kRowBytesBf16 + c[u] * 16);
+      } else {
+        const char* row = pool + slot[u] * kRowBytesFp8;
+        const u32x2_t codes = *reinterpret_cast<const u32x2_t*>(row + c[u] * 8);
+        const float ks = *reinterpret_cast<const float*>(row + kRow);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[u][k] = bf16x2_of_products(codes[k >> 1] >> (16 * (k & 1)), ks);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + 256 * u < n) *reinterpret_cast<u32x4_t*>(out + r[u] * out_stride + c[u] * 8) = v[u];
   }
 }
 
-// One thread per 8 elements of a row; the row's LSE goes out with its first chunk.
+// One thread per 8 elements of a row, kMergeUnroll chunks 256 apart per round (their
+// loads in flight together); the row's LSE goes out with its first chunk.
+constexpr int kMergeUnroll = 4;
+
 __global__ __launch_bounds__(256) void merge_states_kernel(
     const uint16_t* __restrict__ po, const float* __restrict__ plse, const uint16_t* __restrict__ so,
     const float* __restrict__ slse, int64_t T, int32_t N, int32_t D, int64_t o_st, int64_t o_sh,
     int64_t l_st, int64_t l_sh, uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+  constexpr int U = kMergeUnroll;
   const int cpr = D >> 3;                                 // chunks per row
   const int64_t n = T * N * cpr;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t row = i / cpr;
-    const int c = (int)(i - row * cpr);
-    const int64_t t = row / N;
-    const int h = (int)(row - t * N);
-    const float lp = plse[t * l_st + h * l_sh], ls = slse[t * l_st + h * l_sh];
-    const int64_t off = t * o_st + h * o_sh + 8 * c;
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(po + off);
-    const u32x4_t bb = *reinterpret_cast<const u32x4_t*>(so + off);
-    const float m = fmaxf(lp, ls);
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    float lse = -INFINITY;
-    if (m != -INFINITY) {
-      const float wp = expf(lp - m), ws = expf(ls - m);   // exp(-inf) = 0: an empty state weighs nothing
-      const float wsum = wp + ws;
-      const float fp = wp / wsum, fs = ws / wsum;
+  const int64_t step = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n; base += step) {
+    int64_t off[U], loff[U];
+    int c[U];
+    float lp[U], ls[U];
+    u32x4_t a[U], bb[U];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = fp * bf16_bits_to_f32(a[k] & 0xFFFFu) + fs * bf16_bits_to_f32(bb[k] & 0xFFFFu);
-        const float x1 = fp * bf16_bits_to_f32(a[k] >> 16) + fs * bf16_bits_to_f32(bb[k] >> 16);
-        const bf16x2_t p = {(__bf16)x0, (__bf16)x1};
-        v[k] = *reinterpret_cast<const uint32_t*>(&p);
-      }
-      lse = m + logf(wsum);
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + 256 * u < n ? base + 256 * u : n - 1;   // clamped: in bounds, not stored
+      const int64_t row = i / cpr;
+      c[u] = (int)(i - row * cpr);
+      const int64_t t = row / N;
+      const int h = (int)(row - t * N);
+      loff[u] = t * l_st + h * l_sh;
+      off[u] = t * o_st + h * o_sh + 8 * c[u];
+      lp[u] = plse[loff[u]];
+      ls[u] = slse[loff[u]];
+      a[u] = *reinterpret_cast<const u32x4_t*>(po + off[u]);
+      bb[u] = *reinterpret_cast<const u32x4_t*>(so + off[u]);
     }
-    *reinterpret_cast<u32x4_t*>(out + off) = v;
-    if (out_lse && c == 0) out_lse[t * l_st + h * l_sh] = lse;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float m = fmaxf(lp[u], ls[u]);
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      float lse = -INFINITY;
+      if (m != -INFINITY) {
+        const float wp = expf(lp[u] - m), ws = expf(ls[u] - m);   // exp(-inf) = 0: an empty state weighs nothing
+        const float wsum = wp + ws;
+        const float fp = wp / wsum, fs = ws / wsum;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = fp * bf16_bits_to_f32(a[u][k] & 0xFFFFu) + fs * bf16_bits_to_f32(bb[u][k] & 0xFFFFu);
+          const float x1 = fp * bf16_bits_to_f32(a[u][k] >> 16) + fs * bf16_bits_to_f32(bb[u][k] >> 16);
+          const bf16x2_t p = {(__bf16)x0, (__bf16)x1};
+          v[k] = *reinterpret_cast<const uint32_t*>(&p);
+        }
+        lse = m + logf(wsum);
+      }
+      if (base + 256 * u < n) {
+        *reinterpret_cast<u32x4_t*>(out + off[u]) = v;
+        if (out_lse && c[u] == 0) out_lse[loff[u]] = lse;
+      }
+    }
   }
 }
 
@@ -155,7 +205,7 @@ extern "C" mla_status_t mla_gather_cache(const void* kv_cache, int32_t kv_dtype,
   mla_status_t st = device_info(&di);
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const unsigned grid = stream_grid(total_rows * kGatherChunks, di);
+  const unsigned grid = stream_grid((total_rows * kGatherChunks + kGatherUnroll - 1) / kGatherUnroll, di);
   if (kv_dtype == MLA_KV_BF16)
     hipLaunchKernelGGL(gather_cache_kernel<false>, dim3(grid), dim3(256), 0, s, (const char*)kv_cache, num_pages,
                        block_table, bt_stride_b, max_pages_per_seq, cu_seq_lens, seq_starts, token_to_seq, B,
@@ -185,7 +235,7 @@ extern "C" mla_status_t mla_merge_attn_states(const void* prefix_out, const floa
   mla_status_t st = device_info(&di);
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const unsigned grid = stream_grid(T * N * (D >> 3), di);
+  const unsigned grid = stream_grid((T * N * (D >> 3) + kMergeUnroll - 1) / kMergeUnroll, di);
   hipLaunchKernelGGL(merge_states_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)prefix_out, prefix_lse,
                      (const uint16_t*)suffix_out, suffix_lse, T, N, D, o_stride_t, o_stride_h, lse_stride_t,
                      lse_stride_h, (uint16_t*)out, out_lse);
