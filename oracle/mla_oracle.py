@@ -295,6 +295,35 @@ def decode(q: np.ndarray, pool: np.ndarray, kv_dtype: int, block_table: np.ndarr
     return o, lse
 
 
+def decode_varlen(q: np.ndarray, query_start_loc: np.ndarray, pool: np.ndarray, kv_dtype: int,
+                  block_table: np.ndarray, seq_lens: np.ndarray, causal: bool, scale: float,
+                  row_elems: int = ROW_ELEMS, latent: int = KV_LORA_RANK) -> tuple[np.ndarray, np.ndarray]:
+    """Decode with a different number of query tokens per request.
+
+    [vLLM-MLA] §投机解码 (query 不是 1 时) and §Metadata (QueryLenSupport VARLEN):
+    a verification batch mixes requests with 1, 2, 3 ... query tokens; request
+    ``b`` owns query rows ``query_start_loc[b] .. query_start_loc[b+1]-1`` of the
+    flat ``q[T, N, row_elems]``.  Causal blocks: row ``t`` of the block sees
+    ``seq_lens[b] - q_len_b + 1 + t`` tokens (per-row sequence lengths);
+    non-causal draft blocks: every row sees all ``seq_lens[b]`` tokens.
+    Returns ``o[T, N, latent]``, ``lse[T, N]`` (float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T, N, _ = q.shape
+    o = np.zeros((T, N, latent))
+    lse = np.full((T, N), -np.inf)
+    for b in range(len(seq_lens)):
+        r0, r1 = int(query_start_loc[b]), int(query_start_loc[b + 1])
+        n_all = int(seq_lens[b])
+        if r1 <= r0 or n_all <= 0:
+            continue
+        K_all, V_all = row_views(gather_rows(pool, block_table[b], n_all), kv_dtype, row_elems, latent)
+        for t in range(r1 - r0):
+            n = visible_tokens(n_all, r1 - r0, t) if causal else n_all
+            o[r0 + t], lse[r0 + t] = attend(q[r0 + t], K_all[:n], V_all[:n], scale)
+    return o, lse
+
+
 def merge(o_parts: np.ndarray, lse_parts: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Combine attention partials over disjoint token sets (axis 0 = part).
 

@@ -559,3 +559,45 @@ def test_merge_attn_states_of_a_key_split_equals_attention_over_all_keys():
         os_, ls = O.attend(q, K[cut:], V[cut:], O.default_scale())
         o, lse = O.merge_attn_states(op, lp, os_, ls)
         assert np.allclose(o, o_all, atol=1e-12) and np.allclose(lse, l_all, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# variable query lengths (speculative-decoding verification batches)
+# ----------------------------------------------------------------------------
+def _varlen_case(seed, q_lens, seqs, kd=O.KV_BF16):
+    w = MI.make_workload("vl", len(seqs), 1, 4, seqs, None, kd, False, seed)
+    pool = O.encode_rows(w.kv_rows.reshape(-1, 576), kd).reshape(w.num_pages, 64, -1)
+    rng = np.random.default_rng(seed)
+    qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), 4, 576))
+    return w, pool, qsl, q
+
+
+def test_decode_varlen_with_uniform_lengths_is_the_uniform_decode():
+    w, pool, qsl, q = _varlen_case(40, [2, 2, 2], [70, 129, 3])
+    o, lse = O.decode_varlen(q, qsl, pool, w.kv_dtype, w.block_table, w.seq_lens, True, O.default_scale())
+    o2, lse2 = O.decode(q.reshape(3, 2, 4, 576), pool, w.kv_dtype, w.block_table, w.seq_lens, O.default_scale())
+    assert np.array_equal(o, o2.reshape(6, 4, 512)) and np.array_equal(lse, lse2.reshape(6, 4))
+
+
+def test_decode_varlen_rows_are_single_row_decodes_at_their_lengths():
+    """Causal: row t of a q_len-token block is a one-row decode over seq - q_len + 1 + t
+    tokens; non-causal: over all seq tokens.  Brute force per row."""
+    q_lens = [1, 3, 2, 4]
+    w, pool, qsl, q = _varlen_case(41, q_lens, [65, 130, 2, 200])
+    for causal in (True, False):
+        o, lse = O.decode_varlen(q, qsl, pool, w.kv_dtype, w.block_table, w.seq_lens, causal, O.default_scale())
+        for b, ql in enumerate(q_lens):
+            for t in range(ql):
+                r = qsl[b] + t
+                n = max(0, int(w.seq_lens[b]) - ql + 1 + t) if causal else int(w.seq_lens[b])
+                o1, l1 = O.decode(q[r][None, None], pool, w.kv_dtype, w.block_table[b:b + 1],
+                                  np.array([n], np.int32), O.default_scale())
+                assert np.array_equal(o[r], o1[0, 0]) and np.array_equal(lse[r], l1[0, 0])
+    # non-causal: all rows of a block see the same keys, so equal queries give equal rows
+    q2 = q.copy()
+    q2[qsl[3]:qsl[4]] = q2[qsl[3]]
+    o, _ = O.decode_varlen(q2, qsl, pool, w.kv_dtype, w.block_table, w.seq_lens, False, O.default_scale())
+    assert all(np.array_equal(o[qsl[3]], o[r]) for r in range(qsl[3], qsl[4]))
+    oc, _ = O.decode_varlen(q2, qsl, pool, w.kv_dtype, w.block_table, w.seq_lens, True, O.default_scale())
+    assert not np.array_equal(oc[qsl[3]], oc[qsl[4] - 1])
