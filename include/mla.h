@@ -174,6 +174,48 @@ mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_t, i
                         float* lse, void* stream);
 
 /*
+ * mla_decode_varlen_workspace_size -- bytes of workspace mla_decode_varlen needs
+ * for T query rows of N heads, the split mode and the block-table width.
+ * Returns 0 for shapes mla_decode_varlen would reject.  No device call.
+ */
+size_t mla_decode_varlen_workspace_size(int64_t T, int32_t N, int32_t num_splits,
+                                        int32_t max_pages_per_seq);
+
+/*
+ * mla_decode_varlen -- decode with a different number of query tokens per
+ * request ([vLLM-MLA] §投机解码 and §Metadata, QueryLenSupport VARLEN: a
+ * verification batch mixes 1-, 2-, 3-token queries; causal blocks give each row
+ * its own sequence length, non-causal draft blocks give every row the whole
+ * prefix).
+ *
+ *   q                bf16 [T, N, 576] flat query rows, strides (q_stride_t,
+ *                    q_stride_h); request b owns rows query_start_loc[b] ..
+ *                    query_start_loc[b + 1] - 1
+ *   query_start_loc  int32 [B + 1] (device), non-decreasing, [0] = 0, [B] = T
+ *   seq_lens         int32 [B] (device): cached tokens of request b including
+ *                    its query_len new ones
+ *   causal           nonzero: row t of a q-token block sees seq_lens[b] - q + 1 + t
+ *                    tokens; zero: every row sees seq_lens[b] tokens
+ *   out              bf16 [T, N, 512], strides (o_stride_t, o_stride_h)
+ *   lse              float32 [T, N] contiguous
+ *   other arguments  as mla_decode; workspace of mla_decode_varlen_workspace_size()
+ *                    bytes (it holds each row's length and a copy of its request's
+ *                    block-table row, T * max_pages_per_seq int32)
+ *
+ * Each row runs as a one-row decode (same kernels, same split plan and merge),
+ * so a request's pages are read once per query row.  Rows outside every
+ * request's range see no token (o = 0, lse = -inf).  T <= 2^24.
+ */
+mla_status_t mla_decode_varlen(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                               const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                               const int32_t* block_table, int64_t bt_stride_b,
+                               int32_t max_pages_per_seq, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, int32_t B, int64_t T, int32_t N,
+                               int32_t causal, float softmax_scale, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* out,
+                               int64_t o_stride_t, int64_t o_stride_h, float* lse, void* stream);
+
+/*
  * mla_up_v -- per-head V up-projection of the latent attention output
  * ([vLLM-MLA] §两套算法, _v_up_proj: [N, T, L] @ W_UV[N, L, V] written through a
  * transposed view into a token-major [T, N * V] buffer).

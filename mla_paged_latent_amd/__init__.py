@@ -7,7 +7,8 @@ when the caller does not pass them.  There is no CPU fallback: if the library is
 missing, :func:`lib` raises.
 
 The calls mirror ``include/mla.h``: :func:`cache_write`, :func:`absorb_q`,
-:func:`decode` and :func:`up_v`, plus :func:`decode_workspace_size`, and the two
+:func:`decode` and :func:`up_v`, plus :func:`decode_workspace_size`, the
+variable-query-length decode :func:`decode_varlen`, and the two
 steps either side of decode in chunked prefill, :func:`gather_cache` and
 :func:`merge_attn_states`.
 """
@@ -63,6 +64,11 @@ def lib() -> ctypes.CDLL:
     L.mla_decode.restype = i32
     L.mla_up_v.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.mla_up_v.restype = i32
+    L.mla_decode_varlen_workspace_size.argtypes = [i64, i32, i32, i32]
+    L.mla_decode_varlen_workspace_size.restype = ctypes.c_size_t
+    L.mla_decode_varlen.argtypes = [vp, i64, i64, vp, i32, i64, vp, i64, i32, vp, vp, i32, i64, i32, i32,
+                                    ctypes.c_float, i32, vp, ctypes.c_size_t, vp, i64, i64, vp, vp]
+    L.mla_decode_varlen.restype = i32
     L.mla_gather_cache.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp, i32, i64, vp, i64, vp]
     L.mla_gather_cache.restype = i32
     L.mla_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, i32, i64, i64, i64, i64, vp, vp, vp]
@@ -219,3 +225,35 @@ def merge_attn_states(prefix_out: torch.Tensor, prefix_lse: torch.Tensor, suffix
         prefix_out.stride(0), prefix_out.stride(1), prefix_lse.stride(0), prefix_lse.stride(1),
         _ptr(out), _ptr(out_lse), _stream(stream)))
     return out, out_lse
+
+
+def decode_varlen(q: torch.Tensor, query_start_loc: torch.Tensor, kv_cache: torch.Tensor, kv_dtype: int,
+                  block_table: torch.Tensor, seq_lens: torch.Tensor, causal: bool = True,
+                  softmax_scale: float = DEFAULT_SCALE, num_splits: int = 0,
+                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Decode of ``q`` bf16 ``[T, N, 576]`` whose request ``b`` owns rows
+    ``query_start_loc[b] .. query_start_loc[b+1]-1``; returns ``out [T, N, 512]``, ``lse [T, N]``."""
+    T, N, D = q.shape
+    assert D == ROW_ELEMS and q.dtype == torch.bfloat16 and q.stride(-1) == 1
+    assert query_start_loc.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.dtype == torch.int32 and block_table.stride(-1) == 1
+    B = seq_lens.numel()
+    assert query_start_loc.numel() == B + 1
+    num_pages = kv_cache.numel() * kv_cache.element_size() // (PAGE_TOKENS * ROW_BYTES[kv_dtype])
+    if out is None:
+        out = torch.empty((T, N, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, N), dtype=torch.float32, device=q.device)
+    need = int(lib().mla_decode_varlen_workspace_size(T, N, num_splits, block_table.shape[1]))
+    if need == 0:
+        raise MLAError("mla_decode_varlen_workspace_size", 2)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("mla_decode_varlen", lib().mla_decode_varlen(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(kv_cache), kv_dtype, num_pages, _ptr(block_table),
+        block_table.stride(0), block_table.shape[1], _ptr(query_start_loc), _ptr(seq_lens), B, T, N,
+        int(bool(causal)), float(softmax_scale), num_splits, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0), out.stride(1), _ptr(lse),
+        _stream(stream)))
+    return out, lse

@@ -977,21 +977,22 @@ __device__ __forceinline__ void wide_scores(const MLA_LDS char* blk, const bf16x
 // tokens).  Step s: V^T fragment of feature block fb = two transpose reads (tokens
 // 16s + 8hh + 4r + 0..3, r = 0/1, hh = lane >> 5), P^T fragment of row block rb = one
 // 16-byte read of tokens 16s + 8hh .. +7 of row 32rb + (lane & 31).
-__device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS char* pbuf,
-                                        f32x16_t (&o)[4][2], const uint32_t (&vbase)[2][2],
-                                        const uint32_t (&pbase)[2]) {
+// Operands of one PV step (V^T fragments via transpose reads, P^T rows), requested
+// in two token halves so that the loads can be issued ahead of the MFMAs.
+struct WidePvOps {
   uint32_t va_addr[2][2], pa[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int f1 = 0; f1 < 2; ++f1) va_addr[r][f1] = opaque(lds_addr(blk) + vbase[r][f1]);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) pa[s] = opaque(lds_addr(pbuf) + pbase[s]);
-  // all operands of a token half are requested before its MFMAs, the second half's
-  // while the first half's MFMAs run
   bf16x8_t pb[2][2];
   bf16x4_t lo[2][4], hi[2][4];
-  auto load = [&](int s) {
+  __device__ __forceinline__ void init(const MLA_LDS char* blk, const MLA_LDS char* pbuf, const uint32_t (&vbase)[2][2],
+                                       const uint32_t (&pbase)[2]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int f1 = 0; f1 < 2; ++f1) va_addr[r][f1] = opaque(lds_addr(blk) + vbase[r][f1]);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) pa[s] = opaque(lds_addr(pbuf) + pbase[s]);
+  }
+  __device__ __forceinline__ void load(int s) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) pb[s][rb] = lds_read_b128_at(pa[s] + rb * 2048);
 #pragma unroll
@@ -1000,19 +1001,24 @@ __device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS c
       lo[s][fb] = lds_read_tr16_at(va_addr[0][fb & 1] + off);
       hi[s][fb] = lds_read_tr16_at(va_addr[1][fb & 1] + off);
     }
-  };
-  load(0);
+  }
+};
+
+// O^T += V^T . P^T for one block.  The first token half's operands were requested by
+// the caller (ops.load(0)); the second half's are requested while the first half's
+// MFMAs run.
+__device__ __forceinline__ void wide_pv_mfma(WidePvOps& ops, f32x16_t (&o)[4][2]) {
   __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
-  load(1);
+  ops.load(1);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-      const bf16x8_t va = {lo[s][fb][0], lo[s][fb][1], lo[s][fb][2], lo[s][fb][3],
-                           hi[s][fb][0], hi[s][fb][1], hi[s][fb][2], hi[s][fb][3]};
+      const bf16x8_t va = {ops.lo[s][fb][0], ops.lo[s][fb][1], ops.lo[s][fb][2], ops.lo[s][fb][3],
+                           ops.hi[s][fb][0], ops.hi[s][fb][1], ops.hi[s][fb][2], ops.hi[s][fb][3]};
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s][rb], o[fb][rb], 0, 0, 0);
+        o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, ops.pb[s][rb], o[fb][rb], 0, 0, 0);
         if (s == 0) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (fb * 2 + rb < 5) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -1020,6 +1026,15 @@ __device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS c
       }
     }
   }
+}
+
+__device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS char* pbuf,
+                                        f32x16_t (&o)[4][2], const uint32_t (&vbase)[2][2],
+                                        const uint32_t (&pbase)[2]) {
+  WidePvOps ops;
+  ops.init(blk, pbuf, vbase, pbase);
+  ops.load(0);
+  wide_pv_mfma(ops, o);
 }
 
 // ---- fp8 rows read in place (wide variant) ----
@@ -1694,6 +1709,62 @@ inline WsLayout ws_layout(int32_t B, const Shape& s) {
   return w;
 }
 
+
+// Launches the decode kernels (and the merge) for filled-in parameters: the plan's
+// stream and unit counts, the 32/64-bit plan variant, the kernel variant.
+static mla_status_t decode_launch(DecodeParams p, const Shape& s, int32_t kv_dtype, int32_t num_splits,
+                                  int32_t B, int32_t max_pages_per_seq, const DeviceInfo& di,
+                                  hipStream_t hs) {
+  // One workgroup (256 threads, most of the LDS) per CU.  Automatic plan: one
+  // stream per workgroup and head group, so every unit runs concurrently; with
+  // several head groups the stream count is a multiple of 8 (sibling order).
+  const int64_t cus = ((int64_t)di.cu_count + 7) / 8 * 8;
+  int64_t streams;
+  if (num_splits == 0) {
+    streams = s.n_hg == 1 ? cus : cus / (8 * s.n_hg) * 8;
+    if (streams < 8) streams = 8;
+    if (streams > MLA_AUTO_MAX_EXTRA_PAIRS) streams = MLA_AUTO_MAX_EXTRA_PAIRS;
+  } else {
+    streams = (int64_t)B * num_splits;
+  }
+  const int64_t units = s.n_hg == 1 ? streams : (streams + 7) / 8 * 8 * s.n_hg;
+  if (units > (int64_t)1 << 30) return MLA_ERR_SHAPE;
+  p.n_streams = (int32_t)streams;
+  p.n_units = (int32_t)units;
+  int64_t grid = cus < units ? cus : units;
+  if (grid < 1) grid = 1;
+
+  // The automatic plan's products fit in 32 bits when total * (streams + 1) and
+  // len * pages do (total <= B * (overhead + block-table width), len <= overhead + width);
+  // only batches beyond that bound run the kernels with 64-bit plan arithmetic.
+  const uint64_t stretch = (uint64_t)kSegOverhead + (uint64_t)max_pages_per_seq;
+  const bool p64 = num_splits == 0 && ((uint64_t)B * stretch > 0xFFFFFFFFull / (uint64_t)(streams + 1) ||
+                                       stretch * (uint64_t)max_pages_per_seq > 0xFFFFFFFFull);
+  const dim3 g((unsigned)grid), blk(256);
+  if (kv_dtype == MLA_KV_BF16) {
+    if (p64) {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, true>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<false, true>), g, blk, 0, hs, p);
+    } else {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, false>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<false, false>), g, blk, 0, hs, p);
+    }
+  } else {
+    if (p64) {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true, true>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<true, true>), g, blk, 0, hs, p);
+    } else {
+      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true, false>), g, blk, 0, hs, p);
+      else hipLaunchKernelGGL((decode_narrow_kernel<true, false>), g, blk, 0, hs, p);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  if (num_splits != 1) {
+    dim3 mg((unsigned)(B * s.n_hg), (unsigned)((s.m_wg + 3) / 4));
+    hipLaunchKernelGGL(merge_kernel, mg, dim3(256), 0, hs, p);
+  }
+  return launch_status();
+}
 }  // namespace mla
 
 extern "C" size_t mla_decode_workspace_size(int32_t B, int32_t q_len, int32_t N, int32_t num_splits) {
@@ -1762,54 +1833,144 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   p.num_splits = num_splits;
   p.max_slots = s.max_slots;
-  // One workgroup (256 threads, most of the LDS) per CU.  Automatic plan: one
-  // stream per workgroup and head group, so every unit runs concurrently; with
-  // several head groups the stream count is a multiple of 8 (sibling order).
-  const int64_t cus = ((int64_t)di.cu_count + 7) / 8 * 8;
-  int64_t streams;
-  if (num_splits == 0) {
-    streams = s.n_hg == 1 ? cus : cus / (8 * s.n_hg) * 8;
-    if (streams < 8) streams = 8;
-    if (streams > MLA_AUTO_MAX_EXTRA_PAIRS) streams = MLA_AUTO_MAX_EXTRA_PAIRS;
-  } else {
-    streams = (int64_t)B * num_splits;
-  }
-  const int64_t units = s.n_hg == 1 ? streams : (streams + 7) / 8 * 8 * s.n_hg;
-  if (units > (int64_t)1 << 30) return MLA_ERR_SHAPE;
-  p.n_streams = (int32_t)streams;
-  p.n_units = (int32_t)units;
-  int64_t grid = cus < units ? cus : units;
-  if (grid < 1) grid = 1;
+  return decode_launch(p, s, kv_dtype, num_splits, B, max_pages_per_seq, di,
+                       reinterpret_cast<hipStream_t>(stream));
+}
 
-  // The automatic plan's products fit in 32 bits when total * (streams + 1) and
-  // len * pages do (total <= B * (overhead + block-table width), len <= overhead + width);
-  // only batches beyond that bound run the kernels with 64-bit plan arithmetic.
-  const uint64_t stretch = (uint64_t)kSegOverhead + (uint64_t)max_pages_per_seq;
-  const bool p64 = num_splits == 0 && ((uint64_t)B * stretch > 0xFFFFFFFFull / (uint64_t)(streams + 1) ||
-                                       stretch * (uint64_t)max_pages_per_seq > 0xFFFFFFFFull);
+// ---------------------------------------------------------------------------
+// Variable query lengths ([vLLM-MLA] §投机解码 and §Metadata, QueryLenSupport
+// VARLEN: a verification batch mixes requests with 1, 2, 3 ... query tokens;
+// causal blocks give row t of a q_len-token block seq_len - q_len + 1 + t visible
+// tokens, non-causal draft blocks give every row all of them).  Each query row
+// becomes a one-row request with its own length and a copy of its request's
+// block-table row (in the workspace), and runs through the same decode kernels.
+// ---------------------------------------------------------------------------
+namespace mla {
+
+struct VarlenLayout {
+  size_t decode, seq, bt, total;
+};
+
+inline VarlenLayout varlen_layout(int64_t T, const Shape& s, int32_t max_pages) {
+  VarlenLayout v;
+  v.decode = 0;
+  size_t off = ws_layout((int32_t)T, s).total;
+  v.seq = off;
+  off = align256(off + (size_t)T * sizeof(int32_t));
+  v.bt = off;
+  off = align256(off + (size_t)T * (size_t)max_pages * sizeof(int32_t));
+  v.total = off;
+  return v;
+}
+
+// Row r of the flat query: its request (binary search of query_start_loc), its
+// visible length, and its request's block-table entries up to that length.
+__global__ __launch_bounds__(256) void varlen_expand_kernel(const int32_t* __restrict__ qsl,
+                                                            const int32_t* __restrict__ seq_lens, int32_t B,
+                                                            int64_t T, int32_t causal,
+                                                            const int32_t* __restrict__ bt, int64_t bt_sb,
+                                                            int32_t max_pages, int32_t* __restrict__ seq_out,
+                                                            int32_t* __restrict__ bt_out) {
+  const int64_t r = blockIdx.x;
+  if (r >= T) return;
+  // largest b with qsl[b] <= r (qsl non-decreasing, qsl[0] = 0)
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int64_t r0 = qsl[b], r1 = qsl[b + 1];
+  int seq = 0;
+  if (r >= r0 && r < r1) {
+    const int64_t s = seq_lens[b] < 0 ? 0 : seq_lens[b];
+    const int64_t n = causal ? s - (r1 - r0) + 1 + (r - r0) : s;
+    const int64_t cap = (int64_t)max_pages * kPage;
+    seq = (int)(n < 0 ? 0 : (n > cap ? cap : n));
+  }
+  if (threadIdx.x == 0) seq_out[r] = seq;
+  const int pages = (seq + kPage - 1) / kPage;
+  for (int pg = threadIdx.x; pg < pages; pg += 256) bt_out[r * max_pages + pg] = bt[(int64_t)b * bt_sb + pg];
+}
+
+}  // namespace mla
+
+extern "C" size_t mla_decode_varlen_workspace_size(int64_t T, int32_t N, int32_t num_splits,
+                                                   int32_t max_pages_per_seq) {
+  mla::Shape s;
+  if (T < 1 || T > (1 << 24) || max_pages_per_seq < 1) return 0;
+  if (max_pages_per_seq > mla::kMaxPagesPerSeq) max_pages_per_seq = mla::kMaxPagesPerSeq;
+  if (!mla::decode_shape((int32_t)T, 1, N, num_splits, &s)) return 0;
+  return mla::varlen_layout(T, s, max_pages_per_seq).total;
+}
+
+extern "C" mla_status_t mla_decode_varlen(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                                          const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                                          const int32_t* block_table, int64_t bt_stride_b,
+                                          int32_t max_pages_per_seq, const int32_t* query_start_loc,
+                                          const int32_t* seq_lens, int32_t B, int64_t T, int32_t N,
+                                          int32_t causal, float softmax_scale, int32_t num_splits,
+                                          void* workspace, size_t workspace_bytes, void* out,
+                                          int64_t o_stride_t, int64_t o_stride_h, float* lse, void* stream) {
+  using namespace mla;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_DTYPE;
+  if (T < 1 || T > (1 << 24) || B < 1) return MLA_ERR_SHAPE;
+  Shape s;
+  if (!decode_shape((int32_t)T, 1, N, num_splits, &s)) return MLA_ERR_SHAPE;
+  if (num_pages < 1 || max_pages_per_seq < 1 || bt_stride_b < max_pages_per_seq) return MLA_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || !__builtin_isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+  if (!q || !kv_cache || !block_table || !query_start_loc || !seq_lens || !out || !lse) return MLA_ERR_NULL;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || !mult8(q_stride_t) || !mult8(q_stride_h) ||
+      !mult8(o_stride_t) || !mult8(o_stride_h) || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(query_start_loc) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return MLA_ERR_ALIGN;
+  if (max_pages_per_seq > kMaxPagesPerSeq) max_pages_per_seq = kMaxPagesPerSeq;
+  const VarlenLayout vl = varlen_layout(T, s, max_pages_per_seq);
+  if (workspace_bytes < vl.total) return MLA_ERR_WORKSPACE;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* seq_x = reinterpret_cast<int32_t*>(ws + vl.seq);
+  int32_t* bt_x = reinterpret_cast<int32_t*>(ws + vl.bt);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const dim3 g((unsigned)grid), blk(256);
-  if (kv_dtype == MLA_KV_BF16) {
-    if (p64) {
-      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, true>), g, blk, 0, hs, p);
-      else hipLaunchKernelGGL((decode_narrow_kernel<false, true>), g, blk, 0, hs, p);
-    } else {
-      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, false>), g, blk, 0, hs, p);
-      else hipLaunchKernelGGL((decode_narrow_kernel<false, false>), g, blk, 0, hs, p);
-    }
-  } else {
-    if (p64) {
-      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true, true>), g, blk, 0, hs, p);
-      else hipLaunchKernelGGL((decode_narrow_kernel<true, true>), g, blk, 0, hs, p);
-    } else {
-      if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<true, false>), g, blk, 0, hs, p);
-      else hipLaunchKernelGGL((decode_narrow_kernel<true, false>), g, blk, 0, hs, p);
-    }
-  }
+  hipLaunchKernelGGL(varlen_expand_kernel, dim3((unsigned)T), dim3(256), 0, hs, query_start_loc, seq_lens, B, T,
+                     causal, block_table, bt_stride_b, max_pages_per_seq, seq_x, bt_x);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-  if (num_splits != 1) {
-    dim3 mg((unsigned)(B * s.n_hg), (unsigned)((s.m_wg + 3) / 4));
-    hipLaunchKernelGGL(merge_kernel, mg, dim3(256), 0, hs, p);
-  }
-  return launch_status();
+
+  const WsLayout wl = ws_layout((int32_t)T, s);
+  DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_sb = q_stride_t;
+  p.q_st = 0;
+  p.q_sh = q_stride_h;
+  p.kv = static_cast<const char*>(kv_cache);
+  p.num_pages = num_pages;
+  p.block_table = bt_x;
+  p.bt_sb = max_pages_per_seq;
+  p.max_pages = max_pages_per_seq;
+  p.seq_lens = seq_x;
+  p.B = (int32_t)T;
+  p.q_len = 1;
+  p.N = N;
+  p.n_hg = s.n_hg;
+  p.m_wg = s.m_wg;
+  p.hg_heads = s.hg_heads;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.out = static_cast<uint16_t*>(out);
+  p.o_sb = o_stride_t;
+  p.o_st = 0;
+  p.o_sh = o_stride_h;
+  p.lse = lse;
+  p.req = reinterpret_cast<int4*>(ws + wl.req);
+  p.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
+  p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
+  p.num_splits = num_splits;
+  p.max_slots = s.max_slots;
+  return decode_launch(p, s, kv_dtype, num_splits, (int32_t)T, max_pages_per_seq, di, hs);
 }

@@ -127,3 +127,21 @@ def test_context_calls_reject_bad_arguments_without_a_gpu():
     assert m(T=0) == 0
     assert m(po=None) == 1 and m(out=None) == 1
     assert m(so=vp(264)) == 4 and m(osh=60) == 4 and m(pl=vp(258)) == 4
+
+
+def test_varlen_call_rejects_bad_arguments_without_a_gpu():
+    L = M.lib()
+    vp = ctypes.c_void_p
+    ok = vp(256)
+    ws = L.mla_decode_varlen_workspace_size
+    assert ws(0, 16, 0, 8) == 0 and ws(1 << 25, 16, 0, 8) == 0 and ws(4, 129, 0, 8) == 0 and ws(4, 16, 0, 0) == 0
+    assert ws(4, 16, 0, 8) > 0 and ws(4, 16, 0, 800) > ws(4, 16, 0, 8)      # holds a block-table copy
+    need = ws(4, 16, 0, 8)
+    d = lambda **o: L.mla_decode_varlen(*[o.get(k, v) for k, v in dict(
+        q=ok, qst=9216, qsh=576, kv=ok, kd=0, pages=4, bt=ok, btsb=8, maxp=8, qsl=ok, sl=ok, B=2, T=4, N=16,
+        causal=1, scale=0.07, ns=0, ws=ok, wsb=need, out=ok, ost=8192, osh=512, lse=ok, stream=None).items()])
+    assert d(kd=5) == 3
+    assert d(T=0) == 2 and d(B=0) == 2 and d(N=0) == 2 and d(btsb=7) == 2 and d(scale=0.0) == 2
+    assert d(qsl=None) == 1 and d(lse=None) == 1
+    assert d(ws=None) == 5 and d(wsb=need - 1) == 5
+    assert d(q=vp(264)) == 4 and d(qst=9220) == 4 and d(qsl=vp(258)) == 4 and d(ws=vp(512 + 16)) == 4
