@@ -10,7 +10,7 @@ step's pages to the next.
 
 Prints ONE JSON line (stdout).  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
-    python bench.py --op gather_fp8|gather_bf16|merge_states   (the calls either side of decode)
+    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec   (the other calls)
 """
 
 from __future__ import annotations
@@ -76,15 +76,20 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w: MI.Workload, budget_s: float = 12.0) -> dict:
-    """The oracle (float64 NumPy) running the same step on this host's cores."""
-    from oracle import mla_oracle as O
+def host_cores() -> int:
+    """Threads the oracle's NumPy/BLAS work can use on this host."""
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    cores = min(len(os.sched_getaffinity(0)), blas)
+    return min(len(os.sched_getaffinity(0)), blas)
+
+
+def cpu_baseline(w: MI.Workload, budget_s: float = 12.0) -> dict:
+    """The oracle (float64 NumPy) running the same step on this host's cores."""
+    from oracle import mla_oracle as O
+    cores = host_cores()
     kd = w.kv_dtype
     pool = O.encode_rows(w.kv_rows.reshape(-1, 576), kd).reshape(w.num_pages, 64, -1)
     T = w.B * w.q_len
@@ -345,6 +350,9 @@ CONTEXT_OPS = {
     # merging the context and new-token states of an 8192-token prefill, 128 heads,
     # v_head_dim 128
     "merge_states": dict(kind="merge", T=8192, N=128, D=128),
+    # a speculative-decoding verification batch: 64 requests of 4096 cached tokens
+    # with 1, 2 or 3 query tokens each (causal blocks), 128 heads, bf16 cache
+    "varlen_spec": dict(kind="varlen", B=64, seq=4096, N=128, q_lens=(1, 2, 3)),
 }
 
 
@@ -394,6 +402,45 @@ def run_context_op(args) -> dict:
                 f"to bf16, random page placement, {R} rotating pool copies")
         metric = "context gather GB/s (% of HBM roofline), 1 MI355X"
         dtype = "fp8->bf16" if kd == MI.KV_FP8 else "bf16"
+    elif op["kind"] == "varlen":
+        B, N, seq = op["B"], op["N"], op["seq"]
+        rng = np.random.default_rng(530)
+        q_lens = rng.choice(op["q_lens"], size=B)
+        qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        T = int(qsl[-1])
+        w = MI.make_workload("varlen", B, 1, N, [seq] * B, None, MI.KV_BF16, False, 531, min_pool=8192)
+        rb = 1152
+        R = max(2, math.ceil(3 * MALL_BYTES / (w.num_pages * 64 * rb)))
+        rows = torch.from_numpy(np.ascontiguousarray(w.kv_rows.reshape(-1, 576)).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        slots = torch.arange(w.num_pages * 64, device=dev)
+        pools = []
+        for _ in range(R):
+            pl = torch.empty((w.num_pages, 64, rb), dtype=torch.uint8, device=dev)
+            M.cache_write(rows[:, :512], rows[:, 512:], slots, pl, MI.KV_BF16)
+            pools.append(pl)
+        del rows
+        q = torch.randn(T, N, 576, device=dev).to(torch.bfloat16)
+        bt = torch.from_numpy(w.block_table).to(dev)
+        sl = torch.from_numpy(w.seq_lens).to(dev)
+        tq = torch.from_numpy(qsl).to(dev)
+        out = torch.empty((T, N, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(int(L.mla_decode_varlen_workspace_size(T, N, 0, bt.shape[1])), dtype=torch.uint8,
+                         device=dev)
+        calls = [(q.data_ptr(), q.stride(0), q.stride(1), pools[i].data_ptr(), MI.KV_BF16, w.num_pages,
+                  bt.data_ptr(), bt.stride(0), bt.shape[1], tq.data_ptr(), sl.data_ptr(), B, T, N, 1,
+                  float(M.DEFAULT_SCALE), 0, ws.data_ptr(), ws.numel(), out.data_ptr(), out.stride(0),
+                  out.stride(1), lse.data_ptr(), stream) for i in range(R)]
+        f = L.mla_decode_varlen
+        pages = B * ((seq + 63) // 64)
+        bytes_alg = B * seq * rb + T * N * (1152 + 1024 + 4) + pages * 4 + B * 8
+        vis = sum(max(0, seq - int(ql) + 1 + t) for ql in q_lens for t in range(int(ql)))
+        flops_alg = float(vis) * N * (2 * 576 + 2 * 512)
+        desc = (f"{args.op}: B={B} requests x {seq} cached tokens, query tokens per request drawn from "
+                f"{list(op['q_lens'])} (T={T} rows, causal), {N} heads, bf16 cache, {R} rotating pool copies")
+        metric = "variable-length MLA decode GB/s (roofline: the binding one of HBM / bf16 MFMA), 1 MI355X"
+        dtype = "bf16"
     else:
         T, N, D = op["T"], op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=510)
@@ -422,12 +469,20 @@ def run_context_op(args) -> dict:
     mean_ms = e0.elapsed_time(e1) / args.steps
     gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
     log(f"[bench] {args.op}: {mean_ms * 1e3:.1f} us per call, {gbs:.0f} GB/s")
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if op["kind"] == "varlen" and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
+        tfs = flops_alg / (mean_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+    roof.update({"traffic": None, "kernel": args.op, "algorithmic_bytes": bytes_alg,
+                 "mean_launch_us": round(mean_ms * 1e3, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    if op["kind"] == "varlen":
+        roof["algorithmic_flops"] = flops_alg
     res = {"metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": {"workload": desc},
-           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": args.op,
-                        "algorithmic_bytes": bytes_alg, "mean_launch_us": round(mean_ms * 1e3, 2)}}
+           "roofline": roof}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_context(args.op)
     return res
@@ -451,6 +506,19 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         rb = 1152 if op["kv"] == MI.KV_BF16 else 584
         per_item = rb + 1152 + 4
         sample = f"{c.total} rows (8 requests x 256 tokens) through the oracle gather"
+    elif op["kind"] == "varlen":
+        B, N, seq = 4, op["N"], 1024
+        w = MI.make_workload("varlen", B, 1, N, [seq] * B, None, MI.KV_BF16, False, 532)
+        pool = O.encode_rows(w.kv_rows.reshape(-1, 576), MI.KV_BF16).reshape(w.num_pages, 64, -1)
+        qsl = np.array([0, 1, 3, 6, 8], np.int32)
+        q = np.random.default_rng(533).standard_normal((8, N, 576))
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            O.decode_varlen(q, qsl, pool, MI.KV_BF16, w.block_table, w.seq_lens, True, O.default_scale())
+            times.append(time.perf_counter() - t0)
+        n_items = 1
+        per_item = B * seq * 1152 + 8 * N * (1152 + 1024 + 4)
+        sample = f"{B} requests x {seq} tokens, 8 query rows, {N} heads through the oracle varlen decode"
     else:
         T, N, D = 256, op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=522)
@@ -463,7 +531,7 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         per_item = 3 * D * 2 + 3 * 4
         sample = f"{T} query rows x {N} heads x D={D} through the oracle merge"
     mean = sum(times) / len(times)
-    return {"value": round(n_items * per_item / mean / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(n_items * per_item / mean / 1e9, 3), "unit": "GB/s", "cores": host_cores(), "kind": "oracle",
             "sample": f"{sample}, {len(times)} repetition(s), mean {mean:.3f} s"}
 
 
@@ -475,8 +543,8 @@ def main():
     ap.add_argument("--workload", default="full_head", choices=sorted(MI.CONFIGS))
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--op", default="step", choices=["step"] + sorted(CONTEXT_OPS),
-                    help="step: the decode step (default); the others time one of the two calls either "
-                         "side of decode (context gather, state merge) on their own workload")
+                    help="step: the decode step (default); the others time one other call on its own "
+                         "workload (context gather, state merge, variable-length decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
