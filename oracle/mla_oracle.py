@@ -438,6 +438,28 @@ def merge_attn_states(prefix_o: np.ndarray, prefix_lse: np.ndarray, suffix_o: np
                  np.stack([np.asarray(prefix_lse, np.float64), np.asarray(suffix_lse, np.float64)]))
 
 
+def quantize_groups_fp8(y_bits: np.ndarray, group: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token-group fp8 quantization of a bf16 output ``[T, C]`` (C % group == 0).
+
+    [vLLM-MLA] §QuantKey: when the layer after MLA wants fp8, the W_UV output is
+    quantized dynamically in groups of 128 or 64 consecutive elements of a token,
+    one float32 scale per group (kFp8Dynamic128Sym / kFp8Dynamic64Sym).  The
+    pages do not give the scale rule; the cache write's rule is used (as in
+    :func:`fp8_quantize_row`): ``s = amax / 448`` (float32), ``s = 1`` for an
+    all-zero group, ``code = e4m3(x / s)`` with a float32 division.  Returns
+    ``codes uint8 [T, C]`` and ``scales float32 [T, C // group]``.
+    """
+    y = np.asarray(y_bits, dtype=np.uint16)
+    T, C = y.shape
+    assert C % group == 0
+    xf = bf16_bits_to_f64(y).astype(np.float32).reshape(T, C // group, group)
+    amax = np.max(np.abs(xf), axis=2)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    q = (xf / s[:, :, None]).astype(np.float32)
+    return e4m3_encode(q).reshape(T, C), s
+
+
 # --- the un-absorbed oracle --------------------------------------------------
 def mla_unabsorbed(q_nope: np.ndarray, q_pe: np.ndarray, pool: np.ndarray, kv_dtype: int,
                    block_table: np.ndarray, seq_lens: np.ndarray, w_uk_t: np.ndarray,

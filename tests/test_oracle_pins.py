@@ -601,3 +601,45 @@ def test_decode_varlen_rows_are_single_row_decodes_at_their_lengths():
     assert all(np.array_equal(o[qsl[3]], o[r]) for r in range(qsl[3], qsl[4]))
     oc, _ = O.decode_varlen(q2, qsl, pool, w.kv_dtype, w.block_table, w.seq_lens, True, O.default_scale())
     assert not np.array_equal(oc[qsl[3]], oc[qsl[4] - 1])
+
+
+# ----------------------------------------------------------------------------
+# per-token-group fp8 quantization of the up-projected output
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("group", [64, 128])
+def test_quantize_groups_fp8_properties(group):
+    rng = np.random.default_rng(50)
+    T, C = 6, 512
+    y = MI.to_bf16_bits((rng.standard_normal((T, C)) * 10.0 ** rng.integers(-3, 3, (T, 1))).astype(np.float32))
+    y[2, :group] = 0                                       # an all-zero group: scale 1, codes 0
+    codes, s = O.quantize_groups_fp8(y, group)
+    assert codes.shape == (T, C) and s.shape == (T, C // group) and s.dtype == np.float32
+    x = O.bf16_bits_to_f64(y).reshape(T, C // group, group)
+    c = codes.reshape(T, C // group, group)
+    assert s[2, 0] == 1.0 and np.all(c[2, 0] == 0)
+    for t in range(T):
+        for g in range(C // group):
+            if s[t, g] == 1.0 and np.all(x[t, g] == 0):
+                continue
+            # each group's largest magnitude becomes +-448 (code 0x7E / 0xFE) ...
+            k = np.argmax(np.abs(x[t, g]))
+            assert (c[t, g, k] & 0x7F) == 0x7E and (c[t, g, k] >> 7) == (x[t, g, k] < 0)
+            assert s[t, g] == np.float32(np.float32(np.max(np.abs(x[t, g]))) / np.float32(448.0))
+    # ... and dequantization is within half an e4m3 step of every value (relative 2^-4 above 2^-6 s)
+    deq = O.e4m3_value(codes).reshape(T, C // group, group) * s[:, :, None]
+    err = np.abs(deq - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0**-4, 2.0**-10 * s[:, :, None]) * (1 + 1e-6))
+
+
+def test_quantize_groups_fp8_matches_torch_cast_and_group_boundaries():
+    """Codes equal torch's float8_e4m3fn cast of x / s; groups are consecutive elements."""
+    rng = np.random.default_rng(51)
+    T, C, group = 4, 256, 64
+    y = MI.to_bf16_bits(rng.standard_normal((T, C)).astype(np.float32))
+    y[:, 64:128] = MI.to_bf16_bits(rng.standard_normal((T, 64)).astype(np.float32) * 1000)   # a loud group
+    codes, s = O.quantize_groups_fp8(y, group)
+    xf = torch.from_numpy(O.bf16_bits_to_f64(y).astype(np.float32))
+    st = torch.from_numpy(np.repeat(s, group, axis=1))
+    ref = (xf / st).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    assert np.all(s[:, 1] > 100 * s[:, 0]) and np.all(s[:, 1] > 100 * s[:, 2])
