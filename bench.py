@@ -10,7 +10,7 @@ step's pages to the next.
 
 Prints ONE JSON line (stdout).  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
-    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec   (the other calls)
+    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill
 """
 
 from __future__ import annotations
@@ -353,16 +353,23 @@ CONTEXT_OPS = {
     # a speculative-decoding verification batch: 64 requests of 4096 cached tokens
     # with 1, 2 or 3 query tokens each (causal blocks), 128 heads, bf16 cache
     "varlen_spec": dict(kind="varlen", B=64, seq=4096, N=128, q_lens=(1, 2, 3)),
+    # V up-projection with fp8 output in groups of 128: a 128-request decode batch
+    # and an 8192-token prefill, 128 heads
+    "upv_fp8_decode": dict(kind="upv", T=128, N=128, group=128),
+    "upv_fp8_prefill": dict(kind="upv", T=8192, N=128, group=128),
 }
 
 
 def run_context_op(args) -> dict:
-    """One launch of mla_gather_cache or mla_merge_attn_states, timed back to back.
+    """One launch of mla_gather_cache, mla_merge_attn_states, mla_decode_varlen or
+    mla_up_v_fp8, timed back to back.
 
     Algorithmic bytes: gather reads each source row (1152 or 584 B) and writes a
     1152 B bf16 row, plus 4 B of token_to_seq per row, 4 B per block-table entry
     and 12 B per request; merge reads two bf16 states and two LSEs and writes one
-    of each.  The bound is HBM (no arithmetic to speak of).
+    of each.  The bound is HBM (no arithmetic to speak of).  mla_up_v_fp8 reads
+    W_UV and o_lat once and writes one code byte per output plus a float32 scale
+    per group; at 113 flops per byte it sits below the bf16 MFMA ridge, so HBM.
     """
     import ctypes
     import torch
@@ -441,6 +448,30 @@ def run_context_op(args) -> dict:
                 f"{list(op['q_lens'])} (T={T} rows, causal), {N} heads, bf16 cache, {R} rotating pool copies")
         metric = "variable-length MLA decode GB/s (roofline: the binding one of HBM / bf16 MFMA), 1 MI355X"
         dtype = "bf16"
+    elif op["kind"] == "upv":
+        T, N, G = op["T"], op["N"], op["group"]
+        per_copy = N * 512 * 128 * 2 + T * N * 512 * 2
+        R = max(2, math.ceil(3 * MALL_BYTES / per_copy))
+        gen = torch.Generator(device=dev).manual_seed(540)
+        ws = [(torch.randn(N, 512, 128, device=dev, generator=gen) / math.sqrt(512)).to(torch.bfloat16)
+              for _ in range(R)]
+        ols = [torch.randn(T, N, 512, device=dev, generator=gen).to(torch.bfloat16) for _ in range(R)]
+        codes = torch.empty((T, N * 128), dtype=torch.uint8, device=dev)
+        scales = torch.empty((T, N * 128 // G), dtype=torch.float32, device=dev)
+        calls = [(ols[i].data_ptr(), ols[i].stride(0), ols[i].stride(1), ws[i].data_ptr(), T, N, G,
+                  codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), stream)
+                 for i in range(R)]
+        f = L.mla_up_v_fp8
+        bytes_alg = per_copy + T * N * 128 + T * N * 128 // G * 4
+        flops_alg = 2.0 * T * N * 512 * 128
+        # the bf16-output call on the same inputs, for comparison
+        yb = torch.empty((T, N * 128), dtype=torch.bfloat16, device=dev)
+        ref_calls = [(ols[i].data_ptr(), ols[i].stride(0), ols[i].stride(1), ws[i].data_ptr(), T, N,
+                      yb.data_ptr(), yb.stride(0), stream) for i in range(R)]
+        desc = (f"{args.op}: T={T} tokens x {N} heads, o_lat [T, N, 512] . W_UV [N, 512, 128] -> fp8 "
+                f"e4m3 codes + float32 scales per group of {G}, {R} rotating input copies")
+        metric = "V up-projection with fp8 group-quantized output GB/s (% of HBM roofline), 1 MI355X"
+        dtype = "bf16->fp8"
     else:
         T, N, D = op["T"], op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=510)
@@ -469,6 +500,17 @@ def run_context_op(args) -> dict:
     mean_ms = e0.elapsed_time(e1) / args.steps
     gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
     log(f"[bench] {args.op}: {mean_ms * 1e3:.1f} us per call, {gbs:.0f} GB/s")
+    bf16_out_us = None
+    if op["kind"] == "upv":
+        for i in range(3):
+            L.mla_up_v(*ref_calls[i % len(ref_calls)])
+        e0.record()
+        for i in range(args.steps):
+            L.mla_up_v(*ref_calls[i % len(ref_calls)])
+        e1.record()
+        torch.cuda.synchronize()
+        bf16_out_us = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+        log(f"[bench] mla_up_v (bf16 output) on the same inputs: {bf16_out_us:.1f} us per call")
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
     if op["kind"] == "varlen" and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
@@ -477,8 +519,10 @@ def run_context_op(args) -> dict:
                 "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof.update({"traffic": None, "kernel": args.op, "algorithmic_bytes": bytes_alg,
                  "mean_launch_us": round(mean_ms * 1e3, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-    if op["kind"] == "varlen":
+    if op["kind"] in ("varlen", "upv"):
         roof["algorithmic_flops"] = flops_alg
+    if bf16_out_us is not None:
+        roof["bf16_output_call_us"] = bf16_out_us
     res = {"metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": {"workload": desc},
@@ -519,6 +563,19 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         n_items = 1
         per_item = B * seq * 1152 + 8 * N * (1152 + 1024 + 4)
         sample = f"{B} requests x {seq} tokens, 8 query rows, {N} heads through the oracle varlen decode"
+    elif op["kind"] == "upv":
+        T, N, G = 32, op["N"], op["group"]
+        rng = np.random.default_rng(541)
+        ol = O.bf16_bits_to_f64(MI.to_bf16_bits(rng.standard_normal((T, N, 512)).astype(np.float32)))
+        wv = O.bf16_bits_to_f64(MI.to_bf16_bits((rng.standard_normal((N, 512, 128)) / np.sqrt(512)).astype(np.float32)))
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            y = O.f64_to_bf16_bits(O.up_v(ol, wv).reshape(T, N * 128))
+            O.quantize_groups_fp8(y, G)
+            times.append(time.perf_counter() - t0)
+        n_items = 1
+        per_item = N * 512 * 128 * 2 + T * N * (512 * 2 + 128 + 128 // G * 4)
+        sample = f"T={T} tokens x {N} heads through the oracle up_v and group quantizer"
     else:
         T, N, D = 256, op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=522)

@@ -232,6 +232,30 @@ mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t ol_stride_
                       void* out, int64_t out_stride_t, void* stream);
 
 /*
+ * mla_up_v_fp8 -- mla_up_v with its output quantized to fp8 per token group
+ * ([vLLM-MLA] §QuantKey: when the next layer takes fp8 input, the W_UV output is
+ * quantized dynamically in groups of 128 or 64 consecutive elements of a token,
+ * one float32 scale per group).
+ *
+ *   o_lat, w_uv  as mla_up_v
+ *   group        64 or 128
+ *   out_codes    uint8 [T, N * 128] e4m3fn codes, row stride codes_stride_t bytes
+ *                (>= N * 128, multiple of 8; 8-byte aligned)
+ *   out_scales   float32 [T, N * 128 / group], row stride scales_stride_t
+ *                elements (>= N * 128 / group; 4-byte aligned)
+ *
+ * y = the bf16 value mla_up_v writes; for each group g of a token
+ * s = fl32(amax_g |y| / 448) (s = 1 for an all-zero group), code = e4m3fn of
+ * fl32(y / s), round to nearest even, saturating at +-448.  The scale rule is the
+ * one the fp8 cache rows use; the page names the grouping only.  Results are
+ * defined for finite y.  1 <= N <= 128, 0 <= T <= 65535 * 32.
+ */
+mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int64_t ol_stride_h,
+                          const void* w_uv, int64_t T, int32_t N, int32_t group,
+                          void* out_codes, int64_t codes_stride_t, float* out_scales,
+                          int64_t scales_stride_t, void* stream);
+
+/*
  * mla_gather_cache -- gather context rows of the paged cache into a contiguous
  * bf16 workspace ([vLLM-MLA] §Prefill, chunked context: the rows a chunk needs
  * are collected by block_table, cu_seq_lens and token_to_seq so that kv_b_proj

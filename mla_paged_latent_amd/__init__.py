@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode.restype = i32
     L.mla_up_v.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.mla_up_v.restype = i32
+    L.mla_up_v_fp8.argtypes = [vp, i64, i64, vp, i64, i32, i32, vp, i64, vp, i64, vp]
+    L.mla_up_v_fp8.restype = i32
     L.mla_decode_varlen_workspace_size.argtypes = [i64, i32, i32, i32]
     L.mla_decode_varlen_workspace_size.restype = ctypes.c_size_t
     L.mla_decode_varlen.argtypes = [vp, i64, i64, vp, i32, i64, vp, i64, i32, vp, vp, i32, i64, i32, i32,
@@ -178,6 +180,29 @@ def up_v(o_lat: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor | None = Non
         _ptr(o_lat), o_lat.stride(0), o_lat.stride(1), _ptr(w_uv), T, N, _ptr(out),
         out.stride(0), _stream(stream)))
     return out
+
+
+def up_v_fp8(o_lat: torch.Tensor, w_uv: torch.Tensor, group: int = 128,
+             out_codes: torch.Tensor | None = None, out_scales: torch.Tensor | None = None,
+             stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """:func:`up_v` quantized to fp8 per token group of ``group`` (64 or 128) values.
+
+    Returns ``codes`` uint8 ``[T, N*128]`` (e4m3fn) and ``scales`` float32
+    ``[T, N*128 // group]``.
+    """
+    T, N, Lr = o_lat.shape
+    assert Lr == KV_LORA_RANK and o_lat.dtype == torch.bfloat16 and o_lat.stride(-1) == 1
+    assert w_uv.shape == (N, KV_LORA_RANK, 128) and w_uv.is_contiguous()
+    if out_codes is None:
+        out_codes = torch.empty((T, N * 128), dtype=torch.uint8, device=o_lat.device)
+    if out_scales is None:
+        out_scales = torch.empty((T, N * 128 // group), dtype=torch.float32, device=o_lat.device)
+    assert out_codes.dtype == torch.uint8 and out_codes.stride(-1) == 1
+    assert out_scales.dtype == torch.float32 and out_scales.stride(-1) == 1
+    _check("mla_up_v_fp8", lib().mla_up_v_fp8(
+        _ptr(o_lat), o_lat.stride(0), o_lat.stride(1), _ptr(w_uv), T, N, group, _ptr(out_codes),
+        out_codes.stride(0), _ptr(out_scales), out_scales.stride(0), _stream(stream)))
+    return out_codes, out_scales
 
 
 def gather_cache(kv_cache: torch.Tensor, kv_dtype: int, block_table: torch.Tensor,

@@ -164,6 +164,133 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   }
 }
 
+// mla_up_v with the output quantized to fp8 in groups of QG (64 or 128) consecutive
+// elements of a token, one float32 scale per group ([vLLM-MLA] §QuantKey: the W_UV
+// output is quantized per token group of 128 or 64 when the next layer wants fp8).
+// The bf16 result is formed exactly as mla_up_v forms it (float32 accumulation, one
+// rounding to bf16) and then quantized: s = amax / 448, code = e4m3(x / s).
+// grid = (NN / QG, N heads, token blocks of 32); a workgroup computes its group's
+// 64-column sub-tiles one after the other (the W tile is staged in LDS per sub-tile
+// as in head_gemm_kernel), keeps the bf16 tile in LDS, then quantizes whole groups.
+template <int QG>
+__global__ __launch_bounds__(256) void up_v_fp8_kernel(
+    const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // o_lat [T, N, 512]
+    const uint16_t* __restrict__ W,                                   // W_UV [N, 512, 128]
+    uint8_t* __restrict__ Q, int64_t q_st,                            // codes [T, N * 128]
+    float* __restrict__ S, int64_t s_st,                              // scales [T, N * 128 / QG]
+    int64_t T) {
+  constexpr int KK = 512, NN = 128, NT = 64, KSPLIT = 2;
+  using Cfg = GemmCfg<KK, NN, NT, KSPLIT>;
+  constexpr int kOutPitch = QG * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::kTileBytes + Cfg::kRedBytes + 32 * kOutPitch];
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+  MLA_LDS char* ostage = lds + Cfg::kTileBytes + Cfg::kRedBytes;
+
+  const int h = blockIdx.y;
+  const int64_t tb = (int64_t)blockIdx.z * 32;
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  const int nb = w % Cfg::kNB, kh = w / Cfg::kNB;
+  const int g = l >> 4, lg = l & 15;
+  const uint32_t tr_col = (uint32_t)((nb * 32 + 16 * (g & 1) + 4 * (lg & 3)) * 2);
+  const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
+  constexpr int kChunksPerRow = NT / 8;
+  constexpr int kPerThread = KK * kChunksPerRow / 256;
+
+  // activation fragments of this token block (shared by the sub-tiles)
+  bf16x8_t bfrag[Cfg::kKSteps];
+  {
+    const int64_t trow = tb + (l & 31);
+    const bool t_ok = trow < T;
+    const uint16_t* arow = A + (t_ok ? trow : 0) * a_st + h * a_sh;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
+      const int k0 = kh * Cfg::kKPerWave + ks * 16;
+      bfrag[ks] = *reinterpret_cast<const bf16x8_t*>(arow + k0 + 8 * (l >> 5));
+      if (!t_ok) bfrag[ks] = bf16x8_t{};
+    }
+  }
+#pragma unroll 1
+  for (int sub = 0; sub < QG / NT; ++sub) {
+    const int n0 = blockIdx.x * QG + sub * NT;
+    const uint16_t* wh = W + (int64_t)h * KK * NN + n0;
+    u32x4_t wv[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = tid + 256 * j;
+      wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)(i / kChunksPerRow) * NN + (i % kChunksPerRow) * 8);
+    }
+    if (sub > 0) lds_barrier();                          // the previous sub-tile's W reads are done
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = tid + 256 * j;
+      *reinterpret_cast<MLA_LDS u32x4_t*>(lds + (i / kChunksPerRow) * Cfg::kRowBytes + (i % kChunksPerRow) * 16) = wv[j];
+    }
+    lds_barrier();
+    f32x16_t acc = {};
+#pragma unroll
+    for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
+      const int k0 = kh * Cfg::kKPerWave + ks * 16;
+      const uint32_t r0 = (uint32_t)((k0 + tr_row0) * Cfg::kRowBytes) + tr_col;
+      const bf16x4_t lo = lds_read_tr16(lds, r0);
+      const bf16x4_t hi = lds_read_tr16(lds, r0 + 4 * Cfg::kRowBytes);
+      const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[ks], acc, 0, 0, 0);
+    }
+    MLA_LDS float* red = reinterpret_cast<MLA_LDS float*>(lds + Cfg::kTileBytes);
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[(nb * 16 + i) * 64 + l] = acc[i];
+    }
+    lds_barrier();
+    if (kh == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += red[(nb * 16 + i) * 64 + l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x4_t v = {(__bf16)acc[4 * i], (__bf16)acc[4 * i + 1], (__bf16)acc[4 * i + 2],
+                            (__bf16)acc[4 * i + 3]};
+        *reinterpret_cast<MLA_LDS bf16x4_t*>(ostage + (l & 31) * kOutPitch +
+                                             (sub * NT + nb * 32 + 8 * i + 4 * (l >> 5)) * 2) = v;
+      }
+    }
+  }
+  lds_barrier();
+  // quantize: each group is QG / 8 consecutive lanes, 8 values per lane
+  constexpr int kLanesPerGroup = QG / 8;
+#pragma unroll
+  for (int j = 0; j < QG / 64; ++j) {
+    const int item = tid + 256 * j;
+    const int r = item / kLanesPerGroup, cc = item % kLanesPerGroup;
+    const bool ok = tb + r < T;
+    const u32x4_t raw = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * kOutPitch + cc * 16);
+    float x[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_bits_to_f32(raw[k] & 0xFFFFu);
+      x[2 * k + 1] = bf16_bits_to_f32(raw[k] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(x[2 * k]), fabsf(x[2 * k + 1])));
+    }
+#pragma unroll
+    for (int m = 1; m < kLanesPerGroup; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    float s = __fdiv_rn(amax, 448.0f);
+    if (s == 0.f) s = 1.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= e4m3_encode(__fdiv_rn(x[k], s)) << (8 * k);
+      hi |= e4m3_encode(__fdiv_rn(x[4 + k], s)) << (8 * k);
+    }
+    if (ok) {
+      const int64_t col = (int64_t)h * NN + blockIdx.x * QG + cc * 8;
+      *reinterpret_cast<u32x2_t*>(Q + (tb + r) * q_st + col) = u32x2_t{lo, hi};
+      if (cc == 0) S[(tb + r) * s_st + (h * NN + blockIdx.x * QG) / QG] = s;
+    }
+  }
+}
+
 }  // namespace mla
 
 extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
@@ -216,5 +343,36 @@ extern "C" mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t
                      (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv,
                      (uint16_t*)out, out_stride_t, (int64_t)MLA_V_HEAD_DIM,
                      (const uint16_t*)nullptr, (int64_t)0, (int64_t)0, T);
+  return launch_status();
+}
+
+extern "C" mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int64_t ol_stride_h,
+                                     const void* w_uv, int64_t T, int32_t N, int32_t group, void* out_codes,
+                                     int64_t codes_stride_t, float* out_scales, int64_t scales_stride_t,
+                                     void* stream) {
+  using namespace mla;
+  if (T < 0 || N < 1 || N > MLA_MAX_HEADS || (group != 64 && group != 128)) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (T > (int64_t)65535 * 32) return MLA_ERR_SHAPE;        // token blocks ride grid z
+  if (!o_lat || !w_uv || !out_codes || !out_scales) return MLA_ERR_NULL;
+  if (codes_stride_t < (int64_t)N * MLA_V_HEAD_DIM || scales_stride_t < (int64_t)N * MLA_V_HEAD_DIM / group)
+    return MLA_ERR_SHAPE;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !mult8(ol_stride_t) || !mult8(ol_stride_h) ||
+      (reinterpret_cast<uintptr_t>(out_codes) & 7u) || (codes_stride_t & 7) ||
+      (reinterpret_cast<uintptr_t>(out_scales) & 3u))
+    return MLA_ERR_ALIGN;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(MLA_V_HEAD_DIM / group), (unsigned)N, (unsigned)((T + 31) / 32));
+  if (group == 64)
+    hipLaunchKernelGGL(up_v_fp8_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)o_lat, ol_stride_t,
+                       ol_stride_h, (const uint16_t*)w_uv, (uint8_t*)out_codes, codes_stride_t, out_scales,
+                       scales_stride_t, T);
+  else
+    hipLaunchKernelGGL(up_v_fp8_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)o_lat, ol_stride_t,
+                       ol_stride_h, (const uint16_t*)w_uv, (uint8_t*)out_codes, codes_stride_t, out_scales,
+                       scales_stride_t, T);
   return launch_status();
 }

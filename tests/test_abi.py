@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     fns = declared_functions()
     for f in ("mla_cache_write", "mla_absorb_q", "mla_decode", "mla_up_v",
-              "mla_decode_workspace_size", "mla_status_str"):
+              "mla_up_v_fp8", "mla_decode_workspace_size", "mla_status_str"):
         assert f in fns
 
 
@@ -105,6 +105,17 @@ def test_other_calls_reject_bad_arguments():
     assert L.mla_up_v(p, 512, 512, p, 4, 129, p, 128 * 129, None) == 2
     assert L.mla_up_v(p, 512, 512, p, 4, 16, p, 1024, None) == 2           # out row too short
     assert L.mla_up_v(p, 512, 512, None, 4, 16, p, 2048, None) == 1
+    # up_v with fp8 group quantization of its output
+    f = L.mla_up_v_fp8
+    assert f(p, 512, 512, p, 4, 129, 128, p, 128 * 129, p, 129, None) == 2
+    assert f(p, 512, 512, p, 4, 16, 32, p, 2048, p, 64, None) == 2           # group 32
+    assert f(p, 512, 512, p, 0, 16, 64, p, 2048, p, 32, None) == 0           # T == 0 is a no-op
+    assert f(p, 512, 512, p, 65535 * 32 + 1, 16, 64, p, 2048, p, 32, None) == 2
+    assert f(p, 512, 512, None, 4, 16, 64, p, 2048, p, 32, None) == 1
+    assert f(p, 512, 512, p, 4, 16, 64, p, 1024, p, 32, None) == 2          # codes row too short
+    assert f(p, 512, 512, p, 4, 16, 128, p, 2048, p, 8, None) == 2          # scales row too short
+    assert f(p, 512, 512, p, 4, 16, 64, p, 2052, p, 32, None) == 4          # codes stride % 8
+    assert f(p, 512, 512, p, 4, 16, 64, p, 2048, vp(258), 32, None) == 4    # scales alignment
 
 
 def test_context_calls_reject_bad_arguments_without_a_gpu():
