@@ -232,3 +232,17 @@ def random_attn_states(T: int, N: int, D: int, seed: int, empty_frac: float = 0.
         o[empty] = 0
         l[empty] = -np.inf
     return po, pl, so, sl
+
+
+def rope_cos_sin(max_pos: int, base: float = 10000.0, rope_dim: int = R) -> np.ndarray:
+    """A rotary table ``[max_pos, rope_dim]`` in float32: ``cos(p w_i)`` for the
+    ``rope_dim / 2`` frequencies ``w_i = base^(-2i / rope_dim)``, then ``sin(p w_i)``.
+
+    This is the caller-side table the rope-fused absorption takes as input (the
+    usual geometric frequencies; the pages leave the schedule to the model).
+    """
+    half = rope_dim // 2
+    w = base ** (-np.arange(half, dtype=np.float64) * 2.0 / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * w[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+

@@ -360,6 +360,53 @@ def absorb(q_nope: np.ndarray, q_pe: np.ndarray | None, w_uk_t: np.ndarray) -> n
     return np.concatenate([ql, np.asarray(q_pe, np.float64)], axis=-1)
 
 
+def rope(x_pe: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray, neox: bool) -> np.ndarray:
+    """Rotary position embedding of the 64-wide rope part of a query.
+
+    [vLLM-MLA] §从模型层看: the model layer rotates the last ``qk_rope_head_dim``
+    query values (and the shared ``k_pe``) by ``rotary_emb(positions, ...)``
+    before MLA sees them; [TRTLLM-TP] §吸收 runs that rotation beside the
+    absorption GEMM.  The pages give neither the pairing nor the frequencies,
+    so the caller supplies both: ``cos_sin[p] = [cos(p w_0..w_31) | sin(...)]``
+    (float, ``[max_pos, 64]``) and the pairing, either rotate-half
+    (``neox``: value ``i`` pairs with ``i + 32``) or adjacent pairs (value
+    ``2i`` with ``2i + 1``).  Pair ``(a, b)`` with frequency ``i`` becomes
+    ``(a cos - b sin, b cos + a sin)``.  A row whose position lies outside
+    ``[0, max_pos)`` has no defined rotation: it comes back as NaN.
+
+    ``x_pe[T, N, 64]``, ``positions[T]``.  Returns float64 ``[T, N, 64]``.
+    """
+    x = np.asarray(x_pe, np.float64)
+    T, N, R = x.shape
+    half = R // 2
+    table = np.asarray(cos_sin, np.float64)
+    out = np.full_like(x, np.nan)
+    for t in range(T):
+        p = int(positions[t])
+        if p < 0 or p >= table.shape[0]:
+            continue
+        c, sn = table[p, :half], table[p, half:]
+        if neox:
+            a, b = x[t, :, :half], x[t, :, half:]
+            out[t, :, :half] = a * c - b * sn
+            out[t, :, half:] = b * c + a * sn
+        else:
+            a, b = x[t, :, 0::2], x[t, :, 1::2]
+            out[t, :, 0::2] = a * c - b * sn
+            out[t, :, 1::2] = b * c + a * sn
+    return out
+
+
+def absorb_rope(q_nope: np.ndarray, q_pe: np.ndarray, w_uk_t: np.ndarray, positions: np.ndarray,
+                cos_sin: np.ndarray, neox: bool) -> np.ndarray:
+    """:func:`absorb` with the query's rope part rotated on the way into the tail.
+
+    The fused query of [TRTLLM-TP] §吸收 holds ``[q_nope . W_UK_T[h] | RoPE(q_pe)]``;
+    the rotation is :func:`rope`.  Returns float64 ``[T, N, L + R]``.
+    """
+    return np.concatenate([absorb(q_nope, None, w_uk_t), rope(q_pe, positions, cos_sin, neox)], axis=-1)
+
+
 def up_v(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     """Per-head up-projection ``o_lat[t,h,:] . W_UV[h]`` → ``[T, N, V]``.
 

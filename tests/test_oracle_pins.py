@@ -643,3 +643,87 @@ def test_quantize_groups_fp8_matches_torch_cast_and_group_boundaries():
     ref = (xf / st).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(codes, ref)
     assert np.all(s[:, 1] > 100 * s[:, 0]) and np.all(s[:, 1] > 100 * s[:, 2])
+
+
+# --- rope fused into the absorption -------------------------------------------
+def _angles_table(ang):
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+
+
+def test_rope_is_complex_multiplication_in_both_pairings():
+    """Each pair is a complex number multiplied by exp(i * angle): adjacent pairs
+    (x[2i] + i x[2i+1]) and rotate-half pairs (x[i] + i x[i+32])."""
+    rng = np.random.default_rng(1200)
+    T, N = 5, 3
+    x = rng.standard_normal((T, N, 64))
+    ang = rng.uniform(-10, 10, (T, 32))
+    table = _angles_table(ang)
+    pos = np.arange(T)
+    e = np.exp(1j * ang)[:, None, :]
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * e
+    adj = np.empty_like(x)
+    adj[..., 0::2], adj[..., 1::2] = z.real, z.imag
+    assert np.allclose(O.rope(x, pos, table, False), adj, rtol=0, atol=1e-13)
+    z = (x[..., :32] + 1j * x[..., 32:]) * e
+    assert np.allclose(O.rope(x, pos, table, True), np.concatenate([z.real, z.imag], -1), rtol=0, atol=1e-13)
+
+
+def test_rope_pairings_are_each_other_under_the_deinterleave_permutation():
+    rng = np.random.default_rng(1201)
+    x = rng.standard_normal((4, 2, 64))
+    table = _angles_table(rng.uniform(-3, 3, (4, 32)))
+    perm = np.concatenate([np.arange(0, 64, 2), np.arange(1, 64, 2)])   # adjacent -> halves
+    a = O.rope(x, np.arange(4), table, False)
+    b = O.rope(x[..., perm], np.arange(4), table, True)
+    assert np.allclose(a[..., perm], b, rtol=0, atol=1e-14)
+
+
+def test_rope_hand_values_and_identity():
+    x = np.arange(1.0, 65.0).reshape(1, 1, 64)
+    quarter = _angles_table(np.full((1, 32), np.pi / 2))
+    # a quarter turn: (a, b) -> (-b, a)
+    got = O.rope(x, np.array([0]), quarter, True)[0, 0]
+    assert np.allclose(got[:32], -x[0, 0, 32:], atol=1e-12) and np.allclose(got[32:], x[0, 0, :32], atol=1e-12)
+    got = O.rope(x, np.array([0]), quarter, False)[0, 0]
+    assert np.allclose(got[0::2], -x[0, 0, 1::2], atol=1e-12) and np.allclose(got[1::2], x[0, 0, 0::2], atol=1e-12)
+    ident = _angles_table(np.zeros((1, 32)))
+    for neox in (True, False):
+        assert np.array_equal(O.rope(x, np.array([0]), ident, neox), x)
+
+
+def test_rope_scores_depend_only_on_the_position_difference():
+    """<RoPE(q, p), RoPE(k, p')> is a function of p - p' (the reason for rotating)."""
+    rng = np.random.default_rng(1202)
+    table = MI.rope_cos_sin(64).astype(np.float64)
+    q, k = rng.standard_normal((1, 1, 64)), rng.standard_normal((1, 1, 64))
+    for neox in (True, False):
+        dots = [np.sum(O.rope(q, np.array([p + d]), table, neox) * O.rope(k, np.array([p]), table, neox))
+                for p in (0, 7, 30) for d in (5,)]
+        assert np.allclose(dots, dots[0], rtol=1e-5)
+        far = np.sum(O.rope(q, np.array([12]), table, neox) * O.rope(k, np.array([0]), table, neox))
+        assert abs(far - dots[0]) > 1e-3
+        # and rotation keeps each pair's length
+        r = O.rope(q, np.array([9]), table, neox)
+        assert np.isclose(np.sum(r * r), np.sum(q * q), rtol=1e-6)
+
+
+def test_rope_out_of_range_positions_are_nan_and_absorb_rope_is_absorb_plus_rope():
+    rng = np.random.default_rng(1203)
+    T, N = 4, 2
+    qn, qp = rng.standard_normal((T, N, 128)), rng.standard_normal((T, N, 64))
+    w = rng.standard_normal((N, 128, 512))
+    table = MI.rope_cos_sin(8)
+    pos = np.array([0, 7, 8, -1])
+    r = O.rope(qp, pos, table, True)
+    assert np.all(np.isnan(r[2:])) and not np.any(np.isnan(r[:2]))
+    assert np.array_equal(r[0], qp[0])                                    # position 0: cos 1, sin 0
+    f = O.absorb_rope(qn, qp, w, pos, table, False)
+    assert np.array_equal(f[..., :512], O.absorb(qn, None, w))
+    assert np.array_equal(f[..., 512:], O.rope(qp, pos, table, False), equal_nan=True)
+
+
+def test_rope_table_helper_follows_the_geometric_schedule():
+    t = MI.rope_cos_sin(5, base=100.0, rope_dim=8)
+    assert t.shape == (5, 8) and t.dtype == np.float32
+    assert np.allclose(t[3, 1], math.cos(3 * 100.0 ** -0.25)) and np.allclose(t[3, 5], math.sin(3 * 100.0 ** -0.25))
+    assert np.all(t[0, :4] == 1) and np.all(t[0, 4:] == 0)
