@@ -10,7 +10,7 @@ step's pages to the next.
 
 Prints ONE JSON line (stdout).  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
-    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill
+    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill|absorb_rope_decode
 """
 
 from __future__ import annotations
@@ -357,6 +357,9 @@ CONTEXT_OPS = {
     # and an 8192-token prefill, 128 heads
     "upv_fp8_decode": dict(kind="upv", T=128, N=128, group=128),
     "upv_fp8_prefill": dict(kind="upv", T=8192, N=128, group=128),
+    # query absorption with the rope part rotated on the way (rotate-half pairing,
+    # positions drawn from a 32k table), a 128-request decode batch, 128 heads
+    "absorb_rope_decode": dict(kind="rope", T=128, N=128, max_pos=32768),
 }
 
 
@@ -472,6 +475,31 @@ def run_context_op(args) -> dict:
                 f"e4m3 codes + float32 scales per group of {G}, {R} rotating input copies")
         metric = "V up-projection with fp8 group-quantized output GB/s (% of HBM roofline), 1 MI355X"
         dtype = "bf16->fp8"
+    elif op["kind"] == "rope":
+        T, N = op["T"], op["N"]
+        per_copy = N * 128 * 512 * 2 + T * N * (128 + 64) * 2
+        R = max(2, math.ceil(3 * MALL_BYTES / per_copy))
+        gen = torch.Generator(device=dev).manual_seed(550)
+        ws = [(torch.randn(N, 128, 512, device=dev, generator=gen) / math.sqrt(512)).to(torch.bfloat16)
+              for _ in range(R)]
+        qs = [torch.randn(T, N, 192, device=dev, generator=gen).to(torch.bfloat16) for _ in range(R)]
+        table = torch.from_numpy(MI.rope_cos_sin(op["max_pos"])).to(dev)
+        pos = torch.randint(0, op["max_pos"], (T,), device=dev, generator=gen)
+        qf = torch.empty((T, N, 576), dtype=torch.bfloat16, device=dev)
+        calls = [(qs[i].data_ptr(), qs[i].stride(0), qs[i].stride(1), qs[i].data_ptr() + 256, qs[i].stride(0),
+                  qs[i].stride(1), ws[i].data_ptr(), T, N, pos.data_ptr(), table.data_ptr(), op["max_pos"], 1,
+                  qf.data_ptr(), qf.stride(0), qf.stride(1), stream) for i in range(R)]
+        f = L.mla_absorb_q_rope
+        bytes_alg = per_copy + T * (8 + 256) + T * N * 576 * 2
+        flops_alg = 2.0 * T * N * 128 * 512
+        ref_calls = [(qs[i].data_ptr(), qs[i].stride(0), qs[i].stride(1), qs[i].data_ptr() + 256, qs[i].stride(0),
+                      qs[i].stride(1), ws[i].data_ptr(), T, N, qf.data_ptr(), qf.stride(0), qf.stride(1), stream)
+                     for i in range(R)]
+        desc = (f"{args.op}: T={T} tokens x {N} heads, q_nope [T, N, 128] . W_UK_T [N, 128, 512] into a "
+                f"[T, N, 576] fused query whose tail is RoPE(q_pe) (rotate-half, {op['max_pos']}-row table), "
+                f"{R} rotating input copies")
+        metric = "query absorption with fused RoPE GB/s (% of HBM roofline), 1 MI355X"
+        dtype = "bf16"
     else:
         T, N, D = op["T"], op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=510)
@@ -501,16 +529,17 @@ def run_context_op(args) -> dict:
     gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
     log(f"[bench] {args.op}: {mean_ms * 1e3:.1f} us per call, {gbs:.0f} GB/s")
     bf16_out_us = None
-    if op["kind"] == "upv":
+    if op["kind"] in ("upv", "rope"):
+        g = L.mla_up_v if op["kind"] == "upv" else L.mla_absorb_q
         for i in range(3):
-            L.mla_up_v(*ref_calls[i % len(ref_calls)])
+            g(*ref_calls[i % len(ref_calls)])
         e0.record()
         for i in range(args.steps):
-            L.mla_up_v(*ref_calls[i % len(ref_calls)])
+            g(*ref_calls[i % len(ref_calls)])
         e1.record()
         torch.cuda.synchronize()
         bf16_out_us = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
-        log(f"[bench] mla_up_v (bf16 output) on the same inputs: {bf16_out_us:.1f} us per call")
+        log(f"[bench] the unfused call on the same inputs: {bf16_out_us:.1f} us per call")
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
     if op["kind"] == "varlen" and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
@@ -519,10 +548,10 @@ def run_context_op(args) -> dict:
                 "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof.update({"traffic": None, "kernel": args.op, "algorithmic_bytes": bytes_alg,
                  "mean_launch_us": round(mean_ms * 1e3, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-    if op["kind"] in ("varlen", "upv"):
+    if op["kind"] in ("varlen", "upv", "rope"):
         roof["algorithmic_flops"] = flops_alg
     if bf16_out_us is not None:
-        roof["bf16_output_call_us"] = bf16_out_us
+        roof["unfused_call_us"] = bf16_out_us
     res = {"metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": {"workload": desc},
@@ -576,6 +605,21 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         n_items = 1
         per_item = N * 512 * 128 * 2 + T * N * (512 * 2 + 128 + 128 // G * 4)
         sample = f"T={T} tokens x {N} heads through the oracle up_v and group quantizer"
+    elif op["kind"] == "rope":
+        T, N = 32, op["N"]
+        rng = np.random.default_rng(551)
+        qn = O.bf16_bits_to_f64(MI.to_bf16_bits(rng.standard_normal((T, N, 128)).astype(np.float32)))
+        qp = O.bf16_bits_to_f64(MI.to_bf16_bits(rng.standard_normal((T, N, 64)).astype(np.float32)))
+        wk = O.bf16_bits_to_f64(MI.to_bf16_bits((rng.standard_normal((N, 128, 512)) / np.sqrt(512)).astype(np.float32)))
+        table = MI.rope_cos_sin(op["max_pos"]).astype(np.float64)
+        pos = rng.integers(0, op["max_pos"], T)
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            O.f64_to_bf16_bits(O.absorb_rope(qn, qp, wk, pos, table, True))
+            times.append(time.perf_counter() - t0)
+        n_items = 1
+        per_item = N * 128 * 512 * 2 + T * N * (192 * 2 + 576 * 2) + T * (8 + 256)
+        sample = f"T={T} tokens x {N} heads through the oracle absorb_rope"
     else:
         T, N, D = 256, op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=522)

@@ -122,6 +122,31 @@ mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_st
                           void* stream);
 
 /*
+ * mla_absorb_q_rope -- mla_absorb_q with the rotary position embedding of q_pe
+ * applied on the way into the tail ([vLLM-MLA] §从模型层看: the model layer
+ * rotates the last 64 query values by rotary_emb(positions, ...) before MLA;
+ * [TRTLLM-TP] §吸收: the rotation runs beside the absorption GEMM).
+ *
+ *   q_nope, w_uk_t, q_fused  as mla_absorb_q; q_pe is required
+ *   positions      int64 [T] (device): the token's position
+ *   cos_sin_cache  float32 [max_pos, 64] contiguous, 16-byte aligned:
+ *                  row p = [cos(p w_0) .. cos(p w_31) | sin(p w_0) .. sin(p w_31)]
+ *   neox           nonzero: rotate-half pairing (value i with i + 32, frequency i);
+ *                  zero: adjacent pairs (value 2i with 2i + 1, frequency i)
+ *
+ * Pair (a, b) of frequency i -> (a cos - b sin, b cos + a sin), float32, bf16
+ * RNE.  A token whose position is outside [0, max_pos) gets a NaN tail (64
+ * quiet NaNs), so a bad position shows in the scores rather than passing
+ * silently.  The frequency schedule (base, scaling) is the table's business.
+ */
+mla_status_t mla_absorb_q_rope(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+                               const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+                               const void* w_uk_t, int64_t T, int32_t N, const int64_t* positions,
+                               const float* cos_sin_cache, int64_t max_pos, int32_t neox,
+                               void* q_fused, int64_t qf_stride_t, int64_t qf_stride_h,
+                               void* stream);
+
+/*
  * mla_decode_workspace_size -- bytes of workspace mla_decode needs for this
  * batch shape and split mode (see num_splits below).  Returns 0 for shapes
  * mla_decode would reject.  Pure host arithmetic; no device call.

@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode.restype = i32
     L.mla_up_v.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.mla_up_v.restype = i32
+    L.mla_absorb_q_rope.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, i64,
+                                    i64, vp]
+    L.mla_absorb_q_rope.restype = i32
     L.mla_up_v_fp8.argtypes = [vp, i64, i64, vp, i64, i32, i32, vp, i64, vp, i64, vp]
     L.mla_up_v_fp8.restype = i32
     L.mla_decode_varlen_workspace_size.argtypes = [i64, i32, i32, i32]
@@ -128,6 +131,31 @@ def absorb_q(q_nope: torch.Tensor, q_pe: torch.Tensor | None, w_uk_t: torch.Tens
     _check("mla_absorb_q", lib().mla_absorb_q(
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), qp_st, qp_sh,
         _ptr(w_uk_t), T, N, _ptr(q_fused), q_fused.stride(0), q_fused.stride(1), _stream(stream)))
+    return q_fused
+
+
+def absorb_q_rope(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk_t: torch.Tensor,
+                  positions: torch.Tensor, cos_sin_cache: torch.Tensor, neox: bool = True,
+                  q_fused: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """``q_fused[t,h] = [q_nope[t,h] . W_UK_T[h] | RoPE(q_pe[t,h], positions[t])]``.
+
+    ``positions`` int64 ``[T]``; ``cos_sin_cache`` float32 ``[max_pos, 64]``
+    (cos of the 32 frequencies, then sin); ``neox`` picks rotate-half pairing,
+    else adjacent pairs.
+    """
+    T, N, P = q_nope.shape
+    assert P == 128 and q_nope.dtype == torch.bfloat16 and w_uk_t.is_contiguous()
+    assert w_uk_t.shape == (N, 128, KV_LORA_RANK) and w_uk_t.dtype == torch.bfloat16
+    assert q_pe.shape == (T, N, 64) and q_pe.stride(-1) == 1
+    assert positions.dtype == torch.int64 and positions.is_contiguous() and positions.numel() == T
+    assert cos_sin_cache.dtype == torch.float32 and cos_sin_cache.is_contiguous()
+    assert cos_sin_cache.dim() == 2 and cos_sin_cache.shape[1] == 64
+    if q_fused is None:
+        q_fused = torch.empty((T, N, ROW_ELEMS), dtype=torch.bfloat16, device=q_nope.device)
+    _check("mla_absorb_q_rope", lib().mla_absorb_q_rope(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
+        _ptr(w_uk_t), T, N, _ptr(positions), _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+        1 if neox else 0, _ptr(q_fused), q_fused.stride(0), q_fused.stride(1), _stream(stream)))
     return q_fused
 
 

@@ -35,13 +35,51 @@ struct GemmCfg {
   static constexpr int kLdsBytes = kTileBytes + kRedBytes + kOutBytes;
 };
 
+// What head_gemm_kernel writes after the NN product columns of each row.
+enum PeTail { kNoTail = 0, kCopyTail = 1, kRopeTail = 2 };
+
+// Rotary position embedding of one token's 16 rope values that share the
+// frequencies f0 .. f0+7 (f0 = 8 * c): with rotate-half pairing they are
+// chunks c and c + 4 of the 64-value row (value i pairs with i + 32), with
+// adjacent pairing chunks 2c and 2c + 1 (value 2k pairs with 2k + 1, frequency
+// k).  Pair (a, b) -> (a cos - b sin, b cos + a sin) in float32, bf16 RNE.
+// cs = cos(f0..f0+7), sin(f0..f0+7).  A position outside the table gives NaN.
+__device__ __forceinline__ void rope_chunks(const uint4& xa, const uint4& xb, const float (&cs)[16],
+                                            bool ok, bool neox, uint4& ya, uint4& yb) {
+  const uint32_t in[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_bits_to_f32(in[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_bits_to_f32(in[i] >> 16);
+  }
+  float r[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // the pair of frequency f0 + j: (v[ia], v[ib])
+    const int ia = neox ? j : 2 * j, ib = neox ? j + 8 : 2 * j + 1;
+    r[ia] = v[ia] * cs[j] - v[ib] * cs[8 + j];
+    r[ib] = v[ib] * cs[j] + v[ia] * cs[8 + j];
+  }
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x2_t pr = {(__bf16)r[2 * i], (__bf16)r[2 * i + 1]};
+    out[i] = ok ? __builtin_bit_cast(uint32_t, pr) : 0x7FC07FC0u;
+  }
+  ya = uint4{out[0], out[1], out[2], out[3]};
+  yb = uint4{out[4], out[5], out[6], out[7]};
+}
+
 // grid = (NN / NT, N heads); block = 256 threads.
-template <int KK, int NN, int NT, int KSPLIT, bool COPY_PE>
+template <int KK, int NN, int NT, int KSPLIT, int PE>
 __global__ __launch_bounds__(256) void head_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // [T, N, KK]
     const uint16_t* __restrict__ W,                                   // [N, KK, NN]
     uint16_t* __restrict__ C, int64_t c_st, int64_t c_sh,            // [T, N, NN]
-    const uint16_t* __restrict__ pe, int64_t pe_st, int64_t pe_sh,   // [T, N, 64] (COPY_PE)
+    const uint16_t* __restrict__ pe, int64_t pe_st, int64_t pe_sh,   // [T, N, 64] (PE != 0)
+    const int64_t* __restrict__ positions,                            // [T] (kRopeTail)
+    const float* __restrict__ cos_sin, int64_t max_pos, int neox,     // [max_pos, 64] (kRopeTail)
     int64_t T) {
   using Cfg = GemmCfg<KK, NN, NT, KSPLIT>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
@@ -53,13 +91,28 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   const int w = wave_id();
   const int l = lane_id();
 
-  // The first 32 tokens' q_pe chunks (COPY_PE, n-tile 0), W[h][0:KK][n0:n0+NT] and the
-  // first token block's activation fragments are all requested before anything waits,
-  // so a workgroup keeps its whole tile in flight.
-  const bool copy_pe = COPY_PE && blockIdx.x == 0;
-  uint4 pe_v;
-  const bool pe_first = copy_pe && tid < T * 8;
-  if (pe_first) pe_v = *reinterpret_cast<const uint4*>(pe + (tid >> 3) * pe_st + h * pe_sh + (tid & 7) * 8);
+  // The first tokens' q_pe chunks (n-tile 0), W[h][0:KK][n0:n0+NT] and the first token
+  // block's activation fragments are all requested before anything waits, so a
+  // workgroup keeps its whole tile in flight.  A copied tail moves one 16-byte chunk
+  // per item (8 per token); a rotated tail two chunks that share 8 frequencies (4 per
+  // token), chunks c and c + 4 (rotate-half) or 2c and 2c + 1 (adjacent pairs).
+  const bool do_pe = PE != kNoTail && blockIdx.x == 0;
+  constexpr int kPeItems = PE == kRopeTail ? 4 : 8;
+  auto pe_chunks = [&](int c, int& ca, int& cb) {
+    ca = PE == kRopeTail ? (neox ? c : 2 * c) : c;
+    cb = neox ? c + 4 : 2 * c + 1;
+  };
+  uint4 pe_v, pe_w;
+  int64_t pos_v = 0;
+  const bool pe_first = do_pe && tid < T * kPeItems;
+  if (pe_first) {
+    const int t = tid / kPeItems, c = tid % kPeItems;
+    int ca, cb;
+    pe_chunks(c, ca, cb);
+    if (PE == kRopeTail) pos_v = positions[t];
+    pe_v = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + ca * 8);
+    if (PE == kRopeTail) pe_w = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + cb * 8);
+  }
   const uint16_t* wh = W + (int64_t)h * KK * NN + n0;
   constexpr int kChunksPerRow = NT / 8;
   constexpr int kTileChunks = KK * kChunksPerRow;
@@ -72,6 +125,22 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
     const int k = i / kChunksPerRow, c = i % kChunksPerRow;
     wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)k * NN + c * 8);
   }
+  // the rotation's table row, once the position has arrived
+  auto load_cs = [&](int64_t pos, int c, float (&cs)[16]) -> bool {
+    const bool ok = pos >= 0 && pos < max_pos;
+    const float* row = cos_sin + (ok ? pos : 0) * 64 + 8 * c;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float4 a = *reinterpret_cast<const float4*>(row + 4 * q);
+      const float4 b = *reinterpret_cast<const float4*>(row + 32 + 4 * q);
+      cs[4 * q] = a.x; cs[4 * q + 1] = a.y; cs[4 * q + 2] = a.z; cs[4 * q + 3] = a.w;
+      cs[8 + 4 * q] = b.x; cs[8 + 4 * q + 1] = b.y; cs[8 + 4 * q + 2] = b.z; cs[8 + 4 * q + 3] = b.w;
+    }
+    return ok;
+  };
+  float cs_v[16];
+  bool pos_ok = false;
+  if (PE == kRopeTail && pe_first) pos_ok = load_cs(pos_v, tid % kPeItems, cs_v);
 
   const int nb = w % Cfg::kNB;          // n block of this wave
   const int kh = w / Cfg::kNB;          // K slice of this wave
@@ -101,13 +170,34 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
     const int k = i / kChunksPerRow, c = i % kChunksPerRow;
     *reinterpret_cast<MLA_LDS u32x4_t*>(lds + k * Cfg::kRowBytes + c * 16) = wv[j];
   }
-  if (pe_first) *reinterpret_cast<uint4*>(C + (tid >> 3) * c_st + h * c_sh + NN + (tid & 7) * 8) = pe_v;
-  if (copy_pe) {
-    for (int64_t i = tid + 256; i < T * 8; i += 256) {
-      const int64_t t = i >> 3;
-      const int c = (int)(i & 7);
-      const uint4 v = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + c * 8);
-      *reinterpret_cast<uint4*>(C + t * c_st + h * c_sh + NN + c * 8) = v;
+  auto put_tail = [&](int64_t t, int c, const uint4& a, const uint4& b, const float (&cs)[16], bool ok) {
+    int ca, cb;
+    pe_chunks(c, ca, cb);
+    uint16_t* dst = C + t * c_st + h * c_sh + NN;
+    if (PE == kCopyTail) {
+      *reinterpret_cast<uint4*>(dst + ca * 8) = a;
+    } else {
+      uint4 ya, yb;
+      rope_chunks(a, b, cs, ok, neox != 0, ya, yb);
+      *reinterpret_cast<uint4*>(dst + ca * 8) = ya;
+      *reinterpret_cast<uint4*>(dst + cb * 8) = yb;
+    }
+  };
+  if (pe_first) put_tail(tid / kPeItems, tid % kPeItems, pe_v, pe_w, cs_v, pos_ok);
+  if (do_pe) {
+    for (int64_t i = tid + 256; i < T * kPeItems; i += 256) {
+      const int64_t t = i / kPeItems;
+      const int c = (int)(i % kPeItems);
+      int ca, cb;
+      pe_chunks(c, ca, cb);
+      uint4 a = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + ca * 8), b = a;
+      float cs[16];
+      bool ok = false;
+      if (PE == kRopeTail) {
+        b = *reinterpret_cast<const uint4*>(pe + t * pe_st + h * pe_sh + cb * 8);
+        ok = load_cs(positions[t], c, cs);
+      }
+      put_tail(t, c, a, b, cs, ok);
     }
   }
   lds_barrier();
@@ -311,15 +401,44 @@ extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, in
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   dim3 grid(MLA_KV_LORA_RANK / 128, N);
   if (q_pe)
-    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, true>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, kCopyTail>), grid, dim3(256), 0, s,
                        (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
                        (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)q_pe,
-                       qp_stride_t, qp_stride_h, T);
+                       qp_stride_t, qp_stride_h, (const int64_t*)nullptr, (const float*)nullptr,
+                       (int64_t)0, 0, T);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, false>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, kNoTail>), grid, dim3(256), 0, s,
                        (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
                        (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)nullptr,
-                       (int64_t)0, (int64_t)0, T);
+                       (int64_t)0, (int64_t)0, (const int64_t*)nullptr, (const float*)nullptr,
+                       (int64_t)0, 0, T);
+  return launch_status();
+}
+
+extern "C" mla_status_t mla_absorb_q_rope(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+                                          const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+                                          const void* w_uk_t, int64_t T, int32_t N, const int64_t* positions,
+                                          const float* cos_sin_cache, int64_t max_pos, int32_t neox,
+                                          void* q_fused, int64_t qf_stride_t, int64_t qf_stride_h,
+                                          void* stream) {
+  using namespace mla;
+  if (T < 0 || N < 1 || N > MLA_MAX_HEADS || max_pos < 1) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!q_nope || !w_uk_t || !q_fused || !q_pe || !positions || !cos_sin_cache) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk_t) || !aligned16(q_fused) || !mult8(qn_stride_t) ||
+      !mult8(qn_stride_h) || !mult8(qf_stride_t) || !mult8(qf_stride_h) || !aligned16(q_pe) ||
+      !mult8(qp_stride_t) || !mult8(qp_stride_h) || !aligned16(cos_sin_cache) ||
+      (reinterpret_cast<uintptr_t>(positions) & 7u))
+    return MLA_ERR_ALIGN;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid(MLA_KV_LORA_RANK / 128, N);
+  hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, kRopeTail>), grid, dim3(256), 0, s,
+                     (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
+                     (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)q_pe, qp_stride_t,
+                     qp_stride_h, positions, cos_sin_cache, max_pos, neox ? 1 : 0, T);
   return launch_status();
 }
 
@@ -339,10 +458,11 @@ extern "C" mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   dim3 grid(MLA_V_HEAD_DIM / 64, N);
-  hipLaunchKernelGGL((head_gemm_kernel<512, 128, 64, 2, false>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((head_gemm_kernel<512, 128, 64, 2, kNoTail>), grid, dim3(256), 0, s,
                      (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv,
                      (uint16_t*)out, out_stride_t, (int64_t)MLA_V_HEAD_DIM,
-                     (const uint16_t*)nullptr, (int64_t)0, (int64_t)0, T);
+                     (const uint16_t*)nullptr, (int64_t)0, (int64_t)0, (const int64_t*)nullptr,
+                     (const float*)nullptr, (int64_t)0, 0, T);
   return launch_status();
 }
 

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     fns = declared_functions()
     for f in ("mla_cache_write", "mla_absorb_q", "mla_decode", "mla_up_v",
-              "mla_up_v_fp8", "mla_decode_workspace_size", "mla_status_str"):
+              "mla_up_v_fp8", "mla_absorb_q_rope", "mla_decode_workspace_size", "mla_status_str"):
         assert f in fns
 
 
@@ -105,6 +105,16 @@ def test_other_calls_reject_bad_arguments():
     assert L.mla_up_v(p, 512, 512, p, 4, 129, p, 128 * 129, None) == 2
     assert L.mla_up_v(p, 512, 512, p, 4, 16, p, 1024, None) == 2           # out row too short
     assert L.mla_up_v(p, 512, 512, None, 4, 16, p, 2048, None) == 1
+    # absorb with the rope part rotated
+    r = L.mla_absorb_q_rope
+    assert r(p, 128, 128, p, 64, 64, p, 4, 0, p, p, 16, 1, p, 576, 576, None) == 2
+    assert r(p, 128, 128, p, 64, 64, p, 4, 16, p, p, 0, 1, p, 576, 576, None) == 2     # empty table
+    assert r(p, 128, 128, p, 64, 64, p, 0, 16, p, p, 16, 1, p, 576, 576, None) == 0     # T == 0
+    assert r(p, 128, 128, None, 64, 64, p, 4, 16, p, p, 16, 1, p, 576, 576, None) == 1  # q_pe required
+    assert r(p, 128, 128, p, 64, 64, p, 4, 16, None, p, 16, 1, p, 576, 576, None) == 1
+    assert r(p, 128, 128, p, 64, 64, p, 4, 16, p, vp(264), 16, 1, p, 576, 576, None) == 4
+    assert r(p, 128, 128, p, 64, 64, p, 4, 16, vp(260), p, 16, 1, p, 576, 576, None) == 4
+    assert r(p, 128, 128, p, 66, 64, p, 4, 16, p, p, 16, 1, p, 576, 576, None) == 4
     # up_v with fp8 group quantization of its output
     f = L.mla_up_v_fp8
     assert f(p, 512, 512, p, 4, 129, 128, p, 128 * 129, p, 129, None) == 2
