@@ -32,7 +32,10 @@ struct GemmCfg {
   static constexpr int kRedBytes = (KSPLIT > 1) ? (kNB * 32 * 32 * 4) : 0;
   static constexpr int kOutPitch = NT * 2 + 16;       // output staging row (32 tokens x NT)
   static constexpr int kOutBytes = 32 * kOutPitch;
-  static constexpr int kLdsBytes = kTileBytes + kRedBytes + kOutBytes;
+  static constexpr int kAPitch = KK * 2 + 16;         // activation staging row (32 tokens x KK)
+  static constexpr int kABytes = 32 * kAPitch;
+  static constexpr int kAPerThread = 32 * KK / 8 / 256;   // 16-byte chunks per thread
+  static constexpr int kLdsBytes = kTileBytes + kRedBytes + kOutBytes + kABytes;
 };
 
 // What head_gemm_kernel writes after the NN product columns of each row.
@@ -150,16 +153,30 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   const uint32_t tr_col = (uint32_t)((nb * 32 + 16 * (g & 1) + 4 * (lg & 3)) * 2);
   const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
 
-  bf16x8_t bfrag[Cfg::kKSteps];
+  // A token block's activations are staged in LDS: consecutive lanes read consecutive
+  // 16-byte chunks of a token row (whole cache lines per instruction), and each lane
+  // then takes its MFMA fragment (one token, 8 consecutive k) from LDS.  Read straight
+  // from HBM in fragment order, every instruction would touch 32 rows for 32 bytes
+  // each, and the activation reads would cost twice what the rest of the kernel does.
+  // The next block's chunks are loaded while the current block is multiplied.
+  MLA_LDS char* astage = lds + Cfg::kTileBytes + Cfg::kRedBytes + Cfg::kOutBytes;
+  constexpr int kRowChunksA = KK / 8;
+  u32x4_t av[Cfg::kAPerThread];
   auto load_act = [&](int64_t tb) {
-    const int64_t trow = tb + (l & 31);
-    const bool t_ok = trow < T;
-    const uint16_t* arow = A + (t_ok ? trow : 0) * a_st + h * a_sh;
 #pragma unroll
-    for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
-      const int k0 = kh * Cfg::kKPerWave + ks * 16;
-      bfrag[ks] = *reinterpret_cast<const bf16x8_t*>(arow + k0 + 8 * (l >> 5));
-      if (!t_ok) bfrag[ks] = bf16x8_t{};
+    for (int j = 0; j < Cfg::kAPerThread; ++j) {
+      const int i = tid + 256 * j;
+      const int64_t t = tb + i / kRowChunksA;
+      av[j] = t < T ? *reinterpret_cast<const u32x4_t*>(A + t * a_st + h * a_sh + (i % kRowChunksA) * 8)
+                    : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_act = [&]() {
+#pragma unroll
+    for (int j = 0; j < Cfg::kAPerThread; ++j) {
+      const int i = tid + 256 * j;
+      *reinterpret_cast<MLA_LDS u32x4_t*>(astage + (i / kRowChunksA) * Cfg::kAPitch + (i % kRowChunksA) * 16) =
+          av[j];
     }
   };
   load_act(0);
@@ -170,6 +187,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
     const int k = i / kChunksPerRow, c = i % kChunksPerRow;
     *reinterpret_cast<MLA_LDS u32x4_t*>(lds + k * Cfg::kRowBytes + c * 16) = wv[j];
   }
+  stage_act();
   auto put_tail = [&](int64_t t, int c, const uint4& a, const uint4& b, const float (&cs)[16], bool ok) {
     int ca, cb;
     pe_chunks(c, ca, cb);
@@ -203,7 +221,8 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   lds_barrier();
 
   for (int64_t tb = 0; tb < T; tb += 32) {
-    if (tb > 0) load_act(tb);
+    const bool more = tb + 32 < T;
+    if (more) load_act(tb + 32);
     f32x16_t acc = {};
 #pragma unroll
     for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
@@ -212,7 +231,9 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
       const bf16x4_t lo = lds_read_tr16(lds, r0);
       const bf16x4_t hi = lds_read_tr16(lds, r0 + 4 * Cfg::kRowBytes);
       const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[ks], acc, 0, 0, 0);
+      const bf16x8_t b = *reinterpret_cast<const MLA_LDS bf16x8_t*>(astage + (l & 31) * Cfg::kAPitch +
+                                                                     (k0 + 8 * (l >> 5)) * 2);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
     if constexpr (KSPLIT > 1) {
       // waves with kh > 0 hand their partial tile to the kh == 0 wave of the same n block
@@ -251,6 +272,10 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
       }
     }
     lds_barrier();                                      // staging free for the next token block
+    if (more) {
+      stage_act();                                      // every wave's fragment reads ended above
+      lds_barrier();
+    }
   }
 }
 
@@ -272,9 +297,11 @@ __global__ __launch_bounds__(256) void up_v_fp8_kernel(
   constexpr int KK = 512, NN = 128, NT = 64, KSPLIT = 2;
   using Cfg = GemmCfg<KK, NN, NT, KSPLIT>;
   constexpr int kOutPitch = QG * 2 + 16;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kTileBytes + Cfg::kRedBytes + 32 * kOutPitch];
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::kTileBytes + Cfg::kRedBytes + 32 * kOutPitch +
+                                                    Cfg::kABytes];
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
   MLA_LDS char* ostage = lds + Cfg::kTileBytes + Cfg::kRedBytes;
+  MLA_LDS char* astage = ostage + 32 * kOutPitch;
 
   const int h = blockIdx.y;
   const int64_t tb = (int64_t)blockIdx.z * 32;
@@ -288,18 +315,15 @@ __global__ __launch_bounds__(256) void up_v_fp8_kernel(
   constexpr int kChunksPerRow = NT / 8;
   constexpr int kPerThread = KK * kChunksPerRow / 256;
 
-  // activation fragments of this token block (shared by the sub-tiles)
-  bf16x8_t bfrag[Cfg::kKSteps];
-  {
-    const int64_t trow = tb + (l & 31);
-    const bool t_ok = trow < T;
-    const uint16_t* arow = A + (t_ok ? trow : 0) * a_st + h * a_sh;
+  // this token block's activations, read a token row at a time (whole cache lines)
+  // and staged in LDS for the sub-tiles' fragment reads
+  u32x4_t av[Cfg::kAPerThread];
 #pragma unroll
-    for (int ks = 0; ks < Cfg::kKSteps; ++ks) {
-      const int k0 = kh * Cfg::kKPerWave + ks * 16;
-      bfrag[ks] = *reinterpret_cast<const bf16x8_t*>(arow + k0 + 8 * (l >> 5));
-      if (!t_ok) bfrag[ks] = bf16x8_t{};
-    }
+  for (int j = 0; j < Cfg::kAPerThread; ++j) {
+    const int i = tid + 256 * j;
+    const int64_t t = tb + i / (KK / 8);
+    av[j] = t < T ? *reinterpret_cast<const u32x4_t*>(A + t * a_st + h * a_sh + (i % (KK / 8)) * 8)
+                  : u32x4_t{0u, 0u, 0u, 0u};
   }
 #pragma unroll 1
   for (int sub = 0; sub < QG / NT; ++sub) {
@@ -312,6 +336,13 @@ __global__ __launch_bounds__(256) void up_v_fp8_kernel(
       wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)(i / kChunksPerRow) * NN + (i % kChunksPerRow) * 8);
     }
     if (sub > 0) lds_barrier();                          // the previous sub-tile's W reads are done
+    if (sub == 0) {
+#pragma unroll
+      for (int j = 0; j < Cfg::kAPerThread; ++j) {
+        const int i = tid + 256 * j;
+        *reinterpret_cast<MLA_LDS u32x4_t*>(astage + (i / (KK / 8)) * Cfg::kAPitch + (i % (KK / 8)) * 16) = av[j];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int i = tid + 256 * j;
@@ -326,7 +357,9 @@ __global__ __launch_bounds__(256) void up_v_fp8_kernel(
       const bf16x4_t lo = lds_read_tr16(lds, r0);
       const bf16x4_t hi = lds_read_tr16(lds, r0 + 4 * Cfg::kRowBytes);
       const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[ks], acc, 0, 0, 0);
+      const bf16x8_t b = *reinterpret_cast<const MLA_LDS bf16x8_t*>(astage + (l & 31) * Cfg::kAPitch +
+                                                                     (k0 + 8 * (l >> 5)) * 2);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
     MLA_LDS float* red = reinterpret_cast<MLA_LDS float*>(lds + Cfg::kTileBytes);
     if (kh == 1) {
