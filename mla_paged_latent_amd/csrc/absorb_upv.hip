@@ -414,6 +414,133 @@ __global__ __launch_bounds__(256) void up_v_fp8_kernel(
   }
 }
 
+// mla_up_v_fp8 for groups of 128: a group is a head's whole V row, so one workgroup
+// owns all 128 output columns of a head for one 32-token block (wave w: columns
+// 32w .. 32w+31, full K).  W_UV[h] (128 KB) streams through two LDS buffers in
+// chunks of 64 k-rows, the next chunk's loads in flight while the current one is
+// multiplied; the activations are staged once.  Products over k < 256 and k >= 256
+// go to two accumulators that are added at the end, the order mla_up_v's K split
+// uses, so the bf16 values are the ones mla_up_v writes.
+__global__ __launch_bounds__(256) void up_v_fp8_g128_kernel(
+    const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // o_lat [T, N, 512]
+    const uint16_t* __restrict__ W,                                   // W_UV [N, 512, 128]
+    uint8_t* __restrict__ Q, int64_t q_st,                            // codes [T, N * 128]
+    float* __restrict__ S, int64_t s_st,                              // scales [T, N]
+    int64_t T) {
+  constexpr int KK = 512, NN = 128, KC = 64, NCH = KK / KC;
+  constexpr int kRowBytes = NN * 2 + 32;                // padded W row, as in the absorb tile
+  constexpr int kBufBytes = KC * kRowBytes;
+  constexpr int kAPitch = KK * 2 + 16;
+  constexpr int kOutPitch = NN * 2 + 16;
+  constexpr int kWPerThread = KC * (NN / 8) / 256;      // 4 chunks of 16 B
+  constexpr int kAPerThread = 32 * KK / 8 / 256;        // 8
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + 32 * kAPitch + 32 * kOutPitch];
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+  MLA_LDS char* astage = lds + 2 * kBufBytes;
+  MLA_LDS char* ostage = astage + 32 * kAPitch;
+
+  const int h = blockIdx.y;
+  const int64_t tb = (int64_t)blockIdx.z * 32;
+  const int tid = threadIdx.x;
+  const int nb = wave_id();
+  const int l = lane_id();
+  const int g = l >> 4, lg = l & 15;
+  const uint32_t tr_col = (uint32_t)((nb * 32 + 16 * (g & 1) + 4 * (lg & 3)) * 2);
+  const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
+  const uint16_t* wh = W + (int64_t)h * KK * NN;
+
+  u32x4_t av[kAPerThread], wv[kWPerThread];
+#pragma unroll
+  for (int j = 0; j < kAPerThread; ++j) {
+    const int i = tid + 256 * j;
+    const int64_t t = tb + i / (KK / 8);
+    av[j] = t < T ? *reinterpret_cast<const u32x4_t*>(A + t * a_st + h * a_sh + (i % (KK / 8)) * 8)
+                  : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  auto load_w = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < kWPerThread; ++j) {
+      const int i = tid + 256 * j;
+      wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)(kc * KC + i / (NN / 8)) * NN + (i % (NN / 8)) * 8);
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kWPerThread; ++j) {
+      const int i = tid + 256 * j;
+      *reinterpret_cast<MLA_LDS u32x4_t*>(lds + buf * kBufBytes + (i / (NN / 8)) * kRowBytes + (i % (NN / 8)) * 16) =
+          wv[j];
+    }
+  };
+  load_w(0);
+#pragma unroll
+  for (int j = 0; j < kAPerThread; ++j) {
+    const int i = tid + 256 * j;
+    *reinterpret_cast<MLA_LDS u32x4_t*>(astage + (i / (KK / 8)) * kAPitch + (i % (KK / 8)) * 16) = av[j];
+  }
+  store_w(0);
+  lds_barrier();
+
+  f32x16_t acc_lo = {}, acc_hi = {};
+#pragma unroll
+  for (int kc = 0; kc < NCH; ++kc) {
+    if (kc + 1 < NCH) load_w(kc + 1);
+    f32x16_t& acc = kc < NCH / 2 ? acc_lo : acc_hi;
+    const uint32_t base = (uint32_t)((kc & 1) * kBufBytes);
+#pragma unroll
+    for (int ks = 0; ks < KC / 16; ++ks) {
+      const uint32_t r0 = base + (uint32_t)((ks * 16 + tr_row0) * kRowBytes) + tr_col;
+      const bf16x4_t lo = lds_read_tr16(lds, r0);
+      const bf16x4_t hi = lds_read_tr16(lds, r0 + 4 * kRowBytes);
+      const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8_t b = *reinterpret_cast<const MLA_LDS bf16x8_t*>(
+          astage + (l & 31) * kAPitch + (kc * KC + ks * 16 + 8 * (l >> 5)) * 2);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    if (kc + 1 < NCH) {
+      store_w((kc + 1) & 1);                            // that buffer's last reader was chunk kc - 1
+      lds_barrier();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float y0 = acc_lo[4 * i] + acc_hi[4 * i], y1 = acc_lo[4 * i + 1] + acc_hi[4 * i + 1];
+    const float y2 = acc_lo[4 * i + 2] + acc_hi[4 * i + 2], y3 = acc_lo[4 * i + 3] + acc_hi[4 * i + 3];
+    const bf16x4_t v = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+    *reinterpret_cast<MLA_LDS bf16x4_t*>(ostage + (l & 31) * kOutPitch + (nb * 32 + 8 * i + 4 * (l >> 5)) * 2) = v;
+  }
+  lds_barrier();
+  // quantize: a token's group is 16 consecutive lanes of 8 values
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int item = tid + 256 * j;
+    const int r = item / 16, cc = item % 16;
+    const u32x4_t raw = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * kOutPitch + cc * 16);
+    float x[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_bits_to_f32(raw[k] & 0xFFFFu);
+      x[2 * k + 1] = bf16_bits_to_f32(raw[k] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(x[2 * k]), fabsf(x[2 * k + 1])));
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    float sc = __fdiv_rn(amax, 448.0f);
+    if (sc == 0.f) sc = 1.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= e4m3_encode(__fdiv_rn(x[k], sc)) << (8 * k);
+      hi |= e4m3_encode(__fdiv_rn(x[4 + k], sc)) << (8 * k);
+    }
+    if (tb + r < T) {
+      *reinterpret_cast<u32x2_t*>(Q + (tb + r) * q_st + (int64_t)h * NN + cc * 8) = u32x2_t{lo, hi};
+      if (cc == 0) S[(tb + r) * s_st + h] = sc;
+    }
+  }
+}
+
 }  // namespace mla
 
 extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
@@ -524,7 +651,7 @@ extern "C" mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int
                        ol_stride_h, (const uint16_t*)w_uv, (uint8_t*)out_codes, codes_stride_t, out_scales,
                        scales_stride_t, T);
   else
-    hipLaunchKernelGGL(up_v_fp8_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)o_lat, ol_stride_t,
+    hipLaunchKernelGGL(up_v_fp8_g128_kernel, grid, dim3(256), 0, s, (const uint16_t*)o_lat, ol_stride_t,
                        ol_stride_h, (const uint16_t*)w_uv, (uint8_t*)out_codes, codes_stride_t, out_scales,
                        scales_stride_t, T);
   return launch_status();
