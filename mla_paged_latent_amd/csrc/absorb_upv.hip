@@ -287,6 +287,8 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
 // grid = (NN / QG, N heads, token blocks of 32); a workgroup computes its group's
 // 64-column sub-tiles one after the other (the W tile is staged in LDS per sub-tile
 // as in head_gemm_kernel), keeps the bf16 tile in LDS, then quantizes whole groups.
+// mla_up_v_fp8 launches it for QG = 64 (one sub-tile); groups of 128 go to
+// up_v_fp8_g128_kernel below, which streams W instead of staging it twice.
 template <int QG>
 __global__ __launch_bounds__(256) void up_v_fp8_kernel(
     const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // o_lat [T, N, 512]
