@@ -451,7 +451,7 @@ __global__ __launch_bounds__(256) void up_v_fp8_g128_kernel(
   const int tr_row0 = 8 * (g >> 1) + (lg >> 2);
   const uint16_t* wh = W + (int64_t)h * KK * NN;
 
-  u32x4_t av[kAPerThread], wv[kWPerThread];
+  u32x4_t av[kAPerThread], wv[2][kWPerThread];      // two chunks of W in flight
 #pragma unroll
   for (int j = 0; j < kAPerThread; ++j) {
     const int i = tid + 256 * j;
@@ -459,34 +459,37 @@ __global__ __launch_bounds__(256) void up_v_fp8_g128_kernel(
     av[j] = t < T ? *reinterpret_cast<const u32x4_t*>(A + t * a_st + h * a_sh + (i % (KK / 8)) * 8)
                   : u32x4_t{0u, 0u, 0u, 0u};
   }
-  auto load_w = [&](int kc) {
+  auto load_w = [&](int kc, u32x4_t (&r)[kWPerThread]) {
 #pragma unroll
     for (int j = 0; j < kWPerThread; ++j) {
       const int i = tid + 256 * j;
-      wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)(kc * KC + i / (NN / 8)) * NN + (i % (NN / 8)) * 8);
+      r[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)(kc * KC + i / (NN / 8)) * NN + (i % (NN / 8)) * 8);
     }
   };
-  auto store_w = [&](int buf) {
+  auto store_w = [&](int buf, const u32x4_t (&r)[kWPerThread]) {
 #pragma unroll
     for (int j = 0; j < kWPerThread; ++j) {
       const int i = tid + 256 * j;
       *reinterpret_cast<MLA_LDS u32x4_t*>(lds + buf * kBufBytes + (i / (NN / 8)) * kRowBytes + (i % (NN / 8)) * 16) =
-          wv[j];
+          r[j];
     }
   };
-  load_w(0);
+  load_w(0, wv[0]);
+  load_w(1, wv[1]);
 #pragma unroll
   for (int j = 0; j < kAPerThread; ++j) {
     const int i = tid + 256 * j;
     *reinterpret_cast<MLA_LDS u32x4_t*>(astage + (i / (KK / 8)) * kAPitch + (i % (KK / 8)) * 16) = av[j];
   }
-  store_w(0);
+  store_w(0, wv[0]);
   lds_barrier();
 
+  // chunk kc + 2 is requested while chunk kc is multiplied and chunk kc + 1 (requested
+  // one step earlier) goes into the other LDS buffer
   f32x16_t acc_lo = {}, acc_hi = {};
 #pragma unroll
   for (int kc = 0; kc < NCH; ++kc) {
-    if (kc + 1 < NCH) load_w(kc + 1);
+    if (kc + 2 < NCH) load_w(kc + 2, wv[kc & 1]);     // chunk kc's registers were stored last step
     f32x16_t& acc = kc < NCH / 2 ? acc_lo : acc_hi;
     const uint32_t base = (uint32_t)((kc & 1) * kBufBytes);
 #pragma unroll
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(256) void up_v_fp8_g128_kernel(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
     if (kc + 1 < NCH) {
-      store_w((kc + 1) & 1);                            // that buffer's last reader was chunk kc - 1
+      store_w((kc + 1) & 1, wv[(kc + 1) & 1]);          // that buffer's last reader was chunk kc - 1
       lds_barrier();
     }
   }
