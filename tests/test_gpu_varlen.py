@@ -92,6 +92,19 @@ def test_graph_capture_replays_match_eager():
     g_out = torch.empty((c.total, 576), dtype=torch.bfloat16, device="cuda")
     mo = torch.empty((4, N, 512), dtype=torch.bfloat16, device="cuda")
     ml = torch.empty((4, N), dtype=torch.float32, device="cuda")
+    # the contractions around decode, with their fused variants
+    gen = torch.Generator(device="cuda").manual_seed(182)
+    qn = torch.randn(37, N, 192, device="cuda", generator=gen).to(torch.bfloat16)
+    wk = (torch.randn(N, 128, 512, device="cuda", generator=gen) / 23).to(torch.bfloat16)
+    wv = (torch.randn(N, 512, 128, device="cuda", generator=gen) / 23).to(torch.bfloat16)
+    ol = torch.randn(37, N, 512, device="cuda", generator=gen).to(torch.bfloat16)
+    pos = torch.randint(0, 64, (37,), device="cuda", generator=gen)
+    table = torch.from_numpy(MI.rope_cos_sin(64)).cuda()
+    qf1 = torch.empty((37, N, 576), dtype=torch.bfloat16, device="cuda")
+    qf2 = torch.empty_like(qf1)
+    yv = torch.empty((37, N * 128), dtype=torch.bfloat16, device="cuda")
+    yc = torch.empty((37, N * 128), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((37, N), dtype=torch.float32, device="cuda")
 
     def work():
         for ns in (0, 1):
@@ -100,9 +113,14 @@ def test_graph_capture_replays_match_eager():
         M.decode_varlen(qv, qsl, pool, MI.KV_BF16, bt, sl, False, SC, 0, workspace=vws, out=vo, lse=vl)
         M.gather_cache(pool, MI.KV_BF16, cbt, ccu, ct2s, out=g_out)
         M.merge_attn_states(outs[0][0].view(4, N, 512), outs[0][1].view(4, N), vo, vl, out=mo, out_lse=ml)
+        M.absorb_q(qn[..., :128], qn[..., 128:], wk, q_fused=qf1)
+        M.absorb_q_rope(qn[..., :128], qn[..., 128:], wk, pos, table, True, q_fused=qf2)
+        M.up_v(ol, wv, out=yv)
+        M.up_v_fp8(ol, wv, 128, out_codes=yc, out_scales=ys)
 
     def snapshot():
-        return [t.clone() for t in (outs[0][0], outs[0][1], outs[1][0], outs[1][1], vo, vl, g_out, mo, ml)]
+        return [t.clone() for t in (outs[0][0], outs[0][1], outs[1][0], outs[1][1], vo, vl, g_out, mo, ml,
+                                    qf1, qf2, yv, yc, ys)]
 
     work()                                    # eager, and warm-up before capture
     torch.cuda.synchronize()
@@ -116,7 +134,7 @@ def test_graph_capture_replays_match_eager():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in (outs[0][0], outs[1][0], vo, g_out, mo):       # eager work between replays
+        for t in (outs[0][0], outs[1][0], vo, g_out, mo, qf1, qf2, yv, yc, ys):   # eager work between replays
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
