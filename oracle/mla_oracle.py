@@ -507,6 +507,55 @@ def quantize_groups_fp8(y_bits: np.ndarray, group: int) -> tuple[np.ndarray, np.
     return e4m3_encode(q).reshape(T, C), s
 
 
+# --- prefill of new tokens: kv_b_proj and the 192/128 MHA --------------------
+def kv_b_proj(kv_c: np.ndarray, w_kvb: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-head up-projection of latents into the prefill keys and values.
+
+    [vLLM-MLA] §从模型层看 and §两套算法 (compute-friendly form): every latent
+    ``kv_c[s]`` becomes ``k_nope[s,h] = kv_c[s] W_UK[h]`` (P values) and
+    ``v[s,h] = kv_c[s] W_UV[h]`` (V values); §Prefill: ``kv_b_proj(kv_c)`` gives
+    both at once.  ``w_kvb[N, L, P + V]`` holds ``[W_UK[h] | W_UV[h]]`` per head.
+    Returns float64 ``k_nope[S, N, P]`` and ``v[S, N, V]``.
+    """
+    out = np.einsum("sl,hlc->shc", np.asarray(kv_c, np.float64), np.asarray(w_kvb, np.float64))
+    return out[..., :QK_NOPE_DIM], out[..., QK_NOPE_DIM:]
+
+
+def prefill_mha(q: np.ndarray, k_nope: np.ndarray, k_pe: np.ndarray, v: np.ndarray,
+                cu_q: np.ndarray, cu_k: np.ndarray, scale: float, causal: bool
+                ) -> tuple[np.ndarray, np.ndarray]:
+    """Multi-head attention of a prefill batch with 192-wide keys and 128-wide values.
+
+    [vLLM-MLA] §Prefill (run_prefill_new_tokens): the key of token ``s`` for head
+    ``h`` is ``[k_nope[s,h] | k_pe[s]]`` (the single rope key broadcast to every
+    head), the value ``v[s,h]``; the softmax scale is ``1/sqrt(192)``.  Request
+    ``b`` owns query rows ``cu_q[b] .. cu_q[b+1]-1`` and keys
+    ``cu_k[b] .. cu_k[b+1]-1``; with ``causal`` its query row ``i`` is the token
+    at position ``klen - qlen + i`` and sees keys ``0 .. klen - qlen + i`` (the
+    new tokens come after the request's context).  Returns ``out[T, N, V]`` and
+    the natural-log ``lse[T, N]`` (``o = 0``, ``lse = -inf`` for a row that sees
+    no key), the pair :func:`merge_attn_states` combines with a context part.
+    """
+    q = np.asarray(q, np.float64)
+    kn, kp, vv = (np.asarray(a, np.float64) for a in (k_nope, k_pe, v))
+    T, N, _ = q.shape
+    out = np.zeros((T, N, vv.shape[-1]))
+    lse = np.full((T, N), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        qlen, klen = q1 - q0, k1 - k0
+        for i in range(qlen):
+            nvis = klen - qlen + i + 1 if causal else klen
+            nvis = max(0, min(klen, nvis))
+            if nvis == 0:
+                continue
+            for h in range(N):
+                K = np.concatenate([kn[k0:k0 + nvis, h], kp[k0:k0 + nvis]], axis=-1)
+                o, l = attend(q[q0 + i, h][None, :], K, vv[k0:k0 + nvis, h], scale)
+                out[q0 + i, h], lse[q0 + i, h] = o[0], l[0]
+    return out, lse
+
+
 # --- the un-absorbed oracle --------------------------------------------------
 def mla_unabsorbed(q_nope: np.ndarray, q_pe: np.ndarray, pool: np.ndarray, kv_dtype: int,
                    block_table: np.ndarray, seq_lens: np.ndarray, w_uk_t: np.ndarray,

@@ -727,3 +727,68 @@ def test_rope_table_helper_follows_the_geometric_schedule():
     assert t.shape == (5, 8) and t.dtype == np.float32
     assert np.allclose(t[3, 1], math.cos(3 * 100.0 ** -0.25)) and np.allclose(t[3, 5], math.sin(3 * 100.0 ** -0.25))
     assert np.all(t[0, :4] == 1) and np.all(t[0, 4:] == 0)
+
+
+# --- prefill of new tokens -----------------------------------------------------
+def test_prefill_mha_over_kv_b_proj_equals_absorbed_decode():
+    """The compute-friendly prefill (keys and values up-projected by kv_b_proj, 192/128
+    MHA) equals the absorbed decode over the latent cache followed by the V
+    up-projection, causal rows included (q_len 2: the first row sees one token less)."""
+    rng = np.random.default_rng(1400)
+    N, lens = 3, [37, 100]
+    B, q_len = 2, 2
+    pool = np.zeros((4, 64, 576))
+    bt = np.array([[0, 1], [2, 3]])
+    lat = rng.standard_normal((4 * 64, 576))
+    pool[:] = lat.reshape(4, 64, 576)
+    wk = rng.standard_normal((N, 128, 512)) / 22
+    wv = rng.standard_normal((N, 512, 128)) / 22
+    qn = rng.standard_normal((B, q_len, N, 128))
+    qp = rng.standard_normal((B, q_len, N, 64))
+    sc = O.default_scale()
+    pool_bits = O.f64_to_bf16_bits(pool).reshape(4, 64, 576)
+    qf = O.absorb(qn.reshape(-1, N, 128), qp.reshape(-1, N, 64), wk).reshape(B, q_len, N, 576)
+    o, lse = O.decode(qf, pool_bits.view(np.uint8).reshape(4, 64, 1152), O.KV_BF16, bt, np.array(lens), sc)
+    y = O.up_v(o.reshape(-1, N, 512), wv).reshape(B, q_len, N, 128)
+    # the same tokens, packed per request, through kv_b_proj and the prefill MHA
+    latv = O.bf16_bits_to_f64(pool_bits).reshape(-1, 576)
+    rows = np.concatenate([latv[bt[b].repeat(64) * 64 + np.tile(np.arange(64), 2)][:lens[b]] for b in range(B)])
+    w_kvb = np.concatenate([np.transpose(wk, (0, 2, 1)), wv], axis=-1)        # [N, L, P + V]
+    k_nope, v = O.kv_b_proj(rows[:, :512], w_kvb)
+    cu_k = np.array([0, lens[0], lens[0] + lens[1]])
+    cu_q = np.array([0, 2, 4])
+    q = np.concatenate([qn, qp], axis=-1).reshape(-1, N, 192)
+    out, lse2 = O.prefill_mha(q, k_nope, rows[:, 512:], v, cu_q, cu_k, sc, causal=True)
+    assert np.allclose(out, y.reshape(-1, N, 128), rtol=1e-9, atol=1e-12)
+    assert np.allclose(lse2, lse.reshape(-1, N), rtol=0, atol=1e-10)
+    # non-causal: both rows see the whole request, and differ from the causal first row
+    out_nc, _ = O.prefill_mha(q, k_nope, rows[:, 512:], v, cu_q, cu_k, sc, causal=False)
+    assert np.allclose(out_nc[1], out[1], rtol=1e-12) and not np.allclose(out_nc[0], out[0], rtol=1e-3)
+
+
+def test_prefill_mha_matches_torch_sdpa_and_handles_empty_requests():
+    rng = np.random.default_rng(1401)
+    N, T = 2, 9
+    q = rng.standard_normal((T, N, 192))
+    kn, kp, v = rng.standard_normal((T, N, 128)), rng.standard_normal((T, 64)), rng.standard_normal((T, N, 128))
+    sc = O.default_scale()
+    out, lse = O.prefill_mha(q, kn, kp, v, np.array([0, T]), np.array([0, T]), sc, causal=True)
+    K = np.concatenate([kn, np.broadcast_to(kp[:, None], (T, N, 64))], axis=-1)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2))) for a in (q, K, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=sc)
+    assert np.allclose(out, ref.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+    s = np.einsum("thd,shd->hts", q, K) * sc
+    s = np.where(np.tril(np.ones((T, T), bool))[None], s, -np.inf)
+    assert np.allclose(lse, torch.logsumexp(torch.from_numpy(s), dim=-1).numpy().T, atol=1e-12)
+    # a request with queries but no keys, and one with keys but no queries
+    out2, lse2 = O.prefill_mha(q[:3], kn[:4], kp[:4], v[:4], np.array([0, 3, 3]), np.array([0, 0, 4]), sc, True)
+    assert np.all(out2 == 0) and np.all(np.isneginf(lse2))
+
+
+def test_kv_b_proj_splits_keys_and_values():
+    rng = np.random.default_rng(1402)
+    c = rng.standard_normal((5, 512))
+    w = rng.standard_normal((3, 512, 256))
+    kn, v = O.kv_b_proj(c, w)
+    assert kn.shape == (5, 3, 128) and v.shape == (5, 3, 128)
+    assert np.allclose(kn[2, 1], c[2] @ w[1, :, :128]) and np.allclose(v[4, 2], c[4] @ w[2, :, 128:])
