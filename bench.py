@@ -10,7 +10,7 @@ step's pages to the next.
 
 Prints ONE JSON line (stdout).  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
-    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill|absorb_rope_decode
+    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill|absorb_rope_decode|prefill_mha
 """
 
 from __future__ import annotations
@@ -360,6 +360,9 @@ CONTEXT_OPS = {
     # query absorption with the rope part rotated on the way (rotate-half pairing,
     # positions drawn from a 32k table), a 128-request decode batch, 128 heads
     "absorb_rope_decode": dict(kind="rope", T=128, N=128, max_pos=32768),
+    # prefill of new tokens: 4 requests of 2048 new tokens each (no context), causal,
+    # 128 heads, keys [k_nope | k_pe] 192 wide, values 128 wide
+    "prefill_mha": dict(kind="prefill", B=4, L=2048, N=128),
 }
 
 
@@ -500,6 +503,28 @@ def run_context_op(args) -> dict:
                 f"{R} rotating input copies")
         metric = "query absorption with fused RoPE GB/s (% of HBM roofline), 1 MI355X"
         dtype = "bf16"
+    elif op["kind"] == "prefill":
+        Bq, Lq, N = op["B"], op["L"], op["N"]
+        T = S = Bq * Lq
+        gen = torch.Generator(device=dev).manual_seed(560)
+        q = torch.randn(T, N, 192, device=dev, generator=gen).to(torch.bfloat16)
+        kvb = torch.randn(S, N, 256, device=dev, generator=gen).to(torch.bfloat16)
+        kp = torch.randn(S, 64, device=dev, generator=gen).to(torch.bfloat16)
+        cu = torch.arange(0, T + 1, Lq, dtype=torch.int32, device=dev)
+        o = torch.empty(T, N, 128, dtype=torch.bfloat16, device=dev)
+        lse_t = torch.empty(T, N, dtype=torch.float32, device=dev)
+        kn, vv = kvb[..., :128], kvb[..., 128:]
+        calls = [(q.data_ptr(), q.stride(0), q.stride(1), kn.data_ptr(), kn.stride(0), kn.stride(1), kp.data_ptr(),
+                  kp.stride(0), vv.data_ptr(), vv.stride(0), vv.stride(1), cu.data_ptr(), cu.data_ptr(), Bq, T, S, N,
+                  Lq, 1, float(M.DEFAULT_SCALE), o.data_ptr(), o.stride(0), o.stride(1), lse_t.data_ptr(), stream)]
+        f = L.mla_prefill_mha
+        pairs = Bq * Lq * (Lq + 1) / 2
+        flops_alg = pairs * N * (2 * 192 + 2 * 128)
+        bytes_alg = T * N * 192 * 2 + S * N * 256 * 2 + S * 64 * 2 + T * N * (128 * 2 + 4)
+        desc = (f"{args.op}: {Bq} requests x {Lq} new tokens (no context), causal, {N} heads, keys 192 wide "
+                f"([k_nope | shared k_pe]), values 128 wide, bf16")
+        metric = "prefill MHA of new tokens TFLOP/s (% of bf16 MFMA roofline), 1 MI355X"
+        dtype = "bf16"
     else:
         T, N, D = op["T"], op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=510)
@@ -542,13 +567,13 @@ def run_context_op(args) -> dict:
         log(f"[bench] the unfused call on the same inputs: {bf16_out_us:.1f} us per call")
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    if op["kind"] == "varlen" and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
+    if op["kind"] in ("varlen", "prefill") and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
         tfs = flops_alg / (mean_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof.update({"traffic": None, "kernel": args.op, "algorithmic_bytes": bytes_alg,
                  "mean_launch_us": round(mean_ms * 1e3, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-    if op["kind"] in ("varlen", "upv", "rope"):
+    if op["kind"] in ("varlen", "upv", "rope", "prefill"):
         roof["algorithmic_flops"] = flops_alg
     if bf16_out_us is not None:
         roof["unfused_call_us"] = bf16_out_us
@@ -620,6 +645,19 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         n_items = 1
         per_item = N * 128 * 512 * 2 + T * N * (192 * 2 + 576 * 2) + T * (8 + 256)
         sample = f"T={T} tokens x {N} heads through the oracle absorb_rope"
+    elif op["kind"] == "prefill":
+        N, Lq = op["N"], 64
+        rng = np.random.default_rng(561)
+        q = rng.standard_normal((Lq, N, 192))
+        kn, kp, vv = rng.standard_normal((Lq, N, 128)), rng.standard_normal((Lq, 64)), rng.standard_normal((Lq, N, 128))
+        cu = np.array([0, Lq])
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            O.prefill_mha(q, kn, kp, vv, cu, cu, O.default_scale(), True)
+            times.append(time.perf_counter() - t0)
+        n_items = 1
+        per_item = Lq * N * (192 * 2 + 256 * 2 + 128 * 2 + 4) + Lq * 64 * 2
+        sample = f"1 request x {Lq} new tokens x {N} heads through the oracle prefill_mha"
     else:
         T, N, D = 256, op["N"], op["D"]
         po, pl, so, sl = MI.random_attn_states(T, N, D, seed=522)

@@ -281,6 +281,55 @@ mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int64_t ol_str
                           int64_t scales_stride_t, void* stream);
 
 /*
+ * mla_kv_b_proj -- up-projection of latents into prefill keys and values
+ * ([vLLM-MLA] §Prefill: kv_b_proj(kv_c) gives k_nope and v of the new tokens;
+ * §两套算法, compute-friendly form).
+ *
+ *   kv_c   bf16 [S, 512], row stride kc_stride_t (the latent part of cache rows)
+ *   w_kvb  bf16 [N, 512, 256] contiguous: per head [W_UK[h] | W_UV[h]] (P = 128
+ *          key columns, then V = 128 value columns)
+ *   out    bf16 [S, N, 256], strides (out_stride_t, out_stride_h):
+ *          k_nope = out[..., 0:128], v = out[..., 128:256]
+ *
+ * out[s,h,:] = bf16_rne(sum_l kv_c[s,l] * w_kvb[h,l,:]), float32 accumulation.
+ * 1 <= N <= 128, S >= 0.  16-byte alignment, strides multiples of 8.
+ */
+mla_status_t mla_kv_b_proj(const void* kv_c, int64_t kc_stride_t, const void* w_kvb, int64_t S,
+                           int32_t N, void* out, int64_t out_stride_t, int64_t out_stride_h,
+                           void* stream);
+
+/*
+ * mla_prefill_mha -- attention of the new tokens of a prefill batch
+ * ([vLLM-MLA] §Prefill, run_prefill_new_tokens: keys [k_nope | k_pe] with the one
+ * rope key broadcast over heads (192 wide), values 128 wide, softmax scale
+ * 1/sqrt(192); the output and LSE merge with a context part through
+ * mla_merge_attn_states).
+ *
+ *   q             bf16 [T, N, 192] ([q_nope | q_pe]), strides (q_stride_t, q_stride_h)
+ *   k_nope        bf16 [S, N, 128], strides (kn_stride_t, kn_stride_h)
+ *   k_pe          bf16 [S, 64], row stride kp_stride_t
+ *   v             bf16 [S, N, 128], strides (v_stride_t, v_stride_h)
+ *   cu_seqlens_q  int32 [B + 1] (device): request b owns query rows [cu_q[b], cu_q[b+1])
+ *   cu_seqlens_k  int32 [B + 1] (device): and keys [cu_k[b], cu_k[b+1])
+ *   max_q_len     the longest request's query rows (rows past it are not written)
+ *   causal        nonzero: query row i of a request with qlen rows and klen keys
+ *                 sees keys 0 .. klen - qlen + i; zero: all klen keys
+ *   out           bf16 [T, N, 128], strides (o_stride_t, o_stride_h)
+ *   lse           float32 [T, N] contiguous, natural log of the scaled scores
+ *
+ * A row that sees no key gets o = 0, lse = -inf.  Request bounds are clamped to
+ * [0, T] and [0, S].  1 <= N <= 128, 0 <= B <= 65535, T, S < 2^31.  Pointers
+ * 16-byte aligned (lse and cu arrays 4), strides multiples of 8.
+ */
+mla_status_t mla_prefill_mha(const void* q, int64_t q_stride_t, int64_t q_stride_h, const void* k_nope,
+                             int64_t kn_stride_t, int64_t kn_stride_h, const void* k_pe,
+                             int64_t kp_stride_t, const void* v, int64_t v_stride_t, int64_t v_stride_h,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t B,
+                             int64_t T, int64_t S, int32_t N, int32_t max_q_len, int32_t causal,
+                             float softmax_scale, void* out, int64_t o_stride_t, int64_t o_stride_h,
+                             float* lse, void* stream);
+
+/*
  * mla_gather_cache -- gather context rows of the paged cache into a contiguous
  * bf16 workspace ([vLLM-MLA] §Prefill, chunked context: the rows a chunk needs
  * are collected by block_table, cu_seq_lens and token_to_seq so that kv_b_proj

@@ -67,6 +67,11 @@ def lib() -> ctypes.CDLL:
     L.mla_absorb_q_rope.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, i64,
                                     i64, vp]
     L.mla_absorb_q_rope.restype = i32
+    L.mla_kv_b_proj.argtypes = [vp, i64, vp, i64, i32, vp, i64, i64, vp]
+    L.mla_kv_b_proj.restype = i32
+    L.mla_prefill_mha.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, i32, i64, i64,
+                                  i32, i32, i32, ctypes.c_float, vp, i64, i64, vp, vp]
+    L.mla_prefill_mha.restype = i32
     L.mla_up_v_fp8.argtypes = [vp, i64, i64, vp, i64, i32, i32, vp, i64, vp, i64, vp]
     L.mla_up_v_fp8.restype = i32
     L.mla_decode_varlen_workspace_size.argtypes = [i64, i32, i32, i32]
@@ -231,6 +236,49 @@ def up_v_fp8(o_lat: torch.Tensor, w_uv: torch.Tensor, group: int = 128,
         _ptr(o_lat), o_lat.stride(0), o_lat.stride(1), _ptr(w_uv), T, N, group, _ptr(out_codes),
         out_codes.stride(0), _ptr(out_scales), out_scales.stride(0), _stream(stream)))
     return out_codes, out_scales
+
+
+def kv_b_proj(kv_c: torch.Tensor, w_kvb: torch.Tensor, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """``out[s, h] = kv_c[s] . w_kvb[h]`` (bf16 ``[S, N, 256]``: k_nope then v)."""
+    S, Lr = kv_c.shape
+    N = w_kvb.shape[0]
+    assert Lr == KV_LORA_RANK and kv_c.dtype == torch.bfloat16 and kv_c.stride(-1) == 1
+    assert w_kvb.shape == (N, KV_LORA_RANK, 256) and w_kvb.is_contiguous() and w_kvb.dtype == torch.bfloat16
+    if out is None:
+        out = torch.empty((S, N, 256), dtype=torch.bfloat16, device=kv_c.device)
+    _check("mla_kv_b_proj", lib().mla_kv_b_proj(_ptr(kv_c), kv_c.stride(0), _ptr(w_kvb), S, N, _ptr(out),
+                                                out.stride(0), out.stride(1), _stream(stream)))
+    return out
+
+
+def prefill_mha(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Tensor, v: torch.Tensor,
+                cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_q_len: int,
+                causal: bool = True, softmax_scale: float = DEFAULT_SCALE,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Attention of a prefill batch's new tokens: ``q[T, N, 192]`` against keys
+    ``[k_nope[S, N, 128] | k_pe[S, 64]]`` and values ``v[S, N, 128]``; returns
+    ``out[T, N, 128]`` and ``lse[T, N]``."""
+    T, N, D = q.shape
+    S = k_nope.shape[0]
+    assert D == 192 and q.dtype == torch.bfloat16 and q.stride(-1) == 1
+    assert k_nope.shape[1:] == (N, 128) and v.shape == (S, N, 128) and k_pe.shape == (S, 64)
+    assert k_nope.stride(-1) == 1 and v.stride(-1) == 1 and k_pe.stride(-1) == 1
+    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32
+    B = cu_seqlens_q.numel() - 1
+    assert cu_seqlens_k.numel() == B + 1
+    if out is None:
+        out = torch.empty((T, N, 128), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, N), dtype=torch.float32, device=q.device)
+    assert lse.is_contiguous() and lse.shape == (T, N)
+    _check("mla_prefill_mha", lib().mla_prefill_mha(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(k_pe),
+        k_pe.stride(0), _ptr(v), v.stride(0), v.stride(1), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, S, N,
+        int(max_q_len), 1 if causal else 0, float(softmax_scale), _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def gather_cache(kv_cache: torch.Tensor, kv_dtype: int, block_table: torch.Tensor,

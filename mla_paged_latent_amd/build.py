@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_paged_latent.so")
-SOURCES = ["cache_write.hip", "absorb_upv.hip", "decode.hip", "context.hip"]
+SOURCES = ["cache_write.hip", "absorb_upv.hip", "decode.hip", "context.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -661,3 +661,24 @@ extern "C" mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int
                        scales_stride_t, T);
   return launch_status();
 }
+
+extern "C" mla_status_t mla_kv_b_proj(const void* kv_c, int64_t kc_stride_t, const void* w_kvb, int64_t S,
+                                      int32_t N, void* out, int64_t out_stride_t, int64_t out_stride_h,
+                                      void* stream) {
+  using namespace mla;
+  if (S < 0 || N < 1 || N > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  if (S == 0) return MLA_OK;
+  if (!kv_c || !w_kvb || !out) return MLA_ERR_NULL;
+  if (!aligned16(kv_c) || !aligned16(w_kvb) || !aligned16(out) || !mult8(kc_stride_t) || !mult8(out_stride_t) ||
+      !mult8(out_stride_h))
+    return MLA_ERR_ALIGN;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+  // the latent has no head dimension: every head's workgroups read the same rows
+  hipLaunchKernelGGL((head_gemm_kernel<512, 256, 64, 2, kNoTail>), dim3(256 / 64, N), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), (const uint16_t*)kv_c, kc_stride_t, (int64_t)0,
+                     (const uint16_t*)w_kvb, (uint16_t*)out, out_stride_t, out_stride_h, (const uint16_t*)nullptr,
+                     (int64_t)0, (int64_t)0, (const int64_t*)nullptr, (const float*)nullptr, (int64_t)0, 0, S);
+  return launch_status();
+}

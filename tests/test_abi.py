@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     fns = declared_functions()
     for f in ("mla_cache_write", "mla_absorb_q", "mla_decode", "mla_up_v",
-              "mla_up_v_fp8", "mla_absorb_q_rope", "mla_decode_workspace_size", "mla_status_str"):
+              "mla_up_v_fp8", "mla_absorb_q_rope", "mla_kv_b_proj", "mla_prefill_mha",
+              "mla_decode_workspace_size", "mla_status_str"):
         assert f in fns
 
 
@@ -115,6 +116,21 @@ def test_other_calls_reject_bad_arguments():
     assert r(p, 128, 128, p, 64, 64, p, 4, 16, p, vp(264), 16, 1, p, 576, 576, None) == 4
     assert r(p, 128, 128, p, 64, 64, p, 4, 16, vp(260), p, 16, 1, p, 576, 576, None) == 4
     assert r(p, 128, 128, p, 66, 64, p, 4, 16, p, p, 16, 1, p, 576, 576, None) == 4
+    # prefill: kv_b_proj and the 192/128 attention
+    assert L.mla_kv_b_proj(p, 512, p, 4, 129, p, 4096, 256, None) == 2
+    assert L.mla_kv_b_proj(p, 512, p, 0, 16, p, 4096, 256, None) == 0
+    assert L.mla_kv_b_proj(p, 512, None, 4, 16, p, 4096, 256, None) == 1
+    assert L.mla_kv_b_proj(p, 514, p, 4, 16, p, 4096, 256, None) == 4
+    m = L.mla_prefill_mha
+    args = lambda **o: [o.get(k, d) for k, d in [("q", p), ("qt", 3072), ("qh", 192), ("kn", p), ("knt", 2048),
+                                                   ("knh", 128), ("kp", p), ("kpt", 64), ("v", p), ("vt", 2048),
+                                                   ("vh", 128), ("cq", p), ("ck", p), ("B", 2), ("T", 8),
+                                                   ("S", 8), ("N", 16), ("mq", 4), ("c", 1), ("sc", 0.07),
+                                                   ("o", p), ("ot", 2048), ("oh", 128), ("l", p), ("s", None)]]
+    assert m(*args(N=0)) == 2 and m(*args(B=-1)) == 2 and m(*args(B=70000)) == 2
+    assert m(*args(T=0)) == 0 and m(*args(B=0)) == 0 and m(*args(mq=0)) == 0
+    assert m(*args(kp=None)) == 1 and m(*args(ck=None)) == 1
+    assert m(*args(qh=196)) == 4 and m(*args(l=vp(258))) == 4 and m(*args(v=vp(264))) == 4
     # up_v with fp8 group quantization of its output
     f = L.mla_up_v_fp8
     assert f(p, 512, 512, p, 4, 129, 128, p, 128 * 129, p, 129, None) == 2
