@@ -76,10 +76,11 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
 #pragma unroll
   for (int ft = 0; ft < 8; ++ft) o[ft] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < kend; kb += kPK) {
-    // keys kb .. kb+63: 24 chunks of 16 B per key row (16 of k_nope, 8 of k_pe) and
-    // 16 chunks per value row; rows past the request read as zeros
-    u32x4_t kv[6], vv[4];
+  // keys kb .. kb+63: 24 chunks of 16 B per key row (16 of k_nope, 8 of k_pe) and
+  // 16 chunks per value row; rows past the request read as zeros.  The next block's
+  // chunks are loaded while the current block is multiplied.
+  u32x4_t kv[6], vv[4];
+  auto load_block = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
       const int i = tid + 256 * j;
@@ -97,6 +98,9 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
       vv[j] = key < klen ? *reinterpret_cast<const u32x4_t*>(p.v + (k0 + key) * p.v_st + (int64_t)h * p.v_sh + c * 8)
                          : u32x4_t{0u, 0u, 0u, 0u};
     }
+  };
+  if (kend > 0) load_block(0);
+  for (int kb = 0; kb < kend; kb += kPK) {
     lds_barrier();                                      // the previous block's reads are done
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
       }
     }
     lds_barrier();
+    if (kb + kPK < kend) load_block(kb + kPK);
 
     // S^T: four 16-key tiles; s[kt][r] = score of key kb + 16kt + 4g + r, query l16
     f32x4_t s[4];
