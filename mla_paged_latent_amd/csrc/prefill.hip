@@ -90,10 +90,12 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
                                    : p.kp + (k0 + key) * p.kp_st + (c - 16) * 8;
       kv[j] = key < klen ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
     }
+    // values: wave w takes keys 16w .. 16w+15, step j chunks 4j .. 4j+3, so that the
+    // transposing 2-byte LDS writes below fall on 16 banks per instruction (with
+    // 16 chunks of one key per 16 lanes they fell on 4)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / 16, c = i % 16;
+      const int r = 16 * w + l16, c = 4 * j + g;
       const int key = kb + r;
       vv[j] = key < klen ? *reinterpret_cast<const u32x4_t*>(p.v + (k0 + key) * p.v_st + (int64_t)h * p.v_sh + c * 8)
                          : u32x4_t{0u, 0u, 0u, 0u};
@@ -109,8 +111,7 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / 16, c = i % 16;
+      const int r = 16 * w + l16, c = 4 * j + g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         vt[(c * 8 + 2 * e) * kVtPitch + r] = (uint16_t)(vv[j][e] & 0xFFFFu);
