@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
   // keys kb .. kb+63: 24 chunks of 16 B per key row (16 of k_nope, 8 of k_pe) and
   // 16 chunks per value row; rows past the request read as zeros.  The next block's
   // chunks are loaded while the current block is multiplied.
-  u32x4_t kv[6], vv[4];
+  u32x4_t kv[6], vv[2][2];
   auto load_block = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -90,15 +90,20 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
                                    : p.kp + (k0 + key) * p.kp_st + (c - 16) * 8;
       kv[j] = key < klen ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    // values: wave w takes keys 16w .. 16w+15, step j chunks 4j .. 4j+3, so that the
-    // transposing 2-byte LDS writes below fall on 16 banks per instruction (with
-    // 16 chunks of one key per 16 lanes they fell on 4)
+    // values: a lane takes one 16-byte chunk (8 features) of two adjacent keys, so
+    // that the transposed rows get 4-byte writes (the two keys' values of one
+    // feature); lanes 0..31 of a wave cover the 32 key pairs of one chunk, lanes
+    // 32..63 the next chunk: 64 distinct banks per write instruction
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * w + l16, c = 4 * j + g;
-      const int key = kb + r;
-      vv[j] = key < klen ? *reinterpret_cast<const u32x4_t*>(p.v + (k0 + key) * p.v_st + (int64_t)h * p.v_sh + c * 8)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 2; ++j) {
+      const int kp = l & 31, c = 2 * (2 * w + j) + (l >> 5);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int key = kb + 2 * kp + d;
+        vv[j][d] = key < klen
+                       ? *reinterpret_cast<const u32x4_t*>(p.v + (k0 + key) * p.v_st + (int64_t)h * p.v_sh + c * 8)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
   };
   if (kend > 0) load_block(0);
@@ -109,13 +114,16 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
       const int i = tid + 256 * j;
       *reinterpret_cast<MLA_LDS u32x4_t*>(lds + (i / 24) * kKPitch * 2 + (i % 24) * 16) = kv[j];
     }
+    MLA_LDS uint32_t* vt32 = reinterpret_cast<MLA_LDS uint32_t*>(vt);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * w + l16, c = 4 * j + g;
+    for (int j = 0; j < 2; ++j) {
+      const int kp = l & 31, c = 2 * (2 * w + j) + (l >> 5);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vt[(c * 8 + 2 * e) * kVtPitch + r] = (uint16_t)(vv[j][e] & 0xFFFFu);
-        vt[(c * 8 + 2 * e + 1) * kVtPitch + r] = (uint16_t)(vv[j][e] >> 16);
+        // features c*8 + 2e and c*8 + 2e + 1 of keys 2kp, 2kp + 1
+        const uint32_t a = vv[j][0][e], b = vv[j][1][e];
+        vt32[((c * 8 + 2 * e) * kVtPitch) / 2 + kp] = (a & 0xFFFFu) | (b << 16);
+        vt32[((c * 8 + 2 * e + 1) * kVtPitch) / 2 + kp] = (a >> 16) | (b & 0xFFFF0000u);
       }
     }
     lds_barrier();
