@@ -42,7 +42,7 @@ constexpr int kPK = 64;              // keys per block
 constexpr int kKPitch = 192 + 8;     // bf16 per staged key row (400 B: 16 rows on distinct banks)
 constexpr int kVtPitch = kPK + 8;    // bf16 per transposed value row (144 B)
 
-__global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_mha_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[(kPK * kKPitch + 128 * kVtPitch) * 2];
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
   MLA_LDS uint16_t* ks = reinterpret_cast<MLA_LDS uint16_t*>(lds);
@@ -77,8 +77,9 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
   for (int ft = 0; ft < 8; ++ft) o[ft] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // keys kb .. kb+63: 24 chunks of 16 B per key row (16 of k_nope, 8 of k_pe) and
-  // 16 chunks per value row; rows past the request read as zeros.  The next block's
-  // chunks are loaded while the current block is multiplied.
+  // 16 chunks per value row; rows past the request read as zeros.  (Loading the next
+  // block during the current one's MFMAs measured no faster and cost the registers
+  // that three waves per SIMD need.)
   u32x4_t kv[6], vv[2][2];
   auto load_block = [&](int kb) {
 #pragma unroll
@@ -106,8 +107,8 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
       }
     }
   };
-  if (kend > 0) load_block(0);
   for (int kb = 0; kb < kend; kb += kPK) {
+    load_block(kb);
     lds_barrier();                                      // the previous block's reads are done
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -127,7 +128,6 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(PrefillParams p) {
       }
     }
     lds_barrier();
-    if (kb + kPK < kend) load_block(kb + kPK);
 
     // S^T: four 16-key tiles; s[kt][r] = score of key kb + 16kt + 4g + r, query l16
     f32x4_t s[4];
