@@ -701,7 +701,7 @@ def main():
         print(json.dumps(rec), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "only --gpus 1 is supported: the decode path shards by "
+        print(json.dumps({"error": "runs on one GPU only (--gpus 1): the decode path shards by "
                                    "request (attention-DP) or heads (TP) with no exchange inside the "
                                    "path, so only --gpus 1 is measured"}), flush=True)
         sys.exit(2)
