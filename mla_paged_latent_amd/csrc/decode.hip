@@ -583,6 +583,22 @@ __device__ __forceinline__ void wait_blocks_after(int later, int w) {
   }
 }
 
+// wait until this wave's query and the blocks issued before it have landed, with
+// `later` (0, 1 or 2) whole blocks issued after the query still allowed in flight
+template <bool FP8>
+__device__ __forceinline__ void wait_query_and_block0(int later, int w) {
+  if (later <= 0) {
+    wait_vmcnt<0>();
+  } else if (later == 1) {
+    wait_blocks_after<FP8>(1, w);
+  } else if constexpr (FP8) {
+    if (w == 3) wait_vmcnt<8>();
+    else wait_vmcnt<10>();
+  } else {
+    wait_vmcnt<18>();
+  }
+}
+
 template <bool FP8, bool P64>
 __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kNLdsBytes];
@@ -695,20 +711,27 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       };
 
       // the piece's first three blocks: in flight already (issued while the previous
-      // piece finished) or issued here, ahead of the query loads.  The stream must be
-      // three blocks ahead before step 0: each step issues only one more.
+      // piece finished) or issued here.  The stream must be three blocks ahead before
+      // step 0: each step issues only one more.
+      // When nothing of the piece is in flight (a unit's first piece), only block 0 goes
+      // out ahead of the query and the rest after it, so that step 0 waits for block 0
+      // and the query only.
       const int issued_at_start = issued;
-      for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      const bool fresh = !q_ready && issued == g0;
+      for (int k = 0; k < (fresh ? 1 : 3) && issued < g0 + 3; ++k) issue_next();
       const bool topped = issued >= g0 + 3;
+      const int before_q = issued;
       if (!q_ready) load_q(b);
       fetch_nxt();
       if (!topped) {
         for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       }
       // the query and the blocks issued before it (block 0 among them) have landed once
-      // at most the operations issued after the query are outstanding: with the query
-      // loaded at the end of the previous piece, at least its 8 output stores per wave
-      if (!q_ready || issued != issued_at_start) wait_vmcnt<0>();
+      // at most the operations issued after the query are outstanding: the blocks issued
+      // after it, or with the query loaded at the end of the previous piece, at least
+      // that piece's 8 output stores per wave
+      if (fresh) wait_query_and_block0<FP8>(issued - before_q, w);
+      else if (!q_ready || issued != issued_at_start) wait_vmcnt<0>();
       else wait_vmcnt<8>();
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[kk]));
@@ -795,7 +818,8 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
           }
 
           // weights p = 2^(x - m), bf16 for the MFMA (fp8: times v_scale); the sums keep
-          // the exact weights (LSE) and the rounded ones (O)
+          // the exact weights (LSE) and the rounded ones (O).  A token whose v_scale is 0
+          // has V = 0 and still counts with its rounded weight.
           {
             f32x4_t vf, ivf;
             if constexpr (FP8) {
@@ -809,7 +833,7 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
               const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
               pk[i] = rr;
               lsum += pr;
-              lrsum += FP8 ? (float)rr * ivf[i] : (float)rr;
+              lrsum += FP8 ? (vf[i] != 0.f ? (float)rr * ivf[i] : (float)(__bf16)pr) : (float)rr;
             }
             if (w < 2) *reinterpret_cast<MLA_LDS bf16x4_t*>(smem + kNP + (j & 1) * kNPBytes + pwrite) = pk;
           }
@@ -1259,10 +1283,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         return v < kBlk ? v : kBlk;
       };
       // the piece's first three blocks: in flight already (issued while the previous
-      // piece finished) or issued here, ahead of the query loads
+      // piece finished) or issued here
+      // When nothing of the piece is in flight (a unit's first piece), only block 0 goes
+      // out ahead of the query and the rest after it, so that step 0 waits for block 0
+      // and the query only.
       const int issued_at_start = issued;
-      for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      const bool fresh = !q_ready && issued == g0;
+      for (int k = 0; k < (fresh ? 1 : 3) && issued < g0 + 3; ++k) issue_next();
       const bool topped = issued >= g0 + 3;
+      const int before_q = issued;
 
       if (!q_ready) load_q(b);
       fetch_nxt();
@@ -1270,10 +1299,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
       }
       // The query and the blocks issued before it (block 0 among them) have landed once
-      // at most the vector-memory operations issued after the query are outstanding.
-      // With the query loaded at the end of the previous piece these are at least that
-      // piece's output stores.
-      if (!q_ready || issued != issued_at_start || stores_after_q == 0) wait_vmcnt<0>();
+      // at most the vector-memory operations issued after the query are outstanding: the
+      // blocks issued after it, or with the query loaded at the end of the previous piece
+      // at least that piece's output stores.
+      if (fresh) wait_query_and_block0<FP8>(issued - before_q, w);
+      else if (!q_ready || issued != issued_at_start || stores_after_q == 0) wait_vmcnt<0>();
       else if (stores_after_q == 16) wait_vmcnt<16>();
       else wait_vmcnt<32>();
 #pragma unroll
@@ -1390,7 +1420,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           }
 
           // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
-          // the sums keep both the exact weights (LSE) and the rounded ones (O).
+          // the sums keep both the exact weights (LSE) and the rounded ones (O).  A token
+          // whose v_scale is 0 has V = 0 and still counts with its rounded weight.
           {
             f32x4_t vf, ivf;
             if constexpr (FP8) {
@@ -1411,7 +1442,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
                 const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
                 pk[i] = rr;
                 lsum[rs] += pr;
-                lrsum[rs] += FP8 ? (float)rr * ivf[i] : (float)rr;
+                lrsum[rs] += FP8 ? (vf[i] != 0.f ? (float)rr * ivf[i] : (float)(__bf16)pr) : (float)rr;
               }
               // row R, tokens 16th + 4g4 .. +3: chunk 2th + (g4 >> 1), half g4 & 1
               const int R = 32 * rg + 16 * rs + l16;

@@ -278,6 +278,37 @@ def test_fp8_rows_with_distinct_k_and_v_scales(N):
 
 
 @pytest.mark.parametrize("N", [16, 128])
+def test_fp8_rows_with_zero_v_scale(N):
+    """fp8 rows whose v_scale is 0 have V = 0 but keep their weight in the softmax
+    (a row's output must still be the convex combination the oracle forms), also when
+    such a token holds a row's largest score: in every request one visible token gets
+    a large K scale and a zero V scale."""
+    rng = np.random.default_rng(190 + N)
+    seq = [200, 64, 37]
+    w = MI.make_workload("fp8v0", 3, 1, N, seq, None, MI.KV_FP8, False, 190 + N)
+    rows = MI.random_fp8_rows(rng, w.num_pages * 64, max_code_exp=8)
+    ks = rows[:, 576:580].copy().view("<f4").reshape(-1)
+    vs = rows[:, 580:584].copy().view("<f4").reshape(-1)
+    zero = rng.random(len(vs)) < 0.2
+    for b, n in enumerate(seq):
+        t = int(rng.integers(0, n))
+        slot = int(w.block_table[b, t // 64]) * 64 + t % 64
+        zero[slot] = True
+        ks[slot] = 16.0
+    vs[zero] = 0.0
+    rows[:, 576:580] = ks.astype("<f4").view(np.uint8).reshape(-1, 4)
+    rows[:, 580:584] = vs.astype("<f4").view(np.uint8).reshape(-1, 4)
+    ref_pool = rows.reshape(w.num_pages, 64, 584)
+    pool = torch.from_numpy(ref_pool.copy()).cuda()
+    o_ref, lse_ref = O.decode(O.bf16_bits_to_f64(w.q), ref_pool, MI.KV_FP8, w.block_table, w.seq_lens, SC)
+    for ns in (0, 1):
+        say(f"fp8 zero v_scale N={N} ns={ns}")
+        out, lse = gpu_decode(w, pool, w.q, ns)
+        check_out(to_f64(out), o_ref, "fp8 zero v_scale")
+        check_lse(lse.cpu().numpy(), lse_ref, "fp8 zero v_scale")
+
+
+@pytest.mark.parametrize("N", [16, 128])
 def test_large_score_range_triggers_reference_redo(N):
     """Scores that grow by far more than the reference slack within a unit: the
     kernel redoes the unit with a larger reference and still matches the oracle."""
