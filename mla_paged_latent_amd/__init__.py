@@ -104,6 +104,22 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _need_out(call: str, out: torch.Tensor, shape: tuple) -> None:
+    """A caller-supplied output: bf16 of exactly ``shape`` with a contiguous last dim
+    (the C call writes bf16 rows at the tensor's strides)."""
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(shape) or out.stride(-1) != 1:
+        raise ValueError(f"{call}: out must be bfloat16 {tuple(shape)} with a contiguous last dim, got "
+                         f"{out.dtype} {tuple(out.shape)} strides {out.stride()}")
+
+
+def _need_lse(call: str, lse: torch.Tensor, shape: tuple) -> None:
+    """A caller-supplied LSE: contiguous float32 of exactly ``shape`` (the C call
+    writes it densely, without strides)."""
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous():
+        raise ValueError(f"{call}: lse must be contiguous float32 {tuple(shape)}, got "
+                         f"{lse.dtype} {tuple(lse.shape)} strides {lse.stride()}")
+
+
 def cache_write(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
                 kv_cache: torch.Tensor, kv_dtype: int, stream=None) -> None:
     """Scatter rows ``[kv_c | k_pe]`` into ``kv_cache`` at ``slot_mapping`` (see mla.h).
@@ -187,6 +203,8 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_dtype: int, block_table: 
         out = torch.empty((B, q_len, N, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, q_len, N), dtype=torch.float32, device=q.device)
+    _need_out("decode", out, (B, q_len, N, KV_LORA_RANK))
+    _need_lse("decode", lse, (B, q_len, N))
     need = decode_workspace_size(B, q_len, N, num_splits)
     if need == 0:
         raise MLAError("mla_decode_workspace_size", 2)
@@ -272,7 +290,8 @@ def prefill_mha(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Tensor, v: to
         out = torch.empty((T, N, 128), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, N), dtype=torch.float32, device=q.device)
-    assert lse.is_contiguous() and lse.shape == (T, N)
+    _need_out("prefill_mha", out, (T, N, 128))
+    _need_lse("prefill_mha", lse, (T, N))
     _check("mla_prefill_mha", lib().mla_prefill_mha(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_nope), k_nope.stride(0), k_nope.stride(1), _ptr(k_pe),
         k_pe.stride(0), _ptr(v), v.stride(0), v.stride(1), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, S, N,
@@ -346,6 +365,8 @@ def decode_varlen(q: torch.Tensor, query_start_loc: torch.Tensor, kv_cache: torc
         out = torch.empty((T, N, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, N), dtype=torch.float32, device=q.device)
+    _need_out("decode_varlen", out, (T, N, KV_LORA_RANK))
+    _need_lse("decode_varlen", lse, (T, N))
     need = int(lib().mla_decode_varlen_workspace_size(T, N, num_splits, block_table.shape[1]))
     if need == 0:
         raise MLAError("mla_decode_varlen_workspace_size", 2)

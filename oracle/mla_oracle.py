@@ -619,6 +619,3 @@ def request_bytes(seq_len: int, layers: int, kv_dtype: int) -> int:
     """Cache bytes of one request across ``layers`` layers."""
     return seq_len * layers * row_bytes(kv_dtype)
 
-
-def log2e() -> float:
-    return 1.0 / math.log(2.0)

@@ -14,8 +14,12 @@ import mla_inputs as MI
 import mla_paged_latent_amd as M
 from oracle import mla_oracle as O
 
-# Output gate: max |o_gpu - o_ref| <= OUT_TOL * RMS(o_ref) over the whole output
-# of a call; LSE gate: max |lse_gpu - lse_ref| <= LSE_TOL (absolute, natural log).
+# Output gate (check_out), per request b: the largest element error net of half a bf16
+# ulp of the larger magnitude, max_e (|o_gpu - o_ref| - ulp_bf16(max(|o_gpu|, |o_ref|)) / 2),
+# must stay within OUT_TOL * RMS(o_ref[b]); rows that see no token must be exactly 0.
+# (The half ulp is the unavoidable final bf16 rounding: single elements reach ~9x the
+# RMS on long contexts, so a whole-call max-abs test would fail on that rounding alone.)
+# LSE gate (check_lse): max |lse_gpu - lse_ref| <= LSE_TOL (absolute, natural log).
 OUT_TOL = 2e-2
 LSE_TOL = 1e-3
 

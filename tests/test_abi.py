@@ -13,8 +13,26 @@ import mla_paged_latent_amd as M
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH),
-                                reason="HIP library not built (python -m mla_paged_latent_amd.build)")
+
+
+def _ensure_library() -> None:
+    """Build the library in-tree when it is missing (hipcc cross-compiles without a
+    GPU); skip only if there is no hipcc either."""
+    if os.path.exists(M.LIB_PATH):
+        return
+    from mla_paged_latent_amd import build as B
+    try:
+        B.hipcc()
+    except RuntimeError:
+        pytest.skip("HIP library not built and no hipcc to build it")
+    B.build()
+
+
+# every test here runs in both test jobs: the CPU one (-m "not gpu") and the GPU one
+@pytest.fixture(autouse=True, params=[pytest.param("host"), pytest.param("gpu-job", marks=pytest.mark.gpu)])
+def _library(request):
+    _ensure_library()
+    yield
 
 
 def declared_functions():
@@ -182,3 +200,43 @@ def test_varlen_call_rejects_bad_arguments_without_a_gpu():
     assert d(qsl=None) == 1 and d(lse=None) == 1
     assert d(ws=None) == 5 and d(wsb=need - 1) == 5
     assert d(q=vp(264)) == 4 and d(qst=9220) == 4 and d(qsl=vp(258)) == 4 and d(ws=vp(512 + 16)) == 4
+
+
+def test_binding_rejects_mismatched_out_and_lse():
+    """Caller-supplied out / lse tensors of the wrong dtype, shape or layout raise
+    before the C call (which would write bf16 rows at out's strides and a dense
+    float32 lse)."""
+    import torch
+    B, q_len, N = 2, 1, 16
+    q = torch.zeros((B, q_len, N, 576), dtype=torch.bfloat16)
+    pool = torch.zeros((4, 64, 1152), dtype=torch.uint8)
+    bt = torch.zeros((B, 4), dtype=torch.int32)
+    sl = torch.ones((B,), dtype=torch.int32)
+    good_out = torch.empty((B, q_len, N, 512), dtype=torch.bfloat16)
+    good_lse = torch.empty((B, q_len, N), dtype=torch.float32)
+    bad = [
+        dict(out=torch.empty((B, q_len, N, 512), dtype=torch.float32), lse=good_lse),
+        dict(out=torch.empty((B, q_len, N, 256), dtype=torch.bfloat16), lse=good_lse),
+        dict(out=torch.empty((B, q_len, N, 1024), dtype=torch.bfloat16)[..., ::2], lse=good_lse),
+        dict(out=good_out, lse=torch.empty((B, q_len, N), dtype=torch.bfloat16)),
+        dict(out=good_out, lse=torch.empty((B, q_len, N - 1), dtype=torch.float32)),
+        dict(out=good_out, lse=torch.empty((B, q_len, 2 * N), dtype=torch.float32)[..., ::2]),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            M.decode(q, pool, 0, bt, sl, M.DEFAULT_SCALE, 0, **kw)
+    T = 3
+    qv = torch.zeros((T, N, 576), dtype=torch.bfloat16)
+    qsl = torch.tensor([0, 1, 3], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        M.decode_varlen(qv, qsl, pool, 0, bt, sl, lse=torch.empty((T, N), dtype=torch.float32).t())
+    with pytest.raises(ValueError):
+        M.decode_varlen(qv, qsl, pool, 0, bt, sl, out=torch.empty((T, N, 512), dtype=torch.float16))
+    qp = torch.zeros((T, N, 192), dtype=torch.bfloat16)
+    kn = torch.zeros((T, N, 128), dtype=torch.bfloat16)
+    kp = torch.zeros((T, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        M.prefill_mha(qp, kn, kp, kn, cu, cu, T, out=torch.empty((T, N, 128), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        M.prefill_mha(qp, kn, kp, kn, cu, cu, T, lse=torch.empty((N, T), dtype=torch.float32))

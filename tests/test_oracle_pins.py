@@ -409,6 +409,77 @@ def test_fp8_views_use_their_own_scales():
     assert not np.allclose(o2, o, rtol=1e-3)
 
 
+def _hand_fp8_row(codes, k_scale: float, v_scale: float) -> np.ndarray:
+    """One raw fp8 cache row written byte by byte: 576 code bytes, then the float32
+    K scale, then the float32 V scale (the row format of [vLLM-MLA] §缓存的形状:
+    scales appended after the data, one for K and one for V)."""
+    import struct
+    row = np.zeros(584, dtype=np.uint8)
+    row[:576] = np.asarray(codes, dtype=np.uint8)
+    row[576:580] = np.frombuffer(struct.pack("<f", k_scale), dtype=np.uint8)
+    row[580:584] = np.frombuffer(struct.pack("<f", v_scale), dtype=np.uint8)
+    return row
+
+
+def test_fp8_scale_slots_hand_row():
+    """Bytes 576..579 scale the K view (all 576 elements), bytes 580..583 the V view
+    (the first 512).  Codes by the e4m3fn definition: 0x38 = +1.0 (exponent field 7 =
+    bias, mantissa 0), 0x40 = +2.0, 0xB8 = -1.0, 0x30 = +0.5."""
+    codes = np.full(576, 0x38, dtype=np.uint8)
+    codes[1], codes[2], codes[3] = 0x40, 0xB8, 0x30
+    row = _hand_fp8_row(codes, 2.0, 3.0)
+    K, V = O.row_views(row[None], O.KV_FP8)
+    assert K.shape == (1, 576) and V.shape == (1, 512)
+    want = np.ones(576)
+    want[1], want[2], want[3] = 2.0, -1.0, 0.5
+    assert np.array_equal(K[0], 2.0 * want)
+    assert np.array_equal(V[0], 3.0 * want[:512])
+
+
+def test_fp8_one_token_context_returns_v_scale_times_code():
+    """A one-token fp8 context: the softmax weight is exactly 1, so the output is
+    code * v_scale element by element (3 * code here, never 2 * code), and the LSE is
+    the single scaled score, scale * sum_i q_i * code_i * k_scale."""
+    rng = np.random.default_rng(17)
+    codes = rng.choice(np.array([0x38, 0x40, 0xB8, 0x30], dtype=np.uint8), size=576)
+    vals = {0x38: 1.0, 0x40: 2.0, 0xB8: -1.0, 0x30: 0.5}
+    c = np.array([vals[int(x)] for x in codes])
+    pool = np.zeros((1, 64, 584), dtype=np.uint8)
+    pool[0, 0] = _hand_fp8_row(codes, 2.0, 3.0)
+    q = rng.standard_normal((1, 1, 2, 576))
+    sc = O.default_scale()
+    o, lse = O.decode(q, pool, O.KV_FP8, np.array([[0]]), np.array([1]), sc)
+    for h in range(2):
+        assert np.array_equal(o[0, 0, h], 3.0 * c[:512])
+        s = sc * sum(float(q[0, 0, h, i]) * c[i] * 2.0 for i in range(576))
+        assert abs(lse[0, 0, h] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_fp8_two_token_context_closed_form():
+    """Two fp8 tokens with all codes 1.0, K scales (1, 2), V scales (3, 5), query of
+    ones: scores s_j = scale * 576 * k_j, so every output element is
+    (3 e^{s_0} + 5 e^{s_1}) / (e^{s_0} + e^{s_1}) and lse = ln(e^{s_0} + e^{s_1}).
+    Swapping the two scale slots of either row breaks both."""
+    ones = np.full(576, 0x38, dtype=np.uint8)
+    pool = np.zeros((1, 64, 584), dtype=np.uint8)
+    pool[0, 0] = _hand_fp8_row(ones, 1.0, 3.0)
+    pool[0, 1] = _hand_fp8_row(ones, 2.0, 5.0)
+    q = np.ones((1, 1, 1, 576))
+    sc = O.default_scale()
+    o, lse = O.decode(q, pool, O.KV_FP8, np.array([[0]]), np.array([2]), sc)
+    s0, s1 = sc * 576 * 1.0, sc * 576 * 2.0
+    m = max(s0, s1)
+    e0, e1 = math.exp(s0 - m), math.exp(s1 - m)
+    want = (3.0 * e0 + 5.0 * e1) / (e0 + e1)
+    assert np.allclose(o[0, 0, 0], want, rtol=1e-13, atol=0)
+    assert abs(lse[0, 0, 0] - (m + math.log(e0 + e1))) <= 1e-12
+    for j in range(2):
+        sw = pool.copy()
+        sw[0, j, 576:580], sw[0, j, 580:584] = pool[0, j, 580:584], pool[0, j, 576:580]
+        o2, l2 = O.decode(q, sw, O.KV_FP8, np.array([[0]]), np.array([2]), sc)
+        assert not np.allclose(o2[0, 0, 0], want, rtol=1e-6) or abs(l2[0, 0, 0] - lse[0, 0, 0]) > 1e-6
+
+
 def test_absorb_and_up_v_against_loops():
     rng = np.random.default_rng(16)
     qn = rng.standard_normal((2, 3, 4))
