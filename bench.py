@@ -8,7 +8,12 @@ resident in HBM before timing starts.  The KV pool is replicated R times and the
 steps rotate over the copies so that the 256 MB Infinity Cache cannot serve one
 step's pages to the next.
 
-Prints ONE JSON line (stdout).  Usage:
+Prints ONE JSON line (stdout).  Besides the headline step (default workload
+full_head), the line carries one record per decode workload (tp_share, full_head,
+fp8, spec_long: median / p10 / p90 of the mla_decode launch over >= 50 rounds,
+fractions of the published and of the measured HBM and bf16 MFMA peaks, and the
+throughput bar each is held to), the per-kernel launch durations of the step, the
+measured peaks, and the CPU oracle baseline.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
     python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill|absorb_rope_decode|prefill_mha
 """
@@ -76,193 +81,392 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def host_cores() -> int:
-    """Threads the oracle's NumPy/BLAS work can use on this host."""
+def blas_threads() -> int:
+    """Threads NumPy's BLAS uses on this host."""
     try:
         from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    return min(len(os.sched_getaffinity(0)), blas)
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
 
 
-def cpu_baseline(w: MI.Workload, budget_s: float = 12.0) -> dict:
-    """The oracle (float64 NumPy) running the same step on this host's cores."""
+def host_cores() -> int:
+    """Threads the oracle's NumPy/BLAS work can use on this host."""
+    return min(len(os.sched_getaffinity(0)), blas_threads())
+
+
+# north_star's throughput bars: (bound they are stated against, fraction)
+TARGETS = {"tp_share": ("hbm", 0.75), "full_head": ("binding", 0.50), "fp8": ("binding", 0.50),
+           "spec_long": ("binding", 0.50)}
+
+
+def cpu_baseline(w: MI.Workload, budget_s: float = 10.0) -> dict:
+    """The decode-level oracle (the plain MQA definition over the paged cache) timed on
+    this host: float32 on every core the process may use (the reported value), the same
+    pinned to one core with BLAS limited to one thread, and float64 (the parity
+    precision) on every core.  A bounded sample of the workload's requests is used; the
+    rate is in decode tokens (query rows) per second."""
     from oracle import mla_oracle as O
-    cores = host_cores()
     kd = w.kv_dtype
     pool = O.encode_rows(w.kv_rows.reshape(-1, 576), kd).reshape(w.num_pages, 64, -1)
-    T = w.B * w.q_len
     sc = O.default_scale()
+    if w.q is None:
+        T = w.B * w.q_len
+        q = O.round_to_bf16(O.absorb(O.bf16_bits_to_f64(w.q_nope.reshape(T, w.N, 128)),
+                                     O.bf16_bits_to_f64(w.q_pe.reshape(T, w.N, 64)),
+                                     O.bf16_bits_to_f64(w.w_uk_t))).reshape(w.B, w.q_len, w.N, 576)
+    else:
+        q = O.bf16_bits_to_f64(w.q)
 
-    def step():
-        p = O.cache_write(pool, w.new_rows[:, :512], w.new_rows[:, 512:], w.new_slots, kd)
-        if w.q is None:
-            q = O.round_to_bf16(O.absorb(O.bf16_bits_to_f64(w.q_nope.reshape(T, w.N, 128)),
-                                         O.bf16_bits_to_f64(w.q_pe.reshape(T, w.N, 64)),
-                                         O.bf16_bits_to_f64(w.w_uk_t))).reshape(w.B, w.q_len, w.N, 576)
-        else:
-            q = O.bf16_bits_to_f64(w.q)
-        o, _ = O.decode(q, p, kd, w.block_table, w.seq_lens, sc)
-        if w.w_uv is not None:
-            O.up_v(O.round_to_bf16(o).reshape(T, w.N, 512), O.bf16_bits_to_f64(w.w_uv))
+    def timed(n_req: int, dtype, budget: float):
+        qq = q[:n_req].astype(dtype)
+        times = []
+        t_all = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            O.decode(qq, pool, kd, w.block_table[:n_req], w.seq_lens[:n_req], sc, dtype=dtype)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_all >= budget or len(times) >= 20:
+                break
+        mean = sum(times) / len(times)
+        return n_req * w.q_len / mean, len(times), mean
 
-    times = []
-    t_all = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        step()
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_all >= budget_s or len(times) >= 20:
-            break
-    mean = sum(times) / len(times)
-    return {"value": T / mean, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full {w.name} batch ({w.B} requests x q_len {w.q_len}) through the "
-                      f"float64 oracle step (cache write, absorb, decode, up-projection), "
-                      f"{len(times)} repetition(s), mean {mean:.3f} s"}
+    cores, blas = host_cores(), blas_threads()
+    n_all = min(w.B, 16)
+    v32, r32, m32 = timed(n_all, np.float32, budget_s)
+    v64, r64, m64 = timed(n_all, np.float64, budget_s / 2)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        keep = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(keep)})
+        try:
+            with threadpool_limits(limits=1):
+                v1, r1, m1 = timed(max(1, n_all // 4), np.float32, budget_s / 2)
+            one = {"value": v1, "cores": 1, "sample": f"{max(1, n_all // 4)} requests, {r1} repetition(s), "
+                                                      f"mean {m1:.3f} s"}
+        finally:
+            os.sched_setaffinity(0, keep)
+    except Exception as e:                      # threadpoolctl missing: report why
+        one = {"value": None, "error": str(e)}
+    return {"value": v32, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {n_all} of the {w.name} batch's {w.B} requests (q_len {w.q_len}, {w.N} heads) "
+                      f"through the float32 decode oracle, {r32} repetition(s), mean {m32:.3f} s",
+            "blas_threads": blas, "one_core": one,
+            "float64": {"value": v64, "cores": cores, "sample": f"{n_all} requests, {r64} repetition(s), "
+                                                                 f"mean {m64:.3f} s"}}
+
+
+class Probe:
+    """The measurement probes (libmla_probe.so): achievable HBM read and bf16 MFMA rates."""
+
+    def __init__(self):
+        import ctypes
+        path = os.path.join(ROOT, "mla_paged_latent_amd", "libmla_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} not found: build with `python -m mla_paged_latent_amd.build`")
+        P = ctypes.CDLL(path)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        P.mla_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        P.mla_probe_hbm_read.restype = i32
+        P.mla_probe_mfma_bf16.argtypes = [vp, i32, vp]
+        P.mla_probe_mfma_bf16.restype = i32
+        P.mla_probe_sink_bytes.argtypes = []
+        P.mla_probe_sink_bytes.restype = ctypes.c_size_t
+        P.mla_probe_mfma_flops.argtypes = [i32]
+        P.mla_probe_mfma_flops.restype = ctypes.c_double
+        self.P = P
+
+    def measure(self) -> dict:
+        import torch
+        P = self.P
+        st = torch.cuda.current_stream().cuda_stream
+        sink = torch.empty(P.mla_probe_sink_bytes(), dtype=torch.uint8, device="cuda")
+        nb = 4 << 30                                        # 16x the 256 MB Infinity Cache
+        buf = torch.ones(nb // 4, dtype=torch.int32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            assert P.mla_probe_hbm_read(buf.data_ptr(), nb, sink.data_ptr(), st) == 0
+        reads = []
+        for _ in range(8):
+            e0.record()
+            assert P.mla_probe_hbm_read(buf.data_ptr(), nb, sink.data_ptr(), st) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            reads.append(nb / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        del buf
+        iters = 20000
+        for _ in range(2):
+            assert P.mla_probe_mfma_bf16(sink.data_ptr(), iters, st) == 0
+        rates = []
+        for _ in range(5):
+            e0.record()
+            assert P.mla_probe_mfma_bf16(sink.data_ptr(), iters, st) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            rates.append(P.mla_probe_mfma_flops(iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        return {"hbm_read_gbs": round(max(reads), 1), "mfma_bf16_tflops": round(max(rates), 1),
+                "method": "mla_probe_hbm_read: one pass over a 4 GiB buffer, 16-byte nontemporal loads, 8 in "
+                          "flight per lane, 8 workgroups of 256 per CU (best of 8); mla_probe_mfma_bf16: four "
+                          "independent v_mfma_f32_32x32x16_bf16 chains per wave, two waves per SIMD, register "
+                          "operands (best of 5)"}
+
+
+class DecodeSetup:
+    """One workload's decode call on the device with R rotating copies of its cache pool,
+    its C arguments marshalled once per copy."""
+
+    def __init__(self, w: MI.Workload, num_splits: int, with_step: bool):
+        import torch
+        import mla_paged_latent_amd as M
+        self.w = w
+        kd = w.kv_dtype
+        dev = torch.device("cuda:0")
+        T = w.B * w.q_len
+        self.bytes_alg, self.flops_alg, self.kv_bytes = algorithmic_work(w)
+        row = M.ROW_BYTES[kd]
+        # enough pool copies that consecutive reuse of one copy is >= 3 MALL capacities apart
+        R = min(8, max(2, math.ceil(3 * MALL_BYTES / max(self.kv_bytes, 1))))
+        self.R = R
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        rows = bf16(w.kv_rows.reshape(-1, 576))
+        slots = torch.arange(w.num_pages * 64, dtype=torch.int64, device=dev)
+        self.pools = []
+        for _ in range(R):
+            pool = torch.empty((w.num_pages, 64, row), dtype=torch.uint8, device=dev)
+            M.cache_write(rows[:, :512], rows[:, 512:], slots, pool, kd)
+            self.pools.append(pool)
+        del rows, slots
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sl = torch.from_numpy(w.seq_lens).to(dev)
+        self.new = bf16(w.new_rows)
+        self.new_slots = torch.from_numpy(w.new_slots).to(dev)
+        self.with_w = with_step and w.w_uk_t is not None
+        if self.with_w:
+            self.q_nope = bf16(w.q_nope.reshape(T, w.N, 128))
+            self.q_pe = bf16(w.q_pe.reshape(T, w.N, 64))
+            self.w_uk_t = bf16(w.w_uk_t)
+            self.w_uv = bf16(w.w_uv)
+            self.qf = torch.empty((T, w.N, 576), dtype=torch.bfloat16, device=dev)
+            self.y = torch.empty((T, w.N * 128), dtype=torch.bfloat16, device=dev)
+        elif w.q is not None:
+            self.qf = bf16(w.q.reshape(T, w.N, 576))
+        else:                                   # decode only on a weights workload: absorb once
+            self.qf = M.absorb_q(bf16(w.q_nope.reshape(T, w.N, 128)), bf16(w.q_pe.reshape(T, w.N, 64)),
+                                 bf16(w.w_uk_t))
+        self.out = torch.empty((w.B, w.q_len, w.N, 512), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.B, w.q_len, w.N), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(M.decode_workspace_size(w.B, w.q_len, w.N, num_splits), dtype=torch.uint8,
+                              device=dev)
+        self.num_splits = num_splits
+        L = M.lib()
+        self.L = L
+        st = torch.cuda.current_stream().cuda_stream
+        qv = self.qf.view(w.B, w.q_len, w.N, 576)
+        kc_new, kp_new = self.new[:, :512], self.new[:, 512:]
+        self.cw_args = [(kc_new.data_ptr(), kc_new.stride(0), kp_new.data_ptr(), kp_new.stride(0),
+                         self.new_slots.data_ptr(), self.new.shape[0], p.data_ptr(), kd, w.num_pages, st)
+                        for p in self.pools]
+        self.dec_args = [(qv.data_ptr(), qv.stride(0), qv.stride(1), qv.stride(2), p.data_ptr(), kd, w.num_pages,
+                          self.bt.data_ptr(), self.bt.stride(0), self.bt.shape[1], self.sl.data_ptr(), w.B,
+                          w.q_len, w.N, float(M.DEFAULT_SCALE), num_splits, self.ws.data_ptr(), self.ws.numel(),
+                          self.out.data_ptr(), self.out.stride(0), self.out.stride(1), self.out.stride(2),
+                          self.lse.data_ptr(), st) for p in self.pools]
+        if self.with_w:
+            ol = self.out.view(T, w.N, 512)
+            self.ab_args = (self.q_nope.data_ptr(), self.q_nope.stride(0), self.q_nope.stride(1),
+                            self.q_pe.data_ptr(), self.q_pe.stride(0), self.q_pe.stride(1), self.w_uk_t.data_ptr(),
+                            T, w.N, self.qf.data_ptr(), self.qf.stride(0), self.qf.stride(1), st)
+            self.uv_args = (ol.data_ptr(), ol.stride(0), ol.stride(1), self.w_uv.data_ptr(), T, w.N,
+                            self.y.data_ptr(), self.y.stride(0), st)
+
+    def step_api(self, i: int):
+        """The step through the checked Python wrappers (used once, to check the fast path)."""
+        import mla_paged_latent_amd as M
+        w = self.w
+        T = w.B * w.q_len
+        pool = self.pools[i % self.R]
+        M.cache_write(self.new[:, :512], self.new[:, 512:], self.new_slots, pool, w.kv_dtype)
+        if self.with_w:
+            M.absorb_q(self.q_nope, self.q_pe, self.w_uk_t, q_fused=self.qf)
+        M.decode(self.qf.view(w.B, w.q_len, w.N, 576), pool, w.kv_dtype, self.bt, self.sl, M.DEFAULT_SCALE,
+                 self.num_splits, workspace=self.ws, out=self.out, lse=self.lse)
+        if self.with_w:
+            M.up_v(self.out.view(T, w.N, 512), self.w_uv, out=self.y)
+
+    def step(self, i: int):
+        j = i % self.R
+        L = self.L
+        rc = L.mla_cache_write(*self.cw_args[j])
+        if self.with_w:
+            rc |= L.mla_absorb_q(*self.ab_args)
+        rc |= L.mla_decode(*self.dec_args[j])
+        if self.with_w:
+            rc |= L.mla_up_v(*self.uv_args)
+        if rc != 0:
+            raise RuntimeError(f"an mla_* call failed in step {i} (status bits {rc})")
+
+    def outputs(self):
+        return (self.out, self.lse, self.y) if self.with_w else (self.out, self.lse)
+
+
+def time_back_to_back(fn, n: int, warm: int = 3) -> float:
+    """Mean time (ms) of n calls of fn(i) enqueued back to back, one event pair around them."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def decode_distribution(s: DecodeSetup, rounds: int) -> list[float]:
+    """Per-call mla_decode time (us) in each of `rounds` rounds; a round is R calls back to
+    back (one per pool copy) under one event pair, so the copies rotate and no event sits
+    between two calls."""
+    import torch
+    f = s.L.mla_decode
+    for i in range(2 * s.R):
+        f(*s.dec_args[i % s.R])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    for r in range(rounds):
+        ev[r][0].record()
+        for j in range(s.R):
+            f(*s.dec_args[j])
+        ev[r][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 / s.R for a, b in ev]
+
+
+def pct(xs: list[float], q: float) -> float:
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))]
+
+
+def roofline_record(bytes_alg: int, flops_alg: float, us: float, peaks: dict | None) -> dict:
+    """Fractions of the published (and, when measured, the achievable) HBM and bf16 MFMA
+    peaks for one launch of `us` microseconds; `binding` is the larger of the two
+    published-peak times."""
+    gbs = bytes_alg / (us * 1e-6) / 1e9
+    tfs = flops_alg / (us * 1e-6) / 1e12
+    t_hbm = bytes_alg / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_alg / (MFMA_BF16_PEAK_TFS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    rec = {"bound": bound, "hbm_gbs": round(gbs, 1), "mfma_tflops": round(tfs, 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac_bf16": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+           "binding_frac": round(max(t_hbm, t_mfma) / (us * 1e-6), 4)}
+    if peaks:
+        m_hbm = bytes_alg / (peaks["hbm_read_gbs"] * 1e9)
+        m_mfma = flops_alg / (peaks["mfma_bf16_tflops"] * 1e12)
+        rec["hbm_frac_measured_peak"] = round(gbs / peaks["hbm_read_gbs"], 4)
+        rec["mfma_frac_measured_peak"] = round(tfs / peaks["mfma_bf16_tflops"], 4)
+        rec["binding_frac_measured_peaks"] = round(max(m_hbm, m_mfma) / (us * 1e-6), 4)
+    return rec
+
+
+def config_record(name: str, rounds: int, peaks: dict | None) -> dict:
+    """mla_decode on one workload: distribution over rounds, rates, roofline fractions and
+    the benchmark spec bar."""
+    import torch
+    w = MI.CONFIGS[name]()
+    s = DecodeSetup(w, 0, with_step=False)
+    us = decode_distribution(s, rounds)
+    med = pct(us, 0.5)
+    roof = roofline_record(s.bytes_alg, s.flops_alg, med, peaks)
+    kind, bar = TARGETS.get(name, ("binding", None))
+    got = roof["hbm_frac"] if kind == "hbm" else roof["binding_frac"]
+    rec = {"workload": f"B={w.B}, q_len={w.q_len}, heads={w.N}, kv={'bf16' if w.kv_dtype == 0 else 'fp8'}, "
+                       f"{w.tokens} cached tokens, {s.R} rotating pool copies",
+           "us_median": round(med, 2), "us_p10": round(pct(us, 0.1), 2), "us_p90": round(pct(us, 0.9), 2),
+           "rounds": rounds, "calls_per_round": s.R,
+           "decode_tokens_per_s": round(w.B * w.q_len / (med * 1e-6), 1),
+           "latent_kv_tbs": round(s.kv_bytes / (med * 1e-6) / 1e12, 3),
+           "algorithmic_bytes": s.bytes_alg, "algorithmic_flops": s.flops_alg, **roof,
+           "target": {"against": kind, "frac": bar, "met": (got >= bar) if bar is not None else None}}
+    log(f"[bench] {name}: mla_decode median {med:.1f} us (p10 {rec['us_p10']:.1f}, p90 {rec['us_p90']:.1f}), "
+        f"{roof['hbm_frac']:.3f} of HBM, {roof['mfma_frac_bf16']:.3f} of bf16 MFMA")
+    del s
+    torch.cuda.empty_cache()
+    return rec
 
 
 def run(args) -> dict:
     import torch
     import mla_paged_latent_amd as M
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = Probe().measure()
+        log(f"[bench] measured peaks: HBM read {peaks['hbm_read_gbs']:.0f} GB/s, "
+            f"bf16 MFMA {peaks['mfma_bf16_tflops']:.0f} TFLOP/s")
+
     w = MI.CONFIGS[args.workload]()
     kd = w.kv_dtype
-    dev = torch.device("cuda:0")
     T = w.B * w.q_len
-    bytes_alg, flops_alg, kv_bytes = algorithmic_work(w)
-    row = M.ROW_BYTES[kd]
-    # enough pool copies that consecutive reuse of one copy is >= 3 MALL capacities apart
-    R = min(8, max(2, math.ceil(3 * MALL_BYTES / max(kv_bytes, 1))))
+    s = DecodeSetup(w, args.num_splits, with_step=True)
     log(f"[bench] workload {w.name}: B={w.B} q_len={w.q_len} N={w.N} kv={'bf16' if kd == 0 else 'fp8'} "
-        f"pages={w.num_pages} KV bytes/step={kv_bytes / 1e6:.1f} MB, pool copies={R}")
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    rows = bf16(w.kv_rows.reshape(-1, 576))
-    slots = torch.arange(w.num_pages * 64, dtype=torch.int64, device=dev)
-    pools = []
-    for _ in range(R):
-        pool = torch.empty((w.num_pages, 64, row), dtype=torch.uint8, device=dev)
-        M.cache_write(rows[:, :512], rows[:, 512:], slots, pool, kd)
-        pools.append(pool)
-    del rows, slots
-    bt = torch.from_numpy(w.block_table).to(dev)
-    sl = torch.from_numpy(w.seq_lens).to(dev)
-    new = bf16(w.new_rows)
-    new_slots = torch.from_numpy(w.new_slots).to(dev)
-    with_w = w.w_uk_t is not None
-    if with_w:
-        q_nope = bf16(w.q_nope.reshape(T, w.N, 128))
-        q_pe = bf16(w.q_pe.reshape(T, w.N, 64))
-        w_uk_t = bf16(w.w_uk_t)
-        w_uv = bf16(w.w_uv)
-        qf = torch.empty((T, w.N, 576), dtype=torch.bfloat16, device=dev)
-        y = torch.empty((T, w.N * 128), dtype=torch.bfloat16, device=dev)
-    else:
-        qf = bf16(w.q.reshape(T, w.N, 576))
-    out = torch.empty((w.B, w.q_len, w.N, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.B, w.q_len, w.N), dtype=torch.float32, device=dev)
-    ws = torch.empty(M.decode_workspace_size(w.B, w.q_len, w.N, args.num_splits), dtype=torch.uint8,
-                     device=dev)
+        f"pages={w.num_pages} KV bytes/step={s.kv_bytes / 1e6:.1f} MB, pool copies={s.R}")
     if args.copy_calibration_mb > 0:
         # one device-to-device copy of a known size: under a --pmc run its FETCH_SIZE /
         # WRITE_SIZE give the counters' scale (see --traffic-record)
         nb = args.copy_calibration_mb * 2**20
-        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    # The timed loops call the C entry points with their arguments marshalled once (the
+    # tensor-checking Python wrappers cost tens of microseconds per call, enough to leave
+    # the GPU idle between the step's kernels); checked here against the wrappers.
+    s.step_api(0)
     torch.cuda.synchronize()
-
-    def step_api(i: int):
-        pool = pools[i % R]
-        M.cache_write(new[:, :512], new[:, 512:], new_slots, pool, kd)
-        if with_w:
-            M.absorb_q(q_nope, q_pe, w_uk_t, q_fused=qf)
-        M.decode(qf.view(w.B, w.q_len, w.N, 576), pool, kd, bt, sl, M.DEFAULT_SCALE, args.num_splits,
-                 workspace=ws, out=out, lse=lse)
-        if with_w:
-            M.up_v(out.view(T, w.N, 512), w_uv, out=y)
-
-    # The timed loops call the same C entry points with their arguments marshalled once
-    # (the tensor-checking Python wrappers cost tens of microseconds per call, enough to
-    # leave the GPU idle between the step's kernels); checked below against step_api.
-    L = M.lib()
-    stream = torch.cuda.current_stream().cuda_stream
-    qv = qf.view(w.B, w.q_len, w.N, 576)
-    kc_new, kp_new = new[:, :512], new[:, 512:]
-    cw_args = [(kc_new.data_ptr(), kc_new.stride(0), kp_new.data_ptr(), kp_new.stride(0), new_slots.data_ptr(),
-                new.shape[0], pool.data_ptr(), kd, w.num_pages, stream) for pool in pools]
-    dec_args = [(qv.data_ptr(), qv.stride(0), qv.stride(1), qv.stride(2), pool.data_ptr(), kd, w.num_pages,
-                 bt.data_ptr(), bt.stride(0), bt.shape[1], sl.data_ptr(), w.B, w.q_len, w.N,
-                 float(M.DEFAULT_SCALE), args.num_splits, ws.data_ptr(), ws.numel(), out.data_ptr(),
-                 out.stride(0), out.stride(1), out.stride(2), lse.data_ptr(), stream) for pool in pools]
-    if with_w:
-        ol = out.view(T, w.N, 512)
-        ab_args = (q_nope.data_ptr(), q_nope.stride(0), q_nope.stride(1), q_pe.data_ptr(), q_pe.stride(0),
-                   q_pe.stride(1), w_uk_t.data_ptr(), T, w.N, qf.data_ptr(), qf.stride(0), qf.stride(1), stream)
-        uv_args = (ol.data_ptr(), ol.stride(0), ol.stride(1), w_uv.data_ptr(), T, w.N, y.data_ptr(), y.stride(0),
-                   stream)
-    f_cw, f_ab, f_dec, f_uv = L.mla_cache_write, L.mla_absorb_q, L.mla_decode, L.mla_up_v
-
-    def step(i: int):
-        j = i % R
-        rc = f_cw(*cw_args[j])
-        if with_w:
-            rc |= f_ab(*ab_args)
-        rc |= f_dec(*dec_args[j])
-        if with_w:
-            rc |= f_uv(*uv_args)
-        if rc != 0:
-            raise RuntimeError(f"an mla_* call failed in step {i} (status bits {rc})")
-
-    def decode_only(i: int):
-        if f_dec(*dec_args[i % R]) != 0:
-            raise RuntimeError(f"mla_decode failed in call {i}")
-
-    # the marshalled step computes what the checked wrappers compute, bit for bit
-    step_api(0)
+    ref = [t.clone() for t in s.outputs()]
+    s.step(0)
     torch.cuda.synchronize()
-    ref = [t.clone() for t in ((out, lse, y) if with_w else (out, lse))]
-    step(0)
-    torch.cuda.synchronize()
-    for a, b in zip(ref, (out, lse, y) if with_w else (out, lse)):
+    for a, b in zip(ref, s.outputs()):
         assert torch.equal(a, b), "marshalled step differs from the API step"
 
     for i in range(args.warmup):
-        step(i)
+        s.step(i)
     torch.cuda.synchronize()
     # timed region 1: K whole steps, bracketed by one event pair (no events inside: an
     # event record between two kernels delays the next launch by several microseconds)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        step(i)
+        s.step(i)
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
-    # timed region 2: K mla_decode calls back to back on the same stream (rotating cache
-    # pools), bracketed by one event pair: the average launch duration of mla_decode
-    for i in range(min(args.warmup, 3)):
-        decode_only(i)
-    torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for i in range(args.steps):
-        decode_only(i)
-    d1.record()
-    torch.cuda.synchronize()
-    dec_mean = d0.elapsed_time(d1) / args.steps
-    log(f"[bench] step {ms_step * 1e3:.1f} us, mla_decode {dec_mean * 1e3:.1f} us per call "
-        f"({args.steps} calls back to back)")
+    # timed region 2: each call of the step on its own, K calls back to back on the same
+    # stream (rotating cache pools): the average launch durations, which add up to the step
+    L = s.L
+    kern = {"mla_cache_write": time_back_to_back(lambda i: L.mla_cache_write(*s.cw_args[i % s.R]), args.steps),
+            "mla_decode": time_back_to_back(lambda i: L.mla_decode(*s.dec_args[i % s.R]), args.steps)}
+    if s.with_w:
+        kern["mla_absorb_q"] = time_back_to_back(lambda i: L.mla_absorb_q(*s.ab_args), args.steps)
+        kern["mla_up_v"] = time_back_to_back(lambda i: L.mla_up_v(*s.uv_args), args.steps)
+    dec_mean = kern["mla_decode"]
+    # timed region 3: the decode launch distribution (median / p10 / p90 over >= 50 rounds)
+    dist = decode_distribution(s, max(50, args.steps))
+    log(f"[bench] step {ms_step * 1e3:.1f} us; back to back per call: " +
+        ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in kern.items()) +
+        f" (sum {sum(kern.values()) * 1e3:.1f} us); mla_decode median {pct(dist, 0.5):.1f} us")
 
-    achieved = bytes_alg / (dec_mean * 1e-3) / 1e9
-    tflops = flops_alg / (dec_mean * 1e-3) / 1e12
-    t_hbm = bytes_alg / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flops_alg / (MFMA_BF16_PEAK_TFS * 1e12)
+    achieved = s.bytes_alg / (dec_mean * 1e-3) / 1e9
+    tflops = s.flops_alg / (dec_mean * 1e-3) / 1e12
+    t_hbm = s.bytes_alg / (HBM_PEAK_GBS * 1e9)
+    t_mfma = s.flops_alg / (MFMA_BF16_PEAK_TFS * 1e12)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
@@ -271,11 +475,17 @@ def run(args) -> dict:
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = traffic_record(args.workload)
     roof["kernel"] = "mla_decode (split-KV decode with in-kernel split plan + LSE merge)"
-    roof["algorithmic_bytes"] = bytes_alg
-    roof["algorithmic_flops"] = flops_alg
+    roof["algorithmic_bytes"] = s.bytes_alg
+    roof["algorithmic_flops"] = s.flops_alg
     roof["mean_launch_us"] = round(dec_mean * 1e3, 2)
+    roof["median_launch_us"] = round(pct(dist, 0.5), 2)
+    roof["p10_launch_us"] = round(pct(dist, 0.1), 2)
+    roof["p90_launch_us"] = round(pct(dist, 0.9), 2)
     roof["mfma_frac_bf16"] = round(tflops / MFMA_BF16_PEAK_TFS, 4)
     roof["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
+    if peaks:
+        roof["frac_measured_peak"] = round(achieved / peaks["hbm_read_gbs"], 4) if roof["bound"] == "hbm" else \
+            round(tflops / peaks["mfma_bf16_tflops"], 4)
 
     res = {
         "metric": METRIC,
@@ -293,12 +503,22 @@ def run(args) -> dict:
         "config": {"workload": f"{w.name}: B={w.B}, q_len={w.q_len}, heads={w.N}, "
                                f"seq_lens={'all ' + str(int(w.seq_lens[0])) if len(set(w.seq_lens.tolist())) == 1 else 'mixed'}, "
                                f"kv={'bf16' if kd == 0 else 'fp8'} 576-d rows, 64-token pages, "
-                               f"absorb + decode + up-proj",
+                               f"{'absorb + ' if s.with_w else ''}cache write + decode{' + up-proj' if s.with_w else ''}",
                    "batch": w.B, "q_len": w.q_len, "heads": w.N, "kv_tokens": w.tokens,
-                   "num_splits": args.num_splits, "pool_copies": R},
-        "decode_latent_kv_tbs": round(kv_bytes / (dec_mean * 1e-3) / 1e12, 3),
+                   "num_splits": args.num_splits, "pool_copies": s.R},
+        "decode_latent_kv_tbs": round(s.kv_bytes / (dec_mean * 1e-3) / 1e12, 3),
         "roofline": roof,
+        "step_kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+        "step_kernels_sum_us": round(sum(kern.values()) * 1e3, 2),
     }
+    if peaks:
+        res["measured_peaks"] = peaks
+    del s
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        res["decode_configs"] = {}
+        for name in args.configs.split(","):
+            res["decode_configs"][name] = config_record(name, max(50, args.steps), peaks)
     return res
 
 
@@ -577,7 +797,8 @@ def run_context_op(args) -> dict:
         roof["algorithmic_flops"] = flops_alg
     if bf16_out_us is not None:
         roof["unfused_call_us"] = bf16_out_us
-    res = {"metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+    value, unit = (roof["achieved"], roof["unit"]) if roof["bound"] == "mfma" else (round(gbs, 1), "GB/s")
+    res = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": {"workload": desc},
            "roofline": roof}
@@ -685,6 +906,11 @@ def main():
                     help="step: the decode step (default); the others time one other call on its own "
                          "workload (context gather, state merge, variable-length decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM / MFMA peaks")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the --workload step, not the per-config decode records")
+    ap.add_argument("--configs", default="tp_share,full_head,fp8,spec_long",
+                    help="workloads whose mla_decode gets a record of its own (comma separated)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

@@ -1,7 +1,9 @@
 """Compile the HIP sources of the library into one shared object for gfx950.
 
 Run as ``python -m mla_paged_latent_amd.build``; writes
-``mla_paged_latent_amd/libmla_paged_latent.so`` next to this file.
+``mla_paged_latent_amd/libmla_paged_latent.so`` next to this file, and the
+measurement probes bench.py uses (achievable HBM read and MFMA rates) as
+``libmla_probe.so`` beside it.
 """
 
 from __future__ import annotations
@@ -15,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_paged_latent.so")
 SOURCES = ["cache_write.hip", "absorb_upv.hip", "decode.hip", "context.hip", "prefill.hip"]
+PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -32,25 +36,32 @@ def flags(extra: list[str] | None = None) -> list[str]:
             "-Wno-unused-command-line-argument"] + (extra or [])
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libmla_paged_latent.so``; returns its path."""
+def _link(sources: list[str], lib: str, verbose: bool) -> str:
     cc = hipcc()
     objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, *flags(), "-shared", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link ``libmla_paged_latent.so`` and the probe library;
+    returns the main library's path."""
+    _link(SOURCES, LIB, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

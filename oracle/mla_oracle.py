@@ -211,7 +211,7 @@ def encode_rows(rows_bits: np.ndarray, kv_dtype: int) -> np.ndarray:
 
 
 def row_views(rows: np.ndarray, kv_dtype: int, row_elems: int = ROW_ELEMS,
-              latent: int = KV_LORA_RANK) -> tuple[np.ndarray, np.ndarray]:
+              latent: int = KV_LORA_RANK, dtype=np.float64) -> tuple[np.ndarray, np.ndarray]:
     """Decode raw cache rows into the K view (all elements) and V view (latent).
 
     bf16: both views are the stored values.  fp8: K = code * k_scale over all
@@ -220,13 +220,13 @@ def row_views(rows: np.ndarray, kv_dtype: int, row_elems: int = ROW_ELEMS,
     """
     rows = np.asarray(rows, dtype=np.uint8)
     if kv_dtype == KV_BF16:
-        vals = bf16_bits_to_f64(rows.reshape(rows.shape[0], -1).view("<u2"))
+        vals = bf16_bits_to_f64(rows.reshape(rows.shape[0], -1).view("<u2")).astype(dtype, copy=False)
         return vals, vals[:, :latent]
     codes = rows[:, :row_elems]
     k_scale = rows[:, row_elems:row_elems + 4].copy().view("<f4").astype(np.float64)
     v_scale = rows[:, row_elems + 4:row_elems + 8].copy().view("<f4").astype(np.float64)
     vals = e4m3_value(codes)
-    return vals * k_scale, vals[:, :latent] * v_scale
+    return (vals * k_scale).astype(dtype, copy=False), (vals[:, :latent] * v_scale).astype(dtype, copy=False)
 
 
 def gather_rows(pool: np.ndarray, block_table_row: np.ndarray, n: int) -> np.ndarray:
@@ -259,7 +259,7 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
     """
     H = q.shape[0]
     if K.shape[0] == 0:
-        return np.zeros((H, V.shape[1])), np.full(H, -np.inf)
+        return np.zeros((H, V.shape[1]), dtype=q.dtype), np.full(H, -np.inf, dtype=q.dtype)
     s = scale * (q @ K.T)
     m = s.max(axis=1, keepdims=True)
     lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
@@ -269,7 +269,7 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
 
 def decode(q: np.ndarray, pool: np.ndarray, kv_dtype: int, block_table: np.ndarray,
            seq_lens: np.ndarray, scale: float, row_elems: int = ROW_ELEMS,
-           latent: int = KV_LORA_RANK) -> tuple[np.ndarray, np.ndarray]:
+           latent: int = KV_LORA_RANK, dtype=np.float64) -> tuple[np.ndarray, np.ndarray]:
     """Absorbed-MQA decode over the paged cache, as its plain definition.
 
     ``q`` is ``[B, q_len, N, row_elems]`` (absorbed query ``[q_l,nope | q_pe]``);
@@ -277,21 +277,23 @@ def decode(q: np.ndarray, pool: np.ndarray, kv_dtype: int, block_table: np.ndarr
     Every head scores against the whole row and the latent part is V
     ([vLLM-MLA] §两套算法 data-movement-friendly form; §FlashMLA: one KV head
     shared by all query heads; [Triton-MLA] §Datenfluss).  No splits, no online
-    softmax: the gathered keys are attended in one pass.
+    softmax: the gathered keys are attended in one pass.  ``dtype`` float32 runs the
+    same definition in single precision (the timed CPU baseline only; parity uses
+    float64).
     """
-    q = np.asarray(q, dtype=np.float64)
+    q = np.asarray(q, dtype=dtype)
     B, q_len, N, _ = q.shape
-    o = np.zeros((B, q_len, N, latent))
-    lse = np.full((B, q_len, N), -np.inf)
+    o = np.zeros((B, q_len, N, latent), dtype=dtype)
+    lse = np.full((B, q_len, N), -np.inf, dtype=dtype)
     for b in range(B):
         n_all = int(seq_lens[b])
         if n_all <= 0:
             continue
         K_all, V_all = row_views(gather_rows(pool, block_table[b], n_all), kv_dtype,
-                                 row_elems, latent)
+                                 row_elems, latent, dtype)
         for t in range(q_len):
             n = visible_tokens(n_all, q_len, t)
-            o[b, t], lse[b, t] = attend(q[b, t], K_all[:n], V_all[:n], scale)
+            o[b, t], lse[b, t] = attend(q[b, t], K_all[:n], V_all[:n], dtype(scale))
     return o, lse
 
 

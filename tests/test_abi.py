@@ -35,8 +35,8 @@ def _library(request):
     yield
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
@@ -53,6 +53,21 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for f in declared_functions():
         assert hasattr(L, f), f
+
+
+def test_probe_library_exports_its_header():
+    """The measurement probes (libmla_probe.so) export what include/mla_probe.h declares."""
+    import ctypes
+    probe_h = os.path.join(ROOT, "include", "mla_probe.h")
+    probe_so = os.path.join(os.path.dirname(M.LIB_PATH), "libmla_probe.so")
+    if not os.path.exists(probe_so):
+        from mla_paged_latent_amd import build as B
+        B.build()
+    P = ctypes.CDLL(probe_so)
+    own = [f for f in declared_functions(probe_h) if f.startswith("mla_probe_")]
+    assert own == ["mla_probe_hbm_read", "mla_probe_mfma_bf16", "mla_probe_mfma_flops", "mla_probe_sink_bytes"]
+    for f in own:
+        assert hasattr(P, f), f
 
 
 def test_status_strings():
