@@ -199,6 +199,37 @@ mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_t, i
                         float* lse, void* stream);
 
 /*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, runtimes that forbid
+ * hipMalloc): the same kernels, split plan and merge, with the split table and
+ * partials in a scratch array the library keeps on every GPU it runs on
+ * (MLA_DECODE_SCRATCH_BYTES, a file-scope device array held until the process ends)
+ * instead of a caller workspace.
+ *
+ *   arguments  as mla_decode, without workspace / workspace_bytes
+ *
+ * The scratch needs (B + S + 8) * groups * rows * 2052 bytes plus a 16-byte record
+ * per request, where S is the automatic plan's stream count on this GPU (its compute
+ * units, divided among head groups) or B * num_splits, groups * rows = q_len * N
+ * rounded up to 16 (q_len * N <= 16) or 64; num_splits == 1 needs only the records.
+ * Shapes that need more than MLA_DECODE_SCRATCH_BYTES return MLA_ERR_WORKSPACE and
+ * enqueue nothing (the 128-head benchmark batches of up to 128 requests fit).  The
+ * call allocates and frees nothing; the scratch needs no initialisation and keeps the
+ * last call's contents.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (concurrent streams, or host threads enqueuing on different
+ * streams) race and give undefined results; calls ordered on one stream are safe.
+ * Same results as mla_decode for the same inputs and num_splits.
+ */
+#define MLA_DECODE_SCRATCH_BYTES (96u << 20)
+mla_status_t mla_decode_noalloc(const void* q, int64_t q_stride_b, int64_t q_stride_t, int64_t q_stride_h,
+                                const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                                const int32_t* block_table, int64_t bt_stride_b, int32_t max_pages_per_seq,
+                                const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t N,
+                                float softmax_scale, int32_t num_splits,
+                                void* out, int64_t o_stride_b, int64_t o_stride_t, int64_t o_stride_h,
+                                float* lse, void* stream);
+
+/*
  * mla_decode_varlen_workspace_size -- bytes of workspace mla_decode_varlen needs
  * for T query rows of N heads, the split mode and the block-table width.
  * Returns 0 for shapes mla_decode_varlen would reject.  No device call.

@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode.argtypes = [vp, i64, i64, i64, vp, i32, i64, vp, i64, i32, vp, i32, i32, i32,
                              ctypes.c_float, i32, vp, ctypes.c_size_t, vp, i64, i64, i64, vp, vp]
     L.mla_decode.restype = i32
+    L.mla_decode_noalloc.argtypes = [vp, i64, i64, i64, vp, i32, i64, vp, i64, i32, vp, i32, i32, i32,
+                                     ctypes.c_float, i32, vp, i64, i64, i64, vp, vp]
+    L.mla_decode_noalloc.restype = i32
     L.mla_up_v.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.mla_up_v.restype = i32
     L.mla_absorb_q_rope.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i32, vp, vp, i64, i32, vp, i64,
@@ -215,6 +218,31 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_dtype: int, block_table: 
         _ptr(block_table), block_table.stride(0), block_table.shape[1], _ptr(seq_lens),
         B, q_len, N, float(softmax_scale), num_splits, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0), out.stride(1),
+        out.stride(2), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, kv_dtype: int, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, softmax_scale: float = DEFAULT_SCALE, num_splits: int = 0,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """:func:`decode` through ``mla_decode_noalloc``: no workspace, the library's
+    per-GPU scratch array instead (calls that overlap on one GPU race)."""
+    B, q_len, N, D = q.shape
+    assert D == ROW_ELEMS and q.dtype == torch.bfloat16 and q.stride(-1) == 1
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.stride(-1) == 1
+    num_pages = kv_cache.numel() * kv_cache.element_size() // (PAGE_TOKENS * ROW_BYTES[kv_dtype])
+    if out is None:
+        out = torch.empty((B, q_len, N, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, q_len, N), dtype=torch.float32, device=q.device)
+    _need_out("decode_noalloc", out, (B, q_len, N, KV_LORA_RANK))
+    _need_lse("decode_noalloc", lse, (B, q_len, N))
+    _check("mla_decode_noalloc", lib().mla_decode_noalloc(
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2), _ptr(kv_cache), kv_dtype, num_pages,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1], _ptr(seq_lens),
+        B, q_len, N, float(softmax_scale), num_splits, _ptr(out), out.stride(0), out.stride(1),
         out.stride(2), _ptr(lse), _stream(stream)))
     return out, lse
 

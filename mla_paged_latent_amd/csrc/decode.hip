@@ -27,6 +27,7 @@
 //                        pages double-buffered, the 4 waves split each page's tokens
 //   Both write the final output (single split) or float32 partials; then
 //   merge_kernel         LSE-weighted combine of the partials of split requests
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -1741,6 +1742,18 @@ inline WsLayout ws_layout(int32_t B, const Shape& s) {
 }
 
 
+// Streams of the plan: in automatic mode one per workgroup and head group, so every
+// unit runs concurrently, with a multiple of 8 streams when there are several head
+// groups (sibling order); forced mode: B * num_splits.
+inline int64_t plan_streams(const Shape& s, int32_t num_splits, int32_t B, const DeviceInfo& di) {
+  const int64_t cus = ((int64_t)di.cu_count + 7) / 8 * 8;
+  if (num_splits != 0) return (int64_t)B * num_splits;
+  int64_t streams = s.n_hg == 1 ? cus : cus / (8 * s.n_hg) * 8;
+  if (streams < 8) streams = 8;
+  if (streams > MLA_AUTO_MAX_EXTRA_PAIRS) streams = MLA_AUTO_MAX_EXTRA_PAIRS;
+  return streams;
+}
+
 // Launches the decode kernels (and the merge) for filled-in parameters: the plan's
 // stream and unit counts, the 32/64-bit plan variant, the kernel variant.
 static mla_status_t decode_launch(DecodeParams p, const Shape& s, int32_t kv_dtype, int32_t num_splits,
@@ -1750,14 +1763,7 @@ static mla_status_t decode_launch(DecodeParams p, const Shape& s, int32_t kv_dty
   // stream per workgroup and head group, so every unit runs concurrently; with
   // several head groups the stream count is a multiple of 8 (sibling order).
   const int64_t cus = ((int64_t)di.cu_count + 7) / 8 * 8;
-  int64_t streams;
-  if (num_splits == 0) {
-    streams = s.n_hg == 1 ? cus : cus / (8 * s.n_hg) * 8;
-    if (streams < 8) streams = 8;
-    if (streams > MLA_AUTO_MAX_EXTRA_PAIRS) streams = MLA_AUTO_MAX_EXTRA_PAIRS;
-  } else {
-    streams = (int64_t)B * num_splits;
-  }
+  const int64_t streams = plan_streams(s, num_splits, B, di);
   const int64_t units = s.n_hg == 1 ? streams : (streams + 7) / 8 * 8 * s.n_hg;
   if (units > (int64_t)1 << 30) return MLA_ERR_SHAPE;
   p.n_streams = (int32_t)streams;
@@ -1804,35 +1810,36 @@ extern "C" size_t mla_decode_workspace_size(int32_t B, int32_t q_len, int32_t N,
   return mla::ws_layout(B, s).total;
 }
 
-extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_t,
-                                   int64_t q_stride_h, const void* kv_cache, int32_t kv_dtype,
-                                   int64_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
-                                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
-                                   int32_t q_len, int32_t N, float softmax_scale, int32_t num_splits,
-                                   void* workspace, size_t workspace_bytes, void* out,
-                                   int64_t o_stride_b, int64_t o_stride_t, int64_t o_stride_h,
-                                   float* lse, void* stream) {
-  using namespace mla;
+namespace mla {
+
+// Argument checks of mla_decode and mla_decode_noalloc (everything but the workspace)
+inline mla_status_t decode_check(const void* q, int64_t q_stride_b, int64_t q_stride_t, int64_t q_stride_h,
+                                 const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                                 const int32_t* block_table, int64_t bt_stride_b, int32_t max_pages_per_seq,
+                                 const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t N,
+                                 float softmax_scale, int32_t num_splits, const void* out, int64_t o_stride_b,
+                                 int64_t o_stride_t, int64_t o_stride_h, const float* lse, Shape* s) {
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_DTYPE;
-  Shape s;
-  if (!decode_shape(B, q_len, N, num_splits, &s)) return MLA_ERR_SHAPE;
+  if (!decode_shape(B, q_len, N, num_splits, s)) return MLA_ERR_SHAPE;
   if (num_pages < 1 || max_pages_per_seq < 1 || bt_stride_b < max_pages_per_seq) return MLA_ERR_SHAPE;
   if (!(softmax_scale > 0.f) || !__builtin_isfinite(softmax_scale)) return MLA_ERR_SHAPE;
   if (!q || !kv_cache || !block_table || !seq_lens || !out || !lse) return MLA_ERR_NULL;
-  if (!workspace) return MLA_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || !mult8(q_stride_b) ||
-      !mult8(q_stride_t) || !mult8(q_stride_h) || !mult8(o_stride_b) || !mult8(o_stride_t) ||
-      !mult8(o_stride_h) || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || !mult8(q_stride_b) || !mult8(q_stride_t) ||
+      !mult8(q_stride_h) || !mult8(o_stride_b) || !mult8(o_stride_t) || !mult8(o_stride_h) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return MLA_ERR_ALIGN;
-  const WsLayout wl = ws_layout(B, s);
-  if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
-  DeviceInfo di;
-  mla_status_t st = device_info(&di);
-  if (st != MLA_OK) return st;
+  return MLA_OK;
+}
 
-  char* ws = static_cast<char*>(workspace);
+// Parameters of one decode call whose workspace is `ws` laid out as `wl` with
+// `max_slots` partial slots
+inline DecodeParams decode_params(const void* q, int64_t q_stride_b, int64_t q_stride_t, int64_t q_stride_h,
+                                  const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                  int64_t bt_stride_b, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                  int32_t B, int32_t q_len, int32_t N, float softmax_scale, int32_t num_splits,
+                                  char* ws, const WsLayout& wl, int32_t max_slots, const Shape& s, void* out,
+                                  int64_t o_stride_b, int64_t o_stride_t, int64_t o_stride_h, float* lse) {
   DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.q_sb = q_stride_b;
@@ -1842,9 +1849,6 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   p.num_pages = num_pages;
   p.block_table = block_table;
   p.bt_sb = bt_stride_b;
-  // a seq_len is an int32, so no request reaches past page 2^25 - 1: wider tables are
-  // read only that far (this also keeps the kernels' page * 64 arithmetic in 32 bits)
-  if (max_pages_per_seq > kMaxPagesPerSeq) max_pages_per_seq = kMaxPagesPerSeq;
   p.max_pages = max_pages_per_seq;
   p.seq_lens = seq_lens;
   p.B = B;
@@ -1863,7 +1867,118 @@ extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_
   p.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
   p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   p.num_splits = num_splits;
-  p.max_slots = s.max_slots;
+  p.max_slots = max_slots;
+  return p;
+}
+
+}  // namespace mla
+
+extern "C" mla_status_t mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_t,
+                                   int64_t q_stride_h, const void* kv_cache, int32_t kv_dtype,
+                                   int64_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
+                                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
+                                   int32_t q_len, int32_t N, float softmax_scale, int32_t num_splits,
+                                   void* workspace, size_t workspace_bytes, void* out,
+                                   int64_t o_stride_b, int64_t o_stride_t, int64_t o_stride_h,
+                                   float* lse, void* stream) {
+  using namespace mla;
+  Shape s;
+  mla_status_t st = decode_check(q, q_stride_b, q_stride_t, q_stride_h, kv_cache, kv_dtype, num_pages, block_table,
+                                 bt_stride_b, max_pages_per_seq, seq_lens, B, q_len, N, softmax_scale, num_splits,
+                                 out, o_stride_b, o_stride_t, o_stride_h, lse, &s);
+  if (st != MLA_OK) return st;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MLA_ERR_ALIGN;
+  const WsLayout wl = ws_layout(B, s);
+  if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MLA_OK) return st;
+  // a seq_len is an int32, so no request reaches past page 2^25 - 1: wider tables are
+  // read only that far (this also keeps the kernels' page * 64 arithmetic in 32 bits)
+  if (max_pages_per_seq > kMaxPagesPerSeq) max_pages_per_seq = kMaxPagesPerSeq;
+  const DecodeParams p = decode_params(q, q_stride_b, q_stride_t, q_stride_h, kv_cache, num_pages, block_table,
+                                       bt_stride_b, max_pages_per_seq, seq_lens, B, q_len, N, softmax_scale,
+                                       num_splits, static_cast<char*>(workspace), wl, s.max_slots, s, out,
+                                       o_stride_b, o_stride_t, o_stride_h, lse);
+  return decode_launch(p, s, kv_dtype, num_splits, B, max_pages_per_seq, di,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate: the split
+// table and partials live in one file-scope device array per GPU.
+// ---------------------------------------------------------------------------
+namespace mla {
+
+static __device__ __align__(256) char scratch[MLA_DECODE_SCRATCH_BYTES];
+
+// This GPU's address of `scratch`, looked up once per device with that device current
+// (in host code the array's name is only a host-side handle, not a device address)
+inline mla_status_t scratch_ptr(char** out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> state[kMaxDev];   // 0 = not looked up, 1 = ptrs[dev] valid
+  static char* ptrs[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return MLA_ERR_HIP;
+  if (state[dev].load(std::memory_order_acquire) == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MLA_ERR_HIP;
+    ptrs[dev] = static_cast<char*>(ptr);     // every racing thread stores the same value
+    state[dev].store(1, std::memory_order_release);
+  }
+  *out = ptrs[dev];
+  return MLA_OK;
+}
+
+// Workspace layout with exactly the partial slots this device's plan can use: automatic
+// mode B + streams (+ the 8 spare of decode_shape), forced mode B * num_splits (+ 8);
+// num_splits == 1 writes no partials, so only the request table is laid out.
+inline WsLayout ws_layout_exact(int32_t B, const Shape& s, int32_t num_splits, int64_t streams,
+                                int32_t* max_slots) {
+  WsLayout w;
+  w.req = 0;
+  size_t off = align256((size_t)B * sizeof(int4));
+  const int64_t slots = num_splits == 1 ? 0 : (num_splits == 0 ? (int64_t)B + streams + 8 : s.max_slots);
+  *max_slots = (int32_t)slots;
+  const size_t rows = (size_t)slots * s.n_hg * s.m_wg;
+  w.part_lse = off;
+  off = align256(off + rows * sizeof(float));
+  w.part_o = off;
+  off = align256(off + rows * kLatent * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace mla
+
+extern "C" mla_status_t mla_decode_noalloc(const void* q, int64_t q_stride_b, int64_t q_stride_t,
+                                           int64_t q_stride_h, const void* kv_cache, int32_t kv_dtype,
+                                           int64_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
+                                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
+                                           int32_t q_len, int32_t N, float softmax_scale, int32_t num_splits,
+                                           void* out, int64_t o_stride_b, int64_t o_stride_t,
+                                           int64_t o_stride_h, float* lse, void* stream) {
+  using namespace mla;
+  Shape s;
+  mla_status_t st = decode_check(q, q_stride_b, q_stride_t, q_stride_h, kv_cache, kv_dtype, num_pages, block_table,
+                                 bt_stride_b, max_pages_per_seq, seq_lens, B, q_len, N, softmax_scale, num_splits,
+                                 out, o_stride_b, o_stride_t, o_stride_h, lse, &s);
+  if (st != MLA_OK) return st;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MLA_OK) return st;
+  int32_t max_slots = 0;
+  const WsLayout wl = ws_layout_exact(B, s, num_splits, plan_streams(s, num_splits, B, di), &max_slots);
+  if (wl.total > (size_t)MLA_DECODE_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  char* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != MLA_OK) return st;
+  if (max_pages_per_seq > kMaxPagesPerSeq) max_pages_per_seq = kMaxPagesPerSeq;
+  const DecodeParams p = decode_params(q, q_stride_b, q_stride_t, q_stride_h, kv_cache, num_pages, block_table,
+                                       bt_stride_b, max_pages_per_seq, seq_lens, B, q_len, N, softmax_scale,
+                                       num_splits, ws, wl, max_slots, s, out, o_stride_b, o_stride_t, o_stride_h,
+                                       lse);
   return decode_launch(p, s, kv_dtype, num_splits, B, max_pages_per_seq, di,
                        reinterpret_cast<hipStream_t>(stream));
 }
