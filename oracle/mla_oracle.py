@@ -473,6 +473,51 @@ def gather_cache(pool: np.ndarray, kv_dtype: int, block_table: np.ndarray, cu_se
     return out
 
 
+def prefill_workspace_rows(max_model_len: int, max_num_seqs: int, page_tokens: int = PAGE_TOKENS) -> int:
+    """Row budget W of the chunked-context workspace.
+
+    [vLLM-MLA] §Prefill (determine_chunked_prefill_workspace_size):
+    ``W = min(max(8 * L_max, 4 * B_seq * P_block), 64 * 1024)`` -- room for eight
+    full-length requests or four pages per concurrent request, capped at 64k rows so
+    that the workspace does not crowd out the KV cache.
+    """
+    return min(max(8 * int(max_model_len), 4 * int(max_num_seqs) * int(page_tokens)), 64 * 1024)
+
+
+def plan_context_chunks(context_lens, row_budget: int, page_tokens: int = PAGE_TOKENS
+                        ) -> list[list[tuple[int, int, int]]]:
+    """Pack a prefill batch's context rows into chunks of at most ``row_budget`` rows.
+
+    [vLLM-MLA] §Prefill (plan_mla_context_chunks, align_chunk_to_block): the requests'
+    contexts are packed in request order; a request that does not fit in what is left
+    of the current chunk is cut on a page boundary and continues in the next chunk, so
+    that every chunk starts a request on a block boundary (the gather takes no other
+    start).  Returns, per chunk, the ``(request, first token, tokens)`` pieces in order.
+    A budget below one page cannot make progress and is rejected.
+    """
+    if row_budget < page_tokens:
+        raise ValueError("row budget below one page")
+    chunks: list[list[tuple[int, int, int]]] = []
+    cur: list[tuple[int, int, int]] = []
+    used = 0
+    for b, n in enumerate(context_lens):
+        n = max(0, int(n))
+        pos = 0
+        while pos < n:
+            room = row_budget - used
+            take = n - pos if n - pos <= room else room // page_tokens * page_tokens
+            if take == 0:                      # no whole page left: the next chunk
+                chunks.append(cur)
+                cur, used = [], 0
+                continue
+            cur.append((b, pos, take))
+            used += take
+            pos += take
+    if cur:
+        chunks.append(cur)
+    return chunks
+
+
 def merge_attn_states(prefix_o: np.ndarray, prefix_lse: np.ndarray, suffix_o: np.ndarray,
                       suffix_lse: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Merge two attention states of the same query rows over disjoint key sets.

@@ -863,3 +863,61 @@ def test_kv_b_proj_splits_keys_and_values():
     kn, v = O.kv_b_proj(c, w)
     assert kn.shape == (5, 3, 128) and v.shape == (5, 3, 128)
     assert np.allclose(kn[2, 1], c[2] @ w[1, :, :128]) and np.allclose(v[4, 2], c[4] @ w[2, :, 128:])
+
+
+def test_prefill_workspace_rows_page_numbers():
+    """[vLLM-MLA] §Prefill: W = min(max(8 L_max, 4 B_seq P_block), 64 * 1024); at the cap
+    the 576-wide bf16 gather workspace is about 72 MiB (the page's 64 x 1024 x 576 x 2
+    ~ 75.5 MB of its arithmetic section), and eight full requests or four pages per
+    request decide below it."""
+    W = O.prefill_workspace_rows
+    assert W(163840, 256) == 65536 and W(65536, 1024) == 65536
+    assert 65536 * 576 * 2 == 75497472 and abs(65536 * 576 * 2 / 2**20 - 72.0) < 1e-9
+    assert W(4096, 16) == 8 * 4096                      # eight full-length requests
+    assert W(1024, 64) == 4 * 64 * 64                   # four pages per request
+    assert W(2048, 8, 128) == max(8 * 2048, 4 * 8 * 128)
+
+
+def _check_chunk_plan(lens, W, chunks, P=64):
+    seen = {b: [] for b in range(len(lens))}
+    for ch in chunks:
+        assert ch, "no empty chunk"
+        assert sum(t for _, _, t in ch) <= W
+        bs = [b for b, _, _ in ch]
+        assert bs == sorted(bs) and len(set(bs)) == len(bs), "requests in order, once per chunk"
+        for b, start, t in ch:
+            assert t > 0 and start % P == 0
+            seen[b].append((start, t))
+    for b, n in enumerate(lens):
+        pos = 0
+        for start, t in seen[b]:
+            assert start == pos
+            pos += t
+        assert pos == max(0, n)
+    # only the first piece of a chunk can continue a request begun in an earlier chunk
+    for ch in chunks:
+        for b, start, _ in ch[1:]:
+            assert start == 0
+
+
+def test_plan_context_chunks_by_hand():
+    W = 1024
+    chunks = O.plan_context_chunks([700, 3000, 130], W)
+    assert chunks == [[(0, 0, 700), (1, 0, 320)], [(1, 320, 1024)], [(1, 1344, 1024)],
+                      [(1, 2368, 632), (2, 0, 130)]]
+    _check_chunk_plan([700, 3000, 130], W, chunks)
+    # a chunk with less than a page left closes; an exact fill closes too
+    assert O.plan_context_chunks([1000, 100], W) == [[(0, 0, 1000)], [(1, 0, 100)]]
+    assert O.plan_context_chunks([1024, 64], W) == [[(0, 0, 1024)], [(1, 0, 64)]]
+    assert O.plan_context_chunks([0, 0], W) == []
+    with pytest.raises(ValueError):
+        O.plan_context_chunks([10], 63)
+
+
+def test_plan_context_chunks_invariants():
+    rng = np.random.default_rng(2700)
+    for _ in range(300):
+        B = int(rng.integers(1, 40))
+        lens = (rng.integers(0, 9000, B) * (rng.random(B) > 0.2)).tolist()
+        W = int(rng.choice([64, 100, 512, 1000, 4096, 65536]))
+        _check_chunk_plan(lens, W, O.plan_context_chunks(lens, W), 64)
