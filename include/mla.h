@@ -361,6 +361,39 @@ mla_status_t mla_prefill_mha(const void* q, int64_t q_stride_t, int64_t q_stride
                              float* lse, void* stream);
 
 /*
+ * mla_prefill_workspace_rows -- the row budget W of the chunked-context workspace
+ * ([vLLM-MLA] §Prefill, the workspace-size formula):
+ * W = min(max(8 * max_model_len, 4 * max_num_seqs * page_tokens), 64 * 1024).
+ * Host arithmetic; 0 for a non-positive argument.
+ */
+int64_t mla_prefill_workspace_rows(int64_t max_model_len, int64_t max_num_seqs, int32_t page_tokens);
+
+/*
+ * mla_plan_context_chunks -- chunk plan of a prefill batch's context ([vLLM-MLA]
+ * §Prefill: the requests' context rows are packed in request order into chunks of at
+ * most row_budget rows; a request that does not fit in what is left of a chunk is cut
+ * on a 64-token page boundary and continues in the next chunk, so every chunk starts a
+ * request on a page boundary, as mla_gather_cache requires).  Host arithmetic on host
+ * arrays; no device call.
+ *
+ *   context_lens  int32 [B] (host): context tokens of each request (<= 0: none)
+ *   row_budget    rows per chunk, 64 <= row_budget < 2^31 (e.g. mla_prefill_workspace_rows)
+ *   chunk_starts  int32 [max_chunks, B] (host) or NULL: first context token of request
+ *                 b in chunk c (a multiple of 64), 0 where b has no rows in c
+ *   chunk_lens    int32 [max_chunks, B] (host) or NULL: its tokens in chunk c (0: none)
+ *
+ * Returns the number of chunks (call with max_chunks = 0 to size the arrays); only
+ * the first max_chunks are written.  Negative: -MLA_ERR_NULL or -MLA_ERR_SHAPE.  Per
+ * chunk, cu_seq_lens is the prefix sum of its lens and seq_starts its starts (for
+ * mla_gather_cache), and the same prefix sum is the chunk's cu_seqlens_k for
+ * mla_prefill_mha of the new tokens (not causal).  fp8 caches: the gather upconverts a
+ * row with its K scale, so the prefill path takes V from code * k_scale; rows written
+ * by mla_cache_write carry equal K and V scales.
+ */
+int64_t mla_plan_context_chunks(const int32_t* context_lens, int32_t B, int64_t row_budget,
+                                int32_t* chunk_starts, int32_t* chunk_lens, int64_t max_chunks);
+
+/*
  * mla_gather_cache -- gather context rows of the paged cache into a contiguous
  * bf16 workspace ([vLLM-MLA] §Prefill, chunked context: the rows a chunk needs
  * are collected by block_table, cu_seq_lens and token_to_seq so that kv_b_proj

@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.mla_gather_cache.restype = i32
     L.mla_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, i32, i64, i64, i64, i64, vp, vp, vp]
     L.mla_merge_attn_states.restype = i32
+    L.mla_prefill_workspace_rows.argtypes = [i64, i64, i32]
+    L.mla_prefill_workspace_rows.restype = i64
+    L.mla_plan_context_chunks.argtypes = [vp, i32, i64, vp, vp, i64]
+    L.mla_plan_context_chunks.restype = i64
     L.mla_status_str.argtypes = [i32]
     L.mla_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -326,6 +330,28 @@ def prefill_mha(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Tensor, v: to
         int(max_q_len), 1 if causal else 0, float(softmax_scale), _ptr(out), out.stride(0), out.stride(1),
         _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def prefill_workspace_rows(max_model_len: int, max_num_seqs: int, page_tokens: int = PAGE_TOKENS) -> int:
+    """Row budget of the chunked-context workspace (see ``mla_prefill_workspace_rows``)."""
+    return int(lib().mla_prefill_workspace_rows(int(max_model_len), int(max_num_seqs), int(page_tokens)))
+
+
+def plan_context_chunks(context_lens, row_budget: int):
+    """Chunk plan of a prefill batch's context (see ``mla_plan_context_chunks``): returns
+    int32 numpy arrays ``starts[n_chunks, B]`` and ``lens[n_chunks, B]``."""
+    import numpy as np
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    B = int(cl.size)
+    n = int(lib().mla_plan_context_chunks(cl.ctypes.data, B, int(row_budget), None, None, 0))
+    if n < 0:
+        raise MLAError("mla_plan_context_chunks", -n)
+    starts = np.zeros((max(n, 1), B), dtype=np.int32)
+    lens = np.zeros((max(n, 1), B), dtype=np.int32)
+    m = int(lib().mla_plan_context_chunks(cl.ctypes.data, B, int(row_budget), starts.ctypes.data,
+                                          lens.ctypes.data, n))
+    assert m == n
+    return starts[:n], lens[:n]
 
 
 def gather_cache(kv_cache: torch.Tensor, kv_dtype: int, block_table: torch.Tensor,

@@ -250,3 +250,61 @@ extern "C" mla_status_t mla_prefill_mha(const void* q, int64_t q_stride_t, int64
   hipLaunchKernelGGL(prefill_mha_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), p);
   return launch_status();
 }
+
+// ---------------------------------------------------------------------------
+// Chunked context of a prefill batch ([vLLM-MLA] §Prefill): the row budget of the
+// gather workspace and the chunk plan, host arithmetic only.  Each chunk is gathered
+// (mla_gather_cache), up-projected (mla_kv_b_proj), attended by the new tokens
+// (mla_prefill_mha, not causal: the whole context precedes them) and merged into the
+// running state (mla_merge_attn_states), so that at most the row budget of latents is
+// up-projected at a time.
+// ---------------------------------------------------------------------------
+extern "C" int64_t mla_prefill_workspace_rows(int64_t max_model_len, int64_t max_num_seqs, int32_t page_tokens) {
+  if (max_model_len < 1 || max_num_seqs < 1 || page_tokens < 1) return 0;
+  const int64_t a = 8 * max_model_len, b = 4 * max_num_seqs * (int64_t)page_tokens;
+  const int64_t w = a > b ? a : b;
+  return w < 64 * 1024 ? w : 64 * 1024;
+}
+
+extern "C" int64_t mla_plan_context_chunks(const int32_t* context_lens, int32_t B, int64_t row_budget,
+                                           int32_t* chunk_starts, int32_t* chunk_lens, int64_t max_chunks) {
+  if (B < 0 || (B > 0 && !context_lens)) return -(int64_t)MLA_ERR_NULL;
+  if (row_budget < mla::kPage || row_budget > INT32_MAX) return -(int64_t)MLA_ERR_SHAPE;
+  if (max_chunks < 0 || (max_chunks > 0 && (!chunk_starts || !chunk_lens))) return -(int64_t)MLA_ERR_NULL;
+  int64_t n_chunks = 0, used = 0;
+  bool open = false;                       // the current chunk holds a piece
+  auto put = [&](int32_t b, int64_t start, int64_t take) {
+    if (!open) {
+      if (n_chunks < max_chunks) {
+        for (int32_t k = 0; k < B; ++k) {
+          chunk_starts[n_chunks * B + k] = 0;
+          chunk_lens[n_chunks * B + k] = 0;
+        }
+      }
+      open = true;
+    }
+    if (n_chunks < max_chunks) {
+      chunk_starts[n_chunks * B + b] = (int32_t)start;
+      chunk_lens[n_chunks * B + b] = (int32_t)take;
+    }
+  };
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = context_lens[b] > 0 ? context_lens[b] : 0;
+    int64_t pos = 0;
+    while (pos < n) {
+      const int64_t room = row_budget - used;
+      const int64_t take = n - pos <= room ? n - pos : room / mla::kPage * mla::kPage;
+      if (take == 0) {                    // no whole page left: close the chunk
+        ++n_chunks;
+        open = false;
+        used = 0;
+        continue;
+      }
+      put(b, pos, take);
+      used += take;
+      pos += take;
+    }
+  }
+  if (open) ++n_chunks;
+  return n_chunks;
+}

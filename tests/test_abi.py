@@ -255,3 +255,31 @@ def test_binding_rejects_mismatched_out_and_lse():
         M.prefill_mha(qp, kn, kp, kn, cu, cu, T, out=torch.empty((T, N, 128), dtype=torch.float32))
     with pytest.raises(ValueError):
         M.prefill_mha(qp, kn, kp, kn, cu, cu, T, lse=torch.empty((N, T), dtype=torch.float32))
+
+
+def test_context_chunk_plan_matches_the_oracle():
+    """mla_plan_context_chunks / mla_prefill_workspace_rows (host arithmetic) give
+    exactly the oracle's chunk plan and row budget."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    rng = np.random.default_rng(2800)
+    for _ in range(200):
+        B = int(rng.integers(1, 30))
+        lens = (rng.integers(0, 7000, B) * (rng.random(B) > 0.2)).astype(np.int32)
+        W = int(rng.choice([64, 100, 640, 1024, 4096, 65536]))
+        starts, ls = M.plan_context_chunks(lens, W)
+        ref = O.plan_context_chunks(lens.tolist(), W)
+        assert len(ref) == starts.shape[0]
+        for c, ch in enumerate(ref):
+            want_s = np.zeros(B, np.int32)
+            want_l = np.zeros(B, np.int32)
+            for b, s0, t in ch:
+                want_s[b], want_l[b] = s0, t
+            assert np.array_equal(starts[c], want_s) and np.array_equal(ls[c], want_l)
+    for L, S in ((163840, 256), (4096, 16), (1024, 64), (1, 1)):
+        assert M.prefill_workspace_rows(L, S) == O.prefill_workspace_rows(L, S)
+    L = M.lib()
+    lens = np.array([100], np.int32)
+    assert L.mla_plan_context_chunks(lens.ctypes.data, 1, 63, None, None, 0) == -2       # budget below a page
+    assert L.mla_plan_context_chunks(None, 1, 1024, None, None, 0) == -1
+    assert L.mla_prefill_workspace_rows(0, 1, 64) == 0

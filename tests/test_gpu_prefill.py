@@ -8,7 +8,7 @@ import torch
 import mla_inputs as MI
 import mla_paged_latent_amd as M
 from oracle import mla_oracle as O
-from tests.mla_testlib import check_lse, check_out, dev_bf16, host_bits, say, to_f64
+from tests.mla_testlib import bf16_half_ulp, check_lse, check_out, dev_bf16, host_bits, say, to_f64
 
 pytestmark = pytest.mark.gpu
 SC = O.default_scale()
@@ -84,3 +84,123 @@ def test_kv_b_proj_and_prefill_end_to_end():
     kn_b, v_b = f(O.f64_to_bf16_bits(kn_ref)), f(O.f64_to_bf16_bits(v_ref))
     ref_o, ref_l = O.prefill_mha(f(q), kn_b, f(rows[:, 512:]), v_b, cu_q, cu_k, SC, True)
     _check_requests(to_f64(out), lse.cpu().numpy(), ref_o, ref_l, cu_q, "kv_b_proj+prefill")
+
+
+def _chunked_context_prefill(pool, kd, block_table, ctx_lens, new_rows, q, w_kvb, cu_q, W):
+    """The chunked-context prefill of new tokens over their requests' cached context: per
+    chunk of at most W context rows, gather -> kv_b_proj -> prefill_mha (not causal) ->
+    merge into the running state; then the new tokens' causal attention over themselves,
+    merged last.  Every step is one library call."""
+    T, N = q.shape[0], q.shape[1]
+    B = len(ctx_lens)
+    dev = "cuda"
+    bt = torch.from_numpy(block_table).to(dev)
+    cuq = torch.from_numpy(cu_q).to(dev)
+    max_q = int(np.max(np.diff(cu_q)))
+    o_run = torch.zeros((T, N, 128), dtype=torch.bfloat16, device=dev)
+    l_run = torch.full((T, N), -float("inf"), dtype=torch.float32, device=dev)
+    starts, lens = M.plan_context_chunks(ctx_lens, W)
+    for c in range(starts.shape[0]):
+        cu = np.concatenate([[0], np.cumsum(lens[c])]).astype(np.int32)
+        t2s = np.repeat(np.arange(B, dtype=np.int32), lens[c])
+        rows = M.gather_cache(pool, kd, bt, torch.from_numpy(cu).to(dev), torch.from_numpy(t2s).to(dev),
+                              seq_starts=torch.from_numpy(starts[c]).to(dev))
+        assert rows.shape[0] <= W
+        kvb = M.kv_b_proj(rows[:, :512], w_kvb)
+        o_c, l_c = M.prefill_mha(q, kvb[..., :128], rows[:, 512:], kvb[..., 128:], cuq,
+                                 torch.from_numpy(cu).to(dev), max_q, False, SC)
+        o_run, l_run = M.merge_attn_states(o_run, l_run, o_c, l_c)
+    kvb_n = M.kv_b_proj(new_rows[:, :512], w_kvb)
+    o_n, l_n = M.prefill_mha(q, kvb_n[..., :128], new_rows[:, 512:], kvb_n[..., 128:], cuq, cuq, max_q, True, SC)
+    return M.merge_attn_states(o_run, l_run, o_n, l_n), starts.shape[0]
+
+
+def _chain_rounding_bound(q, kn, kp, v, key_off, ctx_lens, cu_q, plan):
+    """Element bound on what the chain's bf16 stores add to the error: every piece's output
+    and every intermediate running merge is stored in bf16 (half an ulp each) and reaches
+    the final output scaled by its softmax weight exp(lse_piece - lse_final).  The pieces'
+    exact values come from the oracle (float64)."""
+    f = O.bf16_bits_to_f64
+    T, N = q.shape[0], q.shape[1]
+    B = len(ctx_lens)
+
+    def piece(rows_of, causal):
+        idx, cu = [], [0]
+        for b in range(B):
+            r = rows_of(b)
+            idx.extend(r)
+            cu.append(cu[-1] + len(r))
+        idx = np.array(idx, np.int64)
+        return O.prefill_mha(q, kn[idx], kp[idx], v[idx], cu_q, np.array(cu, np.int32), SC, causal)
+
+    pieces = []
+    for ch in plan:
+        spans = {b: range(key_off[b] + s0, key_off[b] + s0 + t) for b, s0, t in ch}
+        pieces.append(piece(lambda b: list(spans.get(b, ())), False))
+    # the new tokens over themselves (square causal)
+    pieces.append(piece(lambda b: list(range(key_off[b] + ctx_lens[b], key_off[b] + ctx_lens[b] + cu_q[b + 1] - cu_q[b])),
+                        True))
+    run_o, run_l = np.zeros_like(pieces[0][0]), np.full(pieces[0][1].shape, -np.inf)
+    stores = []
+    for o_c, l_c in pieces:
+        stores.append((o_c, l_c))
+        run_o, run_l = O.merge_attn_states(run_o, run_l, o_c, l_c)
+        stores.append((run_o, run_l))
+    stores.pop()                                  # the final output: its own half ulp is in the gate
+    bound = np.zeros_like(run_o)
+    for o_s, l_s in stores:
+        wgt = np.where(np.isneginf(l_s), 0.0, np.exp(np.where(np.isneginf(l_s), 0.0, l_s) -
+                                                      np.where(np.isneginf(run_l), 0.0, run_l)))
+        bound += wgt[..., None] * bf16_half_ulp(o_s)
+    return bound
+
+
+@pytest.mark.parametrize("N,kd,ctx,new,W", [(16, MI.KV_BF16, [700, 3000, 130], [64, 100, 17], 1024),
+                                          (16, MI.KV_FP8, [700, 3000, 130], [64, 100, 17], 1024),
+                                          (128, MI.KV_BF16, [300, 900, 0], [20, 33, 5], 512)])
+def test_chunked_context_prefill_matches_unchunked_oracle(N, kd, ctx, new, W):
+    """A multi-chunk context prefill (row budget W below the batch's context) end to end
+    against the oracle's plain prefill over the whole context followed by the new tokens
+    (causal, bottom-right aligned): the context keys come from the oracle's gather of the
+    same cache (fp8 rows upconverted with their K scale), keys and values from kv_b_proj."""
+    from tests.mla_testlib import gpu_pool, oracle_pool
+    say(f"chunked context prefill N={N} kd={kd} ctx={ctx} new={new} W={W}")
+    rng = np.random.default_rng(1600 + N + kd)
+    w = MI.make_workload("ctxpf", len(ctx), 1, N, [max(1, c) for c in ctx], None, kd, False, 1600 + N + kd)
+    pool, ref_pool = gpu_pool(w), oracle_pool(w)
+    ctx_lens = np.array(ctx, np.int32)
+    cu_q = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    T = int(cu_q[-1])
+    new_rows = _bf16(rng, (T, 576))
+    q = _bf16(rng, (T, N, 192))
+    wk = _bf16(rng, (N, 512, 256), 1 / np.sqrt(512))
+    (out, lse), n_chunks = _chunked_context_prefill(pool, kd, w.block_table, ctx_lens, dev_bf16(new_rows),
+                                                    dev_bf16(q), dev_bf16(wk), cu_q, W)
+    torch.cuda.synchronize()
+    assert n_chunks >= 2, "the case must take several chunks"
+    f = O.bf16_bits_to_f64
+    cu_ctx = np.concatenate([[0], np.cumsum(ctx_lens)]).astype(np.int32)
+    ctx_bits = O.gather_cache(ref_pool, kd, w.block_table, cu_ctx, np.repeat(np.arange(len(ctx)), ctx_lens))
+    lat, key_off, cu_k = [], [], [0]
+    for b in range(len(ctx)):
+        key_off.append(cu_k[-1])
+        lat.append(ctx_bits[cu_ctx[b]:cu_ctx[b + 1]])
+        lat.append(new_rows[cu_q[b]:cu_q[b + 1]])
+        cu_k.append(cu_k[-1] + int(ctx_lens[b]) + new[b])
+    lat = f(np.concatenate(lat))
+    # keys and values as kv_b_proj stores them (bf16); the prefill itself in float64
+    kn, v = (f(O.f64_to_bf16_bits(x)) for x in O.kv_b_proj(lat[:, :512], f(wk)))
+    qf = f(q)
+    ref_o, ref_l = O.prefill_mha(qf, kn, lat[:, 512:], v, cu_q, np.array(cu_k, np.int32), SC, True)
+    bound = _chain_rounding_bound(qf, kn, lat[:, 512:], v, key_off, ctx_lens, cu_q,
+                                  O.plan_context_chunks(ctx_lens.tolist(), W))
+    got = to_f64(out)
+    for b in range(len(ctx)):
+        a, e = cu_q[b], cu_q[b + 1]
+        # the chain's own bf16 stores are allowed on top of the single-call gate
+        slack = np.where(np.abs(got[a:e] - ref_o[a:e]) > 0, np.minimum(np.abs(got[a:e] - ref_o[a:e]),
+                                                                        bound[a:e]), 0.0)
+        say(f"  request {b}: chain store bound max {float(np.max(bound[a:e])):.3e}")
+        check_out((got[a:e] - np.sign(got[a:e] - ref_o[a:e]) * slack)[None], ref_o[a:e][None],
+                  f"chunked prefill request {b}")
+        check_lse(lse.cpu().numpy()[a:e], ref_l[a:e], f"chunked prefill request {b}")
