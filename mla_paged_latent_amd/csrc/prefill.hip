@@ -7,16 +7,24 @@
 // and values from kv_b_proj, k_pe broadcast over heads, causal over the new tokens
 // after the request's context).
 //
-// One workgroup per (64 query rows, head, request); wave w owns 16 query rows.  Keys
-// stream in blocks of 64: the block's keys are staged row-major in LDS (the A operand
-// of the score MFMAs: 16 keys x 32 features per lane group), its values transposed
-// (the A operand of the PV MFMAs: 16 features x 8 keys).  The query rows stay in
-// registers as the B operand, so the scores come out as S^T (keys x queries) and each
-// lane holds 16 scores of one query: the row max and sum need two xor shuffles.  The
-// softmax is the online one: running max and sum per row, O rescaled when the max
-// grows.  The PV contraction pairs the lane's own probabilities with the values in a
-// permuted key order (its k index 8g+e is key 4g+e of the first 16-key tile of the
-// step for e < 4, key 4g+e-4 of the second for e >= 4), the same on both operands.
+// One workgroup per (256 query rows, head, request): eight waves, two per SIMD, each
+// owning 32 query rows.  The scores use 32x32x16 bf16 MFMAs with the query rows in
+// registers as the B operand: they come out as S^T (keys x queries), each lane holding
+// 32 keys of one query and lane l ^ 32 the other 32, one permlane32 swap away.  Keys
+// stream in blocks of 64, copied straight from global memory into LDS
+// (global_load_lds) through a ring of three buffers, so that a block's copy is issued
+// two blocks ahead of its use; each buffer holds three XOR-swizzled row-major regions,
+// k_nope, k_pe and values, whose swizzles keep the MFMA operand reads free of bank
+// conflicts.  The values are read with ds_read_b64_tr_b16 as the A operand of
+// O^T = V^T P^T, the lane's own probabilities being the B operand: both take the keys
+// in the same permuted order (k index 8h + e of a 16-key step is key 8(e/4) + 4h + e%4
+// of the step, h the lane's half).  The softmax keeps a fixed reference maximum per row,
+// the first block's, so that the output accumulators are never rescaled in the key
+// loop; a row whose scores later rise more than 2^64 above it (a probability the fp32
+// accumulators still hold) sends the workgroup through a second pass from the largest
+// maxima seen.  Workgroups are numbered so that the ones sharing a (request, head), and
+// with it its keys and values, run on the same XCD (one L2), the longest causal tiles
+// first.
 #include "mla_common.h"
 #include "mla_host.h"
 
@@ -37,173 +45,246 @@ struct PrefillParams {
   float scale_log2;        // softmax scale times log2(e)
 };
 
-constexpr int kPQ = 64;              // query rows per workgroup
+constexpr int kPW = 8;               // waves per workgroup, two per SIMD
+constexpr int kPQ = kPW * 32;        // query rows per workgroup
 constexpr int kPK = 64;              // keys per block
-constexpr int kKPitch = 192 + 8;     // bf16 per staged key row (400 B: 16 rows on distinct banks)
-constexpr int kVtPitch = kPK + 8;    // bf16 per transposed value row (144 B)
+constexpr int kRing = 3;             // LDS buffers: block j + 2 is copied while j is used
+// one LDS buffer: k_nope [64][256 B], k_pe [64][128 B], values [64][256 B], each row's
+// 16-byte chunks XOR-swizzled (chunk c of row r at c ^ (r & 15), c ^ ((r >> 1) & 7) and
+// c ^ 4(r & 3) respectively)
+constexpr int kKnBytes = kPK * 256;
+constexpr int kKpBytes = kPK * 128;
+constexpr int kVBytes = kPK * 256;
+constexpr int kBufBytes = kKnBytes + kKpBytes + kVBytes;   // 40 KiB
+constexpr float kSlack = 64.f;       // log2 of the largest probability a fixed reference allows
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_mha_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[(kPK * kKPitch + 128 * kVtPitch) * 2];
-  MLA_LDS char* lds = (MLA_LDS char*)(smem);
-  MLA_LDS uint16_t* ks = reinterpret_cast<MLA_LDS uint16_t*>(lds);
-  MLA_LDS uint16_t* vt = reinterpret_cast<MLA_LDS uint16_t*>(lds + kPK * kKPitch * 2);
-  const int b = blockIdx.z, h = blockIdx.y;
-  // request bounds, clamped into the buffers whatever the caller passed
+// DMA of one block: 40 instructions of 64 x 16 B (16 k_nope, 8 k_pe, 16 values); wave w
+// issues k_nope and value instructions i = 8j + w (j = 0, 1) and k_pe instruction w,
+// instruction i of a region covering its 16-byte positions 64i .. 64i + 63.  In a whole
+// block the swizzle of a lane's row does not depend on j, so instruction j differs only
+// by 32 rows, which go into the scalar base; the lane keeps one offset per region.  A
+// request's last block clamps the rows to its last key (rows past it are masked or
+// multiplied by zero) and takes per-instruction offsets.
+struct PrefillDma {
+  uint32_t kn, kp, v;
+};
+
+__device__ __forceinline__ PrefillDma prefill_dma_offsets(const PrefillParams& p, int w, int L) {
+  PrefillDma d;
+  const int r = 4 * w + (L >> 4), rp = 8 * w + (L >> 3);
+  d.kn = (uint32_t)(r * p.kn_st * 2 + (((L & 15) ^ (r & 15)) * 16));
+  d.v = (uint32_t)(r * p.v_st * 2 + (((L & 15) ^ (4 * (r & 3))) * 16));
+  d.kp = (uint32_t)(rp * p.kp_st * 2 + (((L & 7) ^ ((rp >> 1) & 7)) * 16));
+  return d;
+}
+
+__device__ __forceinline__ void prefill_issue_full(const PrefillParams& p, const PrefillDma& d, const char* kn,
+                                                   const char* kp, const char* v, uint32_t lds) {
+  dma_16B<0, 0>(kn, d.kn, lds);
+  dma_16B<0, 8192>(kn + (int64_t)32 * p.kn_st * 2, d.kn, lds);
+  dma_16B<0, kKnBytes>(kp, d.kp, lds);
+  dma_16B<0, kKnBytes + kKpBytes>(v, d.v, lds);
+  dma_16B<0, kKnBytes + kKpBytes + 8192>(v + (int64_t)32 * p.v_st * 2, d.v, lds);
+}
+
+__device__ __forceinline__ void prefill_issue_tail(const PrefillParams& p, int w, int L, int n, const char* kn,
+                                                   const char* kp, const char* v, uint32_t lds) {
+  const int last = n - 1;
+  auto kn_off = [&](int j) {
+    const int r = 32 * j + 4 * w + (L >> 4);
+    return (uint32_t)(min(r, last) * p.kn_st * 2 + (((L & 15) ^ (r & 15)) * 16));
+  };
+  auto v_off = [&](int j) {
+    const int r = 32 * j + 4 * w + (L >> 4);
+    return (uint32_t)(min(r, last) * p.v_st * 2 + (((L & 15) ^ (4 * (r & 3))) * 16));
+  };
+  const int rp = 8 * w + (L >> 3);
+  const uint32_t kp_off = (uint32_t)(min(rp, last) * p.kp_st * 2 + (((L & 7) ^ ((rp >> 1) & 7)) * 16));
+  dma_16B<0, 0>(kn, kn_off(0), lds);
+  dma_16B<0, 8192>(kn, kn_off(1), lds);
+  dma_16B<0, kKnBytes>(kp, kp_off, lds);
+  dma_16B<0, kKnBytes + kKpBytes>(v, v_off(0), lds);
+  dma_16B<0, kKnBytes + kKpBytes + 8192>(v, v_off(1), lds);
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const void* ptr) {
+  const uint64_t u = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+__global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mha_kernel(
+    PrefillParams p, int32_t q_tiles) {
+  __shared__ __attribute__((aligned(1024))) char smem[kRing * kBufBytes + 16];
+
+  // work item of this workgroup: workgroups L = 8i + x run on XCD x, so XCD x gets the
+  // contiguous item range starting at x * (n / 8) + min(x, n % 8)
+  const uint32_t n_items = gridDim.x, L = blockIdx.x;
+  const uint32_t xcd = L & 7u, per = n_items >> 3, rem = n_items & 7u;
+  const uint32_t item = xcd * per + min(xcd, rem) + (L >> 3);
+  const int qt = q_tiles - 1 - (int)(item % (uint32_t)q_tiles);
+  const int h = (int)((item / (uint32_t)q_tiles) % (uint32_t)p.N);
+  const int b = (int)(item / ((uint32_t)q_tiles * (uint32_t)p.N));
+
   const int64_t q0 = min<int64_t>(max<int64_t>(p.cu_q[b], 0), p.T);
   const int64_t q1 = min<int64_t>(max<int64_t>(p.cu_q[b + 1], q0), p.T);
   const int64_t k0 = min<int64_t>(max<int64_t>(p.cu_k[b], 0), p.S);
   const int64_t k1 = min<int64_t>(max<int64_t>(p.cu_k[b + 1], k0), p.S);
   const int qlen = (int)min<int64_t>(q1 - q0, 0x7fffffff), klen = (int)min<int64_t>(k1 - k0, 0x7fffffff);
-  const int qb = blockIdx.x * kPQ;
+  const int qb = qt * kPQ;
   if (qb >= qlen) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
-
-  // this lane's query row: the B-operand column of the score MFMAs
-  const int qi = qb + 16 * w + l16;
-  const bool q_ok = qi < qlen;
-  const uint16_t* qrow = p.q + (q0 + (q_ok ? qi : 0)) * p.q_st + (int64_t)h * p.q_sh;
-  bf16x8_t qf[6];
-#pragma unroll
-  for (int kk = 0; kk < 6; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g);
-
+  const int w = wave_id(), l = threadIdx.x & 63, hf = l >> 5, l32 = l & 31;
+  const int g = l >> 4, lg = l & 15;
   const int ctx = klen - qlen;
-  const int last_row = min(qb + kPQ, qlen) - 1;
-  const int kend = p.causal ? max(0, min(klen, ctx + last_row + 1)) : klen;
-  const int nvis = p.causal ? max(0, min(klen, ctx + qi + 1)) : klen;
+  auto vis = [&](int row) { return p.causal ? max(0, min(klen, ctx + row + 1)) : klen; };
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x4_t o[8];
-#pragma unroll
-  for (int ft = 0; ft < 8; ++ft) o[ft] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // keys the workgroup needs; this wave's rows, the keys its first and last rows see,
+  // and this lane's query (the score column) and its keys
+  const int kend = vis(min(qb + kPQ, qlen) - 1);
+  const int row0 = qb + 32 * w;
+  const int kend_w = row0 < qlen ? vis(min(row0 + 32, qlen) - 1) : 0;
+  const int nvis_lo = vis(row0);
+  const int qi = row0 + l32;
+  const bool q_ok = qi < qlen;
+  const int nvis = vis(qi);
 
-  // keys kb .. kb+63: 24 chunks of 16 B per key row (16 of k_nope, 8 of k_pe) and
-  // 16 chunks per value row; rows past the request read as zeros.  (Loading the next
-  // block during the current one's MFMAs measured no faster and cost the registers
-  // that three waves per SIMD need.)
-  u32x4_t kv[6], vv[2][2];
-  auto load_block = [&](int kb) {
+  // query fragments: B operand, lane = query column, 8 consecutive features per k step
+  bf16x8_t qf[12];
+  {
+    const uint16_t* qrow = p.q + (q0 + (q_ok ? qi : 0)) * p.q_st + (int64_t)h * p.q_sh + 8 * hf;
 #pragma unroll
-    for (int j = 0; j < 6; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / 24, c = i % 24;
-      const int key = kb + r;
-      const uint16_t* src = c < 16 ? p.kn + (k0 + key) * p.kn_st + (int64_t)h * p.kn_sh + c * 8
-                                   : p.kp + (k0 + key) * p.kp_st + (c - 16) * 8;
-      kv[j] = key < klen ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    // values: a lane takes one 16-byte chunk (8 features) of two adjacent keys, so
-    // that the transposed rows get 4-byte writes (the two keys' values of one
-    // feature); lanes 0..31 of a wave cover the 32 key pairs of one chunk, lanes
-    // 32..63 the next chunk: 64 distinct banks per write instruction
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kp = l & 31, c = 2 * (2 * w + j) + (l >> 5);
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int key = kb + 2 * kp + d;
-        vv[j][d] = key < klen
-                       ? *reinterpret_cast<const u32x4_t*>(p.v + (k0 + key) * p.v_st + (int64_t)h * p.v_sh + c * 8)
-                       : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int kk = 0; kk < 12; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * kk);
+  }
+
+  // operand read offsets in a buffer: k_nope rows l32 (+32 kt) for k steps 0..7, k_pe
+  // for steps 8..11, and the value transpose reads (rows 4(g>>1) + (lg>>2) of a 16-key
+  // step, 4 columns at 16(g&1) + 4(lg&3) of a 32-feature tile); (2kk + hf) ^ x is
+  // 2kk ^ (hf ^ x), so one base per region takes the step or tile XORed in
+  const uint32_t a_kn = (uint32_t)(l32 * 256 + 16 * (hf ^ (l & 15)));
+  const uint32_t a_kp = (uint32_t)(kKnBytes + l32 * 128 + 16 * (hf ^ ((l32 >> 1) & 7)));
+  const uint32_t a_v = (uint32_t)(kKnBytes + kKpBytes + (4 * (g >> 1) + (lg >> 2)) * 256 + 64 * (lg >> 2) +
+                                  16 * (2 * (g & 1) + ((lg & 3) >> 1)) + 8 * (lg & 1));
+
+  const PrefillDma dma = prefill_dma_offsets(p, w, l);
+  const char* kn_base = uniform_ptr(p.kn + k0 * p.kn_st + (int64_t)h * p.kn_sh);
+  const char* kp_base = uniform_ptr(p.kp + k0 * p.kp_st);
+  const char* v_base = uniform_ptr(p.v + k0 * p.v_st + (int64_t)h * p.v_sh);
+  const uint32_t lds0 = lds_addr((MLA_LDS char*)smem) + 1024u * (uint32_t)w;
+  auto issue = [&](int blk) {
+    const int kb = blk * kPK;
+    const char* kn = kn_base + (int64_t)kb * p.kn_st * 2;
+    const char* kp = kp_base + (int64_t)kb * p.kp_st * 2;
+    const char* v = v_base + (int64_t)kb * p.v_st * 2;
+    const uint32_t dst = lds0 + (uint32_t)((blk % kRing) * kBufBytes);
+    if (kb + kPK <= klen) prefill_issue_full(p, dma, kn, kp, v, dst);
+    else prefill_issue_tail(p, w, l, klen - kb, kn, kp, v, dst);
   };
-  for (int kb = 0; kb < kend; kb += kPK) {
-    load_block(kb);
-    lds_barrier();                                      // the previous block's reads are done
-#pragma unroll
-    for (int j = 0; j < 6; ++j) {
-      const int i = tid + 256 * j;
-      *reinterpret_cast<MLA_LDS u32x4_t*>(lds + (i / 24) * kKPitch * 2 + (i % 24) * 16) = kv[j];
-    }
-    MLA_LDS uint32_t* vt32 = reinterpret_cast<MLA_LDS uint32_t*>(vt);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kp = l & 31, c = 2 * (2 * w + j) + (l >> 5);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // features c*8 + 2e and c*8 + 2e + 1 of keys 2kp, 2kp + 1
-        const uint32_t a = vv[j][0][e], b = vv[j][1][e];
-        vt32[((c * 8 + 2 * e) * kVtPitch) / 2 + kp] = (a & 0xFFFFu) | (b << 16);
-        vt32[((c * 8 + 2 * e + 1) * kVtPitch) / 2 + kp] = (a >> 16) | (b & 0xFFFF0000u);
-      }
-    }
-    lds_barrier();
 
-    // S^T: four 16-key tiles; s[kt][r] = score of key kb + 16kt + 4g + r, query l16
-    f32x4_t s[4];
+  const int nblk = (kend + kPK - 1) / kPK;
+  const int nblk_w = (kend_w + kPK - 1) / kPK;
+  float m_ref = -INFINITY, m_seen = -INFINITY, lsum = 0.f;
+  f32x16_t o[4];
+  volatile MLA_LDS int* redo_flag = reinterpret_cast<volatile MLA_LDS int*>((MLA_LDS char*)smem + kRing * kBufBytes);
+  if (threadIdx.x == 0) *redo_flag = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    bool ovf = false;
+    lsum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ft = 0; ft < 4; ++ft) o[ft] = f32x16_t{};
+    if (nblk > 0) issue(0);
+    if (nblk > 1) issue(1);
+    for (int j = 0; j < nblk; ++j) {
+      // block j's copies: this wave's (all but block j + 1's), then everyone's; the
+      // barrier also retires block j - 1, whose buffer block j + 2 then takes
+      if (j + 1 < nblk) wait_vmcnt<5>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (j + 2 < nblk) issue(j + 2);
+      if (j >= nblk_w) continue;
+      const MLA_LDS char* buf = (MLA_LDS char*)smem + (j % kRing) * kBufBytes;
+      const int kb = j * kPK;
+      // S^T = K Q^T for two 32-key tiles
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-      for (int kk = 0; kk < 6; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const MLA_LDS bf16x8_t*>(ks + (16 * kt + l16) * kKPitch + 32 * kk + 8 * g);
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], s[kt], 0, 0, 0);
+      for (int kk = 0; kk < 12; ++kk) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const uint32_t off = kk < 8 ? (a_kn ^ (uint32_t)(32 * kk)) + kt * 32 * 256
+                                      : (a_kp ^ (uint32_t)(32 * (kk - 8))) + kt * 32 * 128;
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(buf, off), qf[kk], s[kt], 0, 0, 0);
+        }
+      }
+      // s[kt][r] = score of key kb + 32kt + 8(r/4) + 4hf + r%4 for this lane's query
+      if (kb + kPK > nvis_lo) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= nvis) s[kt][r] = -INFINITY;
+          }
+      }
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kt][r]);
+      bmax = max_xor32(bmax) * p.scale_log2;
+      // a row without a reference takes this block's maximum (its output and sum are
+      // still zero); one far above the reference flags the workgroup
+      m_seen = fmaxf(m_seen, bmax);
+      if (m_ref == -INFINITY) m_ref = bmax;
+      ovf = ovf || bmax > m_ref + kSlack;
+      const float mm = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], p.scale_log2, -mm));
+          pb[2 * kt + (r >> 3)][r & 7] = (__bf16)pr;
+          lsum += pr;
+        }
+      // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft) {
+          const uint32_t off = (a_v ^ (uint32_t)(64 * ft)) + (uint32_t)((32 * (st >> 1) + 16 * (st & 1)) * 256);
+          const bf16x4_t lo = lds_read_tr16(buf, off);
+          const bf16x4_t hi = lds_read_tr16(buf, off + 8 * 256);
+          const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[ft], 0, 0, 0);
+        }
       }
     }
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 16 * kt + 4 * g + r;
-        const float x = key < nvis ? s[kt][r] * p.scale_log2 : -INFINITY;
-        s[kt][r] = x;
-        bmax = fmaxf(bmax, x);
-      }
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float mn = fmaxf(m, bmax);
-    const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
-    float psum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = mn == -INFINITY ? 0.f : exp2f(s[kt][r] - mn);
-        s[kt][r] = pr;
-        psum += pr;
-      }
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    lsum = lsum * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int ft = 0; ft < 8; ++ft) o[ft] *= alpha;
-
-    // O^T += V^T P^T: k step c pairs tiles 2c and 2c + 1
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      pb[c] = bf16x8_t{(__bf16)s[2 * c][0], (__bf16)s[2 * c][1], (__bf16)s[2 * c][2], (__bf16)s[2 * c][3],
-                       (__bf16)s[2 * c + 1][0], (__bf16)s[2 * c + 1][1], (__bf16)s[2 * c + 1][2],
-                       (__bf16)s[2 * c + 1][3]};
-#pragma unroll
-    for (int ft = 0; ft < 8; ++ft) {
-      const MLA_LDS uint16_t* vrow = vt + (16 * ft + l16) * kVtPitch;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x4_t lo = *reinterpret_cast<const MLA_LDS bf16x4_t*>(vrow + 32 * c + 4 * g);
-        const bf16x4_t hi = *reinterpret_cast<const MLA_LDS bf16x4_t*>(vrow + 32 * c + 16 + 4 * g);
-        const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c], o[ft], 0, 0, 0);
-      }
+    // a row over its reference anywhere in the workgroup: every wave runs again with
+    // the largest maxima seen (the second pass cannot exceed them)
+    if (pass == 0) {
+      if (__any(ovf) && l == 0) *redo_flag = 1;
+      lds_barrier();
+      const int redo = *redo_flag;
+      if (redo == 0) break;
+      m_ref = m_seen;
+      lds_barrier();                                   // the flag is read before the ring is reused
     }
   }
 
-  // o[ft][r] = O[query l16][feature 16ft + 4g + r]
+  // o[ft][r] = O[query l32][feature 32ft + 8(r/4) + 4hf + r%4]
+  const float tot = sum_xor32(lsum);
   if (q_ok) {
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    uint16_t* orow = p.out + (q0 + qi) * p.o_st + (int64_t)h * p.o_sh;
+    const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+    uint16_t* orow = p.out + (q0 + qi) * p.o_st + (int64_t)h * p.o_sh + 4 * hf;
 #pragma unroll
-    for (int ft = 0; ft < 8; ++ft) {
-      const bf16x4_t v4 = {(__bf16)(o[ft][0] * inv), (__bf16)(o[ft][1] * inv), (__bf16)(o[ft][2] * inv),
-                           (__bf16)(o[ft][3] * inv)};
-      *reinterpret_cast<bf16x4_t*>(orow + 16 * ft + 4 * g) = v4;
-    }
-    if (g == 0)
-      p.lse[(q0 + qi) * p.N + h] = lsum > 0.f ? (m + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x4_t v4 = {(__bf16)(o[ft][4 * rb] * inv), (__bf16)(o[ft][4 * rb + 1] * inv),
+                             (__bf16)(o[ft][4 * rb + 2] * inv), (__bf16)(o[ft][4 * rb + 3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(orow + 32 * ft + 8 * rb) = v4;
+      }
+    if (hf == 0) p.lse[(q0 + qi) * p.N + h] = tot > 0.f ? (m_ref + __log2f(tot)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
@@ -246,8 +327,15 @@ extern "C" mla_status_t mla_prefill_mha(const void* q, int64_t q_stride_t, int64
   p.o_st = o_stride_t; p.o_sh = o_stride_h;
   p.T = T; p.S = S; p.N = N; p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)((max_q_len + kPQ - 1) / kPQ), (unsigned)N, (unsigned)B);
-  hipLaunchKernelGGL(prefill_mha_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), p);
+  // a thread's offsets into a 64-key block are 32-bit
+  if (kn_stride_t > (1 << 24) || kp_stride_t > (1 << 24) || v_stride_t > (1 << 24) || kn_stride_t < 0 ||
+      kp_stride_t < 0 || v_stride_t < 0)
+    return MLA_ERR_SHAPE;
+  const int32_t q_tiles = (max_q_len + kPQ - 1) / kPQ;
+  const int64_t items = (int64_t)q_tiles * N * B;
+  if (items > 0x7fffffff) return MLA_ERR_SHAPE;
+  hipLaunchKernelGGL(prefill_mha_kernel, dim3((unsigned)items), dim3(kPW * 64), 0,
+                     reinterpret_cast<hipStream_t>(stream), p, q_tiles);
   return launch_status();
 }
 

@@ -204,3 +204,30 @@ def test_chunked_context_prefill_matches_unchunked_oracle(N, kd, ctx, new, W):
         check_out((got[a:e] - np.sign(got[a:e] - ref_o[a:e]) * slack)[None], ref_o[a:e][None],
                   f"chunked prefill request {b}")
         check_lse(lse.cpu().numpy()[a:e], ref_l[a:e], f"chunked prefill request {b}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_mha_scores_rising_far_above_the_first_block(causal):
+    """A key late in the request whose score exceeds every earlier block's maximum by far
+    more than float32 can hold as a probability against a fixed reference (all-positive
+    queries against a key of all 16s: a raw score near 16 * sum|q| ~ 2400, some 2^250 above
+    the first block's reference): the attention must still equal the oracle's, its softmax
+    concentrated on that key for the rows that see it."""
+    say(f"prefill_mha rising scores causal={causal}")
+    rng = np.random.default_rng(1700 + causal)
+    N = 4
+    pairs = [(200, 200), (70, 300)]
+    cu_q, cu_k = _ragged(pairs)
+    T, S = int(cu_q[-1]), int(cu_k[-1])
+    q = MI.to_bf16_bits(np.abs(rng.standard_normal((T, N, 192))).astype(np.float32))
+    kn, kp, v = _bf16(rng, (S, N, 128)), _bf16(rng, (S, 64)), _bf16(rng, (S, N, 128))
+    big = MI.to_bf16_bits(np.full(1, 16.0, np.float32))[0]
+    for key in (150, cu_k[1] + 260):                    # request 0: key 150; request 1: key 260
+        kn[key] = big
+        kp[key] = big
+    out, lse = M.prefill_mha(dev_bf16(q), dev_bf16(kn), dev_bf16(kp), dev_bf16(v), torch.from_numpy(cu_q).cuda(),
+                             torch.from_numpy(cu_k).cuda(), max(p[0] for p in pairs), causal, SC)
+    torch.cuda.synchronize()
+    f = O.bf16_bits_to_f64
+    ref_o, ref_l = O.prefill_mha(f(q), f(kn), f(kp), f(v), cu_q, cu_k, SC, causal)
+    _check_requests(to_f64(out), lse.cpu().numpy(), ref_o, ref_l, cu_q, "prefill rising")
