@@ -48,7 +48,7 @@ struct PrefillParams {
 constexpr int kPW = 8;               // waves per workgroup, two per SIMD
 constexpr int kPQ = kPW * 32;        // query rows per workgroup
 constexpr int kPK = 64;              // keys per block
-constexpr int kRing = 3;             // LDS buffers: block j + 2 is copied while j is used
+constexpr int kRing = 4;             // LDS buffers: blocks j + 2, j + 3 are copied while j, j + 1 are used
 // one LDS buffer: k_nope [64][256 B], k_pe [64][128 B], values [64][256 B], each row's
 // 16-byte chunks XOR-swizzled (chunk c of row r at c ^ (r & 15), c ^ ((r >> 1) & 7) and
 // c ^ 4(r & 3) respectively)
@@ -116,7 +116,7 @@ __device__ __forceinline__ const char* uniform_ptr(const void* ptr) {
 
 __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mha_kernel(
     PrefillParams p, int32_t q_tiles) {
-  __shared__ __attribute__((aligned(1024))) char smem[kRing * kBufBytes + 16];
+  __shared__ __attribute__((aligned(1024))) char smem[kRing * kBufBytes];
 
   // work item of this workgroup: workgroups L = 8i + x run on XCD x, so XCD x gets the
   // contiguous item range starting at x * (n / 8) + min(x, n % 8)
@@ -155,6 +155,11 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* qrow = p.q + (q0 + (q_ok ? qi : 0)) * p.q_st + (int64_t)h * p.q_sh + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * kk);
+    // retire the query loads here: the compiler cannot see the copies' own waits in the
+    // key loop, and would otherwise wait there on counts that include the copies of the
+    // blocks in flight
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) asm volatile("" : "+v"(qf[kk]));
   }
 
   // operand read offsets in a buffer: k_nope rows l32 (+32 kt) for k steps 0..7, k_pe
@@ -185,89 +190,105 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nblk_w = (kend_w + kPK - 1) / kPK;
   float m_ref = -INFINITY, m_seen = -INFINITY, lsum = 0.f;
   f32x16_t o[4];
-  volatile MLA_LDS int* redo_flag = reinterpret_cast<volatile MLA_LDS int*>((MLA_LDS char*)smem + kRing * kBufBytes);
-  if (threadIdx.x == 0) *redo_flag = 0;
+  // one block's scores, softmax and PV (the block is in the ring; this wave has keys in it)
+  bool ovf = false;
+  auto block = [&](int j) {
+    const MLA_LDS char* buf = (MLA_LDS char*)smem + (j % kRing) * kBufBytes;
+    const int kb = j * kPK;
+    // S^T = K Q^T for two 32-key tiles.  The MFMA phases run at raised wave priority,
+    // the softmax at the base one: of the two waves on a SIMD, the one with matrix work
+    // issues first and the other's softmax fills its MFMA latency.
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t off = kk < 8 ? (a_kn ^ (uint32_t)(32 * kk)) + kt * 32 * 256
+                                    : (a_kp ^ (uint32_t)(32 * (kk - 8))) + kt * 32 * 128;
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(buf, off), qf[kk], s[kt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // s[kt][r] = score of key kb + 32kt + 8(r/4) + 4hf + r%4 for this lane's query
+    if (kb + kPK > nvis_lo) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= nvis) s[kt][r] = -INFINITY;
+        }
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kt][r]);
+    bmax = max_xor32(bmax) * p.scale_log2;
+    // a row without a reference takes this block's maximum (its output and sum are
+    // still zero); one far above the reference flags the workgroup
+    m_seen = fmaxf(m_seen, bmax);
+    if (m_ref == -INFINITY) m_ref = bmax;
+    ovf = ovf || bmax > m_ref + kSlack;
+    const float mm = m_ref == -INFINITY ? 0.f : m_ref;
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], p.scale_log2, -mm));
+        pb[2 * kt + (r >> 3)][r & 7] = (__bf16)pr;
+        lsum += pr;
+      }
+    __builtin_amdgcn_s_setprio(1);
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int ft = 0; ft < 4; ++ft) {
+        const uint32_t off = (a_v ^ (uint32_t)(64 * ft)) + (uint32_t)((32 * (st >> 1) + 16 * (st & 1)) * 256);
+        const bf16x4_t lo = lds_read_tr16(buf, off);
+        const bf16x4_t hi = lds_read_tr16(buf, off + 8 * 256);
+        const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[ft], 0, 0, 0);
+      }
+    }
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
-    bool ovf = false;
+    ovf = false;
     lsum = 0.f;
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft) o[ft] = f32x16_t{};
     if (nblk > 0) issue(0);
     if (nblk > 1) issue(1);
-    for (int j = 0; j < nblk; ++j) {
-      // block j's copies: this wave's (all but block j + 1's), then everyone's; the
-      // barrier also retires block j - 1, whose buffer block j + 2 then takes
-      if (j + 1 < nblk) wait_vmcnt<5>();
-      else wait_vmcnt<0>();
+    // blocks in pairs: the barrier before a pair makes both its blocks (this wave waited
+    // for its own copies of them) visible and retires the previous pair, whose buffers
+    // the next pair's copies then take
+    for (int j = 0; j < nblk; j += 2) {
+      wait_vmcnt<0>();
       lds_barrier();
       if (j + 2 < nblk) issue(j + 2);
-      if (j >= nblk_w) continue;
-      const MLA_LDS char* buf = (MLA_LDS char*)smem + (j % kRing) * kBufBytes;
-      const int kb = j * kPK;
-      // S^T = K Q^T for two 32-key tiles
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-      for (int kk = 0; kk < 12; ++kk) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const uint32_t off = kk < 8 ? (a_kn ^ (uint32_t)(32 * kk)) + kt * 32 * 256
-                                      : (a_kp ^ (uint32_t)(32 * (kk - 8))) + kt * 32 * 128;
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(buf, off), qf[kk], s[kt], 0, 0, 0);
-        }
-      }
-      // s[kt][r] = score of key kb + 32kt + 8(r/4) + 4hf + r%4 for this lane's query
-      if (kb + kPK > nvis_lo) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= nvis) s[kt][r] = -INFINITY;
-          }
-      }
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kt][r]);
-      bmax = max_xor32(bmax) * p.scale_log2;
-      // a row without a reference takes this block's maximum (its output and sum are
-      // still zero); one far above the reference flags the workgroup
-      m_seen = fmaxf(m_seen, bmax);
-      if (m_ref == -INFINITY) m_ref = bmax;
-      ovf = ovf || bmax > m_ref + kSlack;
-      const float mm = m_ref == -INFINITY ? 0.f : m_ref;
-      bf16x8_t pb[4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], p.scale_log2, -mm));
-          pb[2 * kt + (r >> 3)][r & 7] = (__bf16)pr;
-          lsum += pr;
-        }
-      // O^T += V^T P^T over four 16-key steps
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int ft = 0; ft < 4; ++ft) {
-          const uint32_t off = (a_v ^ (uint32_t)(64 * ft)) + (uint32_t)((32 * (st >> 1) + 16 * (st & 1)) * 256);
-          const bf16x4_t lo = lds_read_tr16(buf, off);
-          const bf16x4_t hi = lds_read_tr16(buf, off + 8 * 256);
-          const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[ft], 0, 0, 0);
-        }
-      }
+      if (j + 3 < nblk) issue(j + 3);
+      if (j < nblk_w) block(j);
+      if (j + 1 < nblk_w) block(j + 1);
     }
+    __builtin_amdgcn_s_setprio(0);
     // a row over its reference anywhere in the workgroup: every wave runs again with
-    // the largest maxima seen (the second pass cannot exceed them)
+    // the largest maxima seen (the second pass cannot exceed them).  The vote goes
+    // through the first word of buffer 0, idle between passes.
     if (pass == 0) {
+      volatile MLA_LDS int* redo_flag = reinterpret_cast<volatile MLA_LDS int*>((MLA_LDS char*)smem);
+      lds_barrier();                                   // every wave is done with the ring
+      if (threadIdx.x == 0) *redo_flag = 0;
+      lds_barrier();
       if (__any(ovf) && l == 0) *redo_flag = 1;
       lds_barrier();
       const int redo = *redo_flag;
+      lds_barrier();                                   // the flag is read before the ring is reused
       if (redo == 0) break;
       m_ref = m_seen;
-      lds_barrier();                                   // the flag is read before the ring is reused
     }
   }
 
