@@ -494,6 +494,11 @@ constexpr int kNPlan = kNFlag + 16;                    // split-plan scratch
 constexpr int kNLdsBytes = kNPlan + kPlanLdsBytes;
 static_assert(kNLdsBytes <= 160 * 1024, "LDS budget");
 
+// LDS row of query row R in a P buffer: bits 0, 1 XORed with bits 2, 3, so that rows
+// differing only in bits 2, 3 fall in different quarters of the banks
+__device__ __forceinline__ int p_row(int R) { return R ^ ((R >> 2) & 3); }
+
+
 // token of k-slot 4h + i (i = 0..3) of lane group g in the PV contraction
 __device__ __forceinline__ int pv_token(int g, int h) { return 16 * (g >> 1) + 8 * h + 4 * (g & 1); }
 
@@ -635,12 +640,14 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
       vbase[h][f3] = (uint32_t)(2 * w * kBlkGroupBytes + (t * 8 + (cin ^ page_swz(t))) * 16 + 8 * (l16 & 1));
     }
   // P rows: 64 B = 4 chunks; chunk g holds the 8 k-slots of lane group g, at position
-  // g ^ ((row >> 2) & 3).  PV reads chunk g4 of row l16.
-  const uint32_t pbase = (uint32_t)(l16 * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16));
+  // g ^ ((row >> 2) & 3), and row R sits at p_row(R) so that the 8-lane groups of a
+  // 16-byte read (rows with equal bits 0, 1) spread over the four quarters of the banks.
+  // PV reads chunk g4 of row l16.
+  const uint32_t pbase = (uint32_t)(p_row(l16) * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16));
   // score-phase element i of this lane is token 16th + 4g4 + i = k-slot 4(g4 >> 1) + i of
   // lane group 2th + (g4 & 1)
   const int pg_w = 2 * th + (g4 & 1);
-  const uint32_t pwrite = (uint32_t)(l16 * 64 + ((pg_w ^ ((l16 >> 2) & 3)) * 16) + 8 * (g4 >> 1));
+  const uint32_t pwrite = (uint32_t)(p_row(l16) * 64 + ((pg_w ^ ((l16 >> 2) & 3)) * 16) + 8 * (g4 >> 1));
 
   // query row of this lane in both phases: r = l16
   const int hl = l16 / p.q_len, tq = l16 - hl * p.q_len;
@@ -1181,7 +1188,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       vbase[r][f1] = (uint32_t)(2 * w * kBlkGroupBytes + (t * 8 + (cin ^ page_swz(t))) * 16 + 8 * (l16 & 1));
     }
   // P rows: 64 B = 4 chunks of 8 tokens; chunk a of row R sits at position a ^ ((R >> 2) & 3)
-  // so that 16 consecutive rows reading one chunk hit 16 distinct bank groups.
+  // and row R at p_row(R), so that the 8-lane groups of a 16-byte read (rows with equal
+  // bits 0, 1, both chunks of a lane pair) hit 8 distinct bank groups.
   // fp8 (raw rows): K codes of token 16th + l16 at features 32kk + 8g4; the 8-bit
   // transpose read of step s and feature block fb: lane pair (2k, 2k+1) of group g4 gives
   // token 16s + 8(g4 >> 1) + k, features 128w + 32fb + 16(g4 & 1) + 8(l16 & 1) .. +7.
@@ -1192,7 +1200,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int R = l & 31;
-    pbase[s] = (uint32_t)(R * 64 + (((2 * s + (l >> 5)) ^ ((R >> 2) & 3)) * 16));
+    pbase[s] = (uint32_t)(p_row(R) * 64 + (((2 * s + (l >> 5)) ^ ((R >> 2) & 3)) * 16));
   }
 
   MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
@@ -1448,7 +1456,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
               // row R, tokens 16th + 4g4 .. +3: chunk 2th + (g4 >> 1), half g4 & 1
               const int R = 32 * rg + 16 * rs + l16;
               const int a = 2 * th + (g4 >> 1);
-              *reinterpret_cast<MLA_LDS bf16x4_t*>(pw + R * 64 + ((a ^ ((R >> 2) & 3)) * 16) + 8 * (g4 & 1)) = pk;
+              *reinterpret_cast<MLA_LDS bf16x4_t*>(pw + p_row(R) * 64 + ((a ^ ((R >> 2) & 3)) * 16) + 8 * (g4 & 1)) =
+                  pk;
             }
           }
 

@@ -134,33 +134,32 @@ __device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Layout of cache rows in LDS.  A block of T token rows (T = 64 for a page, 32 for
-// a half page) x 72 chunks of 16 B (8 bf16) is stored column-group major: group
-// G = c >> 3 (128 B of every row) holds the T tokens x 8 chunks, and inside a group
-// chunk c of token t sits at position t*8 + ((c & 7) ^ s(t)):
-//     slot(t, c) = (c >> 3) * 8T + t * 8 + ((c & 7) ^ s(t)),  byte = 16 * slot,
-// with s(t) the 3-bit reversal of (t >> 1) & 7.  gfx950 LDS serves 256 B (64 banks)
-// per clock, i.e. 16 slots; a slot's bank group is slot & 15 = 8*(t & 1) + position.
-//  * ds_read_b128 of one chunk by 16 consecutive tokens: for each parity of t the 8
-//    tokens have distinct (t >> 1) & 7, hence distinct s(t): 16 distinct groups.
-//  * transpose reads of 4 consecutive tokens (t0 = 0 mod 4) x 4 chunks (one 4-aligned
-//    chunk quad, 32 lanes): tokens t0 and t0 + 2 differ in bit 0 of (t >> 1), i.e. in
-//    bit 2 of s, so their chunk quads land in different halves of the 8 positions.
-//  * transpose reads of 8 consecutive tokens x 2 chunks: s(t) >> 1 takes 4 distinct
-//    values over the 4 tokens of each parity.
-// A 1 KiB DMA instruction fills 8 consecutive tokens of one group; the swizzle only
-// permutes 16-byte chunks inside each token's 128 B, so each lane's global offset
-// is a per-lane constant plus a wave-uniform term.
+// Layout of cache rows in LDS.  A block of 32 token rows x 72 chunks of 16 B (8 bf16)
+// is stored column-group major: group G = c >> 3 (128 B of every row) holds the 32
+// tokens x 8 chunks, and inside a group
+// chunk c of token t sits at position t*8 + ((c & 7) ^ s(t)), byte 16 * slot, with
+// s(t) = (t2, t1, t1 ^ t2 ^ t3) (bits 0, 1, 2 of s; ti = bit i of t).  gfx950 LDS has
+// 64 banks of 4 bytes, so a 16-byte slot's bank group is slot & 15 = 8*(t & 1) + its
+// position: same-parity tokens share one half of the banks.  Which lanes of an access
+// are served together was read off SQ_LDS_BANK_CONFLICT for several patterns:
+// ds_read_b128 serves groups of 8 lanes with equal lane bits {0, 1, 4} (the only
+// grouping consistent with all of them), ds_read_b64_tr_b16 is consistent with halves
+// of 32 lanes.  Under that model:
+//  * K reads (lane l: token 16th + (l & 15), chunk 4m + (l >> 4)): a group varies token
+//    bits 2, 3 and chunk bit 1 at fixed token parity; s takes t2 and t3 onto position
+//    bits 0 and 2, the chunk bit lands on bit 1, so the 8 lanes hit 8 positions.
+//  * transpose reads (wide: 4 tokens x 4 chunks x 2 halves; narrow: 4 tokens of
+//    consecutive pairs x 2 chunks): within a 32-lane half the token bit that does not
+//    give the parity reaches position bit 2 through t1 (and, narrow, t1 and t2 reach
+//    bits 1 and 2), so 32 lanes x 8 bytes cover the 64 banks once.
+// The previous swizzle (s = the 3-bit reversal of (t >> 1) & 7) was conflict-free under
+// a 16-consecutive-lane model and measured 2-way on every K read.  A 1 KiB DMA
+// instruction fills 8 consecutive tokens of one 128-byte column; the swizzle only
+// permutes 16-byte chunks inside each token's 128 B, so each lane's global offset is a
+// per-lane constant plus a wave-uniform term.
 // ---------------------------------------------------------------------------
-constexpr int kGroupSlots = 512;                      // page: 64 tokens x 8 chunks
-constexpr int kGroupBytes = kGroupSlots * 16;         // 8192
-
 __device__ __forceinline__ int page_swz(int t) {
-  return (((t >> 1) & 1) << 2) | ((t >> 1) & 2) | ((t >> 3) & 1);
-}
-
-__device__ __forceinline__ int page_slot(int t, int c) {
-  return (c >> 3) * kGroupSlots + t * 8 + ((c & 7) ^ page_swz(t));
+  return ((t >> 2) & 1) | (((t >> 1) & 1) << 1) | ((((t >> 1) ^ (t >> 2) ^ (t >> 3)) & 1) << 2);
 }
 
 // ---------------------------------------------------------------------------
