@@ -142,7 +142,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
   // keys the workgroup needs; this wave's rows, the keys its first and last rows see,
   // and this lane's query (the score column) and its keys
   const int kend = vis(min(qb + kPQ, qlen) - 1);
-  const int row0 = qb + 32 * w;
+  // waves w and w + 4 share a SIMD: tiles w and 7 - w, so that every SIMD holds one
+  // short and one long causal tile
+  const int row0 = qb + 32 * (w < 4 ? w : 11 - w);
   const int kend_w = row0 < qlen ? vis(min(row0 + 32, qlen) - 1) : 0;
   const int nvis_lo = vis(row0);
   const int qi = row0 + l32;
@@ -195,9 +197,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto block = [&](int j) {
     const MLA_LDS char* buf = (MLA_LDS char*)smem + (j % kRing) * kBufBytes;
     const int kb = j * kPK;
-    // S^T = K Q^T for two 32-key tiles.  The MFMA phases run at raised wave priority,
-    // the softmax at the base one: of the two waves on a SIMD, the one with matrix work
-    // issues first and the other's softmax fills its MFMA latency.
+    // S^T = K Q^T for two 32-key tiles.  The score MFMAs run at raised wave priority,
+    // the softmax and PV at the base one: of the two waves on a SIMD, the one starting
+    // its scores issues first and the other's softmax and PV fill its MFMA latency
+    // (raising PV's priority too measured 5 % slower).
     __builtin_amdgcn_s_setprio(1);
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
@@ -241,7 +244,6 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
         pb[2 * kt + (r >> 3)][r & 7] = (__bf16)pr;
         lsum += pr;
       }
-    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
