@@ -231,3 +231,33 @@ def test_prefill_mha_scores_rising_far_above_the_first_block(causal):
     f = O.bf16_bits_to_f64
     ref_o, ref_l = O.prefill_mha(f(q), f(kn), f(kp), f(v), cu_q, cu_k, SC, causal)
     _check_requests(to_f64(out), lse.cpu().numpy(), ref_o, ref_l, cu_q, "prefill rising")
+
+
+def test_prefill_mha_bench_size_sampled_rows():
+    """The benchmarked call: 4 requests x 2048 new tokens, causal, 128 heads, keys and
+    values as strided views into one [S, N, 256] kv_b_proj-shaped tensor, seeded normal
+    inputs drawn on the device.  Sampled query rows (first, last and interior rows of every
+    request, all heads) against the oracle over each row's own visible keys, and the whole
+    output and LSE are finite."""
+    say("prefill_mha bench size, sampled rows")
+    N, L, Bq = 128, 2048, 4
+    T = Bq * L
+    g = torch.Generator(device="cuda").manual_seed(1800)
+    q = torch.randn(T, N, 192, device="cuda", generator=g).to(torch.bfloat16)
+    kvb = torch.randn(T, N, 256, device="cuda", generator=g).to(torch.bfloat16)
+    kp = torch.randn(T, 64, device="cuda", generator=g).to(torch.bfloat16)
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    out, lse = M.prefill_mha(q, kvb[..., :128], kp, kvb[..., 128:], cu, cu, L, True, SC)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+    f = O.bf16_bits_to_f64
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, i in ((0, 0), (0, 1), (1, 255), (1, 256), (2, 1000), (2, 2047), (3, 63), (3, 1537)):
+        row = b * L + i
+        keys = slice(b * L, b * L + i + 1)
+        kn_b = f(bits(kvb[keys, :, :128]))
+        v_b = f(bits(kvb[keys, :, 128:]))
+        ref_o, ref_l = O.prefill_mha(f(bits(q[row:row + 1])), kn_b, f(bits(kp[keys])), v_b,
+                                     np.array([0, 1], np.int32), np.array([0, i + 1], np.int32), SC, True)
+        check_out(to_f64(out[row:row + 1])[None], ref_o[None], f"bench-size row {b}:{i}")
+        check_lse(lse[row:row + 1].cpu().numpy(), ref_l, f"bench-size row {b}:{i}")
