@@ -18,11 +18,12 @@
 //                        query rows); each piece's cache rows stream through
 //                        LDS in 32-token blocks (global->LDS DMA ring) and every query
 //                        row of the group scores against each staged block:
-//                          S^T = K . Q^T   (MFMA; wave w: 32 rows x 16 tokens, Q in
-//                                           registers)
+//                          S^T = K . Q^T   (MFMA; 4 score waves, each 32 rows x 16
+//                                           tokens, Q in registers)
 //                          softmax in the log2 domain against a fixed reference max
-//                          O^T += V^T . P^T (MFMA; wave w's 128 latent features of all
-//                                            rows, V^T via LDS transpose reads, P via LDS)
+//                          O^T += V^T . P^T (MFMA; 4 value waves, each 128 latent features
+//                                            of all rows, V^T via LDS transpose reads, P
+//                                            via LDS), one block behind the scores
 //   decode_narrow_kernel q_len * N <= 16 (16-head decode): 16 rows per unit, whole
 //                        pages double-buffered, the 4 waves split each page's tokens
 //   Both write the final output (single split) or float32 partials; then
@@ -157,8 +158,9 @@ struct PlanTotals {
   }
 };
 
-// Thread tid sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
-// pre[tid] receives the exclusive prefix of those sums.
+// Thread tid < 256 sums the costs of requests [tid * K, tid * K + K), K = ceil(B / 256);
+// pre[tid] receives the exclusive prefix of those sums (threads 256 and up of a larger
+// workgroup own no requests and only take part in the barriers).
 // *seq0 receives the clamped seq_len of request tid * K (0 if there is none).
 template <bool P64>
 __device__ __forceinline__ PlanTotals<P64> plan_prefix(const DecodeParams& p, MLA_LDS long long* pre, int tid, int* seq0) {
@@ -181,11 +183,11 @@ __device__ __forceinline__ PlanTotals<P64> plan_prefix(const DecodeParams& p, ML
     if (l >= d) incl += v;
   }
   MLA_LDS long long* wtot = pre + 256;
-  if (l == 63) wtot[tid >> 6] = incl;
+  if (l == 63 && tid < 256) wtot[tid >> 6] = incl;
   lds_barrier();
   long long off = 0;
   for (int k = 0; k < (tid >> 6); ++k) off += wtot[k];
-  pre[tid] = off + incl - local;
+  if (tid < 256) pre[tid] = off + incl - local;
   PlanTotals<P64> r;
   r.total = uniform64(wtot[0] + wtot[1] + wtot[2] + wtot[3]);
   // no more streams than positions, so that no stream is empty (the pieces of a
@@ -204,7 +206,7 @@ __device__ __forceinline__ void plan_find(const DecodeParams& p, MLA_LDS long lo
   const int K = (p.B + 255) >> 8;
   const int b0 = tid * K;
   const int b1 = b0 + K < p.B ? b0 + K : p.B;
-  const long long e0 = pre[tid];
+  const long long e0 = tid < 256 ? pre[tid] : total;
   const long long e1 = tid < 255 ? pre[tid + 1] : total;
   if (b0 < b1 && e0 <= X && X < e1) {
     long long c = e0;
@@ -945,26 +947,30 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide variant: 64 query rows per unit, 4 waves, 32-token blocks
+// Wide variant: 64 query rows per unit, 8 waves in two roles, 32-token blocks
 // ---------------------------------------------------------------------------
-// Division of labour inside a workgroup (w = wave):
-//  * scores: wave w owns query rows 32*(w >> 1) .. +31 and tokens 16*(w & 1) .. +15 of
-//    each block.  S^T = K . Q^T runs on 16x16x32 MFMA: one K fragment (16 tokens x 32
-//    features, from LDS) feeds two MFMAs (row halves), the wave's query rows stay in
-//    registers (B operand).  The bf16 weights P go to LDS.
-//  * values: wave w owns latent features 128w .. 128w+127 of all 64 rows.
-//    O^T += V^T . P^T runs on 32x32x16 MFMA, V^T from LDS transpose reads of the same
-//    staged rows (the latent is V), P^T read back from LDS.
-// With this split every staged K and V byte is read by one wave only, and a wave holds
-// 128 accumulator registers (its O) plus its query fragments.
-// Pipeline over the blocks of a unit (a block = 32 token rows = half a page):
-//    QK(j) -> [softmax(j) interleaved with PV(j-1)] -> P(j) to LDS -> wait for own
-//    DMA of block j+1 -> barrier Y(j) -> DMA of block j+3
-// so the softmax VALU work of one block overlaps the PV MFMAs of the previous one
-// and a block needs one barrier; blocks j+2 and j+3 are in flight while block j+1 is
-// computed.  bf16 blocks land straight in a 4-slot ring; fp8 blocks land raw in a
-// 4-slot ring and are converted into 2 bf16 slots right after Y(j) (one more barrier
-// Z(j+1) before QK(j+1) reads them).
+// Division of labour inside a workgroup (w = wave; waves w and w + 4 share a SIMD, so
+// every SIMD runs one wave of each role):
+//  * score waves (w = 0..3): wave w owns query rows 32*(w >> 1) .. +31 and tokens
+//    16*(w & 1) .. +15 of each block.  S^T = K . Q^T runs on 16x16x32 MFMA: one K
+//    fragment (16 tokens x 32 features, from LDS) feeds two MFMAs (row halves), the
+//    wave's query rows stay in registers (B operand, 144 registers).  The softmax runs
+//    here too; the bf16 weights P go to LDS.
+//  * value waves (w = 4..7, v = w - 4): wave v owns latent features 128v .. 128v+127 of
+//    all 64 rows.  O^T += V^T . P^T runs on 32x32x16 MFMA, V^T from LDS transpose reads
+//    of the same staged rows (the latent is V), P^T read back from LDS; the wave's O is
+//    128 accumulator registers.  These waves also issue the block copies.
+// The roles form a two-stage pipeline: while the score waves compute block j, the value
+// waves accumulate block j-1, so on every SIMD one wave's LDS reads, softmax and waits
+// run under the other's MFMAs.  Every staged K byte is read by two waves, every V byte
+// by one.  Per block (one barrier Y(j) for all eight waves):
+//    score waves:  QK(j) -> softmax(j) -> P(j) to LDS                      -> Y(j)
+//    value waves:  PV(j-1) -> wait for own DMA of block j+1                -> Y(j) -> DMA of block j+3
+// Blocks j+2 and j+3 are in flight while block j+1 is computed.  bf16 blocks land in a
+// 4-slot ring; fp8 blocks land raw in a 4-slot ring and are read in place (codes
+// converted to bf16 in registers, exactly).  Each role's loop is its own code region, so
+// a wave's registers hold only its role's state.
+constexpr int kWWaves = 8;
 constexpr int kWRows = 64;                             // query rows per wide unit
 constexpr int kWP = kStageEnd;                         // P: 2 buffers x 64 rows x 64 B
 constexpr int kWPBytes = kWRows * 64;
@@ -974,7 +980,7 @@ constexpr int kWPlan = kWFlag + 16;                    // split-plan scratch
 constexpr int kWLdsBytes = kWPlan + kPlanLdsBytes;
 constexpr int kWStagePitch32 = 272;                    // epilogue staging: 64 fp32 of a row + pad
 constexpr int kWStagePitch16 = 144;                    // 64 bf16 of a row + pad
-constexpr int kWStageBytes = 32 * kWStagePitch32;      // per wave
+constexpr int kWStageBytes = 32 * kWStagePitch32;      // per value wave
 static_assert(4 * kWStageBytes <= kSlot, "epilogue staging fits one block slot");
 static_assert(kWLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -1153,15 +1159,23 @@ __device__ __forceinline__ void zero_own_tail_fp8(MLA_LDS char* blk, int valid, 
   }
 }
 
-template <bool FP8, bool P64>
-__global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kWLdsBytes];
-  MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
-  const int tid = threadIdx.x;
-  const int w = wave_id();
-  const int l = lane_id();
-  const int rg = w >> 1, th = w & 1;            // score phase: row group, token half
+// wait until the block issued `later` blocks before the newest one has landed
+// (value waves: per-wave instruction counts of a block 9 bf16; 5, 5, 5, 4 fp8)
+template <bool FP8>
+__device__ __forceinline__ void wait_block_before(int later, int v) {
+  if (later <= 0) wait_vmcnt<0>();
+  else if (later == 1) wait_blocks_after<FP8>(1, v);
+  else wait_query_and_block0<FP8>(2, v);
+}
+
+// One role's walk over the workgroup's units (QK: score waves, else value waves).  Both
+// roles run the same sequence of barriers and plan lookups.
+template <bool FP8, bool P64, bool QK>
+__device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* smem, MLA_LDS long long* plan_lds,
+                                          const PlanTotals<P64>& tot, int seq0, int tid, int w, int l) {
   const int l16 = l & 15, g4 = l >> 4;
+  const int rg = (w >> 1) & 1, th = w & 1;      // score waves: row group, token half
+  const int v = w & 3;                          // value waves: feature quarter and DMA share
   MLA_LDS int* ovf_flag = reinterpret_cast<MLA_LDS int*>(smem + kWFlag);
   MLA_LDS f32x4_t* stats = reinterpret_cast<MLA_LDS f32x4_t*>(smem + kWStats);   // [2][64]
 
@@ -1175,8 +1189,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     for (int m = 0; m < 2; ++m) kbase[m] = (uint32_t)(t * 8 + ((4 * m + g4) ^ page_swz(t))) * 16;
   }
   // V^T transpose reads: the 16-lane group g4 reads tokens 16s + 8*(l >> 5) + 4r + (l16 >> 2)
-  // at features 128w + 32fb + 16(g4 & 1) + 4(l16 & 3); chunk 16w + 4fb + 2(g4 & 1) +
-  // ((l16 >> 1) & 1) lies in group 2w + (fb >> 1) at in-group chunk
+  // at features 128v + 32fb + 16(g4 & 1) + 4(l16 & 3); chunk 16v + 4fb + 2(g4 & 1) +
+  // ((l16 >> 1) & 1) lies in group 2v + (fb >> 1) at in-group chunk
   // 4(fb & 1) + 2(g4 & 1) + ((l16 >> 1) & 1).  s and fb >> 1 only add offsets.
   uint32_t vbase[2][2];
 #pragma unroll
@@ -1185,17 +1199,17 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     for (int f1 = 0; f1 < 2; ++f1) {
       const int t = 8 * (l >> 5) + 4 * r + (l16 >> 2);
       const int cin = 4 * f1 + 2 * (g4 & 1) + ((l16 >> 1) & 1);
-      vbase[r][f1] = (uint32_t)(2 * w * kBlkGroupBytes + (t * 8 + (cin ^ page_swz(t))) * 16 + 8 * (l16 & 1));
+      vbase[r][f1] = (uint32_t)(2 * v * kBlkGroupBytes + (t * 8 + (cin ^ page_swz(t))) * 16 + 8 * (l16 & 1));
     }
   // P rows: 64 B = 4 chunks of 8 tokens; chunk a of row R sits at position a ^ ((R >> 2) & 3)
   // and row R at p_row(R), so that the 8-lane groups of a 16-byte read (rows with equal
   // bits 0, 1, both chunks of a lane pair) hit 8 distinct bank groups.
   // fp8 (raw rows): K codes of token 16th + l16 at features 32kk + 8g4; the 8-bit
   // transpose read of step s and feature block fb: lane pair (2k, 2k+1) of group g4 gives
-  // token 16s + 8(g4 >> 1) + k, features 128w + 32fb + 16(g4 & 1) + 8(l16 & 1) .. +7.
+  // token 16s + 8(g4 >> 1) + k, features 128v + 32fb + 16(g4 & 1) + 8(l16 & 1) .. +7.
   const uint32_t kbase8 = (uint32_t)((16 * th + l16) * kRowBytesFp8 + 8 * g4);
   const uint32_t vbase8 =
-      (uint32_t)((8 * (g4 >> 1) + (l16 >> 1)) * kRowBytesFp8 + 128 * w + 16 * (g4 & 1) + 8 * (l16 & 1));
+      (uint32_t)((8 * (g4 >> 1) + (l16 >> 1)) * kRowBytesFp8 + 128 * v + 16 * (g4 & 1) + 8 * (l16 & 1));
   uint32_t pbase[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -1203,10 +1217,6 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     pbase[s] = (uint32_t)(p_row(R) * 64 + (((2 * s + (l >> 5)) ^ ((R >> 2) & 3)) * 16));
   }
 
-  MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
-  PlanTotals<P64> tot{1, 1};
-  int seq0 = 0;
-  if (p.num_splits == 0) tot = plan_prefix<P64>(p, plan_lds, tid, &seq0);
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
     unit_to_stream(u, p.n_hg, &sid, &hg);
@@ -1226,9 +1236,10 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     };
     // Block stream (as in the narrow variant): the issue cursor (piece 0 = cur, 1 = nxt;
     // block jb) runs up to 3 blocks ahead of the block being computed, across the
-    // boundary into nxt.
+    // boundary into nxt.  Both roles keep the cursor; the value waves issue the copies.
     int ic_piece = 0, ic_j = 0;
     int issued = 0;                              // blocks issued in this unit
+    int landed = 0;                              // value waves: blocks [0, landed) waited for
     int g0 = 0;                                  // stream index of cur's block 0
     auto issue_next = [&]() {
       if (ic_piece == 0 && ic_j >= cur.nblk) {
@@ -1237,16 +1248,16 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
         ic_j = 0;
       }
       if (ic_piece == 0) {
-        issue_piece_block<FP8>(cur, p, ic_j, issued, smem, w, l);
+        if constexpr (!QK) issue_piece_block<FP8>(cur, p, ic_j, issued, smem, v, l);
       } else {
         if (ic_j >= nxt.nblk) return;
-        issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, w, l);
+        if constexpr (!QK) issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, v, l);
       }
       ++ic_j;
       ++issued;
     };
 
-    // the two query rows this lane owns in the score phase: 32rg + 16rs + l16
+    // score waves: the two query rows this lane owns, 32rg + 16rs + l16
     bool row_ok[2];
     int qhead[2], qtq[2];
 #pragma unroll
@@ -1257,27 +1268,24 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       qtq[rs] = tq;
       row_ok[rs] = qhead[rs] < p.N;
     }
-    // every row of the head group is a real head: then the epilogue issues a fixed
-    // number of stores per wave
-    const bool group_full = (hg + 1) * p.hg_heads <= p.N;
     // query fragments (B operand of the 16x16x32 MFMA): row 32rg + 16rs + l16, features
     // 32kk + 8*g4 .. +7.  Padding rows (head >= N) compute with head 0's query; their
     // results are never stored.  (Nothing may read the loaded registers before they are
     // needed: a select on them would make the compiler wait for the loads right here.)
-    bf16x8_t qf[2][18];
+    bf16x8_t qf[QK ? 2 : 1][QK ? 18 : 1];
     auto load_q = [&](int bq) {
+      if constexpr (QK) {
 #pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const uint16_t* qrow = p.q + (int64_t)bq * p.q_sb + (int64_t)qtq[rs] * p.q_st +
-                               (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
+        for (int rs = 0; rs < 2; ++rs) {
+          const uint16_t* qrow = p.q + (int64_t)bq * p.q_sb + (int64_t)qtq[rs] * p.q_st +
+                                 (int64_t)(row_ok[rs] ? qhead[rs] : 0) * p.q_sh;
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
+          for (int kk = 0; kk < 18; ++kk) qf[rs][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * g4);
+        }
       }
     };
-    // the next piece's query is loaded at the end of the current piece, before its output
-    // stores, so that waiting for it does not wait for those stores (vmcnt is in order)
+    // the next piece's query is loaded at the end of the current piece's scores
     bool q_ready = false;
-    int stores_after_q = 0;
 
     while (true) {
       const int b = cur.pc.b, t_begin = cur.pc.t_begin, t_end = cur.pc.t_end, seq = cur.pc.seq;
@@ -1288,47 +1296,41 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
       for (int rs = 0; rs < 2; ++rs) nvis[rs] = seq - p.q_len + 1 + qtq[rs];
 
       auto valid_of = [&](int j) {
-        const int v = t_end - (t_begin + kBlk * j);
-        return v < kBlk ? v : kBlk;
+        const int vv = t_end - (t_begin + kBlk * j);
+        return vv < kBlk ? vv : kBlk;
       };
       // the piece's first three blocks: in flight already (issued while the previous
       // piece finished) or issued here
-      // When nothing of the piece is in flight (a unit's first piece), only block 0 goes
-      // out ahead of the query and the rest after it, so that step 0 waits for block 0
-      // and the query only.
-      const int issued_at_start = issued;
-      const bool fresh = !q_ready && issued == g0;
-      for (int k = 0; k < (fresh ? 1 : 3) && issued < g0 + 3; ++k) issue_next();
-      const bool topped = issued >= g0 + 3;
-      const int before_q = issued;
-
-      if (!q_ready) load_q(b);
-      fetch_nxt();
-      if (!topped) {
-        for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      if constexpr (QK) {
+        if (!q_ready) load_q(b);
       }
-      // The query and the blocks issued before it (block 0 among them) have landed once
-      // at most the vector-memory operations issued after the query are outstanding: the
-      // blocks issued after it, or with the query loaded at the end of the previous piece
-      // at least that piece's output stores.
-      if (fresh) wait_query_and_block0<FP8>(issued - before_q, w);
-      else if (!q_ready || issued != issued_at_start || stores_after_q == 0) wait_vmcnt<0>();
-      else if (stores_after_q == 16) wait_vmcnt<16>();
-      else wait_vmcnt<32>();
+      fetch_nxt();
+      if constexpr (QK) {
+        // the compiler waits for the query loads here (score waves issue no copies)
 #pragma unroll
-      for (int rs = 0; rs < 2; ++rs)
+        for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
+          for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
+      } else {
+        // block 0 of the piece: waited for at the end of the previous piece, or now
+        if (landed <= g0) {
+          wait_block_before<FP8>(issued - (g0 + 1), v);
+          landed = g0 + 1;
+        }
+      }
 
-      f32x16_t o[4][2];
+      f32x16_t o[QK ? 1 : 4][QK ? 1 : 2];
       float m[2], lsum[2], lrsum[2], m_seen[2];
       int ovf = 0;
       float m_restart[2] = {-INFINITY, -INFINITY};
       for (int attempt = 0; attempt < 2; ++attempt) {
+        if constexpr (!QK) {
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+          for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) o[fb][rb] = f32x16_t{};
+            for (int rb = 0; rb < 2; ++rb) o[fb][rb] = f32x16_t{};
+        }
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
           m[rs] = m_restart[rs];
@@ -1345,43 +1347,43 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
           ic_piece = 0;
           ic_j = 0;
           g0 = issued;
-          load_page_ids(cur.ids, p, b, cur.pg0, cur.pg1, l);
+          if constexpr (!QK) load_page_ids(cur.ids, p, b, cur.pg0, cur.pg1, l);
           issue_next();
           issue_next();
           issue_next();
           wait_vmcnt<0>();
+          landed = issued;
         }
-        if (nblk == 1) {
-          if constexpr (FP8) zero_own_tail_fp8(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, valid_of(0), w, l);
-          else zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), w, l);
+        if constexpr (!QK) {
+          if (nblk == 1) {
+            if constexpr (FP8) zero_own_tail_fp8(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, valid_of(0), v, l);
+            else zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), v, l);
+          }
         }
         lds_barrier();                           // block 0 visible, flag reset published
 
-        // Block step: scores of block j, their weights into P(j), interleaved (WITH_PV)
-        // with the PV MFMAs of block j-1, then the hand-over to block j+1.  Block 0 runs
-        // without PV (peeled) so that the steady-state body is one straight-line region.
-        auto step = [&](int j, auto with_pv) {
-          constexpr bool WITH_PV = decltype(with_pv)::value;
+        // Block step j: the score waves compute the weights P(j), the value waves the PV
+        // of block j-1; then the hand-over to block j+1.
+        auto step = [&](int j) {
           const int g = g0 + j;
-          const MLA_LDS char* cb = FP8 ? smem + kRaw + (g & (kRing - 1)) * kBlkBytesFp8 : smem + (g & (kRing - 1)) * kSlot;
-          const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
-
-          f32x4_t sc[2];
-          // fp8: {k_scale, v_scale} of this lane's 4 tokens, read from the raw rows
-          f32x2_t kv[4];
-          if constexpr (FP8) {
+          if constexpr (QK) {
+            const MLA_LDS char* cb =
+                FP8 ? smem + kRaw + (g & (kRing - 1)) * kBlkBytesFp8 : smem + (g & (kRing - 1)) * kSlot;
+            const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
+            f32x4_t sc[2];
+            // fp8: {k_scale, v_scale} of this lane's 4 tokens, read from the raw rows
+            f32x2_t kv[4];
+            if constexpr (FP8) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              kv[i] = *reinterpret_cast<const MLA_LDS f32x2_t*>(cb + (16 * th + 4 * g4 + i) * kRowBytesFp8 + kRow);
-            wide_scores_fp8(cb, qf, kbase8, sc);
-          } else {
-            wide_scores(cb, qf, kbase, sc);
-          }
-
-          // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
-          // Element i of row half rs is token tok0 + i.
-          float mt[2];
-          {
+              for (int i = 0; i < 4; ++i)
+                kv[i] = *reinterpret_cast<const MLA_LDS f32x2_t*>(cb + (16 * th + 4 * g4 + i) * kRowBytesFp8 + kRow);
+              wide_scores_fp8(cb, qf, kbase8, sc);
+            } else {
+              wide_scores(cb, qf, kbase, sc);
+            }
+            // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
+            // Element i of row half rs is token tok0 + i.
+            float mt[2];
 #pragma unroll
             for (int rs = 0; rs < 2; ++rs) {
               mt[rs] = -INFINITY;
@@ -1394,9 +1396,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
               }
               mt[rs] = max_xor32(max_xor16(mt[rs]));
             }
-          }
-          if constexpr (!WITH_PV) {
-            if (attempt == 0) {
+            if (j == 0 && attempt == 0) {
               // reference max of each row from the unit's first block: the two token halves
               // of a row live in two waves, so their maxima meet in LDS
               if (g4 == 0) {
@@ -1410,28 +1410,16 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
                 m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
               }
             }
-          }
-          float base[2];
+            float base[2];
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs) {
-            m_seen[rs] = fmaxf(m_seen[rs], mt[rs]);
-            base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
-            ovf |= (mt[rs] > base[rs] + kRefSlack) ? 1 : 0;
-          }
-
-          // PV of the previous block overlaps this block's exponentials
-          if constexpr (WITH_PV) {
-            if constexpr (FP8)
-              wide_pv_fp8(smem + kRaw + ((g - 1) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + ((j - 1) & 1) * kWPBytes, o,
-                          vbase8, pbase);
-            else
-              wide_pv(smem + ((g - 1) & (kRing - 1)) * kSlot, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
-          }
-
-          // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
-          // the sums keep both the exact weights (LSE) and the rounded ones (O).  A token
-          // whose v_scale is 0 has V = 0 and still counts with its rounded weight.
-          {
+            for (int rs = 0; rs < 2; ++rs) {
+              m_seen[rs] = fmaxf(m_seen[rs], mt[rs]);
+              base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
+              ovf |= (mt[rs] > base[rs] + kRefSlack) ? 1 : 0;
+            }
+            // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
+            // the sums keep both the exact weights (LSE) and the rounded ones (O).  A token
+            // whose v_scale is 0 has V = 0 and still counts with its rounded weight.
             f32x4_t vf, ivf;
             if constexpr (FP8) {
 #pragma unroll
@@ -1459,162 +1447,178 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
               *reinterpret_cast<MLA_LDS bf16x4_t*>(pw + p_row(R) * 64 + ((a ^ ((R >> 2) & 3)) * 16) + 8 * (g4 & 1)) =
                   pk;
             }
-          }
-
-          if (j + 1 < nblk) {
-            // this wave's share of block j+1 has landed once only the blocks issued after
-            // it (at most block j+2) are outstanding
-            wait_blocks_after<FP8>(issued - (g + 2), w);
-            if (j + 2 == nblk) {
+          } else {
+            if (j == 0 && attempt == 0) lds_barrier();   // the score waves' reference-max exchange
+            if (j > 0) {
               if constexpr (FP8)
-                zero_own_tail_fp8(smem + kRaw + ((g + 1) & (kRing - 1)) * kBlkBytesFp8, valid_of(j + 1), w, l);
+                wide_pv_fp8(smem + kRaw + ((g - 1) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + ((j - 1) & 1) * kWPBytes,
+                            o, vbase8, pbase);
               else
-                zero_own_tail(smem + ((g + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), w, l);
+                wide_pv(smem + ((g - 1) & (kRing - 1)) * kSlot, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
+            }
+            // this wave's share of stream block g+1 (this piece's or the next one's) has
+            // landed once only the blocks issued after it (at most g+2) are outstanding
+            if (issued > g + 1) {
+              wait_blocks_after<FP8>(issued - (g + 2), v);
+              landed = g + 2;
+              if (j + 2 == nblk) {
+                if constexpr (FP8)
+                  zero_own_tail_fp8(smem + kRaw + ((g + 1) & (kRing - 1)) * kBlkBytesFp8, valid_of(j + 1), v, l);
+                else
+                  zero_own_tail(smem + ((g + 1) & (kRing - 1)) * kSlot, valid_of(j + 1), v, l);
+              }
             }
           }
           lds_barrier();                              // Y(j)
           issue_next();                               // block g+3 of the stream
         };
-        if (nblk > 0) {
-          step(0, std::false_type{});
-          for (int j = 1; j < nblk; ++j) step(j, std::true_type{});
+        for (int j = 0; j < nblk; ++j) step(j);
+        if constexpr (QK) {
+          // This piece's scores are done: the next piece's query loads go out now (a redo
+          // reloads this piece's query).
+          q_ready = has_nxt;
+          if (has_nxt) load_q(nxt.pc.b);
+        } else {
+          if (nblk > 0) {
+            const int jl = nblk - 1;
+            if constexpr (FP8)
+              wide_pv_fp8(smem + kRaw + ((g0 + jl) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + (jl & 1) * kWPBytes, o,
+                          vbase8, pbase);
+            else
+              wide_pv(smem + ((g0 + jl) & (kRing - 1)) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase, pbase);
+          }
         }
-        // This piece's scores are done: the next piece's query loads go out now, ahead of
-        // the last PV and the output stores (a redo reloads this piece's query).
-        q_ready = has_nxt;
-        if (has_nxt) load_q(nxt.pc.b);
-        if (nblk > 0) {
-          const int jl = nblk - 1;
-          if constexpr (FP8)
-            wide_pv_fp8(smem + kRaw + ((g0 + jl) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + (jl & 1) * kWPBytes, o,
-                        vbase8, pbase);
-          else
-            wide_pv(smem + ((g0 + jl) & (kRing - 1)) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase, pbase);
-        }
-        // any row over the reference slack: the whole workgroup redoes the unit
+        // any row over the reference slack: the whole workgroup redoes the piece
         if (ovf) *ovf_flag = 1;
         lds_barrier();
         const int redo = *ovf_flag;
         lds_barrier();
         if (redo == 0) break;
         // restart with the largest score seen in either token half of each row
+        if constexpr (QK) {
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs) {
-          m_seen[rs] = max_xor32(max_xor16(m_seen[rs]));
-        }
-        if (g4 == 0) {
+          for (int rs = 0; rs < 2; ++rs) m_seen[rs] = max_xor32(max_xor16(m_seen[rs]));
+          if (g4 == 0) {
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = m_seen[rs];
+            for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = m_seen[rs];
+          }
         }
         lds_barrier();
+        if constexpr (QK) {
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs) {
-          const int R = 32 * rg + 16 * rs + l16;
-          m_restart[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+          for (int rs = 0; rs < 2; ++rs) {
+            const int R = 32 * rg + 16 * rs + l16;
+            m_restart[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+          }
         }
         lds_barrier();
       }
 
       // ---- epilogue ----
       // lane-dependent addresses below derive from an opaque copy of the lane id, so
-      // the compiler cannot hoist them out of the piece loop (they would stay live,
-      // and spill, across the whole block loop)
+      // the compiler cannot hoist them out of the piece loop (they would stay live
+      // across the whole block loop)
       const int le = (int)opaque((uint32_t)l);
       const size_t slot = (size_t)pslot * p.n_hg + hg;
       const bool single = nsplit == 1;
-      // row sums: over the 4 lane groups of this wave, then over the two token halves
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const float a = sum_xor32(sum_xor16(lsum[rs]));
-        const float c = sum_xor32(sum_xor16(lrsum[rs]));
-        if (g4 == 0) stats[th * kWRows + 32 * rg + 16 * rs + l16] = f32x4_t{m[rs], a, c, 0.f};
-      }
-      lds_barrier();
-      if (th == 0 && g4 == 0) {
+      // row sums: over the 4 lane groups of a score wave, then over the two token halves
+      if constexpr (QK) {
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
-          const int R = 32 * rg + 16 * rs + l16;
-          const float lt = stats[R][1] + stats[kWRows + R][1];
-          const float lse_v = lt > 0.f ? (m[rs] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
-          if (row_ok[rs]) {
-            if (single) p.lse[((int64_t)b * p.q_len + qtq[rs]) * p.N + qhead[rs]] = lse_v;
-            else p.part_lse[slot * p.m_wg + R] = lse_v;
-          }
+          const float a = sum_xor32(sum_xor16(lsum[rs]));
+          const float c = sum_xor32(sum_xor16(lrsum[rs]));
+          if (g4 == 0) stats[th * kWRows + 32 * rg + 16 * rs + l16] = f32x4_t{m[rs], a, c, 0.f};
         }
       }
-      // This lane's accumulators: row 32rb + (l & 31), features 128w + 32fb + 8i + 4(l >> 5)
-      // + 0..3.  They are staged, half a row block at a time, through this wave's part of
-      // the one ring slot the next piece's blocks leave free (the slot of this piece's
-      // last block; fp8: the first converted slot) and stored as whole row segments
-      // (256 B fp32, 128 B bf16 per row and wave).
-      MLA_LDS char* stage = smem + (FP8 ? 0 : ((g0 + nblk + 3) & (kRing - 1)) * kSlot) + w * kWStageBytes;
-      const int c32 = le & 31, h32 = le >> 5;
+      lds_barrier();
+      if constexpr (QK) {
+        if (th == 0 && g4 == 0) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int R = 32 * rb + c32;
-        const float lr_row = stats[R][2] + stats[kWRows + R][2];
-        const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
-#pragma unroll
-        for (int fh = 0; fh < 2; ++fh) {
-          if (single) {
-#pragma unroll
-            for (int fl = 0; fl < 2; ++fl)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int fb = 2 * fh + fl;
-                const bf16x4_t v = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
-                                    (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
-                *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fl + 8 * i + 4 * h32) * 2) = v;
-              }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // all reads first: the global stores may alias LDS as far as the compiler knows,
-            // so interleaving would serialise every read behind the previous store
-            u32x4_t v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              v[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (8 * k + (le >> 3)) * kWStagePitch16 + (le & 7) * 16);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int Rr = 32 * rb + 8 * k + (le >> 3);
-              const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
-              const int head_r = hg * p.hg_heads + hl_r;
-              if (head_r < p.N) {
-                uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
-                *reinterpret_cast<u32x4_t*>(orow + 128 * w + 64 * fh + 8 * (le & 7)) = v[k];
-              }
+          for (int rs = 0; rs < 2; ++rs) {
+            const int R = 32 * rg + 16 * rs + l16;
+            const float lt = stats[R][1] + stats[kWRows + R][1];
+            const float lse_v = lt > 0.f ? (m[rs] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
+            if (row_ok[rs]) {
+              if (single) p.lse[((int64_t)b * p.q_len + qtq[rs]) * p.N + qhead[rs]] = lse_v;
+              else p.part_lse[slot * p.m_wg + R] = lse_v;
             }
-          } else {
+          }
+        }
+      } else {
+        // This lane's accumulators: row 32rb + (l & 31), features 128v + 32fb + 8i +
+        // 4(l >> 5) + 0..3.  They are staged, half a row block at a time, through this
+        // wave's part of the one ring slot the next piece's blocks leave free (the slot of
+        // this piece's last block; fp8: the unused first slot) and stored as whole row
+        // segments (256 B fp32, 128 B bf16 per row and wave).
+        MLA_LDS char* stage = smem + (FP8 ? 0 : ((g0 + nblk + 3) & (kRing - 1)) * kSlot) + v * kWStageBytes;
+        const int c32 = le & 31, h32 = le >> 5;
 #pragma unroll
-            for (int fl = 0; fl < 2; ++fl)
+        for (int rb = 0; rb < 2; ++rb) {
+          const int R = 32 * rb + c32;
+          const float lr_row = stats[R][2] + stats[kWRows + R][2];
+          const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int fb = 2 * fh + fl;
-                const f32x4_t v = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
-                                   o[fb][rb][4 * i + 3] * inv};
-                *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fl + 8 * i + 4 * h32) * 4) = v;
-              }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          for (int fh = 0; fh < 2; ++fh) {
+            if (single) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              u32x4_t v[4];
+              for (int fl = 0; fl < 2; ++fl)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int fb = 2 * fh + fl;
+                  const bf16x4_t vv = {(__bf16)(o[fb][rb][4 * i] * inv), (__bf16)(o[fb][rb][4 * i + 1] * inv),
+                                       (__bf16)(o[fb][rb][4 * i + 2] * inv), (__bf16)(o[fb][rb][4 * i + 3] * inv)};
+                  *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fl + 8 * i + 4 * h32) * 2) =
+                      vv;
+                }
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+              // all reads first: the global stores may alias LDS as far as the compiler knows,
+              // so interleaving would serialise every read behind the previous store
+              u32x4_t vr[4];
 #pragma unroll
               for (int k = 0; k < 4; ++k)
-                v[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (4 * (4 * kb + k) + (le >> 4)) * kWStagePitch32 +
-                                                                 (le & 15) * 16);
+                vr[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (8 * k + (le >> 3)) * kWStagePitch16 +
+                                                                  (le & 7) * 16);
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
-                float* prow = p.part_o + (slot * p.m_wg + 32 * rb + 4 * (4 * kb + k) + (le >> 4)) * kLatent + 128 * w +
-                              64 * fh + 4 * (le & 15);
-                *reinterpret_cast<u32x4_t*>(prow) = v[k];
+                const int Rr = 32 * rb + 8 * k + (le >> 3);
+                const int hl_r = Rr / p.q_len, tq_r = Rr - hl_r * p.q_len;
+                const int head_r = hg * p.hg_heads + hl_r;
+                if (head_r < p.N) {
+                  uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)tq_r * p.o_st + (int64_t)head_r * p.o_sh;
+                  *reinterpret_cast<u32x4_t*>(orow + 128 * v + 64 * fh + 8 * (le & 7)) = vr[k];
+                }
+              }
+            } else {
+#pragma unroll
+              for (int fl = 0; fl < 2; ++fl)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int fb = 2 * fh + fl;
+                  const f32x4_t vv = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
+                                      o[fb][rb][4 * i + 3] * inv};
+                  *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fl + 8 * i + 4 * h32) * 4) =
+                      vv;
+                }
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) {
+                u32x4_t vr[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                  vr[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (4 * (4 * kb + k) + (le >> 4)) * kWStagePitch32 +
+                                                                    (le & 15) * 16);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  float* prow = p.part_o + (slot * p.m_wg + 32 * rb + 4 * (4 * kb + k) + (le >> 4)) * kLatent + 128 * v +
+                                64 * fh + 4 * (le & 15);
+                  *reinterpret_cast<u32x4_t*>(prow) = vr[k];
+                }
               }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
           }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
         }
       }
-      // output stores issued after the next query (per wave): 2 x 2 x 4 bf16 row segments,
-      // all issued only when no row of the group is padding; 2 x 2 x 8 fp32
-      stores_after_q = single ? (group_full ? 16 : 0) : 32;
       lds_barrier();                             // stats and P free for the next piece
 
       fetch_nxt();
@@ -1631,6 +1635,22 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(DecodeParams p) {
     }
     wait_vmcnt<0>();                             // nothing in flight into LDS at the unit's end
   }
+}
+
+template <bool FP8, bool P64>
+__global__ __launch_bounds__(kWWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_wide_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kWLdsBytes];
+  MLA_LDS char* smem = (MLA_LDS char*)(smem_raw);
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  MLA_LDS long long* plan_lds = reinterpret_cast<MLA_LDS long long*>(smem + kWPlan);
+  PlanTotals<P64> tot{1, 1};
+  int seq0 = 0;
+  if (p.num_splits == 0) tot = plan_prefix<P64>(p, plan_lds, tid, &seq0);
+  if (w < 4) wide_role<FP8, P64, true>(p, smem, plan_lds, tot, seq0, tid, w, l);
+  else wide_role<FP8, P64, false>(p, smem, plan_lds, tot, seq0, tid, w, l);
 }
 
 
@@ -1768,7 +1788,7 @@ inline int64_t plan_streams(const Shape& s, int32_t num_splits, int32_t B, const
 static mla_status_t decode_launch(DecodeParams p, const Shape& s, int32_t kv_dtype, int32_t num_splits,
                                   int32_t B, int32_t max_pages_per_seq, const DeviceInfo& di,
                                   hipStream_t hs) {
-  // One workgroup (256 threads, most of the LDS) per CU.  Automatic plan: one
+  // One workgroup (512 threads wide, 256 narrow; most of the LDS) per CU.  Automatic plan: one
   // stream per workgroup and head group, so every unit runs concurrently; with
   // several head groups the stream count is a multiple of 8 (sibling order).
   const int64_t cus = ((int64_t)di.cu_count + 7) / 8 * 8;
@@ -1786,7 +1806,7 @@ static mla_status_t decode_launch(DecodeParams p, const Shape& s, int32_t kv_dty
   const uint64_t stretch = (uint64_t)kSegOverhead + (uint64_t)max_pages_per_seq;
   const bool p64 = num_splits == 0 && ((uint64_t)B * stretch > 0xFFFFFFFFull / (uint64_t)(streams + 1) ||
                                        stretch * (uint64_t)max_pages_per_seq > 0xFFFFFFFFull);
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 g((unsigned)grid), blk(s.wide ? kWWaves * 64 : 256);
   if (kv_dtype == MLA_KV_BF16) {
     if (p64) {
       if (s.wide) hipLaunchKernelGGL((decode_wide_kernel<false, true>), g, blk, 0, hs, p);
