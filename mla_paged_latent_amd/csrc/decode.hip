@@ -1321,7 +1321,9 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
       }
 
       f32x16_t o[QK ? 1 : 4][QK ? 1 : 2];
-      float m[2], lsum[2], lrsum[2], m_seen[2];
+      // score waves, per row half: reference max m and base (m, or 0 while m = -inf), the
+      // weight sums, and this lane's largest y = x - base so far
+      float m[2], base[2], lsum[2], lrsum[2], ym[2];
       int ovf = 0;
       float m_restart[2] = {-INFINITY, -INFINITY};
       for (int attempt = 0; attempt < 2; ++attempt) {
@@ -1334,9 +1336,10 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
           m[rs] = m_restart[rs];
+          base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
           lsum[rs] = 0.f;
           lrsum[rs] = 0.f;
-          m_seen[rs] = -INFINITY;
+          ym[rs] = -INFINITY;
         }
         ovf = 0;
         if (tid == 0) *ovf_flag = 0;
@@ -1381,24 +1384,29 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
             } else {
               wide_scores(cb, qf, kbase, sc);
             }
-            // scores -> log2 domain, causal / length mask, max over this wave's 16 tokens.
-            // Element i of row half rs is token tok0 + i.
-            float mt[2];
+            // scores -> log2 domain relative to the reference: y = x - base with x = score *
+            // scale * log2 e (fp8: times k_scale), -inf where the causal / length mask hides the
+            // token.  Element i of row half rs is token tok0 + i.
+            f32x4_t kf;
 #pragma unroll
-            for (int rs = 0; rs < 2; ++rs) {
-              mt[rs] = -INFINITY;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float x = sc[rs][i] * (FP8 ? kv[i][0] * p.scale_log2 : p.scale_log2);
-                x = (tok0 + i < nvis[rs]) ? x : -INFINITY;
-                sc[rs][i] = x;
-                mt[rs] = fmaxf(mt[rs], x);
-              }
-              mt[rs] = max_xor32(max_xor16(mt[rs]));
-            }
+            for (int i = 0; i < 4; ++i) kf[i] = FP8 ? kv[i][0] * p.scale_log2 : p.scale_log2;
+            float y[2][4];
             if (j == 0 && attempt == 0) {
               // reference max of each row from the unit's first block: the two token halves
               // of a row live in two waves, so their maxima meet in LDS
+              float mt[2];
+#pragma unroll
+              for (int rs = 0; rs < 2; ++rs) {
+                mt[rs] = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  float x = sc[rs][i] * kf[i];
+                  x = (tok0 + i < nvis[rs]) ? x : -INFINITY;
+                  y[rs][i] = x;
+                  mt[rs] = fmaxf(mt[rs], x);
+                }
+                mt[rs] = max_xor32(max_xor16(mt[rs]));
+              }
               if (g4 == 0) {
 #pragma unroll
                 for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = mt[rs];
@@ -1408,18 +1416,36 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
               for (int rs = 0; rs < 2; ++rs) {
                 const int R = 32 * rg + 16 * rs + l16;
                 m[rs] = fmaxf(stats[R][0], stats[kWRows + R][0]);
+                base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[rs][i] -= base[rs];
+              }
+            } else {
+#pragma unroll
+              for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[rs][i] = __builtin_fmaf(sc[rs][i], kf[i], -base[rs]);
+              // the mask only matters where the block reaches past the shortest visible length
+              if (t_begin + kBlk * (j + 1) > seq - p.q_len + 1) {
+#pragma unroll
+                for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    if (tok0 + i >= nvis[rs]) y[rs][i] = -INFINITY;
               }
             }
-            float base[2];
+            // this lane's largest y of each row: the slack check and the restart reference
+            // (maximum: no canonicalising moves; y is never NaN for finite inputs)
 #pragma unroll
             for (int rs = 0; rs < 2; ++rs) {
-              m_seen[rs] = fmaxf(m_seen[rs], mt[rs]);
-              base[rs] = m[rs] == -INFINITY ? 0.f : m[rs];
-              ovf |= (mt[rs] > base[rs] + kRefSlack) ? 1 : 0;
+              const float bm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(y[rs][0], y[rs][1]),
+                                                             __builtin_elementwise_maximum(y[rs][2], y[rs][3]));
+              ym[rs] = __builtin_elementwise_maximum(ym[rs], bm);
+              ovf |= (bm > kRefSlack) ? 1 : 0;
             }
-            // weights: p = 2^(x - m), rounded to bf16 for the MFMA (fp8: times v_scale);
-            // the sums keep both the exact weights (LSE) and the rounded ones (O).  A token
-            // whose v_scale is 0 has V = 0 and still counts with its rounded weight.
+            // weights: p = 2^y, rounded to bf16 for the MFMA (fp8: times v_scale); the sums
+            // keep both the exact weights (LSE) and the rounded ones (O).  A token whose
+            // v_scale is 0 has V = 0 and still counts with its rounded weight.
             f32x4_t vf, ivf;
             if constexpr (FP8) {
 #pragma unroll
@@ -1435,11 +1461,17 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
               bf16x4_t pk;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const float pr = __builtin_amdgcn_exp2f(sc[rs][i] - base[rs]);
+                const float pr = __builtin_amdgcn_exp2f(y[rs][i]);
                 const __bf16 rr = (__bf16)(FP8 ? pr * vf[i] : pr);
                 pk[i] = rr;
                 lsum[rs] += pr;
-                lrsum[rs] += FP8 ? (vf[i] != 0.f ? (float)rr * ivf[i] : (float)(__bf16)pr) : (float)rr;
+                if constexpr (FP8) lrsum[rs] += vf[i] != 0.f ? (float)rr * ivf[i] : (float)(__bf16)pr;
+              }
+              if constexpr (!FP8) {
+                // sum of the rounded weights, two at a time
+                const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+                lrsum[rs] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pk[0], pk[1]}, one2, lrsum[rs], false);
+                lrsum[rs] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pk[2], pk[3]}, one2, lrsum[rs], false);
               }
               // row R, tokens 16th + 4g4 .. +3: chunk 2th + (g4 >> 1), half g4 & 1
               const int R = 32 * rg + 16 * rs + l16;
@@ -1496,8 +1528,9 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
         if (redo == 0) break;
         // restart with the largest score seen in either token half of each row
         if constexpr (QK) {
+          float m_seen[2];
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs) m_seen[rs] = max_xor32(max_xor16(m_seen[rs]));
+          for (int rs = 0; rs < 2; ++rs) m_seen[rs] = max_xor32(max_xor16(ym[rs] + base[rs]));
           if (g4 == 0) {
 #pragma unroll
             for (int rs = 0; rs < 2; ++rs) stats[th * kWRows + 32 * rg + 16 * rs + l16][0] = m_seen[rs];
