@@ -1168,11 +1168,18 @@ __device__ __forceinline__ void wait_block_before(int later, int v) {
   else wait_query_and_block0<FP8>(2, v);
 }
 
+// The role that issues the block copies (and waits for them before each hand-over).
+constexpr bool kCopyByScore = false;
+// Blocks of the stream issued ahead of the one being computed (at most kRing - 1).
+constexpr int kWDepth = 3;
+static_assert(kWDepth >= 2 && kWDepth < kRing, "copy depth");
+
 // One role's walk over the workgroup's units (QK: score waves, else value waves).  Both
 // roles run the same sequence of barriers and plan lookups.
 template <bool FP8, bool P64, bool QK>
 __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* smem, MLA_LDS long long* plan_lds,
                                           const PlanTotals<P64>& tot, int seq0, int tid, int w, int l) {
+  constexpr bool COPY = QK == kCopyByScore;     // this role issues the block copies
   const int l16 = l & 15, g4 = l >> 4;
   const int rg = (w >> 1) & 1, th = w & 1;      // score waves: row group, token half
   const int v = w & 3;                          // value waves: feature quarter and DMA share
@@ -1248,10 +1255,10 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
         ic_j = 0;
       }
       if (ic_piece == 0) {
-        if constexpr (!QK) issue_piece_block<FP8>(cur, p, ic_j, issued, smem, v, l);
+        if constexpr (COPY) issue_piece_block<FP8>(cur, p, ic_j, issued, smem, v, l);
       } else {
         if (ic_j >= nxt.nblk) return;
-        if constexpr (!QK) issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, v, l);
+        if constexpr (COPY) issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, v, l);
       }
       ++ic_j;
       ++issued;
@@ -1301,23 +1308,24 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
       };
       // the piece's first three blocks: in flight already (issued while the previous
       // piece finished) or issued here
-      for (int k = 0; k < 3 && issued < g0 + 3; ++k) issue_next();
+      for (int k = 0; k < kWDepth && issued < g0 + kWDepth; ++k) issue_next();
       if constexpr (QK) {
         if (!q_ready) load_q(b);
       }
       fetch_nxt();
-      if constexpr (QK) {
-        // the compiler waits for the query loads here (score waves issue no copies)
-#pragma unroll
-        for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-          for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
-      } else {
+      if constexpr (COPY) {
         // block 0 of the piece: waited for at the end of the previous piece, or now
         if (landed <= g0) {
           wait_block_before<FP8>(issued - (g0 + 1), v);
           landed = g0 + 1;
         }
+      }
+      if constexpr (QK) {
+        // the compiler waits for the query loads here
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[rs][kk]));
       }
 
       f32x16_t o[QK ? 1 : 4][QK ? 1 : 2];
@@ -1350,14 +1358,12 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
           ic_piece = 0;
           ic_j = 0;
           g0 = issued;
-          if constexpr (!QK) load_page_ids(cur.ids, p, b, cur.pg0, cur.pg1, l);
-          issue_next();
-          issue_next();
-          issue_next();
+          if constexpr (COPY) load_page_ids(cur.ids, p, b, cur.pg0, cur.pg1, l);
+          for (int k = 0; k < kWDepth; ++k) issue_next();
           wait_vmcnt<0>();
           landed = issued;
         }
-        if constexpr (!QK) {
+        if constexpr (COPY) {
           if (nblk == 1) {
             if constexpr (FP8) zero_own_tail_fp8(smem + kRaw + (g0 & (kRing - 1)) * kBlkBytesFp8, valid_of(0), v, l);
             else zero_own_tail(smem + (g0 & (kRing - 1)) * kSlot, valid_of(0), v, l);
@@ -1488,6 +1494,8 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
               else
                 wide_pv(smem + ((g - 1) & (kRing - 1)) * kSlot, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
             }
+          }
+          if constexpr (COPY) {
             // this wave's share of stream block g+1 (this piece's or the next one's) has
             // landed once only the blocks issued after it (at most g+2) are outstanding
             if (issued > g + 1) {
