@@ -964,9 +964,12 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
 // waves accumulate block j-1, so on every SIMD one wave's LDS reads, softmax and waits
 // run under the other's MFMAs.  Every staged K byte is read by two waves, every V byte
 // by one.  Per block (one barrier Y(j) for all eight waves):
-//    score waves:  QK(j) -> softmax(j) -> P(j) to LDS                      -> Y(j)
-//    value waves:  PV(j-1) -> wait for own DMA of block j+1                -> Y(j) -> DMA of block j+3
-// Blocks j+2 and j+3 are in flight while block j+1 is computed.  bf16 blocks land in a
+//    score waves:  QK(j) -> softmax(j) -> P(j) to LDS                                  -> Y(j)
+//    value waves:  PV(j-1) with the copy of block j+2 spread over it -> wait for own
+//                  copy of block j+1                                                   -> Y(j)
+// A copy instruction holds its wave while the CU's memory pipeline takes it, so each
+// wave's share goes out in three smaller bursts between MFMAs.  Blocks j+1 and j+2 are in
+// flight while block j is computed.  bf16 blocks land in a
 // 4-slot ring; fp8 blocks land raw in a 4-slot ring and are read in place (codes
 // converted to bf16 in registers, exactly).  Each role's loop is its own code region, so
 // a wave's registers hold only its role's state.
@@ -1042,10 +1045,18 @@ struct WidePvOps {
   }
 };
 
+// Work placed between a PV's MFMAs: mid() after the first token half's, end() after the
+// last (the value waves issue parts of the next block's copy there).
+struct NoHook {
+  __device__ __forceinline__ void mid() const {}
+  __device__ __forceinline__ void end() const {}
+};
+
 // O^T += V^T . P^T for one block.  The first token half's operands were requested by
 // the caller (ops.load(0)); the second half's are requested while the first half's
 // MFMAs run.
-__device__ __forceinline__ void wide_pv_mfma(WidePvOps& ops, f32x16_t (&o)[4][2]) {
+template <class Hook = NoHook>
+__device__ __forceinline__ void wide_pv_mfma(WidePvOps& ops, f32x16_t (&o)[4][2], const Hook& hook = Hook{}) {
   __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
   ops.load(1);
 #pragma unroll
@@ -1063,16 +1074,19 @@ __device__ __forceinline__ void wide_pv_mfma(WidePvOps& ops, f32x16_t (&o)[4][2]
         }
       }
     }
+    if (s == 0) hook.mid();
   }
+  hook.end();
 }
 
+template <class Hook = NoHook>
 __device__ __forceinline__ void wide_pv(const MLA_LDS char* blk, const MLA_LDS char* pbuf,
                                         f32x16_t (&o)[4][2], const uint32_t (&vbase)[2][2],
-                                        const uint32_t (&pbase)[2]) {
+                                        const uint32_t (&pbase)[2], const Hook& hook = Hook{}) {
   WidePvOps ops;
   ops.init(blk, pbuf, vbase, pbase);
   ops.load(0);
-  wide_pv_mfma(ops, o);
+  wide_pv_mfma(ops, o, hook);
 }
 
 // ---- fp8 rows read in place (wide variant) ----
@@ -1120,8 +1134,9 @@ __device__ __forceinline__ void wide_scores_fp8(const MLA_LDS char* blk, const b
 
 // O^T += V^T . P^T over one raw fp8 block: per step of 16 tokens and feature block fb,
 // one 8-bit transpose read gives each lane its feature's 8 tokens.
+template <class Hook = NoHook>
 __device__ __forceinline__ void wide_pv_fp8(const MLA_LDS char* blk, const MLA_LDS char* pbuf, f32x16_t (&o)[4][2],
-                                            uint32_t vbase8, const uint32_t (&pbase)[2]) {
+                                            uint32_t vbase8, const uint32_t (&pbase)[2], const Hook& hook = Hook{}) {
   const uint32_t va = opaque(lds_addr(blk) + vbase8);
   uint32_t pa[2];
 #pragma unroll
@@ -1141,7 +1156,9 @@ __device__ __forceinline__ void wide_pv_fp8(const MLA_LDS char* blk, const MLA_L
       for (int rb = 0; rb < 2; ++rb)
         o[fb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb], o[fb][rb], 0, 0, 0);
     }
+    if (s == 0) hook.mid();
   }
+  hook.end();
 }
 
 // Bytes of rows >= valid inside this wave's share of a raw fp8 block (flat 16-byte
@@ -1167,6 +1184,72 @@ __device__ __forceinline__ void wait_block_before(int later, int v) {
   else if (later == 1) wait_blocks_after<FP8>(1, v);
   else wait_query_and_block0<FP8>(2, v);
 }
+
+// One value wave's share of a block copy, looked up ahead of its instructions: the half
+// page in the cache and the wave's LDS destination in the ring slot.
+struct BlockCopy {
+  const char* src;
+  uint32_t lds;
+};
+
+template <bool FP8>
+__device__ __forceinline__ BlockCopy prepare_copy(StagedPiece& sp, const DecodeParams& p, int jb, int g,
+                                                  MLA_LDS char* smem, int v, int l) {
+  jb = __builtin_amdgcn_readfirstlane(jb);
+  g = __builtin_amdgcn_readfirstlane(g);
+  const char* pg = page_ptr(sp.ids, p, sp.pc.b, sp.pg0 + (jb >> 1), sp.pg1, l, FP8);
+  BlockCopy c;
+  if constexpr (FP8) {
+    c.src = pg + (jb & 1) * kBlkBytesFp8;
+    c.lds = lds_addr(smem + kRaw + (g & (kRing - 1)) * kBlkBytesFp8) + 1024u * (uint32_t)v;
+  } else {
+    c.src = pg + (jb & 1) * kBlkBytesBf16;
+    c.lds = lds_addr(smem + (g & (kRing - 1)) * kSlot) + 1024u * (uint32_t)v;
+  }
+  return c;
+}
+
+// Instruction I of the wave's share (the split of issue_blk_bf16 / issue_blk_fp8: bf16
+// instruction I = tokens 8v .. 8v+7 of 128-byte column I, I < 9; fp8 instruction I = flat
+// chunks 64(v + 4I) + lane, I < 5, while inside the block).  voff: the lane's offset in
+// that split (bf16: token row and swizzled chunk; fp8: 1024v + 16 lane).
+template <bool FP8, int I>
+__device__ __forceinline__ void copy_insn(const BlockCopy& c, uint32_t voff, int v, int l) {
+  // (the LDS base is wave-uniform; readfirstlane states it to the compiler)
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(c.lds);
+  if constexpr (FP8) {
+    if constexpr (I < 5) {
+      if ((v + 4 * I) * 64 + l < kBlkChunksFp8) dma_16B<0, 4096 * I>(c.src + 4096 * I, voff, lds);
+    }
+  } else {
+    if constexpr (I < 9) dma_16B<128 * I, kBlkGroupBytes * I>(c.src, voff, lds);
+  }
+}
+
+// Instructions [B, E) of the share, issued only when the copy exists (`on`, uniform)
+template <bool FP8, int B, int E>
+__device__ __forceinline__ void copy_part(const BlockCopy& c, bool on, uint32_t voff, int v, int l) {
+  if constexpr (B < E) {
+    if (on) copy_insn<FP8, B>(c, voff, v, l);
+    copy_part<FP8, B + 1, E>(c, on, voff, v, l);
+  }
+}
+
+// A block copy spread over a PV: one third before it (begin), one after its first token
+// half (mid), the rest after it (end), so that the copy instructions, which hold their
+// wave while the CU's memory pipeline takes them, go out in smaller bursts.
+template <bool FP8>
+struct SpreadCopy {
+  static constexpr int kN = FP8 ? 5 : 9;
+  static constexpr int kA = (kN + 2) / 3, kB = 2 * (kN + 2) / 3;
+  const BlockCopy& c;
+  bool on;
+  uint32_t voff;
+  int v, l;
+  __device__ __forceinline__ void begin() const { copy_part<FP8, 0, kA>(c, on, voff, v, l); }
+  __device__ __forceinline__ void mid() const { copy_part<FP8, kA, kB>(c, on, voff, v, l); }
+  __device__ __forceinline__ void end() const { copy_part<FP8, kB, kN>(c, on, voff, v, l); }
+};
 
 // The role that issues the block copies (and waits for them before each hand-over).
 constexpr bool kCopyByScore = false;
@@ -1223,6 +1306,14 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
     const int R = l & 31;
     pbase[s] = (uint32_t)(p_row(R) * 64 + (((2 * s + (l >> 5)) ^ ((R >> 2) & 3)) * 16));
   }
+  // copying waves: this lane's offset in the wave's share of a block copy
+  uint32_t copy_voff;
+  if constexpr (FP8) {
+    copy_voff = (uint32_t)(1024 * v + 16 * l);
+  } else {
+    const int t = 8 * v + (l >> 3);
+    copy_voff = (uint32_t)(t * kRowBytesBf16 + ((l & 7) ^ page_swz(t)) * 16);
+  }
 
   for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
     int sid, hg;
@@ -1248,20 +1339,28 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
     int issued = 0;                              // blocks issued in this unit
     int landed = 0;                              // value waves: blocks [0, landed) waited for
     int g0 = 0;                                  // stream index of cur's block 0
-    auto issue_next = [&]() {
+    // the cursor's next block: false when nothing is left to issue; the copying role
+    // also gets the block's copy (its instructions are issued by the caller)
+    auto next_copy = [&](BlockCopy& c) -> bool {
       if (ic_piece == 0 && ic_j >= cur.nblk) {
-        if (!nxt_known || !has_nxt) return;
+        if (!nxt_known || !has_nxt) return false;
         ic_piece = 1;
         ic_j = 0;
       }
       if (ic_piece == 0) {
-        if constexpr (COPY) issue_piece_block<FP8>(cur, p, ic_j, issued, smem, v, l);
+        if constexpr (COPY) c = prepare_copy<FP8>(cur, p, ic_j, issued, smem, v, l);
       } else {
-        if (ic_j >= nxt.nblk) return;
-        if constexpr (COPY) issue_piece_block<FP8>(nxt, p, ic_j, issued, smem, v, l);
+        if (ic_j >= nxt.nblk) return false;
+        if constexpr (COPY) c = prepare_copy<FP8>(nxt, p, ic_j, issued, smem, v, l);
       }
       ++ic_j;
       ++issued;
+      return true;
+    };
+    auto issue_next = [&]() {
+      BlockCopy c;
+      const bool on = next_copy(c);
+      if constexpr (COPY) copy_part<FP8, 0, FP8 ? 5 : 9>(c, on, copy_voff, v, l);
     };
 
     // score waves: the two query rows this lane owns, 32rg + 16rs + l16
@@ -1376,6 +1475,10 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
         auto step = [&](int j) {
           const int g = g0 + j;
           if constexpr (QK) {
+            if (j > 0) {
+              BlockCopy c;
+              next_copy(c);                           // the cursor moves as in the value waves
+            }
             const MLA_LDS char* cb =
                 FP8 ? smem + kRaw + (g & (kRing - 1)) * kBlkBytesFp8 : smem + (g & (kRing - 1)) * kSlot;
             const int tok0 = t_begin + kBlk * j + 16 * th + 4 * g4;   // token of this lane's element 0
@@ -1488,11 +1591,16 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
           } else {
             if (j == 0 && attempt == 0) lds_barrier();   // the score waves' reference-max exchange
             if (j > 0) {
+              // PV of block j-1, with the copy of stream block g+2 spread over it
+              BlockCopy c;
+              const bool on = next_copy(c);
+              const SpreadCopy<FP8> cp{c, on, copy_voff, v, l};
+              cp.begin();
+              const MLA_LDS char* pbuf = smem + kWP + ((j - 1) & 1) * kWPBytes;
               if constexpr (FP8)
-                wide_pv_fp8(smem + kRaw + ((g - 1) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + ((j - 1) & 1) * kWPBytes,
-                            o, vbase8, pbase);
+                wide_pv_fp8(smem + kRaw + ((g - 1) & (kRing - 1)) * kBlkBytesFp8, pbuf, o, vbase8, pbase, cp);
               else
-                wide_pv(smem + ((g - 1) & (kRing - 1)) * kSlot, smem + kWP + ((j - 1) & 1) * kWPBytes, o, vbase, pbase);
+                wide_pv(smem + ((g - 1) & (kRing - 1)) * kSlot, pbuf, o, vbase, pbase, cp);
             }
           }
           if constexpr (COPY) {
@@ -1510,22 +1618,30 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
             }
           }
           lds_barrier();                              // Y(j)
-          issue_next();                               // block g+3 of the stream
         };
         for (int j = 0; j < nblk; ++j) step(j);
         if constexpr (QK) {
+          if (nblk > 0) {
+            BlockCopy c;
+            next_copy(c);
+          }
           // This piece's scores are done: the next piece's query loads go out now (a redo
           // reloads this piece's query).
           q_ready = has_nxt;
           if (has_nxt) load_q(nxt.pc.b);
         } else {
           if (nblk > 0) {
+            // the last block's PV, with the copy of stream block g0 + nblk + kWDepth - 1
             const int jl = nblk - 1;
+            BlockCopy c;
+            const bool on = next_copy(c);
+            const SpreadCopy<FP8> cp{c, on, copy_voff, v, l};
+            cp.begin();
+            const MLA_LDS char* pbuf = smem + kWP + (jl & 1) * kWPBytes;
             if constexpr (FP8)
-              wide_pv_fp8(smem + kRaw + ((g0 + jl) & (kRing - 1)) * kBlkBytesFp8, smem + kWP + (jl & 1) * kWPBytes, o,
-                          vbase8, pbase);
+              wide_pv_fp8(smem + kRaw + ((g0 + jl) & (kRing - 1)) * kBlkBytesFp8, pbuf, o, vbase8, pbase, cp);
             else
-              wide_pv(smem + ((g0 + jl) & (kRing - 1)) * kSlot, smem + kWP + (jl & 1) * kWPBytes, o, vbase, pbase);
+              wide_pv(smem + ((g0 + jl) & (kRing - 1)) * kSlot, pbuf, o, vbase, pbase, cp);
           }
         }
         // any row over the reference slack: the whole workgroup redoes the piece
