@@ -1413,8 +1413,10 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
       }
       fetch_nxt();
       if constexpr (COPY) {
-        // block 0 of the piece: waited for at the end of the previous piece, or now
-        if (landed <= g0) {
+        // block 0 of the piece: waited for at the end of the previous piece, or now (an
+        // empty piece has no block 0: stream block g0 belongs to a later piece and may not
+        // be issued yet)
+        if (nblk > 0 && landed <= g0) {
           wait_block_before<FP8>(issued - (g0 + 1), v);
           landed = g0 + 1;
         }
