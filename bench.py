@@ -15,7 +15,7 @@ fractions of the published and of the measured HBM and bf16 MFMA peaks, and the
 throughput bar each is held to), the per-kernel launch durations of the step, the
 measured peaks, and the CPU oracle baseline.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_head]
-    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill|absorb_rope_decode|prefill_mha
+    python bench.py --op gather_fp8|gather_bf16|merge_states|varlen_spec|upv_fp8_decode|upv_fp8_prefill|absorb_rope_decode|kv_b_proj_prefill|prefill_mha
 """
 
 from __future__ import annotations
@@ -583,6 +583,9 @@ CONTEXT_OPS = {
     # prefill of new tokens: 4 requests of 2048 new tokens each (no context), causal,
     # 128 heads, keys [k_nope | k_pe] 192 wide, values 128 wide
     "prefill_mha": dict(kind="prefill", B=4, L=2048, N=128),
+    # the keys and values those 8192 new tokens attend over, up-projected from their
+    # latents: [k_nope | v][s, h] = kv_c[s] . W_KVB[h], 128 heads
+    "kv_b_proj_prefill": dict(kind="kvb", S=8192, N=128),
 }
 
 
@@ -723,6 +726,24 @@ def run_context_op(args) -> dict:
                 f"{R} rotating input copies")
         metric = "query absorption with fused RoPE GB/s (% of HBM roofline), 1 MI355X"
         dtype = "bf16"
+    elif op["kind"] == "kvb":
+        S, N = op["S"], op["N"]
+        per_copy = N * 512 * 256 * 2 + S * 512 * 2
+        R = max(2, min(8, math.ceil(3 * MALL_BYTES / per_copy)))
+        gen = torch.Generator(device=dev).manual_seed(570)
+        ws = [(torch.randn(N, 512, 256, device=dev, generator=gen) / math.sqrt(512)).to(torch.bfloat16)
+              for _ in range(R)]
+        kcs = [torch.randn(S, 576, device=dev, generator=gen).to(torch.bfloat16) for _ in range(R)]
+        out = torch.empty((S, N, 256), dtype=torch.bfloat16, device=dev)
+        calls = [(kcs[i].data_ptr(), kcs[i].stride(0), ws[i].data_ptr(), S, N, out.data_ptr(), out.stride(0),
+                  out.stride(1), stream) for i in range(R)]
+        f = L.mla_kv_b_proj
+        bytes_alg = per_copy + S * N * 256 * 2
+        flops_alg = 2.0 * S * N * 512 * 256
+        desc = (f"{args.op}: S={S} latent rows (the [S, 576] rows' first 512) x {N} heads, "
+                f"kv_c [S, 512] . W_KVB [N, 512, 256] -> [k_nope | v] [S, N, 256] bf16, {R} rotating input copies")
+        metric = "prefill key / value up-projection TFLOP/s (% of bf16 MFMA roofline), 1 MI355X"
+        dtype = "bf16"
     elif op["kind"] == "prefill":
         Bq, Lq, N = op["B"], op["L"], op["N"]
         T = S = Bq * Lq
@@ -787,13 +808,13 @@ def run_context_op(args) -> dict:
         log(f"[bench] the unfused call on the same inputs: {bf16_out_us:.1f} us per call")
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    if op["kind"] in ("varlen", "prefill") and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
+    if op["kind"] in ("varlen", "prefill", "kvb") and flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
         tfs = flops_alg / (mean_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof.update({"traffic": None, "kernel": args.op, "algorithmic_bytes": bytes_alg,
                  "mean_launch_us": round(mean_ms * 1e3, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-    if op["kind"] in ("varlen", "upv", "rope", "prefill"):
+    if op["kind"] in ("varlen", "upv", "rope", "prefill", "kvb"):
         roof["algorithmic_flops"] = flops_alg
     if bf16_out_us is not None:
         roof["unfused_call_us"] = bf16_out_us
@@ -803,15 +824,16 @@ def run_context_op(args) -> dict:
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": {"workload": desc},
            "roofline": roof}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_context(args.op)
+        res["cpu_baseline"] = cpu_baseline_context(args.op, unit)
     return res
 
 
-def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
-    """The oracle's gather / merge on a bounded sample of the same workload."""
+def cpu_baseline_context(name: str, unit: str = "GB/s", budget_s: float = 10.0) -> dict:
+    """The oracle on a bounded sample of the same workload, in the record's unit (GB/s, or
+    TFLOP/s for the calls whose record is priced against the MFMA peak)."""
     from oracle import mla_oracle as O
     op = CONTEXT_OPS[name]
-    times, n_items = [], 0
+    times, n_items, flops_item = [], 0, None
     t_all = time.perf_counter()
     if op["kind"] == "gather":
         c = MI.make_context_chunk([256] * 8, [0] * 8, 32, seed=520)
@@ -866,6 +888,19 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         n_items = 1
         per_item = N * 128 * 512 * 2 + T * N * (192 * 2 + 576 * 2) + T * (8 + 256)
         sample = f"T={T} tokens x {N} heads through the oracle absorb_rope"
+    elif op["kind"] == "kvb":
+        S, N = 64, op["N"]
+        rng = np.random.default_rng(571)
+        kc = rng.standard_normal((S, 512))
+        w = rng.standard_normal((N, 512, 256)) / np.sqrt(512)
+        while time.perf_counter() - t_all < budget_s and len(times) < 20:
+            t0 = time.perf_counter()
+            O.f64_to_bf16_bits(np.concatenate(O.kv_b_proj(kc, w), axis=-1))
+            times.append(time.perf_counter() - t0)
+        n_items = 1
+        per_item = N * 512 * 256 * 2 + S * 512 * 2 + S * N * 256 * 2
+        flops_item = 2.0 * S * N * 512 * 256
+        sample = f"S={S} latent rows x {N} heads through the oracle kv_b_proj"
     elif op["kind"] == "prefill":
         N, Lq = op["N"], 64
         rng = np.random.default_rng(561)
@@ -878,6 +913,7 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
             times.append(time.perf_counter() - t0)
         n_items = 1
         per_item = Lq * N * (192 * 2 + 256 * 2 + 128 * 2 + 4) + Lq * 64 * 2
+        flops_item = Lq * (Lq + 1) / 2 * N * (2 * 192 + 2 * 128)
         sample = f"1 request x {Lq} new tokens x {N} heads through the oracle prefill_mha"
     else:
         T, N, D = 256, op["N"], op["D"]
@@ -891,7 +927,11 @@ def cpu_baseline_context(name: str, budget_s: float = 10.0) -> dict:
         per_item = 3 * D * 2 + 3 * 4
         sample = f"{T} query rows x {N} heads x D={D} through the oracle merge"
     mean = sum(times) / len(times)
-    return {"value": round(n_items * per_item / mean / 1e9, 3), "unit": "GB/s", "cores": host_cores(), "kind": "oracle",
+    if unit == "TFLOP/s" and flops_item is not None:
+        value = round(n_items * flops_item / mean / 1e12, 6)
+    else:
+        value, unit = round(n_items * per_item / mean / 1e9, 3), "GB/s"
+    return {"value": value, "unit": unit, "cores": host_cores(), "kind": "oracle",
             "sample": f"{sample}, {len(times)} repetition(s), mean {mean:.3f} s"}
 
 
