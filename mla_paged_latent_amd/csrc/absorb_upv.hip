@@ -715,6 +715,231 @@ __global__ __launch_bounds__(256, 2) void head_gemm_big_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head GEMM for many tokens, weight-stationary form (the same products as
+// head_gemm_big_kernel): C[t, h, n0 : n0+128] = A[t, h, 0:512] . W[h][0:512][n0 : n0+128].
+// A workgroup of four waves owns one head, one 128-column half and a contiguous range of
+// 16-token stages; grid = (parts, heads, NN / 128), about two workgroups per CU.  Each
+// wave keeps the weights of its 32 columns over all of K = 512 in registers (the MFMA
+// A operand of two 16x16x32 products per 32 k, 128 VGPRs), loaded once through LDS in
+// two halves with transpose reads, so the weights leave HBM once per workgroup instead
+// of once per token tile.  The token rows then stream through a ring of four LDS slots:
+// one global->LDS copy per row moves a token's whole 1 KiB (512 bf16) of this head in one
+// instruction, rows padded to 1056 B (with 1040 B the fragment reads measured about five
+// times the bank conflicts).  One barrier per stage: after it, the copy of stage c + 3
+// goes into the slot stage c - 1 has left, the tile of stage c - 1 leaves from one of two
+// LDS staging buffers, and stage c is multiplied into the other.  Tiles leave as whole
+// row segments (bf16) or quantized per token (fp8 codes in groups of the 128 columns, one
+// float32 scale), with nontemporal stores (the outputs are not read again by this call).
+// Rows past T are copied from row T - 1 and never stored, so every wave issues the same
+// number of copies per stage and the vmcnt values below are exact.  About 75 KB of LDS.
+// ---------------------------------------------------------------------------
+constexpr int kHsTok = 16;                                   // tokens per stage
+constexpr int kHsSlots = 4;                                  // ring slots (3 stages ahead)
+constexpr int kHsRowPitch = 1024 + 32;                       // one token's 512 bf16, padded
+constexpr int kHsSlot = kHsTok * kHsRowPitch;                // 16896
+constexpr int kHsOutPitch = 128 * 2 + 16;                    // 272
+constexpr int kHsOutBytes = kHsTok * kHsOutPitch;            // one staging buffer
+constexpr int kHsOut = kHsSlots * kHsSlot;                   // two staging buffers from here
+constexpr int kHsLds = kHsOut + 2 * kHsOutBytes;             // 76288
+constexpr int kHsCopies = kHsTok / 4;                        // row copies per wave and stage
+static_assert(kHsSlots * kHsSlot >= 256 * 256, "half of a head's weights fits the ring for the transpose pass");
+static_assert(kHsTok * 16 == 256, "the epilogue gives one 16-byte chunk to each thread");
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// e4m3fn codes of four float32 values already within [-448, 448] (round to nearest even,
+// subnormals kept): the same codes as e4m3_encode, by the conversion instruction
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+// One 1 KiB global->LDS row copy as dma_16B<0, 0>, marked nontemporal: for activations
+// that are read exactly once, so their lines go first when the caches need room
+__device__ __forceinline__ void dma_16B_nt(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %2, 0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 offset:0 nt"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "scc");
+}
+
+// STREAM_A: every activation row is read by one workgroup only (a head's own rows), so
+// the copies are nontemporal; the shared latent rows of kv_b_proj are read by every head
+// and stay cacheable.
+template <bool FP8OUT, bool STREAM_A>
+__global__ __launch_bounds__(256, 2) void head_gemm_stream_kernel(
+    const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // [T, N or shared, 512]
+    const uint16_t* __restrict__ W, int nn,                           // [N, 512, nn]
+    uint16_t* __restrict__ C, int64_t c_st, int64_t c_sh,            // bf16 [T, N, nn]
+    uint8_t* __restrict__ Q, int64_t q_st,                            // fp8 codes [T, N * 128]
+    float* __restrict__ S, int64_t s_st,                              // scales [T, N]
+    int64_t T, int parts) {
+  __shared__ __attribute__((aligned(16))) char smem[kHsLds];
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+  const uint32_t lbase = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds));
+  const int h = blockIdx.y;
+  const int n0 = blockIdx.z * 128;
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  const int g = l >> 4, lg = l & 15;
+  const int64_t chunks = (T + kHsTok - 1) / kHsTok;
+  const int64_t c0 = chunks * blockIdx.x / parts, c1 = chunks * (blockIdx.x + 1) / parts;
+
+  // weights: two passes of 256 k rows x 128 columns (256 B per row, unpadded: a copy
+  // instruction fills four rows), read back transposed into the MFMA A operand: for
+  // column half c and step s, lane l holds column 32 w + 16 c + (l & 15) and k rows
+  // 32 s + 8 (l >> 4) + 0..7
+  bf16x8_t wf[2][16];
+  const char* wsrc = reinterpret_cast<const char*>(W + (int64_t)h * 512 * nn + n0);
+  const uint32_t wvoff = (uint32_t)((l >> 4) * nn * 2 + (l & 15) * 16);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = w * 16 + j;                          // rows 4 i .. 4 i + 3 of the pass
+      dma_16B<0, 0>(uniform_ptr(wsrc + (int64_t)(256 * q + 4 * i) * nn * 2), wvoff, lbase + 1024 * i);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t r0 = lbase + (uint32_t)((32 * s + 8 * g + (lg >> 2)) * 256 + (32 * w + 16 * c + 4 * (lg & 3)) * 2);
+        const bf16x4_t lo = lds_read_tr16_at(r0);
+        const bf16x4_t hi = lds_read_tr16_at(r0 + 4 * 256);
+        wf[c][8 * q + s] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    lds_barrier();
+  }
+
+  const char* asrc = reinterpret_cast<const char*>(A + (int64_t)h * a_sh);
+  const uint32_t avoff = (uint32_t)(l * 16);
+  // the copies of one stage: wave w moves rows 4 w .. 4 w + 3 (token rows past T repeat
+  // row T - 1; their products are not stored)
+  auto issue = [&](int64_t ci) {
+    const int64_t tb = ci * kHsTok;
+    const int slot = (int)((ci - c0) % kHsSlots);
+#pragma unroll
+    for (int j = 0; j < kHsCopies; ++j) {
+      const int r = w * kHsCopies + j;
+      const int64_t t = tb + r < T ? tb + r : T - 1;
+      const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(lbase + slot * kHsSlot + r * kHsRowPitch);
+      if constexpr (STREAM_A)
+        dma_16B_nt(uniform_ptr(asrc + t * a_st * 2), avoff, dst);
+      else
+        dma_16B<0, 0>(uniform_ptr(asrc + t * a_st * 2), avoff, dst);
+    }
+  };
+
+  // activation fragments (B operand): token l & 15 of the stage, k 32 s + 8 (l >> 4)
+  const uint32_t bread = lbase + (uint32_t)((l & 15) * kHsRowPitch + 16 * (l >> 4));
+  const int r = tid / 16, cc = tid % 16;                 // epilogue: token row, 16-byte chunk
+
+  // the finished tile of stage ci leaves from staging buffer ci & 1 one stage later
+  auto epilogue = [&](int64_t ci) {
+    const MLA_LDS char* ostage = lds + kHsOut + (int)(ci & 1) * kHsOutBytes;
+    const int64_t tb = ci * kHsTok;
+    if constexpr (!FP8OUT) {
+      if (tb + r < T) {
+        const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * kHsOutPitch + cc * 16);
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(C + (tb + r) * c_st + (int64_t)h * c_sh + n0 + cc * 8));
+      }
+    } else {
+      // a token's group of 128 values is 16 consecutive lanes of 8 values
+      const u32x4_t raw = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * kHsOutPitch + cc * 16);
+      float x[8];
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_bits_to_f32(raw[k] & 0xFFFFu);
+        x[2 * k + 1] = bf16_bits_to_f32(raw[k] >> 16);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * k]), fabsf(x[2 * k + 1])));
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      float sc = __fdiv_rn(amax, 448.0f);
+      if (sc == 0.f) sc = 1.0f;
+      // |x / sc| <= 448 (1 + 2^-23) after rounding: clamping to 448 keeps every code
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = fminf(fmaxf(__fdiv_rn(x[k], sc), -448.0f), 448.0f);
+      const uint32_t lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
+      const uint32_t hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
+      if (tb + r < T) {
+        __builtin_nontemporal_store(u32x2_t{lo, hi},
+                                    reinterpret_cast<u32x2_t*>(Q + (tb + r) * q_st + (int64_t)h * 128 + cc * 8));
+        if (cc == 0) S[(tb + r) * s_st + h] = sc;
+      }
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < kHsSlots - 1; ++k)
+    if (c0 + k < c1) issue(c0 + k);
+#pragma unroll 1
+  for (int64_t ci = c0; ci < c1; ++ci) {
+    // wait for this stage's copies: the newer ones in flight are those of the next
+    // min(2, c1 - 1 - ci) stages (stores of earlier stages may finish in any order; the
+    // count covers copies only, which complete in order)
+    const int64_t ahead = c1 - 1 - ci;
+    if (ahead >= 2) wait_vmcnt<2 * kHsCopies>();
+    else if (ahead == 1) wait_vmcnt<kHsCopies>();
+    else wait_vmcnt<0>();
+    // one barrier per stage: stage ci landed for every wave; stage ci - 1's slot has been
+    // read by every wave, and its tile staged
+    lds_barrier();
+    if (ci + kHsSlots - 1 < c1) issue(ci + kHsSlots - 1);   // into the slot of stage ci - 1
+    if (ci > c0) epilogue(ci - 1);
+    f32x4_t acc[2] = {};
+    const uint32_t b0 = bread + (uint32_t)(((ci - c0) % kHsSlots) * kHsSlot);
+    // fragment reads run four steps ahead of the products (the scheduler would otherwise
+    // pull each read down next to its use)
+    bf16x8_t x[16];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] = lds_read_b128_at(b0 + 64 * s);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s + 4 < 16) x[s + 4] = lds_read_b128_at(b0 + 64 * (s + 4));
+      __builtin_amdgcn_sched_barrier(0);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[0][s], x[s], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[1][s], x[s], acc[1], 0, 0, 0);
+    }
+    // lane (l & 15) is token l & 15 of the stage, columns 32 w + 16 c + 4 (l >> 4) + 0..3;
+    // staging buffer ci & 1 was last read by the epilogue of stage ci - 2, before the barrier
+    MLA_LDS char* ostage = lds + kHsOut + (int)(ci & 1) * kHsOutBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x4_t v = {(__bf16)acc[c][0], (__bf16)acc[c][1], (__bf16)acc[c][2], (__bf16)acc[c][3]};
+      *reinterpret_cast<MLA_LDS bf16x4_t*>(ostage + (l & 15) * kHsOutPitch + (32 * w + 16 * c + 4 * (l >> 4)) * 2) = v;
+    }
+  }
+  if (c0 < c1) {
+    lds_barrier();                                       // the last tile is staged
+    epilogue(c1 - 1);
+  }
+}
+
+// workgroups per (head, column half) of head_gemm_stream_kernel: about two per CU over
+// the grid, never more than the 32-token stages
+static int stream_parts(int64_t T, int units, int cu_count) {
+  const int64_t stages = (T + kHsTok - 1) / kHsTok;
+  int64_t p = (2 * (int64_t)(cu_count > 0 ? cu_count : 256) + units - 1) / units;
+  if (p > stages) p = stages;
+  return (int)(p < 1 ? 1 : p);
+}
+
 }  // namespace mla
 
 extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
@@ -792,10 +1017,11 @@ extern "C" mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T >= kBigGemmMinT) {
-    hipLaunchKernelGGL(head_gemm_big_kernel<false>, dim3((unsigned)((T + 127) / 128), N, 1), dim3(256), 0, s,
+    const int parts = stream_parts(T, N, di.cu_count);
+    hipLaunchKernelGGL((head_gemm_stream_kernel<false, true>), dim3((unsigned)parts, N, 1), dim3(256), 0, s,
                        (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv, MLA_V_HEAD_DIM,
                        (uint16_t*)out, out_stride_t, (int64_t)MLA_V_HEAD_DIM, (uint8_t*)nullptr, (int64_t)0,
-                       (float*)nullptr, (int64_t)0, T);
+                       (float*)nullptr, (int64_t)0, T, parts);
     return launch_status();
   }
   dim3 grid(MLA_V_HEAD_DIM / 64, N);
@@ -827,11 +1053,13 @@ extern "C" mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(MLA_V_HEAD_DIM / group), (unsigned)N, (unsigned)((T + 31) / 32));
-  if (group == 128 && T >= kBigGemmMinT)
-    hipLaunchKernelGGL(head_gemm_big_kernel<true>, dim3((unsigned)((T + 127) / 128), N, 1), dim3(256), 0, s,
+  if (group == 128 && T >= kBigGemmMinT) {
+    const int parts = stream_parts(T, N, di.cu_count);
+    hipLaunchKernelGGL((head_gemm_stream_kernel<true, true>), dim3((unsigned)parts, N, 1), dim3(256), 0, s,
                        (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv, MLA_V_HEAD_DIM,
                        (uint16_t*)nullptr, (int64_t)0, (int64_t)0, (uint8_t*)out_codes, codes_stride_t, out_scales,
-                       scales_stride_t, T);
+                       scales_stride_t, T, parts);
+  }
   else if (group == 64)
     hipLaunchKernelGGL(up_v_fp8_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)o_lat, ol_stride_t,
                        ol_stride_h, (const uint16_t*)w_uv, (uint8_t*)out_codes, codes_stride_t, out_scales,
@@ -858,10 +1086,11 @@ extern "C" mla_status_t mla_kv_b_proj(const void* kv_c, int64_t kc_stride_t, con
   if (st != MLA_OK) return st;
   // the latent has no head dimension: every head's workgroups read the same rows
   if (S >= kBigGemmMinT) {
-    hipLaunchKernelGGL(head_gemm_big_kernel<false>, dim3((unsigned)((S + 127) / 128), N, 2), dim3(256), 0,
+    const int parts = stream_parts(S, 2 * N, di.cu_count);
+    hipLaunchKernelGGL((head_gemm_stream_kernel<false, false>), dim3((unsigned)parts, N, 2), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), (const uint16_t*)kv_c, kc_stride_t, (int64_t)0,
                        (const uint16_t*)w_kvb, 256, (uint16_t*)out, out_stride_t, out_stride_h, (uint8_t*)nullptr,
-                       (int64_t)0, (float*)nullptr, (int64_t)0, S);
+                       (int64_t)0, (float*)nullptr, (int64_t)0, S, parts);
     return launch_status();
   }
   hipLaunchKernelGGL((head_gemm_kernel<512, 256, 64, 2, kNoTail>), dim3(256 / 64, N), dim3(256), 0,
