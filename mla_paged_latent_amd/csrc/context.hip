@@ -9,15 +9,13 @@
 // merge_attn_states, re-weighting by exp(lse - max_lse) with empty states at
 // weight zero).
 //
-// Both are pure streaming kernels (HBM-bound): one thread per 16 output bytes, so
-// a row's threads are consecutive and every load and store is a whole 16-byte (fp8
-// codes: 8-byte) piece of a contiguous row.
+// Both are pure streaming kernels (HBM-bound) whose consecutive threads cover
+// consecutive 16-byte pieces of a row, so loads and stores are contiguous runs.
 #include "mla_common.h"
 #include "mla_host.h"
 
 namespace mla {
 
-constexpr int kGatherChunks = kRow * 2 / 16;            // 72 output chunks of 8 bf16 per row
 
 // bfloat16 bits of the exact product v * s, rounded once (nearest, ties to even).
 // v has at most 4 significant bits, so v * s has at most 28: p = fl(v * s) holds the
@@ -53,14 +51,15 @@ __device__ __forceinline__ uint32_t bf16x2_of_products(uint32_t two, float ks) {
   return *reinterpret_cast<const uint32_t*>(&r);
 }
 
-// Chunk i of the grid is output row i / 72, bytes 16 (i % 72) .. +15.  Each thread
-// takes kGatherUnroll chunks 256 apart per round and runs their dependent loads
+constexpr int kGatherChunks = kRow * 2 / 16;            // 72 output chunks of 8 bf16 per row
+
+// bf16 rows: chunk i of the grid is output row i / 72, bytes 16 (i % 72) .. +15.  Each
+// thread takes kGatherUnroll chunks 256 apart per round and runs their dependent loads
 // (row -> request -> page id -> data) side by side, so that several chains are in
 // flight per thread.
 constexpr int kGatherUnroll = 4;
 
-template <bool FP8>
-__global__ __launch_bounds__(256) void gather_cache_kernel(
+__global__ __launch_bounds__(256) void gather_bf16_kernel(
     const char* __restrict__ pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     int64_t bt_sb, int32_t max_pages, const int32_t* __restrict__ cu_seq_lens,
     const int32_t* __restrict__ seq_starts, const int32_t* __restrict__ token_to_seq, int32_t B,
@@ -100,21 +99,95 @@ __global__ __launch_bounds__(256) void gather_cache_kernel(
     u32x4_t v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      v[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (slot[u] < 0) continue;
-      if constexpr (!FP8) {
-        v[u] = *reinterpret_cast<const u32x4_t*>(pool + slot[u] * kRowBytesBf16 + c[u] * 16);
-      } else {
-        const char* row = pool + slot[u] * kRowBytesFp8;
-        const u32x2_t codes = *reinterpret_cast<const u32x2_t*>(row + c[u] * 8);
-        const float ks = *reinterpret_cast<const float*>(row + kRow);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[u][k] = bf16x2_of_products(codes[k >> 1] >> (16 * (k & 1)), ks);
-      }
+      v[u] = slot[u] >= 0 ? *reinterpret_cast<const u32x4_t*>(pool + slot[u] * kRowBytesBf16 + c[u] * 16)
+                          : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (base + 256 * u < n) *reinterpret_cast<u32x4_t*>(out + r[u] * out_stride + c[u] * 8) = v[u];
+  }
+}
+
+// fp8 rows: a workgroup gathers blocks of kGatherRows rows.  The row -> request -> page
+// chain is walked once per row (one thread each, the results shared through LDS with
+// the row's K scale); then every thread issues its share of the block's data loads
+// together, with no dependent load in front of them: 9 pieces of 16 codes per thread,
+// as two 8-byte loads each (fp8 rows are 584 bytes, so only 8-byte aligned), each
+// piece converted to 32 bytes of bf16.  Per-chunk lookup chains as in the bf16 kernel
+// above measured 34 us against 28 us for this on the 65,536-row workload; for bf16
+// rows, which need no conversion, the chains measured faster (28 vs 31 us).
+constexpr int kGatherRows = 64;
+constexpr int kGatherPieces = kRow / 16;                 // 36 pieces of 16 codes per row
+
+__global__ __launch_bounds__(256) void gather_fp8_kernel(
+    const char* __restrict__ pool, int64_t num_pages, const int32_t* __restrict__ block_table,
+    int64_t bt_sb, int32_t max_pages, const int32_t* __restrict__ cu_seq_lens,
+    const int32_t* __restrict__ seq_starts, const int32_t* __restrict__ token_to_seq, int32_t B,
+    int64_t total, uint16_t* __restrict__ out, int64_t out_stride) {
+  constexpr int kPieces = kGatherPieces;
+  constexpr int kRows = kGatherRows;
+  constexpr int kPerThread = kRows * kPieces / 256;
+  static_assert(kRows * kPieces % 256 == 0, "pieces per thread");
+  __shared__ int64_t slot_s[kRows];
+  __shared__ float scale_s[kRows];
+  const int tid = threadIdx.x;
+  const int64_t nblk = (total + kRows - 1) / kRows;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t r0 = blk * kRows;
+    if (tid < kRows) {
+      // request, logical token and physical slot of the row; anything out of range
+      // leaves the row zero (no access outside the caller's buffers)
+      const int64_t r = r0 + tid;
+      int64_t slot = -1;
+      float ks = 0.f;
+      if (r < total) {
+        const int b = token_to_seq[r];
+        if (b >= 0 && b < B) {
+          const int64_t j = (int64_t)(seq_starts ? seq_starts[b] : 0) + (r - cu_seq_lens[b]);
+          if (j >= 0 && j < (int64_t)max_pages * kPage) {
+            const int id = block_table[(int64_t)b * bt_sb + (j >> 6)];
+            if (id >= 0 && id < num_pages) slot = (int64_t)id * kPage + (j & (kPage - 1));
+          }
+        }
+      }
+      if (slot >= 0) ks = *reinterpret_cast<const float*>(pool + slot * kRowBytesFp8 + kRow);
+      slot_s[tid] = slot;
+      scale_s[tid] = ks;
+    }
+    __syncthreads();
+    {
+      u32x2_t lo[kPerThread], hi[kPerThread];
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const int q = tid + 256 * k, row = q / kPieces, c = q % kPieces;
+        const int64_t slot = slot_s[row];
+        if (slot >= 0) {
+          const char* src = pool + slot * kRowBytesFp8 + c * 16;
+          lo[k] = *reinterpret_cast<const u32x2_t*>(src);
+          hi[k] = *reinterpret_cast<const u32x2_t*>(src + 8);
+        } else {
+          lo[k] = u32x2_t{0u, 0u};
+          hi[k] = u32x2_t{0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const int q = tid + 256 * k, row = q / kPieces, c = q % kPieces;
+        if (r0 + row >= total) continue;
+        const float ks = scale_s[row];
+        const uint32_t codes[4] = {lo[k][0], lo[k][1], hi[k][0], hi[k][1]};
+        u32x4_t a, b;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          a[m] = bf16x2_of_products(codes[m >> 1] >> (16 * (m & 1)), ks);
+          b[m] = bf16x2_of_products(codes[2 + (m >> 1)] >> (16 * (m & 1)), ks);
+        }
+        uint16_t* dst = out + (r0 + row) * out_stride + c * 16;
+        *reinterpret_cast<u32x4_t*>(dst) = a;
+        *reinterpret_cast<u32x4_t*>(dst + 8) = b;
+      }
+    }
+    __syncthreads();                                   // the row table is reused by the next block
   }
 }
 
@@ -205,15 +278,18 @@ extern "C" mla_status_t mla_gather_cache(const void* kv_cache, int32_t kv_dtype,
   mla_status_t st = device_info(&di);
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const unsigned grid = stream_grid((total_rows * kGatherChunks + kGatherUnroll - 1) / kGatherUnroll, di);
-  if (kv_dtype == MLA_KV_BF16)
-    hipLaunchKernelGGL(gather_cache_kernel<false>, dim3(grid), dim3(256), 0, s, (const char*)kv_cache, num_pages,
+  if (kv_dtype == MLA_KV_BF16) {
+    const unsigned grid = stream_grid((total_rows * kGatherChunks + kGatherUnroll - 1) / kGatherUnroll, di);
+    hipLaunchKernelGGL(gather_bf16_kernel, dim3(grid), dim3(256), 0, s, (const char*)kv_cache, num_pages,
                        block_table, bt_stride_b, max_pages_per_seq, cu_seq_lens, seq_starts, token_to_seq, B,
                        total_rows, (uint16_t*)out, out_stride);
-  else
-    hipLaunchKernelGGL(gather_cache_kernel<true>, dim3(grid), dim3(256), 0, s, (const char*)kv_cache, num_pages,
+  } else {
+    const int64_t row_blocks = (total_rows + kGatherRows - 1) / kGatherRows;
+    const unsigned grid = (unsigned)(row_blocks < 1048576 ? row_blocks : 1048576);
+    hipLaunchKernelGGL(gather_fp8_kernel, dim3(grid), dim3(256), 0, s, (const char*)kv_cache, num_pages,
                        block_table, bt_stride_b, max_pages_per_seq, cu_seq_lens, seq_starts, token_to_seq, B,
                        total_rows, (uint16_t*)out, out_stride);
+  }
   return launch_status();
 }
 

@@ -84,22 +84,23 @@ def test_gather_cache_fp8_nan_codes_and_hand_values():
     assert np.array_equal(got[~nan_r], ref[~nan_r])
 
 
-def test_gather_cache_out_of_range_rows_are_zero():
+@pytest.mark.parametrize("kd", [MI.KV_BF16, MI.KV_FP8])
+def test_gather_cache_out_of_range_rows_are_zero(kd):
+    say(f"gather out-of-range rows kd={kd}")
     c = MI.make_context_chunk([100, 50], [0, 64], 10, seed=125)
-    w = _pool_workload(c.num_pages, MI.KV_BF16, 126)
-    pool = gpu_pool(w, MI.KV_BF16)
+    w = _pool_workload(c.num_pages, kd, 126)
+    pool = gpu_pool(w, kd)
     t2s = c.token_to_seq.copy()
     t2s[[3, 120]] = [-1, 7]                               # no such request
     bt = c.block_table.copy()
     bt[1, 1] = 10**6                                      # page id outside the pool
-    out = M.gather_cache(pool, MI.KV_BF16, torch.from_numpy(bt).cuda(), torch.from_numpy(c.cu_seq_lens).cuda(),
+    out = M.gather_cache(pool, kd, torch.from_numpy(bt).cuda(), torch.from_numpy(c.cu_seq_lens).cuda(),
                          torch.from_numpy(t2s).cuda(), torch.from_numpy(c.seq_starts).cuda())
     got = host_bits(out)
     assert np.all(got[3] == 0) and np.all(got[120] == 0)
     # request 1 starts at its token 64 = page 1: its first 50 rows come from that page
     assert np.all(got[100:150] == 0)
-    ref = O.gather_cache(oracle_pool(w, MI.KV_BF16), MI.KV_BF16, c.block_table, c.cu_seq_lens,
-                         c.token_to_seq, c.seq_starts)
+    ref = O.gather_cache(oracle_pool(w, kd), kd, c.block_table, c.cu_seq_lens, c.token_to_seq, c.seq_starts)
     keep = np.ones(150, bool)
     keep[[3, 120]] = False
     keep[100:150] = False
