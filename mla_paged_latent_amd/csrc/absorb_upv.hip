@@ -546,178 +546,16 @@ __global__ __launch_bounds__(256) void up_v_fp8_g128_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Head GEMM for many tokens (mla_up_v, mla_up_v_fp8 with groups of 128, mla_kv_b_proj
-// at T >= kBigGemmMinT): C[t, h, n0 : n0+128] = A[t, h, 0:512] . W[h][0:512][n0 : n0+128].
-// One workgroup computes a 128-token x 128-column tile over the full K = 512 in 8
-// chunks of 64 k; grid = (token tiles, heads, NN / 128).  Four waves split the tile
-// 2 x 2 (64 tokens x 64 columns each, four 32x32x16 MFMA accumulators).  A chunk's
-// activations ([128 t][64 k], rows padded to 144 B: the 16-byte fragment reads of a
-// column are conflict-free) and weights ([64 k][128 n], rows padded to 288 B for the
-// transpose reads) go through registers into one of two LDS buffers: the loads of chunk
-// c + 1 are in flight while chunk c is multiplied, one barrier per chunk.  About 72 KB
-// of LDS, so two workgroups share a CU.  The product is formed transposed as in
-// head_gemm_kernel (weights as the A operand, activation rows as the B operand), so a
-// lane's accumulator holds 4 consecutive columns of one token; the finished tile is
-// staged in LDS and leaves as whole row segments (bf16), or is quantized per token
-// (fp8 codes in groups of the 128 columns, one float32 scale).
-// ---------------------------------------------------------------------------
-constexpr int64_t kBigGemmMinT = 512;
-
-template <bool FP8OUT>
-__global__ __launch_bounds__(256, 2) void head_gemm_big_kernel(
-    const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // [T, N or shared, 512]
-    const uint16_t* __restrict__ W, int nn,                           // [N, 512, nn]
-    uint16_t* __restrict__ C, int64_t c_st, int64_t c_sh,            // bf16 [T, N, nn]
-    uint8_t* __restrict__ Q, int64_t q_st,                            // fp8 codes [T, N * 128]
-    float* __restrict__ S, int64_t s_st,                              // scales [T, N]
-    int64_t T) {
-  constexpr int KK = 512, TM = 128, TN = 128, KC = 64, NCH = KK / KC;
-  constexpr int kAPitch = KC * 2 + 16;                  // 144
-  constexpr int kWPitch = TN * 2 + 32;                  // 288
-  constexpr int kABytes = TM * kAPitch;                 // 18432
-  constexpr int kWBytes = KC * kWPitch;                 // 18432
-  constexpr int kStage = kABytes + kWBytes;
-  constexpr int kOutPitch = TN * 2 + 16;                // 272
-  static_assert(TM * kOutPitch <= 2 * kStage, "output staging fits the buffers");
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
-  MLA_LDS char* lds = (MLA_LDS char*)(smem);
-
-  const int64_t t0 = (int64_t)blockIdx.x * TM;
-  const int h = blockIdx.y;
-  const int n0 = blockIdx.z * TN;
-  const int tid = threadIdx.x;
-  const int w = wave_id();
-  const int l = lane_id();
-  const int wt = w & 1, wn = w >> 1;                   // this wave's 64 tokens, 64 columns
-  const int g = l >> 4, lg = l & 15;
-
-  const uint16_t* ah = A + (int64_t)h * a_sh;
-  const uint16_t* wh = W + (int64_t)h * KK * nn + n0;
-  // per thread and chunk: 4 activation chunks of 16 B (row i / 8, piece i % 8) and 4
-  // weight chunks (row i / 16, piece i % 16), i = tid + 256 j
-  u32x4_t av[4], wv[4];
-  auto load = [&](int kc) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;
-      const int64_t t = t0 + i / 8;
-      av[j] = t < T ? *reinterpret_cast<const u32x4_t*>(ah + t * a_st + kc * KC + (i % 8) * 8) : u32x4_t{0u, 0u, 0u, 0u};
-      wv[j] = *reinterpret_cast<const u32x4_t*>(wh + (int64_t)(kc * KC + i / 16) * nn + (i % 16) * 8);
-    }
-  };
-  auto store = [&](int buf) {
-    MLA_LDS char* b = lds + buf * kStage;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;
-      *reinterpret_cast<MLA_LDS u32x4_t*>(b + (i / 8) * kAPitch + (i % 8) * 16) = av[j];
-      *reinterpret_cast<MLA_LDS u32x4_t*>(b + kABytes + (i / 16) * kWPitch + (i % 16) * 16) = wv[j];
-    }
-  };
-
-  // weight transpose reads (A operand, rows n): 16-lane group g covers n = 16(g & 1) +
-  // [0, 16) of a 32-column block and k rows 8(g >> 1) + 4r + (lg >> 2); the lane supplies
-  // column 4(lg & 3).  Activation fragments (B operand): token 32 ti + (l & 31), k 8(l >> 5).
-  uint32_t wrd[2], ard[2];
-#pragma unroll
-  for (int nj = 0; nj < 2; ++nj)
-    wrd[nj] = (uint32_t)(kABytes + (8 * (g >> 1) + (lg >> 2)) * kWPitch +
-                         (64 * wn + 32 * nj + 16 * (g & 1) + 4 * (lg & 3)) * 2);
-#pragma unroll
-  for (int ti = 0; ti < 2; ++ti) ard[ti] = (uint32_t)((64 * wt + 32 * ti + (l & 31)) * kAPitch + 16 * (l >> 5));
-
-  f32x16_t acc[2][2] = {};                             // [column block nj][token block ti]
-  load(0);
-  store(0);
-  lds_barrier();
-#pragma unroll 1
-  for (int kc = 0; kc < NCH; ++kc) {
-    if (kc + 1 < NCH) load(kc + 1);
-    const uint32_t base = lds_addr(lds) + (uint32_t)((kc & 1) * kStage);
-#pragma unroll
-    for (int ks = 0; ks < KC / 16; ++ks) {
-      bf16x8_t wf[2], af[2];
-#pragma unroll
-      for (int nj = 0; nj < 2; ++nj) {
-        const uint32_t r0 = base + wrd[nj] + (uint32_t)(16 * ks * kWPitch);
-        const bf16x4_t lo = lds_read_tr16_at(r0);
-        const bf16x4_t hi = lds_read_tr16_at(r0 + 4 * kWPitch);
-        wf[nj] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) af[ti] = lds_read_b128_at(base + ard[ti] + (uint32_t)(32 * ks));
-#pragma unroll
-      for (int nj = 0; nj < 2; ++nj)
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-          acc[nj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nj], af[ti], acc[nj][ti], 0, 0, 0);
-    }
-    if (kc + 1 < NCH) store((kc + 1) & 1);              // that buffer's last readers were chunk kc - 1
-    lds_barrier();
-  }
-
-  // the tile, rounded to bf16, staged as [128 tokens][128 columns]: lane (l & 31) is token
-  // 64 wt + 32 ti + (l & 31), columns 64 wn + 32 nj + 8 i + 4 (l >> 5) + 0..3
-  MLA_LDS char* ostage = lds;
-#pragma unroll
-  for (int nj = 0; nj < 2; ++nj)
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x4_t v = {(__bf16)acc[nj][ti][4 * i], (__bf16)acc[nj][ti][4 * i + 1], (__bf16)acc[nj][ti][4 * i + 2],
-                            (__bf16)acc[nj][ti][4 * i + 3]};
-        *reinterpret_cast<MLA_LDS bf16x4_t*>(ostage + (64 * wt + 32 * ti + (l & 31)) * kOutPitch +
-                                             (64 * wn + 32 * nj + 8 * i + 4 * (l >> 5)) * 2) = v;
-      }
-  lds_barrier();
-  if constexpr (!FP8OUT) {
-#pragma unroll
-    for (int j = 0; j < TM * TN / 8 / 256; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / 16, cc = i % 16;
-      if (t0 + r < T) {
-        const u32x4_t v = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * kOutPitch + cc * 16);
-        *reinterpret_cast<u32x4_t*>(C + (t0 + r) * c_st + (int64_t)h * c_sh + n0 + cc * 8) = v;
-      }
-    }
-  } else {
-    // a token's group of 128 values is 16 consecutive lanes of 8 values
-#pragma unroll
-    for (int j = 0; j < TM * TN / 8 / 256; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / 16, cc = i % 16;
-      const u32x4_t raw = *reinterpret_cast<const MLA_LDS u32x4_t*>(ostage + r * kOutPitch + cc * 16);
-      float x[8];
-      float amax = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = bf16_bits_to_f32(raw[k] & 0xFFFFu);
-        x[2 * k + 1] = bf16_bits_to_f32(raw[k] >> 16);
-        amax = fmaxf(amax, fmaxf(fabsf(x[2 * k]), fabsf(x[2 * k + 1])));
-      }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-      float sc = __fdiv_rn(amax, 448.0f);
-      if (sc == 0.f) sc = 1.0f;
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lo |= e4m3_encode(__fdiv_rn(x[k], sc)) << (8 * k);
-        hi |= e4m3_encode(__fdiv_rn(x[4 + k], sc)) << (8 * k);
-      }
-      if (t0 + r < T) {
-        *reinterpret_cast<u32x2_t*>(Q + (t0 + r) * q_st + (int64_t)h * TN + cc * 8) = u32x2_t{lo, hi};
-        if (cc == 0) S[(t0 + r) * s_st + h] = sc;
-      }
-    }
-  }
-}
+// Token counts from which the up-projections take head_gemm_stream_kernel (measured
+// crossovers with 128 heads and cold weights: up_v 19.6 vs 19.2 us at T = 256, 26.3 vs
+// 22.9 at 384; kv_b_proj 22.3 vs 16.9 us at S = 128, 50.0 vs 24.3 at 384, the shared
+// latent rows making each token tile's weight re-read costlier there).
+constexpr int64_t kBigGemmMinT = 256;
+constexpr int64_t kKvbStreamMinS = 128;
 
 // ---------------------------------------------------------------------------
-// Head GEMM for many tokens, weight-stationary form (the same products as
-// head_gemm_big_kernel): C[t, h, n0 : n0+128] = A[t, h, 0:512] . W[h][0:512][n0 : n0+128].
+// Head GEMM for many tokens, weight-stationary form (mla_up_v, mla_up_v_fp8 with groups of
+// 128, mla_kv_b_proj): C[t, h, n0 : n0+128] = A[t, h, 0:512] . W[h][0:512][n0 : n0+128].
 // A workgroup of four waves owns one head, one 128-column half and a contiguous range of
 // 16-token stages; grid = (parts, heads, NN / 128), about two workgroups per CU.  Each
 // wave keeps the weights of its 32 columns over all of K = 512 in registers (the MFMA
@@ -1085,7 +923,7 @@ extern "C" mla_status_t mla_kv_b_proj(const void* kv_c, int64_t kc_stride_t, con
   mla_status_t st = device_info(&di);
   if (st != MLA_OK) return st;
   // the latent has no head dimension: every head's workgroups read the same rows
-  if (S >= kBigGemmMinT) {
+  if (S >= kKvbStreamMinS) {
     const int parts = stream_parts(S, 2 * N, di.cu_count);
     hipLaunchKernelGGL((head_gemm_stream_kernel<false, false>), dim3((unsigned)parts, N, 2), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), (const uint16_t*)kv_c, kc_stride_t, (int64_t)0,
