@@ -548,18 +548,30 @@ __global__ __launch_bounds__(256) void up_v_fp8_g128_kernel(
   }
 }
 
-// Token counts from which the up-projections take head_gemm_stream_kernel (measured
-// crossovers with 128 heads and cold weights: up_v 19.6 vs 19.2 us at T = 256, 26.3 vs
-// 22.9 at 384; kv_b_proj 22.3 vs 16.9 us at S = 128, 50.0 vs 24.3 at 384, the shared
-// latent rows making each token tile's weight re-read costlier there).
-constexpr int64_t kBigGemmMinT = 256;
+// When the up-projections take head_gemm_stream_kernel and with how many workgroups per
+// CU, from sweeps of T with 128 heads and cold weights (8 rotating copies):
+//  * up_v from T = 128 (T = 64: 9.0 us for the tile kernel against 10.6), one workgroup
+//    per CU at every size measured (each workgroup loads its head's weights once, so
+//    fewer workgroups load them fewer times: T = 4096 118.9 against 132.1 us with two,
+//    T = 8192 227 against 251);
+//  * up_v_fp8 with groups of 128 from T = 192 (the tile kernel 12.3 against 14.0 us at
+//    128), one workgroup per CU below T = 1024 (T = 512: 26.8 against 29.3 us) and two
+//    from 1024, where the second workgroup's waves hide the quantizing epilogue (T = 4096:
+//    133.9 against 149.0 us);
+//  * kv_b_proj from S = 128 (22.3 us for the tile kernel against 14.2), one workgroup per
+//    CU below S = 512 and two from 512, where the MFMA work needs the second workgroup's
+//    waves (S = 4096: 144.9 against 169.4 us).
+constexpr int64_t kUpvStreamMinT = 128;
+constexpr int64_t kUpvFp8StreamMinT = 192;
+constexpr int64_t kUpvFp8TwoPerCuMinT = 1024;
 constexpr int64_t kKvbStreamMinS = 128;
+constexpr int64_t kKvbTwoPerCuMinS = 512;
 
 // ---------------------------------------------------------------------------
 // Head GEMM for many tokens, weight-stationary form (mla_up_v, mla_up_v_fp8 with groups of
 // 128, mla_kv_b_proj): C[t, h, n0 : n0+128] = A[t, h, 0:512] . W[h][0:512][n0 : n0+128].
 // A workgroup of four waves owns one head, one 128-column half and a contiguous range of
-// 16-token stages; grid = (parts, heads, NN / 128), about two workgroups per CU.  Each
+// 16-token stages; grid = (parts, heads, NN / 128), one or two workgroups per CU.  Each
 // wave keeps the weights of its 32 columns over all of K = 512 in registers (the MFMA
 // A operand of two 16x16x32 products per 32 k, 128 VGPRs), loaded once through LDS in
 // two halves with transpose reads, so the weights leave HBM once per workgroup instead
@@ -771,11 +783,11 @@ __global__ __launch_bounds__(256, 2) void head_gemm_stream_kernel(
   }
 }
 
-// workgroups per (head, column half) of head_gemm_stream_kernel: about two per CU over
-// the grid, never more than the 32-token stages
-static int stream_parts(int64_t T, int units, int cu_count) {
+// workgroups per (head, column half) of head_gemm_stream_kernel: about per_cu of them per
+// CU over the grid, never more than the 16-token stages
+static int stream_parts(int64_t T, int units, int cu_count, int per_cu) {
   const int64_t stages = (T + kHsTok - 1) / kHsTok;
-  int64_t p = (2 * (int64_t)(cu_count > 0 ? cu_count : 256) + units - 1) / units;
+  int64_t p = ((int64_t)per_cu * (cu_count > 0 ? cu_count : 256) + units - 1) / units;
   if (p > stages) p = stages;
   return (int)(p < 1 ? 1 : p);
 }
@@ -856,8 +868,8 @@ extern "C" mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t
   mla_status_t st = device_info(&di);
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (T >= kBigGemmMinT) {
-    const int parts = stream_parts(T, N, di.cu_count);
+  if (T >= kUpvStreamMinT) {
+    const int parts = stream_parts(T, N, di.cu_count, 1);
     hipLaunchKernelGGL((head_gemm_stream_kernel<false, true>), dim3((unsigned)parts, N, 1), dim3(256), 0, s,
                        (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv, MLA_V_HEAD_DIM,
                        (uint16_t*)out, out_stride_t, (int64_t)MLA_V_HEAD_DIM, (uint8_t*)nullptr, (int64_t)0,
@@ -893,8 +905,8 @@ extern "C" mla_status_t mla_up_v_fp8(const void* o_lat, int64_t ol_stride_t, int
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(MLA_V_HEAD_DIM / group), (unsigned)N, (unsigned)((T + 31) / 32));
-  if (group == 128 && T >= kBigGemmMinT) {
-    const int parts = stream_parts(T, N, di.cu_count);
+  if (group == 128 && T >= kUpvFp8StreamMinT) {
+    const int parts = stream_parts(T, N, di.cu_count, T >= kUpvFp8TwoPerCuMinT ? 2 : 1);
     hipLaunchKernelGGL((head_gemm_stream_kernel<true, true>), dim3((unsigned)parts, N, 1), dim3(256), 0, s,
                        (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv, MLA_V_HEAD_DIM,
                        (uint16_t*)nullptr, (int64_t)0, (int64_t)0, (uint8_t*)out_codes, codes_stride_t, out_scales,
@@ -926,7 +938,7 @@ extern "C" mla_status_t mla_kv_b_proj(const void* kv_c, int64_t kc_stride_t, con
   if (st != MLA_OK) return st;
   // the latent has no head dimension: every head's workgroups read the same rows
   if (S >= kKvbStreamMinS) {
-    const int parts = stream_parts(S, 2 * N, di.cu_count);
+    const int parts = stream_parts(S, 2 * N, di.cu_count, S >= kKvbTwoPerCuMinS ? 2 : 1);
     hipLaunchKernelGGL((head_gemm_stream_kernel<false, false>), dim3((unsigned)parts, N, 2), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), (const uint16_t*)kv_c, kc_stride_t, (int64_t)0,
                        (const uint16_t*)w_kvb, 256, (uint16_t*)out, out_stride_t, out_stride_h, (uint8_t*)nullptr,

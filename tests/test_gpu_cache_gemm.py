@@ -113,7 +113,7 @@ def test_absorb_q_strided_views_without_pe():
     assert np.all(np.isnan(g[..., 512:]))                     # untouched padding
 
 
-@pytest.mark.parametrize("T,N", [(2, 16), (32, 128), (1, 5), (77, 128), (255, 16), (256, 16), (300, 24), (700, 16), (513, 40)])
+@pytest.mark.parametrize("T,N", [(2, 16), (32, 128), (1, 5), (77, 128), (127, 16), (128, 16), (256, 16), (300, 24), (700, 16), (513, 40)])
 def test_up_v(T, N):
     say(f"up_v T={T} N={N}")
     rng = np.random.default_rng(50 + T + N)

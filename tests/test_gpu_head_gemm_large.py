@@ -1,7 +1,7 @@
-"""GPU parity of the large-token path of the per-head up-projections: mla_up_v and
-mla_up_v_fp8 with groups of 128 from 256 tokens, mla_kv_b_proj from 128 rows, where a
+"""GPU parity of the large-token path of the per-head up-projections (mla_up_v from 128
+tokens, mla_up_v_fp8 with groups of 128 from 192, mla_kv_b_proj from 128 rows), where a
 workgroup keeps one head's weights for 128 output columns in registers and streams the
-token rows.
+token rows; one or two such workgroups per CU depending on the call and its size.
 
 Ragged and strided cases are checked in full against the oracle; the prefill sizes
 (8192 rows, 128 heads, as bench.py times them) on sampled rows, the oracle computing
@@ -70,7 +70,7 @@ def test_up_v_large_t_strided_views():
     assert np.all(np.isnan(g[:, N * 128:]))
 
 
-@pytest.mark.parametrize("S,N", [(600, 16), (513, 5), (512, 1), (130, 8), (128, 3)])
+@pytest.mark.parametrize("S,N", [(600, 16), (513, 5), (512, 1), (511, 8), (130, 8), (128, 3), (127, 4)])
 def test_kv_b_proj_large_s(S, N):
     """Latent rows taken from [S, 576] cache rows, output with a padded head stride."""
     say(f"kv_b_proj large S={S} N={N}")

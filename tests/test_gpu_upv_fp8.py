@@ -67,7 +67,8 @@ def _selection_case(rng, T, N, group):
 
 @pytest.mark.parametrize("T,N,group", [(1, 16, 128), (33, 16, 64), (64, 128, 128), (77, 5, 64),
                                        (100, 128, 64), (3, 40, 128), (600, 16, 128), (517, 7, 128),
-                                       (600, 16, 64), (256, 16, 128), (301, 9, 128)])
+                                       (600, 16, 64), (191, 8, 128), (192, 8, 128), (301, 9, 128),
+                                       (1030, 8, 128)])
 def test_up_v_fp8_bit_exact_on_exact_products(T, N, group):
     say(f"up_v_fp8 selection T={T} N={N} group={group}")
     rng = np.random.default_rng(900 + T * 7 + N + group)
@@ -101,7 +102,8 @@ def _deq(codes, scales, group):
     return (v * scales.astype(np.float64)[:, :, None]).reshape(T, C)
 
 
-@pytest.mark.parametrize("T,N,group", [(2, 16, 128), (32, 128, 64), (45, 128, 128), (7, 3, 64), (700, 16, 128), (270, 16, 128)])
+@pytest.mark.parametrize("T,N,group", [(2, 16, 128), (32, 128, 64), (45, 128, 128), (7, 3, 64), (700, 16, 128), (270, 16, 128),
+                                       (1100, 8, 128)])
 def test_up_v_fp8_random_weights_within_bound(T, N, group):
     say(f"up_v_fp8 random T={T} N={N} group={group}")
     rng = np.random.default_rng(950 + T + N + group)
