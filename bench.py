@@ -456,9 +456,11 @@ def run(args) -> dict:
     if s.with_w:
         kern["mla_absorb_q"] = time_back_to_back(lambda i: L.mla_absorb_q(*s.ab_args), args.steps)
         kern["mla_up_v"] = time_back_to_back(lambda i: L.mla_up_v(*s.uv_args), args.steps)
-    dec_mean = kern["mla_decode"]
-    # timed region 3: the decode launch distribution (median / p10 / p90 over >= 50 rounds)
+    # timed region 3: the decode launch distribution (median / p10 / p90 over >= 50 rounds
+    # of R back-to-back calls); its mean is the average launch duration the roofline uses
+    # (150+ calls: region 2's K calls alone leave the mean to a few slow ones)
     dist = decode_distribution(s, max(50, args.steps))
+    dec_mean = sum(dist) / len(dist) * 1e-3
     log(f"[bench] step {ms_step * 1e3:.1f} us; back to back per call: " +
         ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in kern.items()) +
         f" (sum {sum(kern.values()) * 1e3:.1f} us); mla_decode median {pct(dist, 0.5):.1f} us")
