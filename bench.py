@@ -334,9 +334,13 @@ def decode_distribution(s: DecodeSetup, rounds: int) -> list[float]:
     between two calls."""
     import torch
     f = s.L.mla_decode
-    for i in range(2 * s.R):
-        f(*s.dec_args[i % s.R])
-    torch.cuda.synchronize()
+    # settle first: back-to-back calls for 0.2 s (the same steady state the step loop
+    # is timed in; right after a setup the first ~100 calls run ~10 % slower)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        for i in range(20 * s.R):
+            f(*s.dec_args[i % s.R])
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
     for r in range(rounds):
         ev[r][0].record()
@@ -436,6 +440,17 @@ def run(args) -> dict:
     for a, b in zip(ref, s.outputs()):
         assert torch.equal(a, b), "marshalled step differs from the API step"
 
+    # Untimed settling before the W warmup steps: right after the setup (host-side input
+    # generation leaves the GPU idle for seconds) the step runs ~10 % slower for its
+    # first ~100 repetitions; serving runs it back to back, so the timed steps start
+    # from that steady state.  Steps are repeated until 0.2 s of them have run.
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.2:
+        for i in range(50):
+            s.step(settle + i)
+        settle += 50
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         s.step(i)
     torch.cuda.synchronize()
@@ -497,6 +512,7 @@ def run(args) -> dict:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "settle_steps": settle,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
