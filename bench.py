@@ -803,6 +803,14 @@ def run_context_op(args) -> dict:
         if f(*calls[i % len(calls)]) != 0:
             raise RuntimeError(f"{args.op} failed")
     torch.cuda.synchronize()
+    # settle as the decode step does: 0.2 s of back-to-back calls before the timed ones
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < 0.2:
+        for _ in range(10):
+            f(*calls[i % len(calls)])
+            i += 1
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
