@@ -282,6 +282,8 @@ class DecodeSetup:
                             T, w.N, self.qf.data_ptr(), self.qf.stride(0), self.qf.stride(1), st)
             self.uv_args = (ol.data_ptr(), ol.stride(0), ol.stride(1), self.w_uv.data_ptr(), T, w.N,
                             self.y.data_ptr(), self.y.stride(0), st)
+            # the step's absorption and cache write as one launch (mla_absorb_q_cache_write)
+            self.abcw_args = [self.ab_args[:-1] + a[:-1] + (st,) for a in self.cw_args]
 
     def step_api(self, i: int):
         """The step through the checked Python wrappers (used once, to check the fast path)."""
@@ -300,9 +302,10 @@ class DecodeSetup:
     def step(self, i: int):
         j = i % self.R
         L = self.L
-        rc = L.mla_cache_write(*self.cw_args[j])
         if self.with_w:
-            rc |= L.mla_absorb_q(*self.ab_args)
+            rc = L.mla_absorb_q_cache_write(*self.abcw_args[j])
+        else:
+            rc = L.mla_cache_write(*self.cw_args[j])
         rc |= L.mla_decode(*self.dec_args[j])
         if self.with_w:
             rc |= L.mla_up_v(*self.uv_args)
@@ -471,14 +474,21 @@ def run(args) -> dict:
     if s.with_w:
         kern["mla_absorb_q"] = time_back_to_back(lambda i: L.mla_absorb_q(*s.ab_args), args.steps)
         kern["mla_up_v"] = time_back_to_back(lambda i: L.mla_up_v(*s.uv_args), args.steps)
+        kern["mla_absorb_q_cache_write"] = time_back_to_back(
+            lambda i: L.mla_absorb_q_cache_write(*s.abcw_args[i % s.R]), args.steps)
     # timed region 3: the decode launch distribution (median / p10 / p90 over >= 50 rounds
     # of R back-to-back calls); its mean is the average launch duration the roofline uses
     # (150+ calls: region 2's K calls alone leave the mean to a few slow ones)
     dist = decode_distribution(s, max(50, args.steps))
     dec_mean = sum(dist) / len(dist) * 1e-3
+    # the launches the step makes (the separate cache write and absorption are reported
+    # beside them for reference)
+    step_launches = (["mla_absorb_q_cache_write", "mla_decode", "mla_up_v"] if s.with_w
+                     else ["mla_cache_write", "mla_decode"])
+    step_sum = sum(kern[k] for k in step_launches)
     log(f"[bench] step {ms_step * 1e3:.1f} us; back to back per call: " +
         ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in kern.items()) +
-        f" (sum {sum(kern.values()) * 1e3:.1f} us); mla_decode median {pct(dist, 0.5):.1f} us")
+        f" (step's launches: sum {step_sum * 1e3:.1f} us); mla_decode median {pct(dist, 0.5):.1f} us")
 
     achieved = s.bytes_alg / (dec_mean * 1e-3) / 1e9
     tflops = s.flops_alg / (dec_mean * 1e-3) / 1e12
@@ -527,7 +537,8 @@ def run(args) -> dict:
         "decode_latent_kv_tbs": round(s.kv_bytes / (dec_mean * 1e-3) / 1e12, 3),
         "roofline": roof,
         "step_kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
-        "step_kernels_sum_us": round(sum(kern.values()) * 1e3, 2),
+        "step_launches": step_launches,
+        "step_kernels_sum_us": round(step_sum * 1e3, 2),
     }
     if peaks:
         res["measured_peaks"] = peaks

@@ -122,6 +122,30 @@ mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, int64_t qn_st
                           void* stream);
 
 /*
+ * mla_absorb_q_cache_write -- mla_absorb_q and mla_cache_write in one launch (the
+ * two steps the pages place before attention in a decode step, [vLLM-MLA] §写缓存
+ * and §两套算法): the cache rows of the step's T_new new tokens are written by
+ * workgroups launched beside the absorption's, so the step pays one launch for
+ * both.  The two operations are independent (the absorption reads no cache row).
+ *
+ *   q_nope .. qf_stride_h     as mla_absorb_q (T query rows, N heads)
+ *   kv_c .. num_pages         as mla_cache_write (T_new rows into kv_cache)
+ *
+ * Results are bit for bit those of the two calls; statuses are theirs (checked
+ * before anything is enqueued); additionally MLA_ERR_SHAPE when N plus
+ * ceil(T_new / 16) exceeds 65535 grid rows.  T == 0 runs the cache write alone.
+ */
+mla_status_t mla_absorb_q_cache_write(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+                                      const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+                                      const void* w_uk_t, int64_t T, int32_t N,
+                                      void* q_fused, int64_t qf_stride_t, int64_t qf_stride_h,
+                                      const void* kv_c, int64_t kv_c_stride_t,
+                                      const void* k_pe, int64_t k_pe_stride_t,
+                                      const int64_t* slot_mapping, int64_t T_new,
+                                      void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                                      void* stream);
+
+/*
  * mla_absorb_q_rope -- mla_absorb_q with the rotary position embedding of q_pe
  * applied on the way into the tail ([vLLM-MLA] §从模型层看: the model layer
  * rotates the last 64 query values by rotary_emb(positions, ...) before MLA;

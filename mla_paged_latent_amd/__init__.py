@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
     L.mla_cache_write.restype = i32
     L.mla_absorb_q.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i32, vp, i64, i64, vp]
     L.mla_absorb_q.restype = i32
+    L.mla_absorb_q_cache_write.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i32, vp, i64, i64,
+                                           vp, i64, vp, i64, vp, i64, vp, i32, i64, vp]
+    L.mla_absorb_q_cache_write.restype = i32
     L.mla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     L.mla_decode_workspace_size.restype = ctypes.c_size_t
     L.mla_decode.argtypes = [vp, i64, i64, i64, vp, i32, i64, vp, i64, i32, vp, i32, i32, i32,
@@ -159,6 +162,32 @@ def absorb_q(q_nope: torch.Tensor, q_pe: torch.Tensor | None, w_uk_t: torch.Tens
     _check("mla_absorb_q", lib().mla_absorb_q(
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), qp_st, qp_sh,
         _ptr(w_uk_t), T, N, _ptr(q_fused), q_fused.stride(0), q_fused.stride(1), _stream(stream)))
+    return q_fused
+
+
+def absorb_q_cache_write(q_nope: torch.Tensor, q_pe: torch.Tensor | None, w_uk_t: torch.Tensor,
+                         kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
+                         kv_cache: torch.Tensor, kv_dtype: int, q_fused: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """:func:`absorb_q` and :func:`cache_write` in one launch (same arguments, same
+    results); returns ``q_fused``."""
+    T, N, P = q_nope.shape
+    assert P == 128 and q_nope.dtype == torch.bfloat16 and w_uk_t.is_contiguous()
+    assert w_uk_t.shape == (N, 128, KV_LORA_RANK) and w_uk_t.dtype == torch.bfloat16
+    k_pe = k_pe.reshape(k_pe.shape[0], -1)
+    assert kv_c.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16
+    assert slot_mapping.dtype == torch.int64 and kv_c.stride(-1) == 1 and k_pe.stride(-1) == 1
+    width = ROW_ELEMS if q_pe is not None else KV_LORA_RANK
+    if q_fused is None:
+        q_fused = torch.empty((T, N, width), dtype=torch.bfloat16, device=q_nope.device)
+    qp_st = q_pe.stride(0) if q_pe is not None else 0
+    qp_sh = q_pe.stride(1) if q_pe is not None else 0
+    num_pages = kv_cache.numel() * kv_cache.element_size() // (PAGE_TOKENS * ROW_BYTES[kv_dtype])
+    _check("mla_absorb_q_cache_write", lib().mla_absorb_q_cache_write(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), qp_st, qp_sh,
+        _ptr(w_uk_t), T, N, _ptr(q_fused), q_fused.stride(0), q_fused.stride(1),
+        _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(slot_mapping), kv_c.shape[0],
+        _ptr(kv_cache), kv_dtype, num_pages, _stream(stream)))
     return q_fused
 
 

@@ -16,6 +16,7 @@
 // operand (16 contiguous bytes of one token row per lane), and each lane of the
 // accumulator holds 4 consecutive n of one token; the 32-token tile is staged in LDS
 // and leaves as contiguous row segments.
+#include "cache_rows.h"
 #include "mla_common.h"
 #include "mla_host.h"
 
@@ -74,8 +75,23 @@ __device__ __forceinline__ void rope_chunks(const uint4& xa, const uint4& xb, co
   yb = uint4{out[4], out[5], out[6], out[7]};
 }
 
-// grid = (NN / NT, N heads); block = 256 threads.
-template <int KK, int NN, int NT, int KSPLIT, int PE>
+// Cache rows written beside the absorption in the same launch (mla_absorb_q_cache_write):
+// the workgroups past the heads' rows of the grid write four tokens each.
+struct CacheRowsArgs {
+  const uint16_t* kv_c;
+  int64_t kv_stride;
+  const uint16_t* k_pe;
+  int64_t pe_stride;
+  const int64_t* slots;
+  int64_t T;
+  char* pool;
+  int64_t num_pages;
+  int32_t n_heads;     // grid rows below this one are heads
+};
+constexpr int kNoRows = 0, kRowsBf16 = 1, kRowsFp8 = 2;
+
+// grid = (NN / NT, N heads [+ cache-row workgroups, CW]); block = 256 threads.
+template <int KK, int NN, int NT, int KSPLIT, int PE, int CW = kNoRows>
 __global__ __launch_bounds__(256) void head_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t a_st, int64_t a_sh,      // [T, N, KK]
     const uint16_t* __restrict__ W,                                   // [N, KK, NN]
@@ -83,10 +99,19 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
     const uint16_t* __restrict__ pe, int64_t pe_st, int64_t pe_sh,   // [T, N, 64] (PE != 0)
     const int64_t* __restrict__ positions,                            // [T] (kRopeTail)
     const float* __restrict__ cos_sin, int64_t max_pos, int neox,     // [max_pos, 64] (kRopeTail)
-    int64_t T) {
+    int64_t T, CacheRowsArgs cw) {
   using Cfg = GemmCfg<KK, NN, NT, KSPLIT>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
+  if constexpr (CW != kNoRows) {
+    if ((int)blockIdx.y >= cw.n_heads) {
+      const int64_t t = ((int64_t)(blockIdx.y - cw.n_heads) * gridDim.x + blockIdx.x) * 4 + (threadIdx.x >> 6);
+      if (t < cw.T)
+        cache_write_row<CW == kRowsFp8>(cw.kv_c, cw.kv_stride, cw.k_pe, cw.pe_stride, cw.slots, cw.pool,
+                                        cw.num_pages, t, lane_id());
+      return;
+    }
+  }
 
   const int h = blockIdx.y;
   const int n0 = blockIdx.x * NT;
@@ -816,13 +841,63 @@ extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, in
                        (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
                        (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)q_pe,
                        qp_stride_t, qp_stride_h, (const int64_t*)nullptr, (const float*)nullptr,
-                       (int64_t)0, 0, T);
+                       (int64_t)0, 0, T, CacheRowsArgs{});
   else
     hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, kNoTail>), grid, dim3(256), 0, s,
                        (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
                        (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)nullptr,
                        (int64_t)0, (int64_t)0, (const int64_t*)nullptr, (const float*)nullptr,
-                       (int64_t)0, 0, T);
+                       (int64_t)0, 0, T, CacheRowsArgs{});
+  return launch_status();
+}
+
+// mla_absorb_q and mla_cache_write in one launch: the cache-row workgroups follow the
+// heads' rows of the absorption grid (four tokens each), so the step's two smallest
+// kernels cost one launch.  The arguments and checks are those of the two calls.
+extern "C" mla_status_t mla_absorb_q_cache_write(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+                                                 const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+                                                 const void* w_uk_t, int64_t T, int32_t N, void* q_fused,
+                                                 int64_t qf_stride_t, int64_t qf_stride_h, const void* kv_c,
+                                                 int64_t kv_c_stride_t, const void* k_pe, int64_t k_pe_stride_t,
+                                                 const int64_t* slot_mapping, int64_t T_new, void* kv_cache,
+                                                 int32_t kv_dtype, int64_t num_pages, void* stream) {
+  using namespace mla;
+  if (T < 0 || N < 1 || N > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  if (T == 0) return mla_cache_write(kv_c, kv_c_stride_t, k_pe, k_pe_stride_t, slot_mapping, T_new, kv_cache,
+                                     kv_dtype, num_pages, stream);
+  if (!q_nope || !w_uk_t || !q_fused) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk_t) || !aligned16(q_fused) || !mult8(qn_stride_t) ||
+      !mult8(qn_stride_h) || !mult8(qf_stride_t) || !mult8(qf_stride_h))
+    return MLA_ERR_ALIGN;
+  if (q_pe && (!aligned16(q_pe) || !mult8(qp_stride_t) || !mult8(qp_stride_h))) return MLA_ERR_ALIGN;
+  const mla_status_t cst = cache_write_check(kv_c, kv_c_stride_t, k_pe, k_pe_stride_t, slot_mapping, T_new,
+                                             kv_cache, kv_dtype, num_pages);
+  if (cst != MLA_OK) return cst;
+  const int64_t row_wgs = (T_new + 3) / 4;               // four tokens per workgroup
+  const int64_t row_lines = (row_wgs + 3) / 4;           // four workgroups per grid row
+  if ((int64_t)N + row_lines > 65535) return MLA_ERR_SHAPE;
+  DeviceInfo di;
+  mla_status_t st = device_info(&di);
+  if (st != MLA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const CacheRowsArgs cw{(const uint16_t*)kv_c, kv_c_stride_t, (const uint16_t*)k_pe, k_pe_stride_t,
+                         slot_mapping, T_new, (char*)kv_cache, num_pages, N};
+  dim3 grid(MLA_KV_LORA_RANK / 128, (unsigned)(N + row_lines));
+  auto go = [&](auto pe_c, auto cw_c) {
+    constexpr int PE = decltype(pe_c)::value, CW = decltype(cw_c)::value;
+    hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, PE, CW>), grid, dim3(256), 0, s,
+                       (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
+                       (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)q_pe, qp_stride_t,
+                       qp_stride_h, (const int64_t*)nullptr, (const float*)nullptr, (int64_t)0, 0, T, cw);
+  };
+  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  if (q_pe) {
+    if (fp8) go(std::integral_constant<int, kCopyTail>{}, std::integral_constant<int, kRowsFp8>{});
+    else go(std::integral_constant<int, kCopyTail>{}, std::integral_constant<int, kRowsBf16>{});
+  } else {
+    if (fp8) go(std::integral_constant<int, kNoTail>{}, std::integral_constant<int, kRowsFp8>{});
+    else go(std::integral_constant<int, kNoTail>{}, std::integral_constant<int, kRowsBf16>{});
+  }
   return launch_status();
 }
 
@@ -849,7 +924,7 @@ extern "C" mla_status_t mla_absorb_q_rope(const void* q_nope, int64_t qn_stride_
   hipLaunchKernelGGL((head_gemm_kernel<128, 512, 128, 1, kRopeTail>), grid, dim3(256), 0, s,
                      (const uint16_t*)q_nope, qn_stride_t, qn_stride_h, (const uint16_t*)w_uk_t,
                      (uint16_t*)q_fused, qf_stride_t, qf_stride_h, (const uint16_t*)q_pe, qp_stride_t,
-                     qp_stride_h, positions, cos_sin_cache, max_pos, neox ? 1 : 0, T);
+                     qp_stride_h, positions, cos_sin_cache, max_pos, neox ? 1 : 0, T, CacheRowsArgs{});
   return launch_status();
 }
 
@@ -881,7 +956,7 @@ extern "C" mla_status_t mla_up_v(const void* o_lat, int64_t ol_stride_t, int64_t
                      (const uint16_t*)o_lat, ol_stride_t, ol_stride_h, (const uint16_t*)w_uv,
                      (uint16_t*)out, out_stride_t, (int64_t)MLA_V_HEAD_DIM,
                      (const uint16_t*)nullptr, (int64_t)0, (int64_t)0, (const int64_t*)nullptr,
-                     (const float*)nullptr, (int64_t)0, 0, T);
+                     (const float*)nullptr, (int64_t)0, 0, T, CacheRowsArgs{});
   return launch_status();
 }
 
@@ -948,6 +1023,7 @@ extern "C" mla_status_t mla_kv_b_proj(const void* kv_c, int64_t kc_stride_t, con
   hipLaunchKernelGGL((head_gemm_kernel<512, 256, 64, 2, kNoTail>), dim3(256 / 64, N), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), (const uint16_t*)kv_c, kc_stride_t, (int64_t)0,
                      (const uint16_t*)w_kvb, (uint16_t*)out, out_stride_t, out_stride_h, (const uint16_t*)nullptr,
-                     (int64_t)0, (int64_t)0, (const int64_t*)nullptr, (const float*)nullptr, (int64_t)0, 0, S);
+                     (int64_t)0, (int64_t)0, (const int64_t*)nullptr, (const float*)nullptr, (int64_t)0, 0, S,
+                     CacheRowsArgs{});
   return launch_status();
 }

@@ -125,3 +125,36 @@ def test_up_v(T, N):
     ref = O.up_v(a, ww)
     g = O.bf16_bits_to_f64(host_bits(got)).reshape(T, N, 128)
     assert np.all(np.abs(g - ref) <= _gemm_bound(a, ww, ref))
+
+
+@pytest.mark.parametrize("kd", [MI.KV_BF16, MI.KV_FP8])
+@pytest.mark.parametrize("T,N,T_new,with_pe", [(32, 128, 32, True), (3, 16, 70, False), (1, 128, 5, True),
+                                               (0, 16, 9, True)])
+def test_absorb_q_cache_write_equals_the_two_calls(kd, T, N, T_new, with_pe):
+    """The single launch writes exactly what mla_absorb_q and mla_cache_write write:
+    q_fused and the whole pool (guard pages included) compared byte for byte, with
+    padding and out-of-range slots among the new rows."""
+    say(f"absorb_q_cache_write kd={kd} T={T} N={N} T_new={T_new} pe={with_pe}")
+    rng = np.random.default_rng(90 + 7 * kd + T + N)
+    pages = 8
+    rb = M.ROW_BYTES[kd]
+    q_nope = dev_bf16(MI.to_bf16_bits(rng.standard_normal((T, N, 128)).astype(np.float32)))
+    q_pe = dev_bf16(MI.to_bf16_bits(rng.standard_normal((T, N, 64)).astype(np.float32))) if with_pe else None
+    w = dev_bf16(MI.to_bf16_bits((rng.standard_normal((N, 128, 512)) / 22.6).astype(np.float32)))
+    rows = dev_bf16(MI.to_bf16_bits(rng.standard_normal((T_new, 576)).astype(np.float32)))
+    slots = rng.permutation(pages * 64)[:T_new].astype(np.int64)
+    slots[::4] = -1
+    if T_new > 2:
+        slots[2] = pages * 64 + 5                         # out of range: skipped
+    slots_d = torch.from_numpy(slots).cuda()
+    guard = torch.from_numpy(rng.integers(0, 256, size=(pages + 2, 64, rb), dtype=np.uint8)).cuda()
+    buf_a, buf_b = guard.clone(), guard.clone()
+    width = 576 if with_pe else 512
+    qf_a = torch.full((T, N, width), 7.0, dtype=torch.bfloat16, device="cuda")
+    qf_b = qf_a.clone()
+    M.absorb_q(q_nope, q_pe, w, q_fused=qf_a)
+    M.cache_write(rows[:, :512], rows[:, 512:], slots_d, buf_a[1:-1], kd)
+    M.absorb_q_cache_write(q_nope, q_pe, w, rows[:, :512], rows[:, 512:], slots_d, buf_b[1:-1], kd, q_fused=qf_b)
+    torch.cuda.synchronize()
+    assert torch.equal(qf_a.view(torch.int16), qf_b.view(torch.int16))
+    assert torch.equal(buf_a, buf_b)
