@@ -202,10 +202,8 @@ size_t mla_decode_workspace_size(int32_t B, int32_t q_len, int32_t N, int32_t nu
  *                request split into up to k page-aligned pieces (k <= 4096)
  *   workspace    device scratch of at least mla_decode_workspace_size() bytes,
  *                256-byte aligned; its contents need no initialisation.  It
- *                holds the split table and the split partials: per partial
- *                row a float32 LSE, four float32 scales and 512 fp16 values
- *                (each 128-value segment divided by its scale, its largest
- *                magnitude; the fp16 rounding errs by at most 2^-12 of it)
+ *                holds the split table and the split partials (per partial row
+ *                a float32 LSE and 512 float32 values)
  *   out          bf16 [B, q_len, N, 512], strides (o_stride_b, o_stride_t,
  *                o_stride_h); last dim contiguous
  *   lse          float32 [B, q_len, N] contiguous: natural-log log-sum-exp of

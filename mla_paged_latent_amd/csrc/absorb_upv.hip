@@ -76,7 +76,8 @@ __device__ __forceinline__ void rope_chunks(const uint4& xa, const uint4& xb, co
 }
 
 // Cache rows written beside the absorption in the same launch (mla_absorb_q_cache_write):
-// the workgroups past the heads' rows of the grid write four tokens each.
+// the first grid rows' workgroups write four tokens each and the heads follow, so the
+// row writes are dispatched first and end inside the absorption's time.
 struct CacheRowsArgs {
   const uint16_t* kv_c;
   int64_t kv_stride;
@@ -86,7 +87,7 @@ struct CacheRowsArgs {
   int64_t T;
   char* pool;
   int64_t num_pages;
-  int32_t n_heads;     // grid rows below this one are heads
+  int32_t row_lines;   // grid rows [0, row_lines) write cache rows, the heads follow
 };
 constexpr int kNoRows = 0, kRowsBf16 = 1, kRowsFp8 = 2;
 
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
   if constexpr (CW != kNoRows) {
-    if ((int)blockIdx.y >= cw.n_heads) {
-      const int64_t t = ((int64_t)(blockIdx.y - cw.n_heads) * gridDim.x + blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if ((int)blockIdx.y < cw.row_lines) {
+      const int64_t t = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + (threadIdx.x >> 6);
       if (t < cw.T)
         cache_write_row<CW == kRowsFp8>(cw.kv_c, cw.kv_stride, cw.k_pe, cw.pe_stride, cw.slots, cw.pool,
                                         cw.num_pages, t, lane_id());
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(
     }
   }
 
-  const int h = blockIdx.y;
+  const int h = (int)blockIdx.y - (CW != kNoRows ? cw.row_lines : 0);
   const int n0 = blockIdx.x * NT;
   const int tid = threadIdx.x;
   const int w = wave_id();
@@ -851,9 +852,9 @@ extern "C" mla_status_t mla_absorb_q(const void* q_nope, int64_t qn_stride_t, in
   return launch_status();
 }
 
-// mla_absorb_q and mla_cache_write in one launch: the cache-row workgroups follow the
-// heads' rows of the absorption grid (four tokens each), so the step's two smallest
-// kernels cost one launch.  The arguments and checks are those of the two calls.
+// mla_absorb_q and mla_cache_write in one launch: the cache-row workgroups (four tokens
+// each) take the first rows of the absorption grid, so the step's two smallest kernels
+// cost one launch.  The arguments and checks are those of the two calls.
 extern "C" mla_status_t mla_absorb_q_cache_write(const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
                                                  const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
                                                  const void* w_uk_t, int64_t T, int32_t N, void* q_fused,
@@ -881,7 +882,7 @@ extern "C" mla_status_t mla_absorb_q_cache_write(const void* q_nope, int64_t qn_
   if (st != MLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const CacheRowsArgs cw{(const uint16_t*)kv_c, kv_c_stride_t, (const uint16_t*)k_pe, k_pe_stride_t,
-                         slot_mapping, T_new, (char*)kv_cache, num_pages, N};
+                         slot_mapping, T_new, (char*)kv_cache, num_pages, (int32_t)row_lines};
   dim3 grid(MLA_KV_LORA_RANK / 128, (unsigned)(N + row_lines));
   auto go = [&](auto pe_c, auto cw_c) {
     constexpr int PE = decltype(pe_c)::value, CW = decltype(cw_c)::value;

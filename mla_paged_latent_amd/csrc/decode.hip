@@ -57,8 +57,7 @@ struct DecodeParams {
   // workspace views
   int4* req;           // per request: {first partial slot, pieces, 0, clamped seq_len}
   float* part_lse;     // [slots * n_hg * m_wg]
-  uint16_t* part_o;    // [slots * n_hg * m_wg * 512] fp16, each 128-feature segment divided by its scale
-  float* part_sc;      // [slots * n_hg * m_wg * 4]: max |o| of each 128-feature segment of a partial row
+  float* part_o;       // [slots * n_hg * m_wg * 512]
   int32_t num_splits;  // 0 automatic, k >= 1 forced
   int32_t n_streams;   // streams of the plan
   int32_t n_units;     // n_streams x head groups, rounded for the sibling order
@@ -924,23 +923,9 @@ __global__ __launch_bounds__(256, 1) void decode_narrow_kernel(DecodeParams p) {
             *reinterpret_cast<bf16x4_t*>(orow + 16 * f) = v;
           }
         } else {
-          // fp16 partial: the segment of features 128w .. +127 (the 4 lane groups of row
-          // l16) divided by its largest magnitude, which is stored beside it
-          float a = 0.f;
+          float* prow = p.part_o + (slot * kNRows + l16) * kLatent + 128 * w + 4 * g4;
 #pragma unroll
-          for (int f = 0; f < 8; ++f)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(o[f][i]));
-          a = max_xor32(max_xor16(a));
-          const float mul = a > 0.f ? 1.0f / a : 0.f;
-          uint16_t* prow = p.part_o + (slot * kNRows + l16) * kLatent + 128 * w + 4 * g4;
-#pragma unroll
-          for (int f = 0; f < 8; ++f) {
-            const f16x4_t v = {(_Float16)(o[f][0] * mul), (_Float16)(o[f][1] * mul), (_Float16)(o[f][2] * mul),
-                               (_Float16)(o[f][3] * mul)};
-            *reinterpret_cast<f16x4_t*>(prow + 16 * f) = v;
-          }
-          if (g4 == 0) p.part_sc[(slot * kNRows + l16) * 4 + w] = a * inv;
+          for (int f = 0; f < 8; ++f) *reinterpret_cast<f32x4_t*>(prow + 16 * f) = o[f] * inv;
         }
       }
       lds_barrier();                             // stats and P free for the next piece
@@ -1726,25 +1711,6 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
         // segments (256 B fp32, 128 B bf16 per row and wave).
         MLA_LDS char* stage = smem + (FP8 ? 0 : ((g0 + nblk + 3) & (kRing - 1)) * kSlot) + v * kWStageBytes;
         const int c32 = le & 31, h32 = le >> 5;
-        // split partials: each row's 128 features of this wave (lanes c32 and c32 + 32)
-        // are stored in fp16 divided by their largest magnitude, which goes beside them
-        float mul[2] = {0.f, 0.f};
-        if (!single) {
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            float a = 0.f;
-#pragma unroll
-            for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(o[fb][rb][i]));
-            a = max_xor32(a);
-            mul[rb] = a > 0.f ? 1.0f / a : 0.f;
-            const int R = 32 * rb + c32;
-            const float lr_row = stats[R][2] + stats[kWRows + R][2];
-            const float inv = lr_row > 0.f ? 1.0f / lr_row : 0.f;
-            if (h32 == 0) p.part_sc[(slot * p.m_wg + R) * 4 + v] = a * inv;
-          }
-        }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int R = 32 * rb + c32;
@@ -1782,30 +1748,30 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
                 }
               }
             } else {
-              // fp16 partial, each wave's 128 features of the row divided by their largest
-              // magnitude (mul = 1 / that, from the lane pair holding the row)
 #pragma unroll
               for (int fl = 0; fl < 2; ++fl)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                   const int fb = 2 * fh + fl;
-                  const f16x4_t vv = {(_Float16)(o[fb][rb][4 * i] * mul[rb]), (_Float16)(o[fb][rb][4 * i + 1] * mul[rb]),
-                                      (_Float16)(o[fb][rb][4 * i + 2] * mul[rb]),
-                                      (_Float16)(o[fb][rb][4 * i + 3] * mul[rb])};
-                  *reinterpret_cast<MLA_LDS f16x4_t*>(stage + c32 * kWStagePitch16 + (32 * fl + 8 * i + 4 * h32) * 2) =
+                  const f32x4_t vv = {o[fb][rb][4 * i] * inv, o[fb][rb][4 * i + 1] * inv, o[fb][rb][4 * i + 2] * inv,
+                                      o[fb][rb][4 * i + 3] * inv};
+                  *reinterpret_cast<MLA_LDS f32x4_t*>(stage + c32 * kWStagePitch32 + (32 * fl + 8 * i + 4 * h32) * 4) =
                       vv;
                 }
               asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-              u32x4_t vr[4];
 #pragma unroll
-              for (int k = 0; k < 4; ++k)
-                vr[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (8 * k + (le >> 3)) * kWStagePitch16 +
-                                                                  (le & 7) * 16);
+              for (int kb = 0; kb < 2; ++kb) {
+                u32x4_t vr[4];
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                uint16_t* prow = p.part_o + (slot * p.m_wg + 32 * rb + 8 * k + (le >> 3)) * kLatent + 128 * v +
-                                 64 * fh + 8 * (le & 7);
-                *reinterpret_cast<u32x4_t*>(prow) = vr[k];
+                for (int k = 0; k < 4; ++k)
+                  vr[k] = *reinterpret_cast<const MLA_LDS u32x4_t*>(stage + (4 * (4 * kb + k) + (le >> 4)) * kWStagePitch32 +
+                                                                    (le & 15) * 16);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  float* prow = p.part_o + (slot * p.m_wg + 32 * rb + 4 * (4 * kb + k) + (le >> 4)) * kLatent + 128 * v +
+                                64 * fh + 4 * (le & 15);
+                  *reinterpret_cast<u32x4_t*>(prow) = vr[k];
+                }
               }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done before reuse
@@ -1878,21 +1844,16 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   auto fold = [&](auto ks_c) {
     constexpr int KS = decltype(ks_c)::value;
     for (int s0 = 0; s0 < nsplit; s0 += KS) {
-      f16x8_t h[KS];
-      float sc[KS], ls[KS];
+      f32x4_t v[KS][2];
+      float ls[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
         const int s = s0 + k < nsplit ? s0 + k : nsplit - 1;        // clamp: in bounds, weight 0 below
         const size_t slot = (size_t)(first + s) * p.n_hg + hg;
-        h[k] = *reinterpret_cast<const f16x8_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
-        sc[k] = p.part_sc[(slot * p.m_wg + r) * 4 + (l >> 4)];
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + (slot * p.m_wg + r) * kLatent + 8 * l);
+        v[k][0] = src[0];
+        v[k][1] = src[1];
         ls[k] = s0 + k < nsplit ? p.part_lse[slot * p.m_wg + r] : -INFINITY;
-      }
-      f32x4_t v[KS][2];
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        v[k][0] = f32x4_t{(float)h[k][0], (float)h[k][1], (float)h[k][2], (float)h[k][3]} * sc[k];
-        v[k][1] = f32x4_t{(float)h[k][4], (float)h[k][5], (float)h[k][6], (float)h[k][7]} * sc[k];
       }
       float mc = M;
 #pragma unroll
@@ -1949,7 +1910,7 @@ inline bool decode_shape(int32_t B, int32_t q_len, int32_t N, int32_t num_splits
 }
 
 struct WsLayout {
-  size_t req, part_lse, part_sc, part_o, total;
+  size_t req, part_lse, part_o, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1962,10 +1923,8 @@ inline WsLayout ws_layout(int32_t B, const Shape& s) {
   const size_t rows = (size_t)s.max_slots * s.n_hg * s.m_wg;
   w.part_lse = off;
   off = align256(off + rows * sizeof(float));
-  w.part_sc = off;
-  off = align256(off + rows * 4 * sizeof(float));
   w.part_o = off;
-  off = align256(off + rows * kLatent * sizeof(uint16_t));
+  off = align256(off + rows * kLatent * sizeof(float));
   w.total = off;
   return w;
 }
@@ -2094,8 +2053,7 @@ inline DecodeParams decode_params(const void* q, int64_t q_stride_b, int64_t q_s
   p.lse = lse;
   p.req = reinterpret_cast<int4*>(ws + wl.req);
   p.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
-  p.part_sc = reinterpret_cast<float*>(ws + wl.part_sc);
-  p.part_o = reinterpret_cast<uint16_t*>(ws + wl.part_o);
+  p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   p.num_splits = num_splits;
   p.max_slots = max_slots;
   return p;
@@ -2174,10 +2132,8 @@ inline WsLayout ws_layout_exact(int32_t B, const Shape& s, int32_t num_splits, i
   const size_t rows = (size_t)slots * s.n_hg * s.m_wg;
   w.part_lse = off;
   off = align256(off + rows * sizeof(float));
-  w.part_sc = off;
-  off = align256(off + rows * 4 * sizeof(float));
   w.part_o = off;
-  off = align256(off + rows * kLatent * sizeof(uint16_t));
+  off = align256(off + rows * kLatent * sizeof(float));
   w.total = off;
   return w;
 }
@@ -2347,8 +2303,7 @@ extern "C" mla_status_t mla_decode_varlen(const void* q, int64_t q_stride_t, int
   p.lse = lse;
   p.req = reinterpret_cast<int4*>(ws + wl.req);
   p.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
-  p.part_sc = reinterpret_cast<float*>(ws + wl.part_sc);
-  p.part_o = reinterpret_cast<uint16_t*>(ws + wl.part_o);
+  p.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   p.num_splits = num_splits;
   p.max_slots = s.max_slots;
   return decode_launch(p, s, kv_dtype, num_splits, (int32_t)T, max_pages_per_seq, di, hs);

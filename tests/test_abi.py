@@ -82,16 +82,14 @@ def test_workspace_size_arithmetic():
     # invalid shapes give 0
     assert ws(0, 1, 16, 0) == 0 and ws(4, 3, 16, 0) == 0 and ws(4, 1, 0, 0) == 0
     assert ws(4, 1, 129, 0) == 0 and ws(4, 1, 16, -1) == 0 and ws(4, 1, 16, 5000) == 0
-    # partials dominate: pairs x head groups x rows x (512 fp16 values, 4 float32
-    # segment scales and a float32 LSE) = 1044 bytes per partial row
-    per_row = 512 * 2 + 4 * 4 + 4
+    # partials dominate: pairs x head groups x rows x (512 + 1) floats
     one = ws(32, 1, 128, 1)
-    assert one >= (32 + 8) * 1 * 128 * per_row
+    assert one >= (32 + 8) * 1 * 128 * 513 * 4
     assert ws(32, 1, 128, 8) > one
-    assert ws(32, 1, 128, 0) >= (32 + 1024 + 8) * 128 * per_row
+    assert ws(32, 1, 128, 0) >= (32 + 1024 + 8) * 128 * 513 * 4
     # q_len 2 with 128 heads needs two head groups of 128 rows
-    assert ws(8, 2, 128, 1) >= (8 + 8) * 2 * 128 * per_row
-    assert ws(64, 1, 16, 1) >= (64 + 8) * 16 * per_row
+    assert ws(8, 2, 128, 1) >= (8 + 8) * 2 * 128 * 513 * 4
+    assert ws(64, 1, 16, 1) >= (64 + 8) * 16 * 513 * 4
     assert ws(64, 1, 16, 1) % 256 == 0
 
 
