@@ -135,6 +135,19 @@ def test_other_calls_reject_bad_arguments():
     assert L.mla_absorb_q(p, 128, 128, None, 0, 0, p, 0, 16, p, 576, 576, None) == 0
     assert L.mla_absorb_q(None, 128, 128, None, 0, 0, p, 4, 16, p, 576, 576, None) == 1
     assert L.mla_absorb_q(p, 130, 128, None, 0, 0, p, 4, 16, p, 576, 576, None) == 4
+    # absorb + cache write in one launch: the statuses of the two calls
+    def acw(**o):
+        a = dict(qn=p, qns=128, qnh=128, qp=p, qps=64, qph=64, w=p, T=4, N=16, qf=p, qfs=576, qfh=576,
+                 kc=p, kcs=512, kp=p, kps=64, sl=p, Tn=4, pool=p, kd=0, pages=4, stream=None)
+        a.update(o)
+        return L.mla_absorb_q_cache_write(*a.values())
+    assert acw(N=0) == 2 and acw(N=129) == 2 and acw(T=-1) == 2
+    assert acw(qn=None) == 1 and acw(kc=None) == 1 and acw(sl=None) == 1
+    assert acw(kd=9) == 3                                                  # MLA_ERR_DTYPE
+    assert acw(kcs=500) == 2                                               # latent row stride < 512
+    assert acw(qns=130) == 4 and acw(qp=vp(264)) == 4 and acw(sl=vp(260)) == 4
+    assert acw(T=0, Tn=0) == 0                                             # nothing to do
+    assert acw(T=0, Tn=4, kd=9) == 3                                       # T == 0: the cache write's checks
     # up_v
     assert L.mla_up_v(p, 512, 512, p, 4, 129, p, 128 * 129, None) == 2
     assert L.mla_up_v(p, 512, 512, p, 4, 16, p, 1024, None) == 2           # out row too short
