@@ -1251,6 +1251,69 @@ struct SpreadCopy {
   __device__ __forceinline__ void end() const { copy_part<FP8, kB, kN>(c, on, voff, v, l); }
 };
 
+// ---- a unit's first query through LDS ----
+// At a unit's first piece the 64 query rows (73,728 B) are copied once into LDS by all
+// eight waves and both token-half score waves of a row group read them from there, so
+// the start-up burst carries each query byte once instead of twice.  Row R sits at
+// R * 1152 with its 16-byte chunk c at position c ^ qswz(R) (the 8 lanes that a
+// ds_read_b128 serves together then hit 8 distinct bank groups).  Region: ring slots 2
+// and 3 for bf16 rows (block 2 is issued once the query has been read), the unused
+// converted slots for fp8 rows.
+constexpr int kQRowBytes = kRow * 2;                   // 1152
+constexpr int kQLdsBytes = kWRows * kQRowBytes;        // 73728
+static_assert(kQLdsBytes <= 2 * kSlot && 2 * kSlot + kQLdsBytes <= kStageEnd, "query staging LDS plan");
+
+__device__ __forceinline__ int qswz(int R) { return (((R >> 2) & 1) << 2) | ((R >> 3) & 1); }
+
+// the query rows' byte offsets from request b's query fit 32 bits (uniform)
+__device__ __forceinline__ bool query_lds_fits(const DecodeParams& p) {
+  const int64_t hi = ((int64_t)(p.q_len - 1) * p.q_st + (int64_t)(p.N - 1) * p.q_sh) * 2 + kQRowBytes;
+  return p.q_st >= 0 && p.q_sh >= 0 && hi < (int64_t)0x7fffffff;
+}
+
+template <int I>
+__device__ __forceinline__ void query_dma_one(const DecodeParams& p, const uint16_t* base, int hg, uint32_t lds, int w,
+                                              int l) {
+  const int e = 64 * (w + 8 * I) + l;                  // LDS chunk of this lane
+  const int R = e / 72;
+  const int col = (e - 72 * R) ^ qswz(R);
+  const int hl = R / p.q_len, tq = R - hl * p.q_len;
+  int head = hg * p.hg_heads + hl;
+  head = head < p.N ? head : 0;                        // padding rows: head 0 (never stored)
+  const uint32_t voff = (uint32_t)(((int64_t)tq * p.q_st + (int64_t)head * p.q_sh) * 2 + col * 16);
+  dma_16B<0, 8192 * I>(base, voff, lds);
+}
+
+template <int... I>
+__device__ __forceinline__ void query_dma_seq(std::integer_sequence<int, I...>, const DecodeParams& p,
+                                              const uint16_t* base, int hg, uint32_t lds, int w, int l) {
+  (query_dma_one<I>(p, base, hg, lds, w, l), ...);
+}
+
+// The same copy through registers, for query strides whose row offsets need 64 bits
+__device__ __forceinline__ void stage_query_lds_wide_strides(const DecodeParams& p, int b, int hg, MLA_LDS char* qs,
+                                                             int w, int l) {
+#pragma unroll 1
+  for (int i = 0; i < 9; ++i) {
+    const int e = 64 * (w + 8 * i) + l;
+    const int R = e / 72;
+    const int col = (e - 72 * R) ^ qswz(R);
+    const int hl = R / p.q_len, tq = R - hl * p.q_len;
+    int head = hg * p.hg_heads + hl;
+    head = head < p.N ? head : 0;
+    const uint16_t* src = p.q + (int64_t)b * p.q_sb + (int64_t)tq * p.q_st + (int64_t)head * p.q_sh + 8 * col;
+    *reinterpret_cast<MLA_LDS u32x4_t*>(qs + 16 * e) = *reinterpret_cast<const u32x4_t*>(src);
+  }
+}
+
+// wave w's share (9 instructions) of the copy of request b's 64 query rows of head group hg
+__device__ __forceinline__ void stage_query_lds(const DecodeParams& p, int b, int hg, MLA_LDS char* qs, int w, int l) {
+  b = __builtin_amdgcn_readfirstlane(b);
+  hg = __builtin_amdgcn_readfirstlane(hg);
+  const uint16_t* base = p.q + (int64_t)b * p.q_sb;
+  query_dma_seq(std::make_integer_sequence<int, 9>{}, p, base, hg, lds_addr(qs) + 1024u * (uint32_t)w, w, l);
+}
+
 // The role that issues the block copies (and waits for them before each hand-over).
 constexpr bool kCopyByScore = false;
 // Blocks of the stream issued ahead of the one being computed (at most kRing - 1).
@@ -1407,9 +1470,46 @@ __device__ __forceinline__ void wide_role(const DecodeParams& p, MLA_LDS char* s
       };
       // the piece's first three blocks: in flight already (issued while the previous
       // piece finished) or issued here
-      for (int k = 0; k < kWDepth && issued < g0 + kWDepth; ++k) issue_next();
-      if constexpr (QK) {
-        if (!q_ready) load_q(b);
+      if (issued == 0 && p.q_len == 1) {
+        // the unit's first piece with one query row per head: block 0, the query (once,
+        // into LDS), block 1 (fp8: and block 2); the copying waves' wait leaves only the
+        // later blocks in flight.  (With two query rows per head the staging measured no
+        // faster than loading the query twice, so those batches keep the direct loads.)
+        MLA_LDS char* qs = smem + (FP8 ? 0 : 2 * kSlot);
+        // lane-dependent addresses from an opaque lane id: hoisted out of the unit loop
+        // they would stay live across it
+        const int lq = (int)opaque((uint32_t)l);
+        issue_next();
+        const int before_q = issued;             // blocks issued before the query copy
+        if (query_lds_fits(p)) stage_query_lds(p, b, hg, qs, w, lq);
+        else stage_query_lds_wide_strides(p, b, hg, qs, w, lq);
+        issue_next();
+        if constexpr (FP8) issue_next();
+        // (a short piece has fewer blocks: only those issued after the query may stay out)
+        if constexpr (COPY) wait_query_and_block0<FP8>(issued - before_q, v);
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if constexpr (QK) {
+          // chunk (4kk + g4) ^ qswz(R) = 4 (kk ^ s2) + (g4 ^ s01), s2 / s01: bit 2 / bits 0-1 of
+          // qswz(R); R and R + 16 share qswz, so one base per parity of kk serves both rows
+          const int R = 32 * rg + (lq & 15);
+          const int sw = qswz(R);
+          const uint32_t a0 = lds_addr(qs) + (uint32_t)(R * kQRowBytes + 16 * ((lq >> 4) ^ (sw & 3)));
+          const uint32_t ae = opaque(a0 + 64u * (uint32_t)(sw >> 2));   // even kk
+          const uint32_t ao = opaque(a0 - 64u * (uint32_t)(sw >> 2));   // odd kk
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+            for (int kk = 0; kk < 18; ++kk)
+              qf[rs][kk] = lds_read_b128_at(((kk & 1) ? ao : ae) + (uint32_t)(rs * 16 * kQRowBytes + 64 * kk));
+        }
+        lds_barrier();                           // the query region is free again
+        if constexpr (!FP8) issue_next();        // block 2, into ring slot 2
+      } else {
+        for (int k = 0; k < kWDepth && issued < g0 + kWDepth; ++k) issue_next();
+        if constexpr (QK) {
+          if (!q_ready) load_q(b);
+        }
       }
       fetch_nxt();
       if constexpr (COPY) {

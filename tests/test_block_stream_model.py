@@ -15,7 +15,10 @@ redo of a piece) and checks, with barriers as the only ordering between waves:
   * a block's tail is zeroed after its copy landed and before any read of it;
   * the epilogue's staging slot holds no copy in flight and no block still to be read.
 The plans come from the split-plan model, so the cases include streams with empty pieces
-and pieces of one block, which exercise the cross-piece prefetch.
+and pieces of one block, which exercise the cross-piece prefetch.  With `query_lds` (bf16
+rows, one query row per head) a unit's first piece also copies its query into ring slots 2
+and 3: block 0, the query, block 1, the wait, a barrier, the query reads, a barrier, and
+only then block 2, which must not be copied over the query before it was read.
 """
 
 from __future__ import annotations
@@ -28,10 +31,11 @@ import test_split_plan_model as plan
 RING = 4
 DEPTH = 3            # blocks issued ahead of the one being computed
 BLK = 32
+QUERY_SLOTS = (2, 3)  # where a unit's first query is staged (bf16 rows)
 
 
 class Stream:
-    def __init__(self, pieces, redo_pieces=(), guard_empty=True):
+    def __init__(self, pieces, redo_pieces=(), guard_empty=True, query_lds=False):
         self.pieces = [max(0, -(-(t1 - t0) // BLK)) if t1 > t0 else 0 for (t0, t1) in pieces]
         self.redo = set(redo_pieces)
         self.guard_empty = guard_empty
@@ -44,6 +48,9 @@ class Stream:
         self.zero_at = {}                 # block -> interval of its tail zeroing
         self.stage = []                   # (interval, slot) of epilogue staging
         self.slot_hist = {s: [] for s in range(RING)}
+        self.query_lds = query_lds
+        self.query_reads = []             # intervals in which the staged query was read
+        self.query_copied_at = None
 
     # ---- events ----
     def barrier(self):
@@ -59,6 +66,9 @@ class Stream:
         for (e, ss) in self.stage:
             if ss == s:
                 assert e < self.bar, f"copy of block {x} into slot {s} during epilogue staging"
+        if s in QUERY_SLOTS and self.query_copied_at is not None:
+            assert self.query_reads and all(e < self.bar for e in self.query_reads), \
+                f"copy of block {x} into slot {s} before the staged query was read"
         self.slot_hist[s].append(x)
         self.issue_at[x] = self.bar
 
@@ -112,10 +122,23 @@ class Stream:
 
         while True:
             nblk = P[cur]
-            for _ in range(DEPTH):
-                if self.issued >= g0 + DEPTH:
-                    break
-                next_copy()
+            if self.query_lds and self.issued == 0:
+                next_copy()                         # block 0
+                for s in QUERY_SLOTS:               # the query copy: nothing of the ring there
+                    assert not self.slot_hist[s], "query staged over a ring block"
+                self.query_copied_at = self.bar
+                before_q = self.issued
+                next_copy()                         # block 1
+                self.land_upto(before_q)            # the query and block 0 have landed
+                self.barrier()
+                self.query_reads.append(self.bar)   # score waves read their query
+                self.barrier()
+                next_copy()                         # block 2, into the query's slot
+            else:
+                for _ in range(DEPTH):
+                    if self.issued >= g0 + DEPTH:
+                        break
+                    next_copy()
             nxt = cur + 1 if cur + 1 < len(P) else None
             nxt_known = True
             if (nblk > 0 or not self.guard_empty) and self.landed <= g0:
@@ -194,10 +217,23 @@ def _cases():
     return out
 
 
+@pytest.mark.parametrize("query_lds", [False, True], ids=["query in registers", "query staged in LDS"])
 @pytest.mark.parametrize("name,seq,n_streams", _cases(), ids=[c[0] for c in _cases()])
-def test_block_stream_orders_copies_waits_and_reads(name, seq, n_streams):
+def test_block_stream_orders_copies_waits_and_reads(name, seq, n_streams, query_lds):
     for s, pcs in stream_pieces(seq, n_streams).items():
-        Stream(pcs).run()
+        Stream(pcs, query_lds=query_lds).run()
+
+
+def test_model_catches_block_2_copied_over_the_unread_query():
+    """Issuing block 2 before the barrier that follows the query reads would copy it over
+    the staged query: the model must reject that order."""
+    st = Stream([(0, 9 * BLK)], query_lds=True)
+    st.query_copied_at = 0
+    st.query_reads.append(1)
+    st.issue(0)
+    st.bar = 1                                   # still the interval of the query reads
+    with pytest.raises(AssertionError):
+        st.issue(2)
 
 
 def test_block_stream_with_redone_pieces():
@@ -206,6 +242,7 @@ def test_block_stream_with_redone_pieces():
     for s, pcs in stream_pieces(seq, 64).items():
         redo = [i for i in range(len(pcs)) if rng.random() < 0.3]
         Stream(pcs, redo_pieces=redo).run()
+        Stream(pcs, redo_pieces=redo, query_lds=True).run()
 
 
 def test_model_catches_an_empty_piece_claiming_the_next_block():
